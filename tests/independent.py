@@ -1,0 +1,69 @@
+"""Implementations that share no code with the oracle, used only to pin it.
+
+* ``textbook_sinkhorn``: multiplicative Sinkhorn-Knopp matrix scaling on a dense
+  matrix (a = 1 / (A b), b = 1 / (A^T a)), no log domain, no band storage.
+* ``dense_autograd``: the stopped-base tail surrogate written with dense [L, L]
+  torch float64 tensors and differentiated by torch autograd on the CPU
+  ("exact autodiff through the surrogate", the pages' validation baseline).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+
+def dense_scores(Q, K, W, eps):
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    L, d = Q.shape
+    S = Q @ K.T / (math.sqrt(d) * eps)
+    i = np.arange(L)
+    mask = np.abs(i[:, None] - i[None, :]) <= W // 2
+    return S, mask
+
+
+def textbook_sinkhorn(A: np.ndarray, steps: int):
+    """Sinkhorn-Knopp scaling of a nonnegative matrix to unit row and column sums.
+    Starts from b = 1; each step sets a = 1/(A b) then b = 1/(A^T a).
+    Returns (a, b) after `steps` steps (a = None when steps == 0)."""
+    b = np.ones(A.shape[1])
+    a = None
+    for _ in range(steps):
+        a = 1.0 / (A @ b)
+        b = 1.0 / (A.T @ a)
+    return a, b
+
+
+def dense_autograd(Q, K, V, dO, W, T, R, eps):
+    """Dense-matrix surrogate: stopped T-step base, R-step tail, O = P^(R,R) V.
+    Returns (O, dQ, dK, dV, duals) with duals = [v0, u1, v1, ..., uR, vR]."""
+    Qt = torch.tensor(np.asarray(Q, np.float64), requires_grad=True)
+    Kt = torch.tensor(np.asarray(K, np.float64), requires_grad=True)
+    Vt = torch.tensor(np.asarray(V, np.float64), requires_grad=True)
+    dOt = torch.tensor(np.asarray(dO, np.float64))
+    L, d = Qt.shape
+    idx = torch.arange(L)
+    mask = (idx[:, None] - idx[None, :]).abs() <= W // 2
+    S = (Qt @ Kt.T) / (math.sqrt(d) * eps)
+    S = S.masked_fill(~mask, float("-inf"))
+    with torch.no_grad():
+        u = torch.zeros(L, dtype=torch.float64)
+        v = torch.zeros(L, dtype=torch.float64)
+        Sd = S.detach()
+        for _ in range(T):
+            u = -torch.logsumexp(Sd + v[None, :], dim=1)
+            v = -torch.logsumexp(Sd + u[:, None], dim=0)
+    v = v.detach()
+    duals = [v]
+    for _ in range(R):
+        u = -torch.logsumexp(S + v[None, :], dim=1)
+        v = -torch.logsumexp(S + u[:, None], dim=0)
+        duals += [u, v]
+    P = torch.exp(S + u[:, None] + v[None, :])
+    O = P @ Vt
+    (O * dOt).sum().backward()
+    return (O.detach().numpy(), Qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy(),
+            np.stack([x.detach().numpy() for x in duals]))

@@ -1,0 +1,53 @@
+"""The pins in test_oracle.py must fail for plausible mistakes in the oracle.
+
+Each case plants one mistake (an update order swapped, a dropped modifier term, a
+flipped sign, a wrong dual in a factor, a transposed contraction, a missing scale,
+a mirrored band offset, the wrong plan on V) in a temporary copy of the oracle and
+runs the pin tests against that copy; every copy must fail.  CPU only.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "sinkhorn_band.py")
+
+MUTATIONS = {
+    "update_order_column_first": (
+        "        u = row_update(S, v, h)\n        v = col_update(S, u, h)\n    duals = [v.copy()]",
+        "        v = col_update(S, u, h)\n        u = row_update(S, v, h)\n    duals = [v.copy()]"),
+    "drop_modifier_C_term": ("- C[None, :] * _row_vec(G, h))", ")"),
+    "sign_of_dv1": ("dv1 = -ev1 * _col_sum", "dv1 = ev1 * _col_sum"),
+    "wrong_dual_in_G": ("ev0 = np.exp(v0 - v2)", "ev0 = np.exp(v1 - v2)"),
+    "transposed_dK": ("dK = s * _band_matvec_cols(dS, Q, h)", "dK = s * _band_matvec_rows(dS, Q, h)"),
+    "missing_epsilon": ("s = 1.0 / (np.sqrt(d) * eps)", "s = 1.0 / np.sqrt(d)"),
+    "du1_missing_column_factor": (
+        "du1 = -eu1 * _row_sum(P22 * _row_vec(ev1 * dv1, h))",
+        "du1 = -eu1 * _row_sum(P22 * _row_vec(dv1, h))"),
+    "direct_four_wrong_P11": ("P11 = staircase_plan(S, u1, v1, h)", "P11 = staircase_plan(S, u2, v1, h)"),
+    "mirrored_band_offset": ("j = i + _offsets(h)[:, None]", "j = i - _offsets(h)[:, None]"),
+    "output_uses_P21": ("    uR, vR = duals[-2], duals[-1]", "    uR, vR = duals[-2], duals[-3]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    before, after = MUTATIONS[name]
+    src = open(SRC).read()
+    assert before in src, f"mutation anchor for {name} no longer present"
+    with tempfile.TemporaryDirectory() as d:
+        shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"),
+                        ignore=shutil.ignore_patterns("__pycache__"))
+        shutil.copytree(os.path.join(ROOT, "tests"), os.path.join(d, "tests"),
+                        ignore=shutil.ignore_patterns("__pycache__", "golden"))
+        with open(os.path.join(d, "oracle", "sinkhorn_band.py"), "w") as f:
+            f.write(src.replace(before, after))
+        r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle.py", "-q", "-x",
+                            "-p", "no:cacheprovider"], cwd=d, capture_output=True, text=True,
+                           timeout=300)
+    assert r.returncode != 0, f"planted mistake {name} passed every pin:\n{r.stdout[-2000:]}"
