@@ -1,0 +1,311 @@
+// C ABI of libsinkhorn_attn.so: argument validation, workspace sizing, launch sequencing.
+// The declarations and the contract (layouts, ownership, errors) are in include/sinkhorn_attn.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "sinkhorn_attn.h"
+#include "ska_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ska_status fail(ska_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+// ---------------------------------------------------------------------------------------------
+// optional per-launch timing with HIP events
+// ---------------------------------------------------------------------------------------------
+struct Timing {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[ska::kTimedKinds];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> free_pairs;
+  double total_ms[ska::kTimedKinds] = {0, 0, 0};
+  int64_t launches[ska::kTimedKinds] = {0, 0, 0};
+};
+thread_local Timing g_timing;
+
+std::pair<hipEvent_t, hipEvent_t> timing_begin(int kind, hipStream_t st) {
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  if (!g_timing.on) return ev;
+  if (!g_timing.free_pairs.empty()) {
+    ev = g_timing.free_pairs.back();
+    g_timing.free_pairs.pop_back();
+  } else {
+    if (hipEventCreate(&ev.first) != hipSuccess || hipEventCreate(&ev.second) != hipSuccess)
+      return {nullptr, nullptr};
+  }
+  (void)hipEventRecord(ev.first, st);
+  (void)kind;
+  return ev;
+}
+
+void timing_end(int kind, std::pair<hipEvent_t, hipEvent_t> ev, hipStream_t st) {
+  if (!ev.first) return;
+  (void)hipEventRecord(ev.second, st);
+  g_timing.pending[kind].push_back(ev);
+}
+
+// ---------------------------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------------------------
+struct Plan {
+  ska::Geometry g;
+  int elt;
+  bool empty;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
+  if (!p) return fail(SKA_ERR_INVALID, "problem pointer is NULL");
+  if (p->bh < 0) return fail(SKA_ERR_INVALID, "bh must be >= 0");
+  if (p->L < 0) return fail(SKA_ERR_INVALID, "L must be >= 0");
+  if (p->W < 0 || (p->W & 1)) return fail(SKA_ERR_INVALID, "W must be even and >= 0");
+  if (p->T < 0) return fail(SKA_ERR_INVALID, "T must be >= 0");
+  if (!(p->epsilon > 0.f) || !std::isfinite(p->epsilon))
+    return fail(SKA_ERR_INVALID, "epsilon must be finite and > 0");
+  if (p->dtype != SKA_F32 && p->dtype != SKA_BF16) return fail(SKA_ERR_INVALID, "unknown dtype");
+  const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
+  const bool dustbin = (op == SKA_OP_DUSTBIN_BLOCK_FWD || op == SKA_OP_DUSTBIN_BLOCK_VJP);
+  if (op < SKA_OP_FWD || op > SKA_OP_DUSTBIN_BLOCK_VJP) return fail(SKA_ERR_INVALID, "unknown op");
+  if (p->R < 1) return fail(SKA_ERR_INVALID, "R must be >= 1");
+  if (vjp && p->R != 2) return fail(SKA_ERR_UNSUPPORTED, "the VJP is built for R == 2");
+  if (p->d != ska::kD) return fail(SKA_ERR_UNSUPPORTED, "head dimension d must be 64");
+  const int64_t Lr = p->L + (dustbin ? 1 : 0);
+  if (Lr > (int64_t(1) << 30)) return fail(SKA_ERR_UNSUPPORTED, "L above 2^30 tokens");
+  if (p->bh > 65535) return fail(SKA_ERR_UNSUPPORTED, "bh above 65535");
+  int64_t h = p->W / 2;
+  if (dustbin && h < p->L) h = p->L;  // widened band: every token reaches the dustbin
+  if (h > Lr) h = Lr;                 // wider than the sequence changes nothing
+  out->elt = p->dtype;
+  out->empty = (p->bh == 0 || Lr == 0);
+  out->g.bh = p->bh;
+  out->g.Lr = (int)Lr;
+  out->g.Lpad = (int)ska::pad_tokens(Lr);
+  out->g.h = (int)h;
+  const double s = 1.0 / (std::sqrt((double)p->d) * (double)p->epsilon);
+  out->g.s = (float)s;
+  out->g.c2 = (float)(s * 1.4426950408889634);
+  return SKA_OK;
+}
+
+size_t workspace_for(const Plan& pl, ska_op op) {
+  if (pl.empty) return 0;
+  const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
+  const int64_t vecs = vjp ? ska::kVjpVecs : ska::kFwdVecs;
+  return (size_t)(vecs * pl.g.bh * (int64_t)pl.g.Lpad) * sizeof(float);
+}
+
+ska_status check_ptr(const void* ptr, const char* name) {
+  if (!ptr) return fail(SKA_ERR_INVALID, std::string(name) + " is NULL");
+  if (!aligned16(ptr)) return fail(SKA_ERR_INVALID, std::string(name) + " is not 16-byte aligned");
+  return SKA_OK;
+}
+
+#define SKA_TRY(expr)                  \
+  do {                                 \
+    ska_status _s = (expr);            \
+    if (_s != SKA_OK) return _s;       \
+  } while (0)
+
+#define SKA_LAUNCH(kind, st, expr)                                                   \
+  do {                                                                               \
+    auto _ev = timing_begin(kind, st);                                               \
+    hipError_t _e = (expr);                                                          \
+    timing_end(kind, _ev, st);                                                       \
+    if (_e != hipSuccess)                                                            \
+      return fail(SKA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(_e)); \
+  } while (0)
+
+ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K, const void* V,
+                   void* O, float* duals, void* workspace, size_t workspace_bytes,
+                   hipStream_t st) {
+  Plan pl;
+  SKA_TRY(check_problem(p, op, &pl));
+  if (pl.empty) return SKA_OK;
+  SKA_TRY(check_ptr(Q, "Q"));
+  SKA_TRY(check_ptr(K, "K"));
+  SKA_TRY(check_ptr(V, "V"));
+  SKA_TRY(check_ptr(O, "O"));
+  if (!duals) return fail(SKA_ERR_INVALID, "duals is NULL");
+  if ((reinterpret_cast<uintptr_t>(duals) & 3u) != 0) return fail(SKA_ERR_INVALID, "duals misaligned");
+  const size_t need = workspace_for(pl, op);
+  if (!workspace || workspace_bytes < need)
+    return fail(SKA_ERR_WORKSPACE, "workspace smaller than ska_workspace_bytes()");
+  if (!aligned16(workspace)) return fail(SKA_ERR_INVALID, "workspace is not 16-byte aligned");
+
+  const ska::Geometry& g = pl.g;
+  const int64_t vs = g.bh * (int64_t)g.Lpad;
+  float* u = static_cast<float*>(workspace);
+  float* v = u + vs;
+  const int64_t nd = 2 * (int64_t)p->R + 1;
+  const int64_t dstride = nd * g.Lr;
+  hipError_t e = ska::launch_fill(u, 2 * vs, 0.f, st);
+  if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+  // stopped base: T full (row, column) steps from u = v = 0
+  for (int t = 0; t < p->T; ++t) {
+    SKA_LAUNCH(ska::kTimedStep, st, ska::launch_lse(pl.elt, Q, K, v, u, nullptr, 0, g, st));
+    SKA_LAUNCH(ska::kTimedStep, st, ska::launch_lse(pl.elt, K, Q, u, v, nullptr, 0, g, st));
+  }
+  e = ska::launch_save_duals(v, duals, dstride, g, st);
+  if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+  // tail: u^(a) from v^(a-1), v^(a) from u^(a); saved as slots 2a-1, 2a
+  for (int a = 1; a <= p->R; ++a) {
+    SKA_LAUNCH(ska::kTimedStep, st,
+               ska::launch_lse(pl.elt, Q, K, v, u, duals + (2 * a - 1) * (int64_t)g.Lr, dstride, g, st));
+    SKA_LAUNCH(ska::kTimedStep, st,
+               ska::launch_lse(pl.elt, K, Q, u, v, duals + (2 * a) * (int64_t)g.Lr, dstride, g, st));
+  }
+  SKA_LAUNCH(ska::kTimedOut, st, ska::launch_out(pl.elt, Q, K, V, u, v, O, g, st));
+  return SKA_OK;
+}
+
+ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K, const void* V,
+                   const float* duals, const void* dO, void* dQ, void* dK, void* dV,
+                   ska_schedule sched, void* workspace, size_t workspace_bytes, hipStream_t st) {
+  Plan pl;
+  SKA_TRY(check_problem(p, op, &pl));
+  if (sched != SKA_ONE_REFERENCE && sched != SKA_DIRECT_FOUR)
+    return fail(SKA_ERR_INVALID, "unknown schedule");
+  if (pl.empty) return SKA_OK;
+  SKA_TRY(check_ptr(Q, "Q"));
+  SKA_TRY(check_ptr(K, "K"));
+  SKA_TRY(check_ptr(V, "V"));
+  SKA_TRY(check_ptr(dO, "dO"));
+  SKA_TRY(check_ptr(dQ, "dQ"));
+  SKA_TRY(check_ptr(dK, "dK"));
+  SKA_TRY(check_ptr(dV, "dV"));
+  if (!duals) return fail(SKA_ERR_INVALID, "duals is NULL");
+  if ((reinterpret_cast<uintptr_t>(duals) & 3u) != 0) return fail(SKA_ERR_INVALID, "duals misaligned");
+  const size_t need = workspace_for(pl, op);
+  if (!workspace || workspace_bytes < need)
+    return fail(SKA_ERR_WORKSPACE, "workspace smaller than ska_workspace_bytes()");
+  if (!aligned16(workspace)) return fail(SKA_ERR_INVALID, "workspace is not 16-byte aligned");
+
+  const ska::Geometry& g = pl.g;
+  float* ws = static_cast<float*>(workspace);
+  const bool d4 = (sched == SKA_DIRECT_FOUR);
+  hipError_t e = ska::launch_vjp_prep(duals, ws, g, st);
+  if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 0, d4, Q, K, V, dO, dV, ws, g, st));
+  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 1, d4, Q, K, V, dO, nullptr, ws, g, st));
+  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 2, d4, Q, K, V, dO, nullptr, ws, g, st));
+  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 3, d4, Q, K, V, dO, dQ, ws, g, st));
+  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 4, d4, Q, K, V, dO, dK, ws, g, st));
+  return SKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ska_status ska_workspace_bytes(const ska_problem* p, ska_op op, size_t* bytes) {
+  Plan pl;
+  SKA_TRY(check_problem(p, op, &pl));
+  if (!bytes) return fail(SKA_ERR_INVALID, "bytes pointer is NULL");
+  *bytes = workspace_for(pl, op);
+  return SKA_OK;
+}
+
+ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K, const void* V,
+                             void* O, float* duals, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  g_err.clear();
+  return run_fwd(p, SKA_OP_FWD, Q, K, V, O, duals, workspace, workspace_bytes, stream);
+}
+
+ska_status sinkhorn_attn_vjp(const ska_problem* p, const void* Q, const void* K, const void* V,
+                             const float* duals, const void* dO, void* dQ, void* dK, void* dV,
+                             ska_schedule schedule, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  g_err.clear();
+  return run_vjp(p, SKA_OP_VJP, Q, K, V, duals, dO, dQ, dK, dV, schedule, workspace,
+                 workspace_bytes, stream);
+}
+
+ska_status sinkhorn_attn_dustbin_block_fwd(const ska_problem* p, const void* Q, const void* K,
+                                           const void* V, void* O, float* duals, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  return run_fwd(p, SKA_OP_DUSTBIN_BLOCK_FWD, Q, K, V, O, duals, workspace, workspace_bytes,
+                 stream);
+}
+
+ska_status sinkhorn_attn_dustbin_block_vjp(const ska_problem* p, const void* Q, const void* K,
+                                           const void* V, const float* duals, const void* dO,
+                                           void* dQ, void* dK, void* dV, ska_schedule schedule,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  g_err.clear();
+  return run_vjp(p, SKA_OP_DUSTBIN_BLOCK_VJP, Q, K, V, duals, dO, dQ, dK, dV, schedule,
+                 workspace, workspace_bytes, stream);
+}
+
+const char* ska_status_string(ska_status s) {
+  switch (s) {
+    case SKA_OK: return "ok";
+    case SKA_ERR_INVALID: return "invalid argument";
+    case SKA_ERR_UNSUPPORTED: return "unsupported problem";
+    case SKA_ERR_WORKSPACE: return "workspace too small";
+    case SKA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* ska_last_error(void) { return g_err.c_str(); }
+
+ska_status ska_timing_enable(int on) {
+  Timing& t = g_timing;
+  if (on) {
+    t.on = true;
+    for (int k = 0; k < ska::kTimedKinds; ++k) {
+      t.total_ms[k] = 0;
+      t.launches[k] = 0;
+    }
+    return SKA_OK;
+  }
+  t.on = false;
+  for (int k = 0; k < ska::kTimedKinds; ++k) {
+    for (auto& ev : t.pending[k]) {
+      (void)hipEventSynchronize(ev.second);
+      t.free_pairs.push_back(ev);
+    }
+    t.pending[k].clear();
+  }
+  for (auto& ev : t.free_pairs) {
+    (void)hipEventDestroy(ev.first);
+    (void)hipEventDestroy(ev.second);
+  }
+  t.free_pairs.clear();
+  return SKA_OK;
+}
+
+ska_status ska_timing_read(int kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= ska::kTimedKinds || !total_ms || !launches)
+    return fail(SKA_ERR_INVALID, "bad timing query");
+  Timing& t = g_timing;
+  for (auto& ev : t.pending[kernel]) {
+    if (hipEventSynchronize(ev.second) != hipSuccess) return fail(SKA_ERR_HIP, "event sync failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ev.first, ev.second) != hipSuccess)
+      return fail(SKA_ERR_HIP, "event elapsed time failed");
+    t.total_ms[kernel] += ms;
+    t.launches[kernel] += 1;
+    t.free_pairs.push_back(ev);
+  }
+  t.pending[kernel].clear();
+  *total_ms = t.total_ms[kernel];
+  *launches = t.launches[kernel];
+  return SKA_OK;
+}
+
+}  // extern "C"

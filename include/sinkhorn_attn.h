@@ -1,0 +1,145 @@
+/*
+ * sinkhorn_attn.h -- C ABI of the MI355X (gfx950) banded balanced Sinkhorn attention library
+ * (libsinkhorn_attn.so).
+ *
+ * Method: arXiv 2605.08123, "Block-Wise Differentiable Sinkhorn Attention: Tail-Refinement
+ * Gradients with a Gap-Aware Dustbin Bridge", as summarised on the pages cited per entry point
+ * (abstract; technical summaries on gist.science, German "Technische Zusammenfassung" and
+ * French "Résumé Technique", §2.1-§2.3; atlas.scime.ai summary, Approach / Key results /
+ * Limitations).
+ *
+ * Problem (one independent problem per batch*head index b, 0 <= b < bh):
+ *   tokens 0..Lr-1 with query/key/value rows q_i, k_i, v_i in R^d (Lr = L, or L+1 for the
+ *   dustbin_block entry points), band half-width h = W/2, scores on the support
+ *   Omega = {(i,j): |i-j| <= h}:  S_ij = q_i . k_j / (sqrt(d) * epsilon).
+ *   Base: u = v = 0, then T steps of  u_i = -log sum_j exp(S_ij + v_j),
+ *                                     v_j = -log sum_i exp(S_ij + u_i);   v^(0) := v (stopped).
+ *   Tail: for a = 1..R:  u^(a) from v^(a-1), then v^(a) from u^(a) (same two updates).
+ *   Output: O = P V with P_ij = exp(S_ij + u^(R)_i + v^(R)_j) on Omega.
+ *   VJP (R = 2): exact gradient of <O, dO> with respect to Q, K, V through the tail, with
+ *   v^(0) held fixed (stop-gradient on the base).
+ *
+ * Tensor layout: Q, K, V, O, dO, dQ, dK, dV are [bh][Lr][d] row-major (d contiguous), element
+ * type given by ska_problem.dtype.  Duals are fp32 [bh][2R+1][Lr] in natural-log units, in the
+ * order v^(0), u^(1), v^(1), ..., u^(R), v^(R).
+ *
+ * Ownership and memory: every pointer is a device pointer owned by the caller, including the
+ * workspace (size from ska_workspace_bytes).  The library allocates and frees nothing, keeps no
+ * state between calls and never synchronises: work is enqueued on `stream` and completes
+ * asynchronously.  Tensor pointers must be 16-byte aligned; outputs must not alias inputs or
+ * the workspace.  Calls on different streams must use different workspaces.
+ *
+ * Errors: argument errors are detected on the host before anything is enqueued and return
+ * SKA_ERR_INVALID / SKA_ERR_UNSUPPORTED / SKA_ERR_WORKSPACE; a failed kernel launch returns
+ * SKA_ERR_HIP.  ska_last_error() gives a human-readable detail for the calling thread.  An
+ * empty problem (bh == 0 or L == 0, dustbin entry points: bh == 0) returns SKA_OK and
+ * enqueues nothing.  Non-finite inputs are not screened: they propagate as NaN/Inf.
+ */
+#ifndef SINKHORN_ATTN_H
+#define SINKHORN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SKA_F32 = 0, SKA_BF16 = 1 } ska_dtype;
+
+/* Adjoint schedule for the R = 2 VJP.
+ * SKA_ONE_REFERENCE: only the reference plan P^(2,2) is exponentiated; the other staircase
+ *   plans enter through the orbit factors exp(u^(a)-u^(2)), exp(v^(b)-v^(2)) (abstract;
+ *   technical summaries §2.2, orbit equation).
+ * SKA_DIRECT_FOUR: every staircase plan P^(2,2), P^(2,1), P^(1,1), P^(1,0) is exponentiated
+ *   on its own (the direct four-plan adjoint, atlas.scime.ai Key results); kept for
+ *   comparison. */
+typedef enum { SKA_ONE_REFERENCE = 0, SKA_DIRECT_FOUR = 1 } ska_schedule;
+
+typedef enum {
+  SKA_OK = 0,
+  SKA_ERR_INVALID = -1,     /* malformed argument (null/misaligned pointer, W odd, eps <= 0, ...) */
+  SKA_ERR_UNSUPPORTED = -2, /* well-formed but not built: d != 64, VJP with R != 2, huge L      */
+  SKA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than ska_workspace_bytes()          */
+  SKA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed                        */
+} ska_status;
+
+typedef enum {
+  SKA_OP_FWD = 0,
+  SKA_OP_VJP = 1,
+  SKA_OP_DUSTBIN_BLOCK_FWD = 2,
+  SKA_OP_DUSTBIN_BLOCK_VJP = 3
+} ska_op;
+
+typedef struct {
+  int64_t bh;      /* independent problems (batch * heads), >= 0                                 */
+  int64_t L;       /* tokens per problem, >= 0 (dustbin_block: real tokens; tensors hold L + 1)  */
+  int64_t d;       /* head dimension; 64 is built                                               */
+  int64_t W;       /* band width, even, >= 0; support |i - j| <= W / 2                          */
+  int32_t T;       /* stopped base steps, >= 0                                                  */
+  int32_t R;       /* tail steps: forward >= 1, VJP == 2                                        */
+  float epsilon;   /* entropic temperature, finite and > 0                                      */
+  int32_t dtype;   /* ska_dtype of Q, K, V, O, dO, dQ, dK, dV (duals are always fp32)           */
+} ska_problem;
+
+/* Workspace bytes the entry point `op` needs for problem *p (O(bh * L) floats; never depends on
+ * d or W).  Returns SKA_OK and writes *bytes, or an error status for an invalid problem. */
+ska_status ska_workspace_bytes(const ska_problem* p, ska_op op, size_t* bytes);
+
+/* Forward pass: stopped T-step balanced Sinkhorn base, R-step tail, O = P^(R,R) V.
+ * Writes O [bh][L][d] and duals [bh][2R+1][L].
+ * (technical summaries §2.1: fixed band support, epsilon absorbed into S, stopped base solve
+ * then differentiable tail; abstract: block-wise cost O((T+R) L W), O(L) extra HBM.) */
+ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K, const void* V,
+                             void* O, float* duals, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Exact R = 2 tail VJP: given the forward's duals and an arbitrary cotangent dO, writes dQ, dK,
+ * dV [bh][L][d].  Scores are recomputed per band tile; extra memory is O(L) vectors.
+ * (abstract: one-reference-tile schedule, score cotangent = reference tile times a modifier
+ * field of vector cotangents and dual differences; atlas.scime.ai Key results: complete
+ * arbitrary-cotangent Q/K/V VJP.) */
+ska_status sinkhorn_attn_vjp(const ska_problem* p, const void* Q, const void* K, const void* V,
+                             const float* duals, const void* dO, void* dQ, void* dK, void* dV,
+                             ska_schedule schedule, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* dustbin_block forward: tensors hold L real tokens followed by the learned dustbin token at
+ * row L ([bh][L+1][d]); duals are [bh][2R+1][L+1].  Tile padding beyond row L acts as the
+ * inactive fill tokens (no support, zero target).  The support is every pair of the L+1 active
+ * tokens within the widened half-width max(W/2, L), so the dustbin row and column connect to
+ * every token; all active tokens, the dustbin included, have unit row and column targets.  The
+ * same balanced surrogate then runs unchanged; cost O(L * max(W, L)).
+ * (technical summaries §2.3; searcharxiv abstract: unit-target surrogate on an augmented
+ * support with a single active dustbin; atlas.scime.ai Limitations: widened band cost.) */
+ska_status sinkhorn_attn_dustbin_block_fwd(const ska_problem* p, const void* Q, const void* K,
+                                           const void* V, void* O, float* duals, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
+
+/* dustbin_block VJP: gradients for all L+1 rows, the dustbin token included. */
+ska_status sinkhorn_attn_dustbin_block_vjp(const ska_problem* p, const void* Q, const void* K,
+                                           const void* V, const float* duals, const void* dO,
+                                           void* dQ, void* dK, void* dV, ska_schedule schedule,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+
+/* Static string for a status code. */
+const char* ska_status_string(ska_status s);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* ska_last_error(void);
+
+/* Kernel timing for measurement.  While enabled, every launch of the kernel family `kernel`
+ * (0: forward Sinkhorn step, 1: forward output, 2: VJP passes) on the calling thread is
+ * bracketed by HIP events on its own stream; ska_timing_read() synchronises on those events
+ * and returns the summed kernel milliseconds and the launch count since ska_timing_enable(1).
+ * Enabling creates HIP events (no device memory); disabling destroys them. */
+ska_status ska_timing_enable(int on);
+ska_status ska_timing_read(int kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKHORN_ATTN_H */

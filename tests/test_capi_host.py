@@ -1,0 +1,149 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports every entry
+point include/sinkhorn_attn.h declares, the ctypes struct matches the C layout, and
+argument errors come back as status codes before anything is enqueued."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from entropic_ot_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkhorn_attn.h")
+
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced on error paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s+(\w+)\s*\(", text, flags=re.M))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"sinkhorn_attn_fwd", "sinkhorn_attn_vjp", "sinkhorn_attn_dustbin_block_fwd",
+            "sinkhorn_attn_dustbin_block_vjp"} <= names
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = names - exported
+    assert not missing, f"declared but not exported: {missing}"
+    assert names == set(B.EXPORTS)
+
+
+def test_problem_struct_layout_matches_c():
+    src = r"""
+    #include <stddef.h>
+    #include <stdio.h>
+    #include "sinkhorn_attn.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(ska_problem),
+             offsetof(ska_problem, bh), offsetof(ska_problem, L), offsetof(ska_problem, d),
+             offsetof(ska_problem, W), offsetof(ska_problem, T), offsetof(ska_problem, R),
+             offsetof(ska_problem, epsilon), offsetof(ska_problem, dtype));
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                              check=True).stdout.split()]
+    P = B.SkaProblem
+    want = [ctypes.sizeof(P)] + [getattr(P, f).offset for f, _ in P._fields_]
+    assert got == want
+
+
+def _prob(**kw):
+    base = dict(bh=2, L=100, d=64, W=16, T=3, R=2, epsilon=1.0, dtype=B.SKA_F32)
+    base.update(kw)
+    return B.SkaProblem(**base)
+
+
+def _ws_bytes(prob, op):
+    n = ctypes.c_size_t(0)
+    st = B.lib.ska_workspace_bytes(ctypes.byref(prob), op, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes_are_linear_in_tokens():
+    for L, Lpad in ((1, 64), (64, 64), (65, 128), (1000, 1024)):
+        st, n = _ws_bytes(_prob(L=L, bh=3), B.SKA_OP_FWD)
+        assert st == 0 and n == 2 * 3 * Lpad * 4
+        st, n = _ws_bytes(_prob(L=L, bh=3), B.SKA_OP_VJP)
+        assert st == 0 and n == 14 * 3 * Lpad * 4
+    st, n = _ws_bytes(_prob(L=4096, bh=4), B.SKA_OP_DUSTBIN_BLOCK_FWD)   # 4097 rows
+    assert st == 0 and n == 2 * 4 * 4160 * 4
+    st, n = _ws_bytes(_prob(L=0), B.SKA_OP_VJP)
+    assert st == 0 and n == 0
+    # independent of W and dtype
+    assert _ws_bytes(_prob(W=4000), B.SKA_OP_VJP) == _ws_bytes(_prob(W=2, dtype=B.SKA_BF16), B.SKA_OP_VJP)
+
+
+@pytest.mark.parametrize("kw,op,status", [
+    (dict(d=32), B.SKA_OP_FWD, -2),
+    (dict(d=128), B.SKA_OP_VJP, -2),
+    (dict(W=7), B.SKA_OP_FWD, -1),
+    (dict(W=-2), B.SKA_OP_FWD, -1),
+    (dict(T=-1), B.SKA_OP_FWD, -1),
+    (dict(R=0), B.SKA_OP_FWD, -1),
+    (dict(R=3), B.SKA_OP_VJP, -2),
+    (dict(R=1), B.SKA_OP_DUSTBIN_BLOCK_VJP, -2),
+    (dict(epsilon=0.0), B.SKA_OP_FWD, -1),
+    (dict(epsilon=float("nan")), B.SKA_OP_VJP, -1),
+    (dict(dtype=7), B.SKA_OP_FWD, -1),
+    (dict(bh=-1), B.SKA_OP_FWD, -1),
+    (dict(bh=70000), B.SKA_OP_FWD, -2),
+])
+def test_invalid_problems_are_rejected(kw, op, status):
+    st, _ = _ws_bytes(_prob(**kw), op)
+    assert st == status
+    assert B.ska_last_error() != ""
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    prob = _prob()
+    _, need = _ws_bytes(prob, B.SKA_OP_FWD)
+    V = ctypes.c_void_p
+    f = B.lib.sinkhorn_attn_fwd
+    # NULL problem
+    assert f(None, V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), need, None) == -1
+    # NULL and misaligned tensors
+    assert f(ctypes.byref(prob), None, V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), need, None) == -1
+    assert f(ctypes.byref(prob), V(FAKE + 4), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), need, None) == -1
+    assert "aligned" in B.ska_last_error()
+    # workspace missing or short
+    assert f(ctypes.byref(prob), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), None, need, None) == -3
+    assert f(ctypes.byref(prob), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), need - 4, None) == -3
+    g = B.lib.sinkhorn_attn_vjp
+    _, needv = _ws_bytes(prob, B.SKA_OP_VJP)
+    args = [V(FAKE)] * 8
+    assert g(ctypes.byref(prob), *args, 5, V(FAKE), needv, None) == -1      # unknown schedule
+    assert g(ctypes.byref(prob), *args, 0, V(FAKE), needv - 1, None) == -3
+    assert g(ctypes.byref(prob), *(args[:5] + [None] + args[6:]), 0, V(FAKE), needv, None) == -1
+
+
+def test_empty_problems_enqueue_nothing():
+    for kw in (dict(bh=0), dict(L=0)):
+        prob = _prob(**kw)
+        assert B.lib.sinkhorn_attn_fwd(ctypes.byref(prob), None, None, None, None, None, None, 0,
+                                       None) == 0
+        assert B.lib.sinkhorn_attn_vjp(ctypes.byref(prob), None, None, None, None, None, None,
+                                       None, None, 0, None, 0, None) == 0
+    prob = _prob(bh=0)
+    assert B.lib.sinkhorn_attn_dustbin_block_fwd(ctypes.byref(prob), None, None, None, None, None,
+                                                 None, 0, None) == 0
+
+
+def test_status_strings():
+    assert B.ska_status_string(0) == "ok"
+    assert B.ska_status_string(-3) == "workspace too small"
+    assert B.ska_status_string(42) == "unknown status"

@@ -1,0 +1,148 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Small cases compare every element and span several tiles, ragged tails, W = 0, a band
+wider than the sequence, T = 0, L = 1 and a non-unit epsilon.  The named workloads run at
+their full sizes in the launch configuration bench.py times; where the oracle cannot finish
+a full long sequence in seconds, rows are sampled (each computed exactly on the window of
+tokens that can influence it, see oracle.sampled_rows)."""
+
+import numpy as np
+import pytest
+import torch
+
+from entropic_ot_attention_amd.workloads import (BATCH_L2048, DUSTBIN_L4096, HEADS8_L32K,
+                                                 LONG_L262K, TINY_L512, Workload, make_inputs)
+from tests.gpu_common import as64, compare, gpu_run, oracle_head, say
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = "f32", "bf16"
+
+SMALL = [
+    # name, bh, L, W, T, eps, dtype
+    ("L1_W4", 2, 1, 4, 2, 1.0, F32),
+    ("L17_W0", 3, 17, 0, 3, 1.0, F32),
+    ("L100_W300_band_wider_than_sequence", 2, 100, 300, 4, 1.0, F32),
+    ("L333_W50_eps07", 2, 333, 50, 4, 0.7, F32),
+    ("L97_W18_T0", 2, 97, 18, 0, 1.0, F32),
+    ("L200_W64_T15", 1, 200, 64, 15, 1.0, F32),
+    ("L1000_W256_T5", 2, 1000, 256, 5, 1.0, F32),
+    ("L65_W30_eps025", 1, 65, 30, 6, 0.25, F32),
+    ("L333_W50_bf16", 2, 333, 50, 4, 1.0, BF16),
+    ("L1000_W256_T5_bf16", 2, 1000, 256, 5, 1.0, BF16),
+    ("L31_W8_bf16", 3, 31, 8, 2, 1.0, BF16),
+]
+
+
+def _inputs(bh, L, W, T, eps, dtype, seed, dustbin=False):
+    w = Workload("case", 1, bh, L, 64, W, T, 2, eps, dtype, seed, dustbin=dustbin)
+    return w, make_inputs(w)
+
+
+@pytest.mark.parametrize("schedule", ["one_reference", "direct_four"])
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases_elementwise(case, schedule):
+    name, bh, L, W, T, eps, dt = case
+    w, x = _inputs(bh, L, W, T, eps, dt, seed=100 + [c[0] for c in SMALL].index(name))
+    say(f"[gpu] small case {name} schedule={schedule} bh={bh} L={L} W={W} T={T} dtype={dt}")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], W, T, 2, eps, schedule)
+    ref = {k: [] for k in ("O", "duals", "dQ", "dK", "dV")}
+    for b in range(bh):
+        r = oracle_head(*(as64(x[k][b]) for k in ("Q", "K", "V", "dO")), W, T, 2, eps, schedule)
+        for k in ref:
+            ref[k].append(r[k])
+    compare(got, ref, w.torch_dtype, f"{name}/{schedule}")
+
+
+@pytest.mark.parametrize("R", [1, 3, 4])
+def test_forward_general_tail_depth(R):
+    w, x = _inputs(2, 150, 40, 5, 1.0, F32, seed=77 + R)
+    say(f"[gpu] forward R={R}")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 40, 5, R)
+    ref = {"O": [], "duals": []}
+    for b in range(2):
+        r = oracle_head(*(as64(x[k][b]) for k in ("Q", "K", "V", "dO")), 40, 5, R)
+        ref["O"].append(r["O"])
+        ref["duals"].append(r["duals"])
+    compare(got, ref, torch.float32, f"forward R={R}")
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w, x = _inputs(2, 700, 128, 6, 1.0, BF16, seed=5)
+    say("[gpu] determinism bf16 L=700")
+    a = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 128, 6)
+    b = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 128, 6)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def _full_oracle(w, x, heads, schedule="one_reference"):
+    ref = {k: [] for k in ("O", "duals", "dQ", "dK", "dV")}
+    for b in heads:
+        r = oracle_head(*(as64(x[k][b]) for k in ("Q", "K", "V", "dO")), w.W, w.T, w.R, w.eps,
+                        schedule, dustbin=w.dustbin)
+        for k in ref:
+            ref[k].append(r[k])
+    return ref
+
+
+def test_tiny_L512_full():
+    w = TINY_L512
+    x = make_inputs(w)
+    say(f"[gpu] {w.name}")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps)
+    compare(got, _full_oracle(w, x, range(w.bh)), w.torch_dtype, w.name)
+
+
+def test_batch4x8_L2048_full():
+    w = BATCH_L2048
+    x = make_inputs(w)
+    say(f"[gpu] {w.name}")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps)
+    compare(got, _full_oracle(w, x, range(w.bh)), w.torch_dtype, w.name)
+
+
+@pytest.mark.parametrize("heads", [(0,), (3,)])
+def test_dustbin_block_L4096_full_heads(heads):
+    w = DUSTBIN_L4096
+    x = make_inputs(w)
+    say(f"[gpu] {w.name} heads {heads}")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps, dustbin=True)
+    compare(got, _full_oracle(w, x, heads), w.torch_dtype, f"{w.name} heads {heads}",
+            heads=list(heads))
+
+
+def _sampled(w, x, got, rows_by_head, label, schedule="one_reference"):
+    import oracle
+    p = oracle.BandProblem(W=w.W, T=w.T, R=w.R, eps=w.eps)
+    ref = {k: [] for k in ("O", "dQ", "dK", "dV")}
+    sub = {k: [] for k in ref}
+    for b, rows in rows_by_head.items():
+        r = oracle.sampled_rows(*(as64(x[k][b]) for k in ("Q", "K", "V", "dO")), p, rows, schedule)
+        for k in ref:
+            ref[k].append(r[k])
+            sub[k].append(got[k][b][rows])
+    compare({k: np.stack(v) for k, v in sub.items()}, {k: np.stack(v) for k, v in ref.items()},
+            w.torch_dtype, label)
+
+
+@pytest.mark.parametrize("schedule", ["one_reference", "direct_four"])
+def test_heads8_L32768_sampled_rows(schedule):
+    w = HEADS8_L32K
+    x = make_inputs(w)
+    say(f"[gpu] {w.name} schedule={schedule}")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps, schedule)
+    rng = np.random.default_rng(2)
+    rows = {0: [0, w.L - 1], 5: [int(rng.integers(0, w.L))], 7: [w.L // 2]}
+    _sampled(w, x, got, rows, f"{w.name}/{schedule}", schedule)
+
+
+def test_long_L262144_sampled_rows():
+    w = LONG_L262K
+    x = make_inputs(w)
+    say(f"[gpu] {w.name}")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps)
+    rng = np.random.default_rng(3)
+    rows = {0: [0, w.L - 1], 1: [int(rng.integers(0, w.L))], 2: [w.L // 2 + 7],
+            3: [int(rng.integers(0, w.L)), w.L - 100]}
+    _sampled(w, x, got, rows, w.name)
