@@ -1,0 +1,190 @@
+"""Benchmark: forward + exact R=2 VJP of banded balanced Sinkhorn attention on one MI355X.
+
+One step = sinkhorn_attn_fwd followed by sinkhorn_attn_vjp (one-reference schedule) on the
+seeded synthetic workload "seq1x4_L262144_W256_bf16" (one sequence, 4 heads, L = 262144
+tokens, d = 64, band W = 256, T = 15 base steps, R = 2, bf16 inputs, fp32 duals).  Inputs are
+resident in HBM before the timed region.  The metric is tokens of the sequence per second:
+L / (t_fwd + t_vjp) for all heads together.
+
+Prints ONE JSON line.  Besides the throughput it reports, for the dominant kernel (the
+forward Sinkhorn half-step, 2(T+R) launches per step), its average launch time measured with
+HIP events on its own stream during the timed steps and the achieved fraction of the VALU
+issue roofline, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X unit counts and clock used for the VALU roofline: 256 CUs x 4 SIMDs x 16 lanes at
+# 2.4 GHz issue 39.3e12 fp32 lane-operations per second (no packed fp32).  v_exp_f32 is a
+# quarter-rate transcendental, so one exponential occupies 4 issue slots.
+VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
+EXP_SLOTS = 4
+# Minimal VALU work of one balanced log-domain half-step per band entry: form the exponent
+# (1 fma), track the running max (1 max), shift (1 sub), exponentiate (1 exp = 4 slots),
+# accumulate (1 add): 8 issue slots.
+SLOTS_PER_ENTRY_STEP = 4 + EXP_SLOTS
+HBM_PEAK_GBS = 8000.0
+
+
+def band_entries(L: int, h: int) -> int:
+    """|{(i, j): 0 <= i, j < L, |i - j| <= h}|."""
+    h = min(h, L - 1) if L > 0 else 0
+    return L * (2 * h + 1) - h * (h + 1)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="seq1x4_L262144_W256_bf16")
+    ap.add_argument("--schedule", default="one_reference", choices=["one_reference", "direct_four"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, sample_tokens: int):
+    """fp64 oracle (as it stands) on a bounded sample: head 0, the first `sample_tokens` tokens
+    of the workload's inputs, forward + one-reference VJP; single-threaded numpy."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from entropic_ot_attention_amd.workloads import make_inputs
+
+    x = make_inputs(w)
+    n = min(sample_tokens, w.tokens)
+    Q, K, V, dO = (x[k][0, :n].float().double().numpy() for k in ("Q", "K", "V", "dO"))
+    p = oracle.BandProblem(W=w.W, T=w.T, R=w.R, eps=w.eps)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O, duals = oracle.forward(Q, K, V, p)
+        oracle.vjp_one_reference(Q, K, V, dO, duals, p)
+        dt = time.perf_counter() - t0
+    # one token of the workload spans all heads: scale the single-head sample accordingly
+    value = n / (w.bh * dt)
+    return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"head 0 of {w.bh}, tokens 0..{n - 1} of {w.tokens}, fwd + one-reference "
+                      f"VJP in fp64 numpy, {dt:.2f} s; tokens/s = tokens / ({w.bh} heads x time)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every problem is independent; sharding over batch*heads is a design note only). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from entropic_ot_attention_amd import binding as B
+    from entropic_ot_attention_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    x = make_inputs(w)
+    Q, K, V, dO = (x[k].to(dev) for k in ("Q", "K", "V", "dO"))
+    L = w.L
+    rows = w.tokens
+    prob = B.make_problem(w.bh, L, w.d, w.W, w.T, w.R, w.eps, w.torch_dtype)
+    fwd_op = B.SKA_OP_DUSTBIN_BLOCK_FWD if w.dustbin else B.SKA_OP_FWD
+    vjp_op = B.SKA_OP_DUSTBIN_BLOCK_VJP if w.dustbin else B.SKA_OP_VJP
+    ws = B.workspace_for(prob, max(fwd_op, vjp_op), dev)
+    ws_f = B.workspace_for(prob, fwd_op, dev)
+    O = torch.empty_like(Q)
+    duals = torch.empty(w.bh, 2 * w.R + 1, rows, dtype=torch.float32, device=dev)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    sched = B.SCHEDULES[args.schedule]
+    fwd = B.sinkhorn_attn_dustbin_block_fwd if w.dustbin else B.sinkhorn_attn_fwd
+    vjp = B.sinkhorn_attn_dustbin_block_vjp if w.dustbin else B.sinkhorn_attn_vjp
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fwd(prob, Q, K, V, O, duals, ws_f)
+        if ev is not None:
+            ev[1].record(stream)
+        vjp(prob, Q, K, V, duals, dO, dQ, dK, dV, sched, ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    B.ska_timing_enable(True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    vjp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+    kstep_ms, kstep_n = B.ska_timing_read(B.TIMED_STEP)
+    kout_ms, kout_n = B.ska_timing_read(B.TIMED_OUT)
+    kvjp_ms, kvjp_n = B.ska_timing_read(B.TIMED_VJP)
+    B.ska_timing_enable(False)
+
+    tokens_per_step = w.batch * L
+    value = tokens_per_step / (step_ms / 1e3)
+    h = min(w.W // 2, rows) if not w.dustbin else rows
+    nnz = band_entries(rows, h) * w.bh                         # band entries per launch
+    avg_launch_s = (kstep_ms / max(kstep_n, 1)) / 1e3
+    achieved = SLOTS_PER_ENTRY_STEP * nnz / avg_launch_s / 1e12     # Tslot/s
+    peak = VALU_LANE_OPS_PER_S / 1e12
+    roofline = {
+        "bound": "alu",
+        "kernel": "lse_kernel (forward Sinkhorn half-step)",
+        "achieved": round(achieved, 3),
+        "peak": round(peak, 3),
+        "unit": "T VALU issue-slots/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None,
+        "avg_launch_us": round(avg_launch_s * 1e6, 2),
+        "launches_timed": kstep_n,
+        "algorithmic_work": f"{SLOTS_PER_ENTRY_STEP} slots x {nnz} band entries per launch",
+    }
+    out = {
+        "metric": "fwd+R=2 VJP tokens/s at L=262144 W=256 d=64",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "L": L, "d": w.d,
+                   "W": w.W, "T": w.T, "R": w.R, "epsilon": w.eps, "schedule": args.schedule},
+        "breakdown": {"fwd_ms": round(fwd_ms, 4), "vjp_ms": round(vjp_ms, 4),
+                      "wall_s": round(wall, 3),
+                      "step_kernels_ms": round(kstep_ms / args.steps, 4),
+                      "out_kernel_ms": round(kout_ms / args.steps, 4),
+                      "vjp_kernels_ms": round(kvjp_ms / args.steps, 4)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -98,11 +98,19 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
   return SKA_OK;
 }
 
+// Forward workspace, fused path (bands up to half-width 192): two column-dual and two row-dual
+// buffers [bh][Lpad] plus two column-partial buffers [bh][nblk][pstride]; split path (wider
+// bands): two dual buffers.  VJP: kVjpVecs vectors [bh][Lpad].  All O(bh L (1 + W/64)) floats.
 size_t workspace_for(const Plan& pl, ska_op op) {
   if (pl.empty) return 0;
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
-  const int64_t vecs = vjp ? ska::kVjpVecs : ska::kFwdVecs;
-  return (size_t)(vecs * pl.g.bh * (int64_t)pl.g.Lpad) * sizeof(float);
+  const int64_t vs = pl.g.bh * (int64_t)pl.g.Lpad;
+  if (vjp) return (size_t)(ska::kVjpVecs * vs) * sizeof(float);
+  const int nt = ska::fused_tiles_for(pl.g.h);
+  if (nt == 0) return (size_t)(ska::kFwdVecs * vs) * sizeof(float);
+  const int64_t nblk = (pl.g.Lr + 63) / 64;
+  const int64_t ps = pl.g.bh * nblk * ska::fused_pstride(nt);
+  return (size_t)(4 * vs + 2 * ps) * sizeof(float);
 }
 
 ska_status check_ptr(const void* ptr, const char* name) {
@@ -145,10 +153,61 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
 
   const ska::Geometry& g = pl.g;
   const int64_t vs = g.bh * (int64_t)g.Lpad;
-  float* u = static_cast<float*>(workspace);
-  float* v = u + vs;
   const int64_t nd = 2 * (int64_t)p->R + 1;
   const int64_t dstride = nd * g.Lr;
+  float* wsf = static_cast<float*>(workspace);
+  const int nt = ska::fused_tiles_for(g.h);
+  if (nt > 0) {
+    // fused path: one launch per full Sinkhorn step, column update finished by the next launch
+    const int nblk = (g.Lr + 63) / 64;
+    const int pst = ska::fused_pstride(nt);
+    const int64_t ps = g.bh * (int64_t)nblk * pst;
+    float* vbuf[2] = {wsf, wsf + vs};
+    float* ubuf[2] = {wsf + 2 * vs, wsf + 3 * vs};
+    float* part[2] = {wsf + 4 * vs, wsf + 4 * vs + ps};
+    hipError_t e = ska::launch_fill(wsf, 4 * vs, 0.f, st);
+    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+    ska::StepArgs a{};
+    a.Q = Q;
+    a.K = K;
+    a.bh = g.bh;
+    a.Lr = g.Lr;
+    a.Lpad = g.Lpad;
+    a.h = g.h;
+    a.nblk = nblk;
+    a.pstride = pst;
+    a.c2 = g.c2;
+    a.save_v_stride = dstride;
+    a.save_u_stride = dstride;
+    const int K_steps = p->T + p->R;
+    for (int k = 1; k <= K_steps; ++k) {
+      a.v_prev = vbuf[(k - 1) % 2];
+      a.part_prev = (k > 1) ? part[(k - 1) % 2] : nullptr;
+      a.u_prev = ubuf[(k - 1) % 2];
+      a.v_next = vbuf[k % 2];
+      a.u_out = ubuf[k % 2];
+      a.part_out = part[k % 2];
+      a.save_v = (k - 1 >= p->T) ? duals + 2 * (int64_t)(k - 1 - p->T) * g.Lr : nullptr;
+      a.save_u = (k > p->T) ? duals + (2 * (int64_t)(k - p->T) - 1) * g.Lr : nullptr;
+      SKA_LAUNCH(ska::kTimedStep, st, ska::launch_fused_step(pl.elt, nt, a, st));
+    }
+    a.v_prev = vbuf[K_steps % 2];
+    a.part_prev = part[K_steps % 2];
+    a.u_prev = ubuf[K_steps % 2];
+    a.v_next = vbuf[(K_steps + 1) % 2];
+    a.u_out = nullptr;
+    a.part_out = nullptr;
+    a.save_v = duals + 2 * (int64_t)p->R * g.Lr;
+    a.save_u = nullptr;
+    e = ska::launch_finish_columns(pl.elt, a, st);
+    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+    SKA_LAUNCH(ska::kTimedOut, st,
+               ska::launch_out(pl.elt, Q, K, V, ubuf[K_steps % 2], vbuf[(K_steps + 1) % 2], O, g, st));
+    return SKA_OK;
+  }
+  // split path (bands wider than the fused step holds, e.g. the dense dustbin support)
+  float* u = wsf;
+  float* v = u + vs;
   hipError_t e = ska::launch_fill(u, 2 * vs, 0.f, st);
   if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
   // stopped base: T full (row, column) steps from u = v = 0

@@ -1,0 +1,227 @@
+// Device-side helpers shared by the HIP kernels of libsinkhorn_attn.so (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "ska_internal.h"
+
+namespace ska {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef float f32x4 __attribute__((__vector_size__(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kChunk = 32;  // window rows staged per LDS round (two 16-row tiles)
+
+template <typename T> struct Lds;
+template <> struct Lds<bf16> { static constexpr int stride = 72; };   // 64 + 8 pad elements
+template <> struct Lds<float> { static constexpr int stride = 68; };  // 64 + 4 pad elements
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------------------------------------
+// Operand fragments of the score contraction over d = 64.
+// bf16: v_mfma_f32_16x16x32_bf16 twice; lane group g = l/16 supplies d in [16g, 16g+16),
+//       split as k-slots 8g..8g+7 of the first MFMA (d = 16g + e) and of the second
+//       (d = 16g + 8 + e).  The same permutation on both operands leaves the dot product intact.
+// fp32: v_mfma_f32_16x16x4_f32 sixteen times; MFMA s takes d = 16g + s in k-slot g.
+// ---------------------------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 a, b; };
+template <> struct Frag<float> { f32x4 v[4]; };
+
+__device__ __forceinline__ void load_frag(Frag<bf16>& f, const bf16* row, bool ok, int g) {
+  if (ok) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + 16 * g);
+    uint4 x = p[0], y = p[1];
+    f.a = __builtin_bit_cast(bf16x8, x);
+    f.b = __builtin_bit_cast(bf16x8, y);
+  } else {
+    uint4 z = {0u, 0u, 0u, 0u};
+    f.a = __builtin_bit_cast(bf16x8, z);
+    f.b = __builtin_bit_cast(bf16x8, z);
+  }
+}
+
+__device__ __forceinline__ void load_frag(Frag<float>& f, const float* row, bool ok, int g) {
+  if (ok) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(row + 16 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.v[i] = p[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+__device__ __forceinline__ f32x4 dot_tile(const Frag<bf16>& w, const Frag<bf16>& o) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w.a, o.a, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w.b, o.b, acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 dot_tile(const Frag<float>& w, const Frag<float>& o) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w.v[i][j], o.v[i][j], acc, 0, 0, 0);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------------------------
+// LDS staging of 32 window rows x 64 columns of the second contraction's operand, per wave.
+// Rows outside [0, Lr) are written as zeros.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void stage_rows(bf16* lds, const bf16* base, int r0, int Lr, int lane) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int c = it * 64 + lane;
+    const int row = c >> 3, col = (c & 7) * 8;
+    const int t = r0 + row;
+    uint4 x = {0u, 0u, 0u, 0u};
+    if (t >= 0 && t < Lr) x = *reinterpret_cast<const uint4*>(base + (int64_t)t * kD + col);
+    *reinterpret_cast<uint4*>(lds + row * Lds<bf16>::stride + col) = x;
+  }
+}
+
+__device__ __forceinline__ void stage_rows(float* lds, const float* base, int r0, int Lr, int lane) {
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int c = it * 64 + lane;
+    const int row = c >> 4, col = (c & 15) * 4;
+    const int t = r0 + row;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (t >= 0 && t < Lr) x = *reinterpret_cast<const f32x4*>(base + (int64_t)t * kD + col);
+    *reinterpret_cast<f32x4*>(lds + row * Lds<float>::stride + col) = x;
+  }
+}
+
+// acc[b][r] (lane l) += sum over the 32 staged rows k of  Op[k][16b + 4g + r] * Z[k][n],
+// where Z[16tt + 4g' + r'] at lane (g', n) is z[tt][r'].  The result layout is
+// acc[b][r] <-> (column 16b + 4g + r of the operand, owned token n = l % 16).
+__device__ __forceinline__ void contract(f32x4 (&acc)[4], const bf16* lds, const float (&z)[2][4],
+                                         int g, int n) {
+  bf16x8 zb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    zb[e] = (bf16)z[0][e];
+    zb[e + 4] = (bf16)z[1][e];
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    bf16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = (e < 4) ? (4 * g + e) : (16 + 4 * g + e - 4);
+      a[e] = lds[row * Lds<bf16>::stride + 16 * b + n];
+    }
+    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, zb, acc[b], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void contract(f32x4 (&acc)[4], const float* lds, const float (&z)[2][4],
+                                         int g, int n) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * tt + 4 * g + r;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(lds[row * Lds<float>::stride + 16 * b + n],
+                                                      z[tt][r], acc[b], 0, 0, 0);
+    }
+}
+
+// Two contractions against the same staged operand (shares the LDS reads).
+__device__ __forceinline__ void contract2(f32x4 (&x)[4], f32x4 (&y)[4], const bf16* lds,
+                                          const float (&z1)[2][4], const float (&z2)[2][4], int g,
+                                          int n) {
+  bf16x8 b1, b2;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    b1[e] = (bf16)z1[0][e];
+    b1[e + 4] = (bf16)z1[1][e];
+    b2[e] = (bf16)z2[0][e];
+    b2[e + 4] = (bf16)z2[1][e];
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    bf16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = (e < 4) ? (4 * g + e) : (16 + 4 * g + e - 4);
+      a[e] = lds[row * Lds<bf16>::stride + 16 * b + n];
+    }
+    x[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, x[b], 0, 0, 0);
+    y[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, y[b], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void contract2(f32x4 (&x)[4], f32x4 (&y)[4], const float* lds,
+                                          const float (&z1)[2][4], const float (&z2)[2][4], int g,
+                                          int n) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * tt + 4 * g + r;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float a = lds[row * Lds<float>::stride + 16 * b + n];
+        x[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z1[tt][r], x[b], 0, 0, 0);
+        y[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z2[tt][r], y[b], 0, 0, 0);
+      }
+    }
+}
+
+// Store acc (scaled) as row `o` of out: lane holds columns 16b + 4g + r, r = 0..3.
+__device__ __forceinline__ void store_row(bf16* out_row, const f32x4 (&acc)[4], float scale, int g) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    typedef __bf16 bf16x4 __attribute__((__vector_size__(8)));
+    bf16x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc[b][r] * scale);
+    *reinterpret_cast<bf16x4*>(out_row + 16 * b + 4 * g) = v;
+  }
+}
+
+__device__ __forceinline__ void store_row(float* out_row, const f32x4 (&acc)[4], float scale, int g) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f32x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = acc[b][r] * scale;
+    *reinterpret_cast<f32x4*>(out_row + 16 * b + 4 * g) = v;
+  }
+}
+
+// Sum of a per-lane value over the 4 lane groups holding the same owned token.
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Does the 16-row window tile starting at w0 meet the band of owned tokens [o0, o0 + 16)?
+__device__ __forceinline__ bool tile_live(int w0, int o0, int h, int Lr) {
+  return w0 < Lr && w0 <= o0 + 15 + h && w0 + 15 >= o0 - h;
+}
+
+__device__ __forceinline__ bool in_band(int w, int o, int h, int Lr) {
+  return w < Lr && o < Lr && abs(w - o) <= h;
+}
+
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+
+}  // namespace ska

@@ -38,6 +38,31 @@ struct Geometry {
   float s;        // score scale in natural units: 1 / (sqrt(d) * eps)
 };
 
+// Arguments of one fused Sinkhorn step launch (see ska_fused.hip).  Vectors are [bh][Lpad] fp32
+// in log2 units; column partials are [bh][nblk][pstride] fp32.
+struct StepArgs {
+  const void* Q;
+  const void* K;
+  const float* v_prev;     // column duals before the previous launch's column update
+  const float* part_prev;  // previous launch's column partials, or nullptr (v_prev is final)
+  const float* u_prev;     // previous launch's row duals (exact fallback of the column finish)
+  float* v_next;           // finished column duals of the owned tokens
+  float* u_out;            // row duals of this step
+  float* part_out;         // column partials of this step
+  float* save_v;           // optional copies in natural units (saved duals), or nullptr
+  int64_t save_v_stride;
+  float* save_u;
+  int64_t save_u_stride;
+  int64_t bh;
+  int Lr, Lpad, h, nblk, pstride;
+  float c2;
+};
+
+// Register-resident step width (16-key tiles per wave) for half-width h, or 0 when the band is
+// too wide for the fused step (the split row/column kernels handle it).
+int fused_tiles_for(int h);
+inline int fused_pstride(int nt) { return 64 + 16 * (nt - 1); }
+
 enum TimedKernel : int { kTimedStep = 0, kTimedOut = 1, kTimedVjp = 2, kTimedKinds = 3 };
 
 // Launchers (return the hipGetLastError() of their launches).  `elt` is 0 for fp32, 1 for bf16.
@@ -48,6 +73,8 @@ hipError_t launch_lse(int elt, const void* own, const void* win, const float* vi
                       float* vsave, int64_t save_stride, const Geometry& g, hipStream_t st);
 hipError_t launch_out(int elt, const void* Q, const void* K, const void* V, const float* u2,
                       const float* v2, void* O, const Geometry& g, hipStream_t st);
+hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, hipStream_t st);
+hipError_t launch_finish_columns(int elt, const StepArgs& a, hipStream_t st);
 hipError_t launch_vjp_prep(const float* duals, float* ws, const Geometry& g, hipStream_t st);
 hipError_t launch_vjp_pass(int elt, int pass, bool direct4, const void* Q, const void* K,
                            const void* V, const void* dO, void* out, float* ws, const Geometry& g,

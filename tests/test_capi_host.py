@@ -74,17 +74,34 @@ def _ws_bytes(prob, op):
     return st, n.value
 
 
-def test_workspace_sizes_are_linear_in_tokens():
+def _fused_fwd_bytes(bh, L, W):
+    """Forward workspace of the register-resident path: 4 dual vectors [bh][Lpad] and two
+    column-partial buffers [bh][ceil(L/64)][64 + 32 * H16] (H16 = tiles of the band halo)."""
+    Lpad = -(-L // 64) * 64
+    h = min(W // 2, L)
+    nt = 1 + 2 * (-(-h // 16))
+    nt = next(c for c in (5, 9, 17, 25) if nt <= c)
+    pst = 64 + 16 * (nt - 1)
+    return (4 * bh * Lpad + 2 * bh * (-(-L // 64)) * pst) * 4
+
+
+def test_workspace_sizes():
     for L, Lpad in ((1, 64), (64, 64), (65, 128), (1000, 1024)):
         st, n = _ws_bytes(_prob(L=L, bh=3), B.SKA_OP_FWD)
-        assert st == 0 and n == 2 * 3 * Lpad * 4
+        assert st == 0 and n == _fused_fwd_bytes(3, L, 16)
         st, n = _ws_bytes(_prob(L=L, bh=3), B.SKA_OP_VJP)
         assert st == 0 and n == 14 * 3 * Lpad * 4
-    st, n = _ws_bytes(_prob(L=4096, bh=4), B.SKA_OP_DUSTBIN_BLOCK_FWD)   # 4097 rows
+    st, n = _ws_bytes(_prob(L=262144, bh=4, W=256), B.SKA_OP_FWD)
+    assert st == 0 and n == _fused_fwd_bytes(4, 262144, 256)
+    assert n < 30 * 4 * 262144 * 4          # O(L): under 30 floats per token and head
+    # bands wider than the register-resident step use the split path: two dual vectors
+    st, n = _ws_bytes(_prob(L=2000, bh=2, W=1000), B.SKA_OP_FWD)
+    assert st == 0 and n == 2 * 2 * 2048 * 4
+    st, n = _ws_bytes(_prob(L=4096, bh=4), B.SKA_OP_DUSTBIN_BLOCK_FWD)   # 4097 rows, dense
     assert st == 0 and n == 2 * 4 * 4160 * 4
     st, n = _ws_bytes(_prob(L=0), B.SKA_OP_VJP)
     assert st == 0 and n == 0
-    # independent of W and dtype
+    # the VJP workspace depends neither on W nor on the dtype
     assert _ws_bytes(_prob(W=4000), B.SKA_OP_VJP) == _ws_bytes(_prob(W=2, dtype=B.SKA_BF16), B.SKA_OP_VJP)
 
 

@@ -31,6 +31,10 @@ SMALL = [
     ("L333_W50_bf16", 2, 333, 50, 4, 1.0, BF16),
     ("L1000_W256_T5_bf16", 2, 1000, 256, 5, 1.0, BF16),
     ("L31_W8_bf16", 3, 31, 8, 2, 1.0, BF16),
+    ("L300_W80_bf16", 2, 300, 80, 4, 1.0, BF16),
+    ("L400_W500_split_path", 2, 400, 500, 3, 1.0, F32),
+    # scores spanning hundreds of nats: column masses underflow fp32, exact column fallback
+    ("L120_W40_eps002_column_fallback", 1, 120, 40, 3, 0.02, F32),
 ]
 
 
@@ -122,7 +126,8 @@ def _sampled(w, x, got, rows_by_head, label, schedule="one_reference"):
         for k in ref:
             ref[k].append(r[k])
             sub[k].append(got[k][b][rows])
-    compare({k: np.stack(v) for k, v in sub.items()}, {k: np.stack(v) for k, v in ref.items()},
+    compare({k: np.concatenate(v) for k, v in sub.items()},
+            {k: np.concatenate(v) for k, v in ref.items()},
             w.torch_dtype, label)
 
 
