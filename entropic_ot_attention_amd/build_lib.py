@@ -22,6 +22,8 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep hipcc from forming packed fp32 instructions (v_pk_fma_f32 and friends)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs (no copies out of the accumulation registers)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -73,21 +73,12 @@ __device__ __forceinline__ float dot64(const float* a, const float* b) {
   return s;
 }
 
-// Finished column dual (log2 units) of key j given the previous dual and the per-block column
-// sums of exp(S + u + v_prev).  Exact fallback: -log2 sum_i 2^(c2 q_i.k_j + u_i) over the band.
+// Exact column update (log2 units): -log2 sum_i 2^(c2 q_i.k_j + u_i) over the band of key j.
+// Used where a column's summed mass underflows; the same arithmetic runs in every block that
+// needs column j, so all of them agree bitwise.
 template <typename T>
-__device__ float finish_column(int j, const float* vprev_h, const float* part_h, const float* u_h,
-                               const T* Qh, const T* Kh, int Lr, int h, int H16, int nblk,
-                               int pstride, float c2) {
-  float s = 0.f;
-  const int lo = max(0, floor_div(j - 16 * H16 - 63, 64));
-  const int hi = min(nblk - 1, floor_div(j + 16 * H16, 64));
-  for (int b = lo; b <= hi; ++b) {
-    const int c = j - (b * 64 - 16 * H16);
-    if (c >= 0 && c < pstride) s += part_h[(int64_t)b * pstride + c];
-  }
-  if (s >= 0x1p-100f) return vprev_h[j] - fast_log2(s);
-  // exact column log-sum-exp (rare path; same arithmetic in every block that needs column j)
+__device__ float exact_column(int j, const float* u_h, const T* Qh, const T* Kh, int Lr, int h,
+                              float c2) {
   float m = -INFINITY;
   const int i0 = max(0, j - h), i1 = min(Lr - 1, j + h);
   for (int i = i0; i <= i1; ++i)
@@ -97,6 +88,36 @@ __device__ float finish_column(int j, const float* vprev_h, const float* part_h,
   for (int i = i0; i <= i1; ++i)
     l += fast_exp2(fmaf(dot64(Qh + (int64_t)i * kD, Kh + (int64_t)j * kD), c2, u_h[i]) - m);
   return -(m + fast_log2(l));
+}
+
+// Blocks whose key window holds column j: windows are [64 b - 16 H16, 64 b + 64 + 16 H16).
+__device__ __forceinline__ int first_block_of(int j, int H16) {
+  return max(0, floor_div(j - 16 * H16 - 63, 64));
+}
+
+// Finished column dual (log2 units) of key j given the previous dual and the per-block column
+// sums of exp(S + u + v_prev), summed in ascending block order.
+template <typename T, int NB>
+__device__ float finish_column(int j, const float* vprev_h, const float* part_h, const float* u_h,
+                               const T* Qh, const T* Kh, int Lr, int h, int H16, int nblk,
+                               int pstride, float c2) {
+  const int lo = first_block_of(j, H16);
+  const int hi = min(nblk - 1, floor_div(j + 16 * H16, 64));
+  float p[NB];
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    const int b = lo + q, c = j - (b * 64 - 16 * H16);
+    const bool ok = (b <= hi) & (c >= 0) & (c < pstride);
+    const int bc = min(b, nblk - 1), cc = min(max(c, 0), pstride - 1);
+    const float x = part_h[(int64_t)bc * pstride + cc];
+    p[q] = ok ? x : 0.f;
+  }
+  const float vp = vprev_h[j];
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < NB; ++q) s += p[q];
+  if (s >= 0x1p-100f) return vp - fast_log2(s);
+  return exact_column<T>(j, u_h, Qh, Kh, Lr, h, c2);
 }
 
 // B-operand fragment of key row `row` of the staged window (LDS), d-slice of lane group g.
@@ -111,21 +132,45 @@ __device__ __forceinline__ void lds_frag(Frag<float>& f, const float* kw, int ro
   for (int i = 0; i < 4; ++i) f.v[i] = p[i];
 }
 
-// Stage `rows` key rows starting at token r0 (zeros outside [0, Lr)) into LDS, whole workgroup.
-__device__ __forceinline__ void stage_block(bf16* lds, const bf16* base, int r0, int rows, int Lr) {
-  for (int c = threadIdx.x; c < rows * 8; c += blockDim.x) {
-    const int row = c >> 3, col = (c & 7) * 8, t = r0 + row;
-    uint4 x = {0u, 0u, 0u, 0u};
-    if (t >= 0 && t < Lr) x = *reinterpret_cast<const uint4*>(base + (int64_t)t * kD + col);
-    *reinterpret_cast<uint4*>(lds + row * Lds<bf16>::stride + col) = x;
+// Stage ROWS key rows starting at token r0 (zeros outside [0, Lr)) into LDS, whole workgroup
+// of 256 threads: every thread issues all of its 16-byte loads before its first LDS store, so the
+// loads overlap instead of each paying the full memory latency.
+template <int ROWS>
+__device__ __forceinline__ void stage_block(bf16* lds, const bf16* base, int r0, int Lr) {
+  constexpr int kPer = ROWS * 8 / 256;
+  static_assert(ROWS * 8 % 256 == 0, "rows must fill the workgroup");
+  uint4 buf[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8, t = r0 + row;
+    const int tc = min(max(t, 0), Lr - 1);          // always a valid row; zeroed below if outside
+    const uint4 x = *reinterpret_cast<const uint4*>(base + (int64_t)tc * kD + col);
+    const bool ok = (t >= 0) & (t < Lr);
+    buf[i] = uint4{ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8;
+    *reinterpret_cast<uint4*>(lds + row * Lds<bf16>::stride + col) = buf[i];
   }
 }
-__device__ __forceinline__ void stage_block(float* lds, const float* base, int r0, int rows, int Lr) {
-  for (int c = threadIdx.x; c < rows * 16; c += blockDim.x) {
-    const int row = c >> 4, col = (c & 15) * 4, t = r0 + row;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (t >= 0 && t < Lr) x = *reinterpret_cast<const f32x4*>(base + (int64_t)t * kD + col);
-    *reinterpret_cast<f32x4*>(lds + row * Lds<float>::stride + col) = x;
+template <int ROWS>
+__device__ __forceinline__ void stage_block(float* lds, const float* base, int r0, int Lr) {
+  constexpr int kPer = ROWS * 16 / 256;
+  static_assert(ROWS * 16 % 256 == 0, "rows must fill the workgroup");
+  f32x4 buf[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = i * 256 + threadIdx.x, row = c >> 4, col = (c & 15) * 4, t = r0 + row;
+    const int tc = min(max(t, 0), Lr - 1);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(base + (int64_t)tc * kD + col);
+    const bool ok = (t >= 0) & (t < Lr);
+    buf[i] = f32x4{ok ? x[0] : 0.f, ok ? x[1] : 0.f, ok ? x[2] : 0.f, ok ? x[3] : 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = i * 256 + threadIdx.x, row = c >> 4, col = (c & 15) * 4;
+    *reinterpret_cast<f32x4*>(lds + row * Lds<float>::stride + col) = buf[i];
   }
 }
 
@@ -146,7 +191,9 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   T* kw = reinterpret_cast<T*>(smem);
   float* cpart = reinterpret_cast<float*>(smem);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  // the wave index is uniform across the wave: keep it scalar so tile tests branch on SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t lb = xcd_logical_block(blockIdx.x, (int64_t)gridDim.x);
   const int64_t head = lb / a.nblk;
   const int blk = (int)(lb % a.nblk);
@@ -157,21 +204,29 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   const T* Kh = static_cast<const T*>(a.K) + head * (int64_t)Lr * kD;
   const int64_t vo = head * (int64_t)a.Lpad;
 
-  // 1. stage keys, finish the previous column update for the window
-  stage_block(kw, Kh, cb, kRows, Lr);
-  for (int c = threadIdx.x; c < kRows; c += blockDim.x) {
-    const int j = cb + c;
-    float v = 0.f;
-    if (j >= 0 && j < Lr) {
-      v = a.part_prev ? finish_column<T>(j, a.v_prev + vo, a.part_prev + head * (int64_t)a.nblk * a.pstride,
-                                         a.u_prev + vo, Qh, Kh, Lr, h, H16, a.nblk, a.pstride, a.c2)
-                      : a.v_prev[vo + j];
-      if (j >= b0 && j < b0 + 64) {
-        a.v_next[vo + j] = v;
-        if (a.save_v) a.save_v[head * a.save_v_stride + j] = v * kLn2;
+  // 1. stage keys, finish the previous column update for the window.  All global loads of the
+  //    block are in flight together: the key rows first, then the column partials.
+  constexpr int kNB = kRows / 64 + 1;   // blocks whose windows can hold one column
+  stage_block<kRows>(kw, Kh, cb, Lr);
+#pragma unroll
+  for (int pass = 0; pass < (kRows + 255) / 256; ++pass) {
+    const int c = pass * 256 + (int)threadIdx.x;
+    if (c < kRows) {
+      const int j = cb + c;
+      float v = 0.f;
+      if (j >= 0 && j < Lr) {
+        v = a.part_prev ? finish_column<T, kNB>(j, a.v_prev + vo,
+                                                 a.part_prev + head * (int64_t)a.nblk * a.pstride,
+                                                 a.u_prev + vo, Qh, Kh, Lr, h, H16, a.nblk,
+                                                 a.pstride, a.c2)
+                        : a.v_prev[vo + j];
+        if (j >= b0 && j < b0 + 64) {
+          a.v_next[vo + j] = v;
+          if (a.save_v) a.save_v[head * a.save_v_stride + j] = v * kLn2;
+        }
       }
+      vwin[c] = v;
     }
-    vwin[c] = v;
   }
   __syncthreads();
 
@@ -180,19 +235,37 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   const int cw = o0 - 16 * H16;        // first key of the wave window; LDS row offset 16 * wave
   Frag<T> fq;
   load_frag(fq, Qh + (int64_t)(o0 + n) * kD, o0 + n < Lr, g);
+  // Tile t covers keys cw + 16t .. cw + 16t + 15; over its entries i - j spans
+  // [16 H16 - 16 t - 15, 16 H16 - 16 t + 15].  Wave-uniform classes: "dead" tiles (no entry on the
+  // band or inside the sequence) skip the MFMA; "clean" tiles (every entry valid) skip the masks.
+  const bool rows_in = (o0 + 15 < Lr);
   float x[NT][4];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
+    const int j0 = cw + 16 * t;
+    const int dlo = 16 * H16 - 16 * t - 15, dhi = 16 * H16 - 16 * t + 15;
+    const bool dead = (dlo > h) | (dhi < -h) | (j0 >= Lr) | (j0 + 15 < 0) | (o0 >= Lr);
+    if (dead) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[t][r] = -INFINITY;
+      continue;
+    }
     Frag<T> fk;
     lds_frag(fk, kw, 16 * wave + 16 * t + n, g);
-    const f32x4 s = dot_tile(fq, fk);
-    const int j = cw + 16 * t + n;
+    const f32x4 sc = dot_tile(fq, fk);
     const float vj = vwin[16 * wave + 16 * t + n];
+    const bool clean = rows_in & (j0 >= 0) & (j0 + 15 < Lr) & (dhi <= h) & (dlo >= -h);
+    if (clean) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = o0 + 4 * g + r;
-      const bool ok = i < Lr && j >= 0 && j < Lr && abs(i - j) <= h;
-      x[t][r] = ok ? fmaf(s[r], a.c2, vj) : -INFINITY;
+      for (int r = 0; r < 4; ++r) x[t][r] = fmaf(sc[r], a.c2, vj);
+    } else {
+      const int j = j0 + n;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = o0 + 4 * g + r;
+        const bool ok = (i < Lr) & (j >= 0) & (j < Lr) & (abs(i - j) <= h);
+        x[t][r] = ok ? fmaf(sc[r], a.c2, vj) : -INFINITY;
+      }
     }
   }
   float m[4], l[4], rinv[4], u[4];
@@ -260,8 +333,8 @@ __global__ __launch_bounds__(256) void finish_columns_kernel(StepArgs a) {
   const T* Qh = static_cast<const T*>(a.Q) + head * (int64_t)a.Lr * kD;
   const T* Kh = static_cast<const T*>(a.K) + head * (int64_t)a.Lr * kD;
   const int64_t vo = head * (int64_t)a.Lpad;
-  const float v = finish_column<T>(j, a.v_prev + vo, a.part_prev + head * (int64_t)a.nblk * a.pstride,
-                                   a.u_prev + vo, Qh, Kh, a.Lr, a.h, H16, a.nblk, a.pstride, a.c2);
+  const float v = finish_column<T, 8>(j, a.v_prev + vo, a.part_prev + head * (int64_t)a.nblk * a.pstride,
+                                      a.u_prev + vo, Qh, Kh, a.Lr, a.h, H16, a.nblk, a.pstride, a.c2);
   a.v_next[vo + j] = v;
   if (a.save_v) a.save_v[head * a.save_v_stride + j] = v * kLn2;
 }
