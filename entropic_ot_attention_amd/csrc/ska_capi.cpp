@@ -99,8 +99,8 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
 }
 
 // Forward workspace, fused path (bands up to half-width 192): two column-dual and two row-dual
-// buffers [bh][Lpad] plus two column-partial buffers [bh][nblk][pstride]; split path (wider
-// bands): two dual buffers.  VJP: kVjpVecs vectors [bh][Lpad].  All O(bh L (1 + W/64)) floats.
+// buffers [bh][Lpad] plus two column-partial buffers [bh][nseg][64 seg_len + 32 H16] (about one
+// float per token); split path (wider bands): two dual buffers.  VJP: kVjpVecs vectors [bh][Lpad].  All O(bh L (1 + W/64)) floats.
 size_t workspace_for(const Plan& pl, ska_op op) {
   if (pl.empty) return 0;
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
@@ -108,8 +108,9 @@ size_t workspace_for(const Plan& pl, ska_op op) {
   if (vjp) return (size_t)(ska::kVjpVecs * vs) * sizeof(float);
   const int nt = ska::fused_tiles_for(pl.g.h);
   if (nt == 0) return (size_t)(ska::kFwdVecs * vs) * sizeof(float);
-  const int64_t nblk = (pl.g.Lr + 63) / 64;
-  const int64_t ps = pl.g.bh * nblk * ska::fused_pstride(nt);
+  int seg_len = 0, nseg = 0;
+  ska::fused_segments(pl.g.bh, pl.g.Lr, nt, &seg_len, &nseg);
+  const int64_t ps = pl.g.bh * (int64_t)nseg * ska::fused_pstride(nt, seg_len);
   return (size_t)(4 * vs + 2 * ps) * sizeof(float);
 }
 
@@ -160,8 +161,10 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
   if (nt > 0) {
     // fused path: one launch per full Sinkhorn step, column update finished by the next launch
     const int nblk = (g.Lr + 63) / 64;
-    const int pst = ska::fused_pstride(nt);
-    const int64_t ps = g.bh * (int64_t)nblk * pst;
+    int seg_len = 0, nseg = 0;
+    ska::fused_segments(g.bh, g.Lr, nt, &seg_len, &nseg);
+    const int pst = ska::fused_pstride(nt, seg_len);
+    const int64_t ps = g.bh * (int64_t)nseg * pst;
     float* vbuf[2] = {wsf, wsf + vs};
     float* ubuf[2] = {wsf + 2 * vs, wsf + 3 * vs};
     float* part[2] = {wsf + 4 * vs, wsf + 4 * vs + ps};
@@ -175,7 +178,10 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
     a.Lpad = g.Lpad;
     a.h = g.h;
     a.nblk = nblk;
+    a.seg_len = seg_len;
+    a.nseg = nseg;
     a.pstride = pst;
+    a.H16 = (nt - 1) / 2;
     a.c2 = g.c2;
     a.save_v_stride = dstride;
     a.save_u_stride = dstride;

@@ -53,15 +53,6 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __device__ __forceinline__ int floor_div(int a, int b) { return (a >= 0) ? a / b : -((-a + b - 1) / b); }
 
-// Map a launch-order block id to a logical (problem, row-block) index so that each of the 8
-// XCDs (which receive block ids round-robin) works on a contiguous run of row blocks: the key
-// windows of neighbouring blocks then overlap inside one XCD's L2.
-__device__ __forceinline__ int64_t xcd_logical_block(int64_t bid, int64_t nblocks) {
-  const int64_t q = nblocks / 8, rem = nblocks % 8;
-  const int64_t x = bid % 8, k = bid / 8;
-  return x * q + (x < rem ? x : rem) + k;
-}
-
 __device__ __forceinline__ float dot64(const bf16* a, const bf16* b) {
   float s = 0.f;
   for (int d = 0; d < kD; ++d) s = fmaf((float)a[d], (float)b[d], s);
@@ -90,37 +81,51 @@ __device__ float exact_column(int j, const float* u_h, const T* Qh, const T* Kh,
   return -(m + fast_log2(l));
 }
 
-// Blocks whose key window holds column j: windows are [64 b - 16 H16, 64 b + 64 + 16 H16).
-__device__ __forceinline__ int first_block_of(int j, int H16) {
-  return max(0, floor_div(j - 16 * H16 - 63, 64));
-}
-
-// Finished column dual (log2 units) of key j given the previous dual and the per-block column
-// sums of exp(S + u + v_prev), summed in ascending block order.
-template <typename T, int NB>
-__device__ float finish_column(int j, const float* vprev_h, const float* part_h, const float* u_h,
-                               const T* Qh, const T* Kh, int Lr, int h, int H16, int nblk,
-                               int pstride, float c2) {
-  const int lo = first_block_of(j, H16);
-  const int hi = min(nblk - 1, floor_div(j + 16 * H16, 64));
-  float p[NB];
+// Finished column dual (log2 units) of key j from the previous dual and the column sums of
+// exp(S + u + v_prev) that the previous launch left per segment.  Segment k of a problem covers
+// columns [S k - 16 H16, S (k + 1) + 16 H16) with S = 64 seg_len, so at most two segments hold a
+// partial for j (seg_len >= H16 / 2); they are added in ascending segment order.
+// Loads of the column finish for key j: the (at most two) segment partials and the previous dual.
+struct ColIn {
+  float p0, p1, vp;
+};
+__device__ __forceinline__ ColIn column_loads(int j, const float* vprev_h, const float* part_h,
+                                              const StepArgs& a) {
+  const int S = 64 * a.seg_len, halo = 16 * a.H16;
+  const int jc = min(max(j, 0), a.Lr - 1);
+  const int k0 = max(0, floor_div(jc - halo, S));
+  const int k1 = min(a.nseg - 1, floor_div(jc + halo, S));
+  float p[2];
 #pragma unroll
-  for (int q = 0; q < NB; ++q) {
-    const int b = lo + q, c = j - (b * 64 - 16 * H16);
-    const bool ok = (b <= hi) & (c >= 0) & (c < pstride);
-    const int bc = min(b, nblk - 1), cc = min(max(c, 0), pstride - 1);
-    const float x = part_h[(int64_t)bc * pstride + cc];
+  for (int q = 0; q < 2; ++q) {
+    const int k = k0 + q, c = jc - (S * k - halo);
+    const bool ok = (k <= k1) & (c >= 0) & (c < a.pstride);
+    const int kc = min(k, a.nseg - 1), cc = min(max(c, 0), a.pstride - 1);
+    const float x = part_h[(int64_t)kc * a.pstride + cc];
     p[q] = ok ? x : 0.f;
   }
-  const float vp = vprev_h[j];
-  float s = 0.f;
-#pragma unroll
-  for (int q = 0; q < NB; ++q) s += p[q];
-  if (s >= 0x1p-100f) return vp - fast_log2(s);
-  return exact_column<T>(j, u_h, Qh, Kh, Lr, h, c2);
+  return ColIn{p[0], p[1], vprev_h[jc]};
 }
 
-// B-operand fragment of key row `row` of the staged window (LDS), d-slice of lane group g.
+// Finished column dual (log2 units) of key j from the previous dual and the column sums of
+// exp(S + u + v_prev) that the previous launch left per segment.  Segment k of a problem covers
+// columns [S k - 16 H16, S (k + 1) + 16 H16) with S = 64 seg_len, so at most two segments hold a
+// partial for j (seg_len >= H16 / 2); they are added in ascending segment order.
+template <typename T>
+__device__ __forceinline__ float column_combine(int j, const ColIn& in, const float* u_h, const T* Qh,
+                                                const T* Kh, const StepArgs& a) {
+  const float s = in.p0 + in.p1;
+  if (s >= 0x1p-100f) return in.vp - fast_log2(s);
+  return exact_column<T>(j, u_h, Qh, Kh, a.Lr, a.h, a.c2);
+}
+
+template <typename T>
+__device__ float finish_column(int j, const float* vprev_h, const float* part_h, const float* u_h,
+                               const T* Qh, const T* Kh, const StepArgs& a) {
+  return column_combine<T>(j, column_loads(j, vprev_h, part_h, a), u_h, Qh, Kh, a);
+}
+
+// B-operand fragment of key row `row` of the staged keys (LDS), d-slice of lane group g.
 __device__ __forceinline__ void lds_frag(Frag<bf16>& f, const bf16* kw, int row, int g) {
   const uint4* p = reinterpret_cast<const uint4*>(kw + row * Lds<bf16>::stride + 16 * g);
   f.a = __builtin_bit_cast(bf16x8, p[0]);
@@ -132,18 +137,18 @@ __device__ __forceinline__ void lds_frag(Frag<float>& f, const float* kw, int ro
   for (int i = 0; i < 4; ++i) f.v[i] = p[i];
 }
 
-// Stage ROWS key rows starting at token r0 (zeros outside [0, Lr)) into LDS, whole workgroup
-// of 256 threads: every thread issues all of its 16-byte loads before its first LDS store, so the
-// loads overlap instead of each paying the full memory latency.
-template <int ROWS>
-__device__ __forceinline__ void stage_block(bf16* lds, const bf16* base, int r0, int Lr) {
+// Copy `rows` consecutive key rows starting at token r0 into the LDS ring (row t lives at ring
+// row t mod RING); rows outside [0, Lr) are zero.  Whole workgroup of 256 threads; all loads are
+// issued before the first store.
+template <int ROWS, int RING>
+__device__ __forceinline__ void ring_store_rows(bf16* ring, const bf16* base, int r0, int Lr) {
   constexpr int kPer = ROWS * 8 / 256;
   static_assert(ROWS * 8 % 256 == 0, "rows must fill the workgroup");
   uint4 buf[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8, t = r0 + row;
-    const int tc = min(max(t, 0), Lr - 1);          // always a valid row; zeroed below if outside
+    const int tc = min(max(t, 0), Lr - 1);
     const uint4 x = *reinterpret_cast<const uint4*>(base + (int64_t)tc * kD + col);
     const bool ok = (t >= 0) & (t < Lr);
     buf[i] = uint4{ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u};
@@ -151,11 +156,12 @@ __device__ __forceinline__ void stage_block(bf16* lds, const bf16* base, int r0,
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8;
-    *reinterpret_cast<uint4*>(lds + row * Lds<bf16>::stride + col) = buf[i];
+    const int rr = (r0 + row + 4 * RING) % RING;
+    *reinterpret_cast<uint4*>(ring + rr * Lds<bf16>::stride + col) = buf[i];
   }
 }
-template <int ROWS>
-__device__ __forceinline__ void stage_block(float* lds, const float* base, int r0, int Lr) {
+template <int ROWS, int RING>
+__device__ __forceinline__ void ring_store_rows(float* ring, const float* base, int r0, int Lr) {
   constexpr int kPer = ROWS * 16 / 256;
   static_assert(ROWS * 16 % 256 == 0, "rows must fill the workgroup");
   f32x4 buf[kPer];
@@ -170,156 +176,296 @@ __device__ __forceinline__ void stage_block(float* lds, const float* base, int r
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int c = i * 256 + threadIdx.x, row = c >> 4, col = (c & 15) * 4;
-    *reinterpret_cast<f32x4*>(lds + row * Lds<float>::stride + col) = buf[i];
+    const int rr = (r0 + row + 4 * RING) % RING;
+    *reinterpret_cast<f32x4*>(ring + rr * Lds<float>::stride + col) = buf[i];
   }
 }
 
-template <typename T, int NT>
-struct StepSmem {
-  static constexpr int kRows = 64 + 16 * (NT - 1);           // block key window (64 + 32 H16)
-  static constexpr int kKwinBytes = kRows * Lds<T>::stride * (int)sizeof(T);
-  static constexpr int kPartBytes = 16 * 16 * NT * 4;        // [wave][group][16 NT] floats
-  static constexpr int kBytes = kKwinBytes > kPartBytes ? kKwinBytes : kPartBytes;
+// The 64 key rows one block adds to the ring, held in registers between load and store.
+template <typename T> struct NewRows;
+template <> struct NewRows<bf16> {
+  uint4 x[2];
+  __device__ void load(const bf16* base, int r0, int Lr) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8, t = r0 + row;
+      const int tc = min(max(t, 0), Lr - 1);
+      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)tc * kD + col);
+      const bool ok = (t >= 0) & (t < Lr);
+      x[i] = uint4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
+    }
+  }
+  template <int RING>
+  __device__ void store(bf16* ring, int r0) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8;
+      const int rr = (r0 + row + 4 * RING) % RING;
+      *reinterpret_cast<uint4*>(ring + rr * Lds<bf16>::stride + col) = x[i];
+    }
+  }
+};
+template <> struct NewRows<float> {
+  f32x4 x[4];
+  __device__ void load(const float* base, int r0, int Lr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = i * 256 + threadIdx.x, row = c >> 4, col = (c & 15) * 4, t = r0 + row;
+      const int tc = min(max(t, 0), Lr - 1);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(base + (int64_t)tc * kD + col);
+      const bool ok = (t >= 0) & (t < Lr);
+      x[i] = f32x4{ok ? v[0] : 0.f, ok ? v[1] : 0.f, ok ? v[2] : 0.f, ok ? v[3] : 0.f};
+    }
+  }
+  template <int RING>
+  __device__ void store(float* ring, int r0) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = i * 256 + threadIdx.x, row = c >> 4, col = (c & 15) * 4;
+      const int rr = (r0 + row + 4 * RING) % RING;
+      *reinterpret_cast<f32x4*>(ring + rr * Lds<float>::stride + col) = x[i];
+    }
+  }
 };
 
 template <typename T, int NT>
+struct StepSmem {
+  static constexpr int kH16 = (NT - 1) / 2;
+  static constexpr int kRing = 64 + 32 * kH16;               // block key window = ring rows
+  static constexpr int kRingBytes = kRing * Lds<T>::stride * (int)sizeof(T);
+};
+
+// One full Sinkhorn step for one segment of consecutive 64-row blocks of one problem.
+template <typename T, int NT>
 __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   constexpr int H16 = (NT - 1) / 2;
-  constexpr int kRows = StepSmem<T, NT>::kRows;
-  __shared__ __attribute__((aligned(16))) char smem[StepSmem<T, NT>::kBytes];
-  __shared__ float vwin[kRows];
-  T* kw = reinterpret_cast<T*>(smem);
-  float* cpart = reinterpret_cast<float*>(smem);
+  constexpr int RING = StepSmem<T, NT>::kRing;
+  static_assert(H16 % 2 == 0, "ring rows must be a multiple of 64");
+  __shared__ __attribute__((aligned(16))) T kring[RING * Lds<T>::stride];
+  __shared__ float vring[RING];            // finished column duals, by key mod RING
+  __shared__ float pring[RING];            // this segment's column sums, by key mod RING
+  __shared__ float cpart[kWaves * RING];          // [wave][RING] block column sums
 
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  // the wave index is uniform across the wave: keep it scalar so tile tests branch on SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t lb = xcd_logical_block(blockIdx.x, (int64_t)gridDim.x);
-  const int64_t head = lb / a.nblk;
-  const int blk = (int)(lb % a.nblk);
-  const int b0 = blk * 64;
-  const int cb = b0 - 16 * H16;                 // first key of the block window
+  const int64_t head = blockIdx.x / a.nseg;
+  const int seg = blockIdx.x % a.nseg;
+  const int blk0 = seg * a.seg_len, blk1 = min(blk0 + a.seg_len, a.nblk);
+  const int c_lo = 64 * blk0 - 16 * H16;    // first column this segment touches
+  const int own_lo = 64 * blk0, own_hi = 64 * blk1;
   const int Lr = a.Lr, h = a.h;
   const T* Qh = static_cast<const T*>(a.Q) + head * (int64_t)Lr * kD;
   const T* Kh = static_cast<const T*>(a.K) + head * (int64_t)Lr * kD;
   const int64_t vo = head * (int64_t)a.Lpad;
+  const float* part_prev_h = a.part_prev ? a.part_prev + head * (int64_t)a.nseg * a.pstride : nullptr;
+  float* part_out_h = a.part_out + (head * (int64_t)a.nseg + seg) * a.pstride;
 
-  // 1. stage keys, finish the previous column update for the window.  All global loads of the
-  //    block are in flight together: the key rows first, then the column partials.
-  constexpr int kNB = kRows / 64 + 1;   // blocks whose windows can hold one column
-  stage_block<kRows>(kw, Kh, cb, Lr);
+  // finished column dual of key j (log2 units) from its loads, and its owner-side copies
+  auto finish_from = [&](int j, const ColIn& in) -> float {
+    if (j < 0 || j >= Lr) return 0.f;
+    const float v = part_prev_h ? column_combine<T>(j, in, a.u_prev + vo, Qh, Kh, a) : in.vp;
+    if (j >= own_lo && j < own_hi) {
+      a.v_next[vo + j] = v;
+      if (a.save_v) a.save_v[head * a.save_v_stride + j] = v * kLn2;
+    }
+    return v;
+  };
+  auto loads_for = [&](int j) -> ColIn {
+    if (part_prev_h) return column_loads(j, a.v_prev + vo, part_prev_h, a);
+    return ColIn{0.f, 0.f, a.v_prev[vo + min(max(j, 0), Lr - 1)]};
+  };
+
+  const bool exact_h = (h == 16 * H16);
+  // per-wave column sums live at columns [16 wave, 16 wave + 16 NT) of a RING-wide row; the
+  // other columns stay zero so the block sum below needs no coverage tests
+  for (int c = threadIdx.x; c < kWaves * RING; c += 256) cpart[c] = 0.f;
+
+  // prologue: the first block's whole window and query fragment
+  Frag<T> fq;
+  load_frag(fq, Qh + (int64_t)(64 * blk0 + 16 * wave + n) * kD, 64 * blk0 + 16 * wave + n < Lr, g);
+  ring_store_rows<RING, RING>(kring, Kh, c_lo, Lr);
+  for (int c = threadIdx.x; c < RING; c += 256) {
+    const int j = c_lo + c;
+    vring[(j + 4 * RING) % RING] = finish_from(j, loads_for(j));
+    pring[c] = 0.f;
+  }
+  __syncthreads();
+
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const int b0 = 64 * blk;
+    const int cb = b0 - 16 * H16;             // block window [cb, cb + RING)
+    const bool more = blk + 1 < blk1;
+    // prefetch the 64 key rows the next block adds: [cb + RING, cb + RING + 64)
+    // (and the next block's query fragment and new column loads), all in flight during compute
+    NewRows<T> nr;
+    ColIn nc{0.f, 0.f, 0.f};
+    Frag<T> fq_next;
+    if (more) {
+      nr.load(Kh, cb + RING, Lr);
+      const int on = b0 + 64 + 16 * wave + n;
+      load_frag(fq_next, Qh + (int64_t)on * kD, on < Lr, g);
+      if (threadIdx.x < 64) nc = loads_for(cb + RING + (int)threadIdx.x);
+    }
+
+    // score strip in registers (wave rows o0 .. o0 + 15), exact row log-sum-exp
+    const int o0 = b0 + 16 * wave;
+    const int cw = o0 - 16 * H16;
+    const bool rows_in = (o0 + 15 < Lr);
+    // Tile t covers keys cw + 16t .. cw + 16t + 15; over its entries i - j spans
+    // [16 H16 - 16 t - 15, 16 H16 - 16 t + 15].  Wave-uniform classes: "dead" tiles (no entry on
+    // the band or inside the sequence) skip the MFMA; "clean" tiles skip the per-entry masks.
+    // All MFMAs are issued first, each into its own accumulator, so LDS reads and matrix-core
+    // latency overlap across tiles; the vector pass follows.
+    auto dead_tile = [&](int t) -> bool {
+      const int j0 = cw + 16 * t;
+      const int dlo = 16 * H16 - 16 * t - 15, dhi = 16 * H16 - 16 * t + 15;
+      return (dlo > h) | (dhi < -h) | (j0 >= Lr) | (j0 + 15 < 0) | (o0 >= Lr);
+    };
+    auto tile_row = [&](int t) -> int { return (cw + 16 * t + 4 * RING) % RING; };  // no straddling
+    // x = log2(e) S + v_j on the band, -inf elsewhere (in place on the MFMA result)
+    auto transform = [&](f32x4& xt, int t, float vjt) {
+      const int j0 = cw + 16 * t;
+      const int dlo = 16 * H16 - 16 * t - 15, dhi = 16 * H16 - 16 * t + 15;
+      const bool clean = rows_in & (j0 >= 0) & (j0 + 15 < Lr) & (dhi <= h) & (dlo >= -h);
+      if (clean) {
 #pragma unroll
-  for (int pass = 0; pass < (kRows + 255) / 256; ++pass) {
-    const int c = pass * 256 + (int)threadIdx.x;
-    if (c < kRows) {
-      const int j = cb + c;
-      float v = 0.f;
-      if (j >= 0 && j < Lr) {
-        v = a.part_prev ? finish_column<T, kNB>(j, a.v_prev + vo,
-                                                 a.part_prev + head * (int64_t)a.nblk * a.pstride,
-                                                 a.u_prev + vo, Qh, Kh, Lr, h, H16, a.nblk,
-                                                 a.pstride, a.c2)
-                        : a.v_prev[vo + j];
-        if (j >= b0 && j < b0 + 64) {
-          a.v_next[vo + j] = v;
-          if (a.save_v) a.save_v[head * a.save_v_stride + j] = v * kLn2;
+        for (int r = 0; r < 4; ++r) xt[r] = fmaf(xt[r], a.c2, vjt);
+      } else {
+        const int j = j0 + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = o0 + 4 * g + r;
+          const bool ok = (i < Lr) & (j >= 0) & (j < Lr) & (abs(i - j) <= h);
+          xt[r] = ok ? fmaf(xt[r], a.c2, vjt) : -INFINITY;
         }
       }
-      vwin[c] = v;
-    }
-  }
-  __syncthreads();
-
-  // 2. score strip in registers, exact row log-sum-exp
-  const int o0 = b0 + 16 * wave;       // owned rows o0 .. o0 + 15 (rows 4g + r in this lane)
-  const int cw = o0 - 16 * H16;        // first key of the wave window; LDS row offset 16 * wave
-  Frag<T> fq;
-  load_frag(fq, Qh + (int64_t)(o0 + n) * kD, o0 + n < Lr, g);
-  // Tile t covers keys cw + 16t .. cw + 16t + 15; over its entries i - j spans
-  // [16 H16 - 16 t - 15, 16 H16 - 16 t + 15].  Wave-uniform classes: "dead" tiles (no entry on the
-  // band or inside the sequence) skip the MFMA; "clean" tiles (every entry valid) skip the masks.
-  const bool rows_in = (o0 + 15 < Lr);
-  float x[NT][4];
+    };
+    f32x4 x[NT];
+    // Interior blocks of a band whose half-width fills its halo class (h = 16 H16): every tile is
+    // on the band and inside the sequence; only the first and last tiles cross the band edge,
+    // along a fixed per-lane pattern (i - j <= h  <=>  4g + r <= n on tile 0, i - j >= -h  <=>
+    // 4g + r >= n on tile NT - 1).  No per-tile tests.
+    const bool interior = exact_h & (cb >= 0) & (cb + RING <= Lr) & (b0 + 64 <= Lr);
+    if (interior) {
+      int row = (cw + 4 * RING) % RING;
+      Frag<T> fk[2];
+      lds_frag(fk[0], kring, row + n, g);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int j0 = cw + 16 * t;
-    const int dlo = 16 * H16 - 16 * t - 15, dhi = 16 * H16 - 16 * t + 15;
-    const bool dead = (dlo > h) | (dhi < -h) | (j0 >= Lr) | (j0 + 15 < 0) | (o0 >= Lr);
-    if (dead) {
+      for (int t = 0; t < NT; ++t) {
+        const int rnext = (row + 16 >= RING) ? row + 16 - RING : row + 16;
+        if (t + 1 < NT) lds_frag(fk[(t + 1) & 1], kring, rnext + n, g);
+        const float vjt = vring[row + n];
+        x[t] = dot_tile(fq, fk[t & 1]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[t][r] = -INFINITY;
-      continue;
-    }
-    Frag<T> fk;
-    lds_frag(fk, kw, 16 * wave + 16 * t + n, g);
-    const f32x4 sc = dot_tile(fq, fk);
-    const float vj = vwin[16 * wave + 16 * t + n];
-    const bool clean = rows_in & (j0 >= 0) & (j0 + 15 < Lr) & (dhi <= h) & (dlo >= -h);
-    if (clean) {
+        for (int r = 0; r < 4; ++r) x[t][r] = fmaf(x[t][r], a.c2, vjt);
+        if (t == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[t][r] = fmaf(sc[r], a.c2, vj);
+          for (int r = 0; r < 4; ++r) x[0][r] = (4 * g + r <= n) ? x[0][r] : -INFINITY;
+        }
+        if (t == NT - 1) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[t][r] = (4 * g + r >= n) ? x[t][r] : -INFINITY;
+        }
+        row = rnext;
+      }
     } else {
-      const int j = j0 + n;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = o0 + 4 * g + r;
-        const bool ok = (i < Lr) & (j >= 0) & (j < Lr) & (abs(i - j) <= h);
-        x[t][r] = ok ? fmaf(sc[r], a.c2, vj) : -INFINITY;
+      for (int t = 0; t < NT; ++t) {
+        if (dead_tile(t)) {
+          x[t] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          continue;
+        }
+        Frag<T> fk;
+        lds_frag(fk, kring, tile_row(t) + n, g);
+        const float vjt = vring[tile_row(t) + n];
+        x[t] = dot_tile(fq, fk);
+        transform(x[t], t, vjt);
       }
     }
-  }
-  float m[4], l[4], rinv[4], u[4];
+    float m[4], rinv[4], u[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float mm = x[0][r];
+    for (int r = 0; r < 4; ++r) {
+      float mm = x[0][r];
 #pragma unroll
-    for (int t = 1; t < NT; ++t) mm = fmaxf(mm, x[t][r]);
-    m[r] = row16_max(mm);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float ms = (m[r] == -INFINITY) ? 0.f : m[r];
-    float ll = 0.f;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      x[t][r] = fast_exp2(x[t][r] - ms);
-      ll += x[t][r];
+      for (int t = 1; t < NT; ++t) mm = fmaxf(mm, x[t][r]);
+      m[r] = row16_max(mm);
     }
-    l[r] = row16_sum(ll);
-    const bool empty = (m[r] == -INFINITY);
-    u[r] = empty ? 0.f : -(m[r] + fast_log2(l[r]));
-    rinv[r] = empty ? 0.f : __builtin_amdgcn_rcpf(l[r]);
-  }
-  if (n < 4) {
-    const int i = o0 + 4 * g + n;
-    const float ui = (n == 0) ? u[0] : (n == 1) ? u[1] : (n == 2) ? u[2] : u[3];
-    if (i < Lr) {
-      a.u_out[vo + i] = ui;
-      if (a.save_u) a.save_u[head * a.save_u_stride + i] = ui * kLn2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ms = (m[r] == -INFINITY) ? 0.f : m[r];
+      float ll = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        x[t][r] = fast_exp2(x[t][r] - ms);
+        ll += x[t][r];
+      }
+      const float l = row16_sum(ll);
+      const bool empty = (m[r] == -INFINITY);
+      u[r] = empty ? 0.f : -(m[r] + fast_log2(l));
+      rinv[r] = empty ? 0.f : __builtin_amdgcn_rcpf(l);
     }
-  }
-
-  // 3. column sums of the new plan over the owned rows
-  float cp[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-    cp[t] = x[t][0] * rinv[0] + x[t][1] * rinv[1] + x[t][2] * rinv[2] + x[t][3] * rinv[3];
-  __syncthreads();                     // every wave is done with the staged keys
-#pragma unroll
-  for (int t = 0; t < NT; ++t) cpart[(wave * 4 + g) * (16 * NT) + 16 * t + n] = cp[t];
-  __syncthreads();
-  float* pout = a.part_out + (head * (int64_t)a.nblk + blk) * a.pstride;
-  for (int c = threadIdx.x; c < a.pstride; c += blockDim.x) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int cc = c - 16 * w;
-      if (cc >= 0 && cc < 16 * NT) {
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) s += cpart[(w * 4 + gg) * (16 * NT) + cc];
+    if (n < 4) {
+      const int i = o0 + 4 * g + n;
+      const float ui = (n == 0) ? u[0] : (n == 1) ? u[1] : (n == 2) ? u[2] : u[3];
+      if (i < Lr) {
+        a.u_out[vo + i] = ui;
+        if (a.save_u) a.save_u[head * a.save_u_stride + i] = ui * kLn2;
       }
     }
-    pout[c] = s;
+    // column sums of the new plan over the wave's 16 rows: in-lane over the 4 rows, then over the
+    // four lane groups (lanes n, n + 16, n + 32, n + 48 hold the same key).  gfx950 lane swaps
+    // reduce four tiles at once: v_permlane32_swap(cp_a, cp_b) leaves a's and b's half sums in the
+    // low and high 32 lanes, v_permlane16_swap of two such pairs leaves the full sums of tiles
+    // a, c, b, d in lane groups 0..3; each lane then stores one tile's sum for its key.
+    float cp[NT + 3];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      cp[t] = x[t][0] * rinv[0] + x[t][1] * rinv[1] + x[t][2] * rinv[2] + x[t][3] * rinv[3];
+#pragma unroll
+    for (int t = NT; t < NT + 3; ++t) cp[t] = 0.f;
+    auto swap32 = [](float a, float b) {
+      const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+      return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    };
+    auto swap16 = [](float a, float b) {
+      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+      return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    };
+    // lane group g of a reduced quad (tiles q, q+1, q+2, q+3) holds tile q + {0, 2, 1, 3}[g]
+    const int gsel = (g == 1) ? 2 : (g == 2) ? 1 : g;
+#pragma unroll
+    for (int q = 0; q < NT; q += 4) {
+      const float ab = swap32(cp[q], cp[q + 1]);
+      const float cd = swap32(cp[q + 2], cp[q + 3]);
+      const float s4 = swap16(ab, cd);
+      const int t = q + gsel;
+      if (t < NT) cpart[wave * RING + 16 * wave + 16 * t + n] = s4;
+    }
+    __syncthreads();
+    // block column sums (fixed wave order) into the segment accumulator
+    for (int c = threadIdx.x; c < RING; c += 256) {
+      const float sacc = ((cpart[c] + cpart[RING + c]) + cpart[2 * RING + c]) + cpart[3 * RING + c];
+      pring[(cb + c + 4 * RING) % RING] += sacc;
+    }
+    __syncthreads();
+    if (more) {
+      // columns [cb, cb + 64) leave the window: write them out, then reuse their ring slots
+      // for the next block's new keys [cb + RING, cb + RING + 64)
+      if (threadIdx.x < 64) {
+        const int j = cb + threadIdx.x, slot = (j + 4 * RING) % RING;
+        part_out_h[j - c_lo] = pring[slot];
+        pring[slot] = 0.f;
+        vring[slot] = finish_from(j + RING, nc);
+      }
+      nr.template store<RING>(kring, cb + RING);
+      fq = fq_next;
+      __syncthreads();
+    } else {
+      for (int c = threadIdx.x; c < RING; c += 256) {
+        const int j = cb + c;
+        part_out_h[j - c_lo] = pring[(j + 4 * RING) % RING];
+      }
+    }
   }
 }
 
@@ -329,28 +475,41 @@ __global__ __launch_bounds__(256) void finish_columns_kernel(StepArgs a) {
   const int64_t head = blockIdx.y;
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= a.Lr) return;
-  const int H16 = (a.pstride - 64) / 32;
   const T* Qh = static_cast<const T*>(a.Q) + head * (int64_t)a.Lr * kD;
   const T* Kh = static_cast<const T*>(a.K) + head * (int64_t)a.Lr * kD;
   const int64_t vo = head * (int64_t)a.Lpad;
-  const float v = finish_column<T, 8>(j, a.v_prev + vo, a.part_prev + head * (int64_t)a.nblk * a.pstride,
-                                      a.u_prev + vo, Qh, Kh, a.Lr, a.h, H16, a.nblk, a.pstride, a.c2);
+  const float v = finish_column<T>(j, a.v_prev + vo, a.part_prev + head * (int64_t)a.nseg * a.pstride,
+                                   a.u_prev + vo, Qh, Kh, a);
   a.v_next[vo + j] = v;
   if (a.save_v) a.save_v[head * a.save_v_stride + j] = v * kLn2;
 }
 
 int fused_tiles_for(int h) {
-  const int nt = 1 + 2 * ((h + 15) / 16);
-  if (nt <= 5) return 5;
-  if (nt <= 9) return 9;
-  if (nt <= 17) return 17;
-  if (nt <= 25) return 25;
+  const int h16 = (h + 15) / 16;     // halo tiles; classes use an even count
+  if (h16 <= 2) return 5;
+  if (h16 <= 4) return 9;
+  if (h16 <= 8) return 17;
+  if (h16 <= 12) return 25;
   return 0;
+}
+
+// Segments: enough workgroups to fill the GPU about once (256 CUs x 3 resident workgroups),
+// and at least H16 / 2 blocks each so a column's partials come from at most two segments.
+void fused_segments(int64_t bh, int Lr, int nt, int* seg_len, int* nseg) {
+  const int64_t nblk = (Lr + 63) / 64;
+  const int64_t target = 768;
+  int64_t sl = (bh * nblk + target - 1) / target;
+  const int64_t min_sl = ((nt - 1) / 2 + 1) / 2;
+  if (sl < min_sl) sl = min_sl;
+  if (sl < 1) sl = 1;
+  if (sl > nblk) sl = nblk;
+  *seg_len = (int)sl;
+  *nseg = (int)((nblk + sl - 1) / sl);
 }
 
 template <typename T, int NT>
 static void launch_step_t(const StepArgs& a, hipStream_t st) {
-  const unsigned blocks = (unsigned)(a.bh * (int64_t)a.nblk);
+  const unsigned blocks = (unsigned)(a.bh * (int64_t)a.nseg);
   sinkhorn_step_kernel<T, NT><<<dim3(blocks), dim3(256), 0, st>>>(a);
 }
 

@@ -39,7 +39,9 @@ struct Geometry {
 };
 
 // Arguments of one fused Sinkhorn step launch (see ska_fused.hip).  Vectors are [bh][Lpad] fp32
-// in log2 units; column partials are [bh][nblk][pstride] fp32.
+// in log2 units.  A launch splits each problem's 64-row blocks into segments of seg_len
+// consecutive blocks, one workgroup per segment; column partial sums are stored per segment,
+// [bh][nseg][pstride] fp32 with pstride = 64 seg_len + 32 H16 (H16 = band halo in 16-key tiles).
 struct StepArgs {
   const void* Q;
   const void* K;
@@ -54,14 +56,16 @@ struct StepArgs {
   float* save_u;
   int64_t save_u_stride;
   int64_t bh;
-  int Lr, Lpad, h, nblk, pstride;
+  int Lr, Lpad, h, nblk, seg_len, nseg, pstride, H16;
   float c2;
 };
 
-// Register-resident step width (16-key tiles per wave) for half-width h, or 0 when the band is
-// too wide for the fused step (the split row/column kernels handle it).
+// Register-resident step width (16-key tiles per wave, 1 + 2 H16 with H16 even) for half-width h,
+// or 0 when the band is too wide for the fused step (the split row/column kernels handle it).
 int fused_tiles_for(int h);
-inline int fused_pstride(int nt) { return 64 + 16 * (nt - 1); }
+// Segment geometry of the fused step for a problem: blocks per segment and segments per problem.
+void fused_segments(int64_t bh, int Lr, int nt, int* seg_len, int* nseg);
+inline int fused_pstride(int nt, int seg_len) { return 64 * seg_len + 16 * (nt - 1); }
 
 enum TimedKernel : int { kTimedStep = 0, kTimedOut = 1, kTimedVjp = 2, kTimedKinds = 3 };
 

@@ -76,13 +76,17 @@ def _ws_bytes(prob, op):
 
 def _fused_fwd_bytes(bh, L, W):
     """Forward workspace of the register-resident path: 4 dual vectors [bh][Lpad] and two
-    column-partial buffers [bh][ceil(L/64)][64 + 32 * H16] (H16 = tiles of the band halo)."""
+    column-partial buffers [bh][nseg][64 seg_len + 32 H16]; segments of seg_len 64-row blocks
+    sized for about 768 workgroups, at least H16 / 2 blocks (H16 = even halo tile count)."""
     Lpad = -(-L // 64) * 64
     h = min(W // 2, L)
-    nt = 1 + 2 * (-(-h // 16))
-    nt = next(c for c in (5, 9, 17, 25) if nt <= c)
-    pst = 64 + 16 * (nt - 1)
-    return (4 * bh * Lpad + 2 * bh * (-(-L // 64)) * pst) * 4
+    h16 = -(-h // 16)
+    H16 = next(c for c in (2, 4, 8, 12) if h16 <= c)
+    nblk = -(-L // 64)
+    sl = min(max(-(-bh * nblk // 768), (H16 + 1) // 2, 1), nblk)
+    nseg = -(-nblk // sl)
+    pst = 64 * sl + 32 * H16
+    return (4 * bh * Lpad + 2 * bh * nseg * pst) * 4
 
 
 def test_workspace_sizes():
@@ -93,7 +97,7 @@ def test_workspace_sizes():
         assert st == 0 and n == 14 * 3 * Lpad * 4
     st, n = _ws_bytes(_prob(L=262144, bh=4, W=256), B.SKA_OP_FWD)
     assert st == 0 and n == _fused_fwd_bytes(4, 262144, 256)
-    assert n < 30 * 4 * 262144 * 4          # O(L): under 30 floats per token and head
+    assert n < 8 * 4 * 262144 * 4           # O(L): under 8 floats per token and head
     # bands wider than the register-resident step use the split path: two dual vectors
     st, n = _ws_bytes(_prob(L=2000, bh=2, W=1000), B.SKA_OP_FWD)
     assert st == 0 and n == 2 * 2 * 2048 * 4
