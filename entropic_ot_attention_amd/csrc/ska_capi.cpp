@@ -105,7 +105,19 @@ size_t workspace_for(const Plan& pl, ska_op op) {
   if (pl.empty) return 0;
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   const int64_t vs = pl.g.bh * (int64_t)pl.g.Lpad;
-  if (vjp) return (size_t)(ska::kVjpVecs * vs) * sizeof(float);
+  if (vjp) {
+    // streaming passes (one-reference schedule, bands LDS holds) add dv1 column partials; the
+    // workspace covers both schedules
+    int nt = 0;
+    const int nw = ska::vjp_stream_waves(pl.elt, pl.g.h, &nt);
+    int64_t part = 0;
+    if (nw > 0) {
+      int seg_len = 0, nseg = 0;
+      ska::vjp_stream_segments(pl.g.bh, pl.g.Lr, nw, nt, &seg_len, &nseg);
+      part = pl.g.bh * (int64_t)nseg * (16 * nw * seg_len + 16 * (nt - 1));
+    }
+    return (size_t)(ska::kVjpVecs * vs + part) * sizeof(float);
+  }
   const int nt = ska::fused_tiles_for(pl.g.h);
   if (nt == 0) return (size_t)(ska::kFwdVecs * vs) * sizeof(float);
   int seg_len = 0, nseg = 0;
@@ -261,6 +273,35 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
   const bool d4 = (sched == SKA_DIRECT_FOUR);
   hipError_t e = ska::launch_vjp_prep(duals, ws, g, st);
   if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+  int nt = 0;
+  const int nw = d4 ? 0 : ska::vjp_stream_waves(pl.elt, g.h, &nt);
+  if (nw > 0) {
+    // streaming passes: dv2 (owns keys), du2 + dv1 column sums (owns queries), du1 + dQ (owns
+    // queries), dK + dV (owns keys)
+    ska::VjpArgs a{};
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.dO = dO;
+    a.ws = ws;
+    a.vec_stride = g.bh * (int64_t)g.Lpad;
+    a.part = ws + ska::kVjpVecs * a.vec_stride;
+    a.bh = g.bh;
+    a.Lr = g.Lr;
+    a.Lpad = g.Lpad;
+    a.h = g.h;
+    a.nblk = (g.Lr + 16 * nw - 1) / (16 * nw);
+    ska::vjp_stream_segments(g.bh, g.Lr, nw, nt, &a.seg_len, &a.nseg);
+    a.pstride = 16 * nw * a.seg_len + 16 * (nt - 1);
+    a.c2 = g.c2;
+    a.s = g.s;
+    for (int pass = 1; pass <= 4; ++pass) {
+      a.out0 = (pass == 3) ? dQ : dK;
+      a.out1 = dV;
+      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_pass(pl.elt, nt, nw, pass, a, st));
+    }
+    return SKA_OK;
+  }
   SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 0, d4, Q, K, V, dO, dV, ws, g, st));
   SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 1, d4, Q, K, V, dO, nullptr, ws, g, st));
   SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 2, d4, Q, K, V, dO, nullptr, ws, g, st));

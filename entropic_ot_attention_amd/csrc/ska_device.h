@@ -224,4 +224,88 @@ __device__ __forceinline__ bool in_band(int w, int o, int h, int Lr) {
 __device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 
+template <int C>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __builtin_amdgcn_update_dpp(0.f, x, C, 0xf, 0xf, false);
+}
+// all-reduce over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1)
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_row<0x128>(x));
+  x = fmaxf(x, dpp_row<0x124>(x));
+  x = fmaxf(x, dpp_row<0x122>(x));
+  x = fmaxf(x, dpp_row<0x121>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_row<0x128>(x);
+  x += dpp_row<0x124>(x);
+  x += dpp_row<0x122>(x);
+  x += dpp_row<0x121>(x);
+  return x;
+}
+
+// gfx950 lane swaps.  swap32(a, b): low 32 lanes get a[l] + a[l + 32], high 32 lanes get
+// b[l - 32] + b[l]; swap16(a, b): lane rows (16 lanes) 0,1,2,3 get a.r0 + a.r1, b.r0 + b.r1,
+// a.r2 + a.r3, b.r2 + b.r3.
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// Sum over the four lane groups (lanes n, n + 16, n + 32, n + 48), result in every lane.
+__device__ __forceinline__ float lane_group_sum(float x) {
+  return swap16_sum(swap32_sum(x, x), swap32_sum(x, x));
+}
+
+__device__ __forceinline__ int floor_div(int a, int b) { return (a >= 0) ? a / b : -((-a + b - 1) / b); }
+
+// MFMA operand fragment of row `row` of a row-major LDS array (d-slice of lane group g).
+__device__ __forceinline__ void lds_frag(Frag<bf16>& f, const bf16* rows, int row, int g) {
+  const uint4* p = reinterpret_cast<const uint4*>(rows + row * Lds<bf16>::stride + 16 * g);
+  f.a = __builtin_bit_cast(bf16x8, p[0]);
+  f.b = __builtin_bit_cast(bf16x8, p[1]);
+}
+__device__ __forceinline__ void lds_frag(Frag<float>& f, const float* rows, int row, int g) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(rows + row * Lds<float>::stride + 16 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.v[i] = p[i];
+}
+
+// ROWS token rows of a [L][64] tensor, starting at token r0 (zeros outside [0, Lr)), held in
+// registers of a workgroup of NTHR threads between their global load and their store into an
+// LDS ring (token t at ring row t mod RING).  All loads are issued before the first store.
+template <typename T, int ROWS, int NTHR>
+struct RowStage {
+  static constexpr int kChunksPerRow = 64 * (int)sizeof(T) / 16;
+  static constexpr int kPer = (ROWS * kChunksPerRow + NTHR - 1) / NTHR;
+  uint4 x[kPer];
+  __device__ __forceinline__ void load(const T* base, int r0, int Lr) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * NTHR + (int)threadIdx.x;
+      const int row = c / kChunksPerRow, col = (c % kChunksPerRow) * (16 / (int)sizeof(T));
+      const int t = r0 + row;
+      const int tc = min(max(t, 0), Lr - 1);
+      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)tc * kD + col);
+      const bool ok = (t >= 0) & (t < Lr) & (row < ROWS);
+      x[i] = uint4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
+    }
+  }
+  template <int RING>
+  __device__ __forceinline__ void store(T* ring, int r0) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * NTHR + (int)threadIdx.x;
+      const int row = c / kChunksPerRow, col = (c % kChunksPerRow) * (16 / (int)sizeof(T));
+      if (ROWS * kChunksPerRow % NTHR == 0 || row < ROWS) {
+        const int rr = (r0 + row + 4 * RING) % RING;
+        *reinterpret_cast<uint4*>(ring + rr * Lds<T>::stride + col) = x[i];
+      }
+    }
+  }
+};
+
 }  // namespace ska

@@ -31,28 +31,6 @@
 
 namespace ska {
 
-template <int C>
-__device__ __forceinline__ float dpp_row(float x) {
-  return __builtin_amdgcn_update_dpp(0.f, x, C, 0xf, 0xf, false);
-}
-// all-reduce over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1)
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_row<0x128>(x));
-  x = fmaxf(x, dpp_row<0x124>(x));
-  x = fmaxf(x, dpp_row<0x122>(x));
-  x = fmaxf(x, dpp_row<0x121>(x));
-  return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_row<0x128>(x);
-  x += dpp_row<0x124>(x);
-  x += dpp_row<0x122>(x);
-  x += dpp_row<0x121>(x);
-  return x;
-}
-
-__device__ __forceinline__ int floor_div(int a, int b) { return (a >= 0) ? a / b : -((-a + b - 1) / b); }
-
 __device__ __forceinline__ float dot64(const bf16* a, const bf16* b) {
   float s = 0.f;
   for (int d = 0; d < kD; ++d) s = fmaf((float)a[d], (float)b[d], s);
@@ -125,109 +103,6 @@ __device__ float finish_column(int j, const float* vprev_h, const float* part_h,
   return column_combine<T>(j, column_loads(j, vprev_h, part_h, a), u_h, Qh, Kh, a);
 }
 
-// B-operand fragment of key row `row` of the staged keys (LDS), d-slice of lane group g.
-__device__ __forceinline__ void lds_frag(Frag<bf16>& f, const bf16* kw, int row, int g) {
-  const uint4* p = reinterpret_cast<const uint4*>(kw + row * Lds<bf16>::stride + 16 * g);
-  f.a = __builtin_bit_cast(bf16x8, p[0]);
-  f.b = __builtin_bit_cast(bf16x8, p[1]);
-}
-__device__ __forceinline__ void lds_frag(Frag<float>& f, const float* kw, int row, int g) {
-  const f32x4* p = reinterpret_cast<const f32x4*>(kw + row * Lds<float>::stride + 16 * g);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.v[i] = p[i];
-}
-
-// Copy `rows` consecutive key rows starting at token r0 into the LDS ring (row t lives at ring
-// row t mod RING); rows outside [0, Lr) are zero.  Whole workgroup of 256 threads; all loads are
-// issued before the first store.
-template <int ROWS, int RING>
-__device__ __forceinline__ void ring_store_rows(bf16* ring, const bf16* base, int r0, int Lr) {
-  constexpr int kPer = ROWS * 8 / 256;
-  static_assert(ROWS * 8 % 256 == 0, "rows must fill the workgroup");
-  uint4 buf[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8, t = r0 + row;
-    const int tc = min(max(t, 0), Lr - 1);
-    const uint4 x = *reinterpret_cast<const uint4*>(base + (int64_t)tc * kD + col);
-    const bool ok = (t >= 0) & (t < Lr);
-    buf[i] = uint4{ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u};
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8;
-    const int rr = (r0 + row + 4 * RING) % RING;
-    *reinterpret_cast<uint4*>(ring + rr * Lds<bf16>::stride + col) = buf[i];
-  }
-}
-template <int ROWS, int RING>
-__device__ __forceinline__ void ring_store_rows(float* ring, const float* base, int r0, int Lr) {
-  constexpr int kPer = ROWS * 16 / 256;
-  static_assert(ROWS * 16 % 256 == 0, "rows must fill the workgroup");
-  f32x4 buf[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = i * 256 + threadIdx.x, row = c >> 4, col = (c & 15) * 4, t = r0 + row;
-    const int tc = min(max(t, 0), Lr - 1);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(base + (int64_t)tc * kD + col);
-    const bool ok = (t >= 0) & (t < Lr);
-    buf[i] = f32x4{ok ? x[0] : 0.f, ok ? x[1] : 0.f, ok ? x[2] : 0.f, ok ? x[3] : 0.f};
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = i * 256 + threadIdx.x, row = c >> 4, col = (c & 15) * 4;
-    const int rr = (r0 + row + 4 * RING) % RING;
-    *reinterpret_cast<f32x4*>(ring + rr * Lds<float>::stride + col) = buf[i];
-  }
-}
-
-// The 64 key rows one block adds to the ring, held in registers between load and store.
-template <typename T> struct NewRows;
-template <> struct NewRows<bf16> {
-  uint4 x[2];
-  __device__ void load(const bf16* base, int r0, int Lr) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8, t = r0 + row;
-      const int tc = min(max(t, 0), Lr - 1);
-      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)tc * kD + col);
-      const bool ok = (t >= 0) & (t < Lr);
-      x[i] = uint4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
-    }
-  }
-  template <int RING>
-  __device__ void store(bf16* ring, int r0) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = i * 256 + threadIdx.x, row = c >> 3, col = (c & 7) * 8;
-      const int rr = (r0 + row + 4 * RING) % RING;
-      *reinterpret_cast<uint4*>(ring + rr * Lds<bf16>::stride + col) = x[i];
-    }
-  }
-};
-template <> struct NewRows<float> {
-  f32x4 x[4];
-  __device__ void load(const float* base, int r0, int Lr) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = i * 256 + threadIdx.x, row = c >> 4, col = (c & 15) * 4, t = r0 + row;
-      const int tc = min(max(t, 0), Lr - 1);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(base + (int64_t)tc * kD + col);
-      const bool ok = (t >= 0) & (t < Lr);
-      x[i] = f32x4{ok ? v[0] : 0.f, ok ? v[1] : 0.f, ok ? v[2] : 0.f, ok ? v[3] : 0.f};
-    }
-  }
-  template <int RING>
-  __device__ void store(float* ring, int r0) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = i * 256 + threadIdx.x, row = c >> 4, col = (c & 15) * 4;
-      const int rr = (r0 + row + 4 * RING) % RING;
-      *reinterpret_cast<f32x4*>(ring + rr * Lds<float>::stride + col) = x[i];
-    }
-  }
-};
-
 template <typename T, int NT>
 struct StepSmem {
   static constexpr int kH16 = (NT - 1) / 2;
@@ -283,7 +158,11 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   // prologue: the first block's whole window and query fragment
   Frag<T> fq;
   load_frag(fq, Qh + (int64_t)(64 * blk0 + 16 * wave + n) * kD, 64 * blk0 + 16 * wave + n < Lr, g);
-  ring_store_rows<RING, RING>(kring, Kh, c_lo, Lr);
+  {
+    RowStage<T, RING, 256> first;
+    first.load(Kh, c_lo, Lr);
+    first.template store<RING>(kring, c_lo);
+  }
   for (int c = threadIdx.x; c < RING; c += 256) {
     const int j = c_lo + c;
     vring[(j + 4 * RING) % RING] = finish_from(j, loads_for(j));
@@ -297,7 +176,7 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     const bool more = blk + 1 < blk1;
     // prefetch the 64 key rows the next block adds: [cb + RING, cb + RING + 64)
     // (and the next block's query fragment and new column loads), all in flight during compute
-    NewRows<T> nr;
+    RowStage<T, 64, 256> nr;
     ColIn nc{0.f, 0.f, 0.f};
     Frag<T> fq_next;
     if (more) {

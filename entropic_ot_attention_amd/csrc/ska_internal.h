@@ -67,6 +67,29 @@ int fused_tiles_for(int h);
 void fused_segments(int64_t bh, int Lr, int nt, int* seg_len, int* nseg);
 inline int fused_pstride(int nt, int seg_len) { return 64 * seg_len + 16 * (nt - 1); }
 
+// Arguments of the streaming VJP passes (see ska_vjp_stream.hip).  Workgroups of NW waves own
+// blocks of 16 NW rows; segments of seg_len blocks per workgroup as in the forward step.  dv1
+// column partials are [bh][nseg][pstride] with pstride = 16 NW seg_len + 32 H16.
+struct VjpArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dO;
+  void* out0;            // pass 3: dQ; pass 4: dK
+  void* out1;            // pass 4: dV
+  float* ws;             // kVjpVecs vectors [bh][Lpad]
+  float* part;           // dv1 column partials
+  int64_t vec_stride;    // floats between consecutive workspace vectors (bh * Lpad)
+  int64_t bh;
+  int Lr, Lpad, h, nblk, seg_len, nseg, pstride;
+  float c2, s;
+};
+
+// Streaming VJP geometry for (dtype, h): waves per workgroup (0 if the streaming passes do not
+// cover this band; the chunked passes handle it) and the register-resident tile count.
+int vjp_stream_waves(int elt, int h, int* nt);
+void vjp_stream_segments(int64_t bh, int Lr, int nw, int nt, int* seg_len, int* nseg);
+
 enum TimedKernel : int { kTimedStep = 0, kTimedOut = 1, kTimedVjp = 2, kTimedKinds = 3 };
 
 // Launchers (return the hipGetLastError() of their launches).  `elt` is 0 for fp32, 1 for bf16.
@@ -79,6 +102,8 @@ hipError_t launch_out(int elt, const void* Q, const void* K, const void* V, cons
                       const float* v2, void* O, const Geometry& g, hipStream_t st);
 hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, hipStream_t st);
 hipError_t launch_finish_columns(int elt, const StepArgs& a, hipStream_t st);
+hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, const VjpArgs& a,
+                                  hipStream_t st);
 hipError_t launch_vjp_prep(const float* duals, float* ws, const Geometry& g, hipStream_t st);
 hipError_t launch_vjp_pass(int elt, int pass, bool direct4, const void* Q, const void* K,
                            const void* V, const void* dO, void* out, float* ws, const Geometry& g,

@@ -83,10 +83,9 @@ typedef struct {
   int32_t dtype;   /* ska_dtype of Q, K, V, O, dO, dQ, dK, dV (duals are always fp32)           */
 } ska_problem;
 
-/* Workspace bytes the entry point `op` needs for problem *p: O(bh * L * (1 + W/64)) floats (dual
- * vectors plus, in the forward, per-64-row-block column sums over the band window); the VJP's
- * depends on bh and L only.  Returns SKA_OK and writes *bytes, or an error status for an invalid
- * problem. */
+/* Workspace bytes the entry point `op` needs for problem *p: O(bh * L) floats (dual and cotangent
+ * vectors plus per-segment column sums over the band window, about one float per token).
+ * Returns SKA_OK and writes *bytes, or an error status for an invalid problem. */
 ska_status ska_workspace_bytes(const ska_problem* p, ska_op op, size_t* bytes);
 
 /* Forward pass: stopped T-step balanced Sinkhorn base, R-step tail, O = P^(R,R) V.

@@ -89,12 +89,36 @@ def _fused_fwd_bytes(bh, L, W):
     return (4 * bh * Lpad + 2 * bh * nseg * pst) * 4
 
 
+def _vjp_bytes(bh, L, W, bf16=False):
+    """VJP workspace: 14 vectors [bh][Lpad], plus dv1 column partials [bh][nseg][pstride] when
+    the streaming passes cover the band (bf16: h <= 128 with 12-wave / 192-token blocks; fp32:
+    h <= 64 with 4-wave / 64-token blocks)."""
+    Lpad = -(-L // 64) * 64
+    base = 14 * bh * Lpad
+    h = min(W // 2, L)
+    h16 = -(-h // 16)
+    H16 = next((c for c in (2, 4, 8) if h16 <= c), 0)
+    if H16 == 0 or (not bf16 and H16 > 4):
+        return base * 4
+    nw = 12 if bf16 else 4
+    br = 16 * nw
+    nblk = -(-L // br)
+    sl = min(max(-(-bh * nblk // 256), -(-(32 * H16) // br), 1), nblk)
+    nseg = -(-nblk // sl)
+    return (base + bh * nseg * (br * sl + 32 * H16)) * 4
+
+
 def test_workspace_sizes():
     for L, Lpad in ((1, 64), (64, 64), (65, 128), (1000, 1024)):
         st, n = _ws_bytes(_prob(L=L, bh=3), B.SKA_OP_FWD)
         assert st == 0 and n == _fused_fwd_bytes(3, L, 16)
         st, n = _ws_bytes(_prob(L=L, bh=3), B.SKA_OP_VJP)
+        assert st == 0 and n == _vjp_bytes(3, L, 16)
+        st, n = _ws_bytes(_prob(L=L, bh=3, W=500), B.SKA_OP_VJP)     # chunked passes only
         assert st == 0 and n == 14 * 3 * Lpad * 4
+    st, n = _ws_bytes(_prob(L=262144, bh=4, W=256, dtype=B.SKA_BF16), B.SKA_OP_VJP)
+    assert st == 0 and n == _vjp_bytes(4, 262144, 256, bf16=True)
+    assert n < 20 * 4 * 262144 * 4          # O(L): under 20 floats per token and head
     st, n = _ws_bytes(_prob(L=262144, bh=4, W=256), B.SKA_OP_FWD)
     assert st == 0 and n == _fused_fwd_bytes(4, 262144, 256)
     assert n < 8 * 4 * 262144 * 4           # O(L): under 8 floats per token and head
@@ -105,8 +129,8 @@ def test_workspace_sizes():
     assert st == 0 and n == 2 * 4 * 4160 * 4
     st, n = _ws_bytes(_prob(L=0), B.SKA_OP_VJP)
     assert st == 0 and n == 0
-    # the VJP workspace depends neither on W nor on the dtype
-    assert _ws_bytes(_prob(W=4000), B.SKA_OP_VJP) == _ws_bytes(_prob(W=2, dtype=B.SKA_BF16), B.SKA_OP_VJP)
+    # bands the streaming passes do not cover need only the vectors, whatever the dtype
+    assert _ws_bytes(_prob(W=4000), B.SKA_OP_VJP) == _ws_bytes(_prob(W=4000, dtype=B.SKA_BF16), B.SKA_OP_VJP)
 
 
 @pytest.mark.parametrize("kw,op,status", [
