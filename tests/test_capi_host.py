@@ -97,7 +97,7 @@ def _vjp_bytes(bh, L, W, bf16=False):
     base = 14 * bh * Lpad
     h = min(W // 2, L)
     h16 = -(-h // 16)
-    H16 = next((c for c in (2, 4, 8) if h16 <= c), 0)
+    H16 = next((c for c in (2, 4, 8) if h16 <= c), 0)   # 0: chunked passes, no partials
     if H16 == 0 or (not bf16 and H16 > 4):
         return base * 4
     nw = 12 if bf16 else 4
@@ -114,8 +114,8 @@ def test_workspace_sizes():
         assert st == 0 and n == _fused_fwd_bytes(3, L, 16)
         st, n = _ws_bytes(_prob(L=L, bh=3), B.SKA_OP_VJP)
         assert st == 0 and n == _vjp_bytes(3, L, 16)
-        st, n = _ws_bytes(_prob(L=L, bh=3, W=500), B.SKA_OP_VJP)     # chunked passes only
-        assert st == 0 and n == 14 * 3 * Lpad * 4
+        st, n = _ws_bytes(_prob(L=L, bh=3, W=500), B.SKA_OP_VJP)     # h = min(W/2, L)
+        assert st == 0 and n == _vjp_bytes(3, L, 500)
     st, n = _ws_bytes(_prob(L=262144, bh=4, W=256, dtype=B.SKA_BF16), B.SKA_OP_VJP)
     assert st == 0 and n == _vjp_bytes(4, 262144, 256, bf16=True)
     assert n < 20 * 4 * 262144 * 4          # O(L): under 20 floats per token and head
