@@ -130,7 +130,8 @@ def test_workspace_sizes():
     st, n = _ws_bytes(_prob(L=0), B.SKA_OP_VJP)
     assert st == 0 and n == 0
     # bands the streaming passes do not cover need only the vectors, whatever the dtype
-    assert _ws_bytes(_prob(W=4000), B.SKA_OP_VJP) == _ws_bytes(_prob(W=4000, dtype=B.SKA_BF16), B.SKA_OP_VJP)
+    assert (_ws_bytes(_prob(L=2000, W=4000), B.SKA_OP_VJP)
+            == _ws_bytes(_prob(L=2000, W=4000, dtype=B.SKA_BF16), B.SKA_OP_VJP))
 
 
 @pytest.mark.parametrize("kw,op,status", [
