@@ -219,8 +219,32 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
     a.save_u = nullptr;
     e = ska::launch_finish_columns(pl.elt, a, st);
     if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
-    SKA_LAUNCH(ska::kTimedOut, st,
-               ska::launch_out(pl.elt, Q, K, V, ubuf[K_steps % 2], vbuf[(K_steps + 1) % 2], O, g, st));
+    int ont = 0;
+    const int onw = ska::vjp_stream_waves(pl.elt, g.h, &ont);
+    if (onw > 0) {
+      // output on the streaming engine (its pass 0)
+      ska::VjpArgs o{};
+      o.Q = Q;
+      o.K = K;
+      o.V = V;
+      o.dO = nullptr;
+      o.out0 = O;
+      o.fu = ubuf[K_steps % 2];
+      o.fv = vbuf[(K_steps + 1) % 2];
+      o.bh = g.bh;
+      o.Lr = g.Lr;
+      o.Lpad = g.Lpad;
+      o.h = g.h;
+      o.nblk = (g.Lr + 16 * onw - 1) / (16 * onw);
+      ska::vjp_stream_segments(g.bh, g.Lr, onw, ont, &o.seg_len, &o.nseg);
+      o.pstride = 16 * onw * o.seg_len + 16 * (ont - 1);
+      o.c2 = g.c2;
+      o.s = g.s;
+      SKA_LAUNCH(ska::kTimedOut, st, ska::launch_vjp_stream_pass(pl.elt, ont, onw, 0, o, st));
+    } else {
+      SKA_LAUNCH(ska::kTimedOut, st,
+                 ska::launch_out(pl.elt, Q, K, V, ubuf[K_steps % 2], vbuf[(K_steps + 1) % 2], O, g, st));
+    }
     return SKA_OK;
   }
   // split path (bands wider than the fused step holds, e.g. the dense dustbin support)

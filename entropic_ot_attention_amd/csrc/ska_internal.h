@@ -75,9 +75,11 @@ struct VjpArgs {
   const void* K;
   const void* V;
   const void* dO;
-  void* out0;            // pass 3: dQ; pass 4: dK
+  void* out0;            // pass 0: O; pass 3: dQ; pass 4: dK
   void* out1;            // pass 4: dV
   float* ws;             // kVjpVecs vectors [bh][Lpad]
+  const float* fu;       // pass 0 (forward output): row duals u^(R), log2 units [bh][Lpad]
+  const float* fv;       // pass 0: column duals v^(R), log2 units [bh][Lpad]
   float* part;           // dv1 column partials
   int64_t vec_stride;    // floats between consecutive workspace vectors (bh * Lpad)
   int64_t bh;

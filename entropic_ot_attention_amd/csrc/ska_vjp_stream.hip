@@ -1,10 +1,12 @@
-// Streaming passes of the exact R = 2 tail VJP, one-reference-tile schedule (gfx950).
+// Streaming passes of the forward output and of the exact R = 2 tail VJP, one-reference-tile
+// schedule (gfx950).
 //
 // The adjoint [abstract: the R = 2 score cotangent is the reference plan tile times a modifier
 // field of vector cotangents and dual differences; technical summaries §2.2: orbit equation
 // P^(a,b) = P^(2,2) exp(u^(a) - u^(2)) exp(v^(b) - v^(2))], with P22 = exp(S + u2 + v2),
 // g_ij = dO_i . V_j and e^{du1} = exp(u1 - u2), e^{dv_b} = exp(v_b - v2), in four passes:
 //
+//   0 (owns queries)  forward output O_i = sum_j P22_ij V_j   [spec output: plan x V]
 //   1 (owns keys)     dv2_j = sum_i P22 g
 //   2 (owns queries)  du2_i = sum_j P22 (g - dv2_j);  per-segment column sums sum_i P22 du2_i
 //   3 (owns queries)  dv1_j = -e^{dv1_j} (column sums)  (finished for the window on arrival)
@@ -34,26 +36,53 @@
 
 namespace ska {
 
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane row, lane i receives element
+// i % 4 of the 8 bytes loaded by lane i / 4 + 4 e, as its element e.  With lane (g, n) loading
+// ring row rb + 4 g + n / 4 at columns c0 + 4 (n % 4) .. + 3, lane (g, n) receives rows
+// rb + 4 g + e (e = 0..3) of column c0 + n: one half of a bf16 MFMA A operand of the
+// transposed ring rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 tr_read(const bf16* ring, int row, int col) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(ring + row * Lds<bf16>::stride + col));
+}
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* ring, int rb0, int rb1, int b, int g, int n) {
+  const int r = 4 * g + (n >> 2), c = 16 * b + 4 * (n & 3);
+  const s16x4 lo = tr_read(ring, rb0 + r, c), hi = tr_read(ring, rb1 + r, c);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // acc[b][r] (lane l) += sum over the 32 window rows of tiles (rb0, rb1) of
 //   Op[row][16 b + 4 g + r] * Z[row][n]    (Op rows read transposed from the LDS ring)
 // z[tt][r] holds Z for row rb_tt + 4 g + r at owned token n.
-__device__ __forceinline__ void contract_ring(f32x4 (&acc)[4], const bf16* ring, int rb0, int rb1,
-                                              const float (&z)[2][4], int g, int n) {
+__device__ __forceinline__ bf16x8 pack_z(const float (&z)[2][4]) {
   bf16x8 zb;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     zb[e] = (bf16)z[0][e];
     zb[e + 4] = (bf16)z[1][e];
   }
+  return zb;
+}
+__device__ __forceinline__ void contract_ring(f32x4 (&acc)[4], const bf16* ring, int rb0, int rb1,
+                                              const float (&z)[2][4], int g, int n) {
+  const bf16x8 zb = pack_z(z);
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(ring, rb0, rb1, b, g, n), zb, acc[b], 0, 0, 0);
+}
+// Two contractions against the same ring rows (shares the transposed reads).
+__device__ __forceinline__ void contract_ring2(f32x4 (&x)[4], f32x4 (&y)[4], const bf16* ring, int rb0,
+                                               int rb1, const float (&z1)[2][4],
+                                               const float (&z2)[2][4], int g, int n) {
+  const bf16x8 zb1 = pack_z(z1), zb2 = pack_z(z2);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    bf16x8 av;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = (e < 4) ? (rb0 + 4 * g + e) : (rb1 + 4 * g + e - 4);
-      av[e] = ring[row * Lds<bf16>::stride + 16 * b + n];
-    }
-    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, zb, acc[b], 0, 0, 0);
+    const bf16x8 av = tr_operand(ring, rb0, rb1, b, g, n);
+    x[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, zb1, x[b], 0, 0, 0);
+    y[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, zb2, y[b], 0, 0, 0);
   }
 }
 __device__ __forceinline__ void contract_ring(f32x4 (&acc)[4], const float* ring, int rb0, int rb1,
@@ -70,10 +99,27 @@ __device__ __forceinline__ void contract_ring(f32x4 (&acc)[4], const float* ring
     }
 }
 
+__device__ __forceinline__ void contract_ring2(f32x4 (&x)[4], f32x4 (&y)[4], const float* ring,
+                                               int rb0, int rb1, const float (&z1)[2][4],
+                                               const float (&z2)[2][4], int g, int n) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = (tt == 0 ? rb0 : rb1) + 4 * g + r;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float av = ring[row * Lds<float>::stride + 16 * b + n];
+        x[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, z1[tt][r], x[b], 0, 0, 0);
+        y[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, z2[tt][r], y[b], 0, 0, 0);
+      }
+    }
+}
+
 template <int PASS> struct VjpPass {
   static constexpr bool owns_keys = (PASS == 1 || PASS == 4);
   // window-side vectors kept in LDS rings
-  static constexpr int nvec = PASS == 1 ? 1 : PASS == 2 ? 2 : PASS == 3 ? 5 : 4;
+  static constexpr int nvec = PASS <= 1 ? 1 : PASS == 2 ? 2 : PASS == 3 ? 5 : 4;
 };
 
 template <typename T, int NT, int NW, int PASS>
@@ -119,7 +165,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   auto window_vec = [&](int k, int j) -> float {
     const int jc = min(max(j, 0), Lr - 1);
     float x;
-    if (PASS == 1) x = vec(kU2)[jc];
+    if (PASS == 0) x = a.fv[vo + jc];
+    else if (PASS == 1) x = vec(kU2)[jc];
     else if (PASS == 2) x = (k == 0) ? vec(kV2)[jc] : vec(kDV2)[jc];
     else if (PASS == 3) {
       const int src[5] = {kV2, kDV2, kEE, kFF, kEG};
@@ -197,7 +244,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   {
     const int o = BR * blk0 + 16 * wave + n;
     load_frag(fA, ownA + (int64_t)o * kD, o < Lr, g);
-    load_frag(fB, ownB + (int64_t)o * kD, o < Lr, g);
+    if (PASS != 0) load_frag(fB, ownB + (int64_t)o * kD, o < Lr, g);
   }
   __syncthreads();
 
@@ -215,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       if ((int)threadIdx.x < BR) nv = vec_loads(cb + RING + (int)threadIdx.x);
       const int on = b0 + BR + 16 * wave + n;
       load_frag(fA_next, ownA + (int64_t)on * kD, on < Lr, g);
-      load_frag(fB_next, ownB + (int64_t)on * kD, on < Lr, g);
+      if (PASS != 0) load_frag(fB_next, ownB + (int64_t)on * kD, on < Lr, g);
     }
 
     const int o0 = b0 + 16 * wave;             // owned tokens o0 .. o0 + 15
@@ -241,7 +288,35 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       return (i < Lr) & (j >= 0) & (j < Lr) & (abs(i - j) <= h);
     };
 
-    if (PASS == 1) {
+    if (PASS == 0) {
+      // ---- O_i = sum_j P22_ij V_j (owned query i across lanes, window keys in registers) ----
+      const float u2o = a.fu[vo + min(o0 + n, Lr - 1)];
+      f32x4 Y[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pq = 0; pq < NP; ++pq) {
+        float z[2][4];
+        int rbs[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int t = 2 * pq + tt;
+          rbs[tt] = (t < NT) ? tile_row(t) : tile_row(2 * pq);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[tt][r] = 0.f;
+          if (t >= NT || dead_tile(t)) continue;
+          const int rr = rbs[tt];
+          Frag<T> fw;
+          lds_frag(fw, ringA, rr + n, g);
+          const f32x4 sc = dot_tile(fw, fA);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            z[tt][r] = keep_w(t, r) ? fast_exp2(fmaf(sc[r], a.c2, u2o + wv[0][rr + 4 * g + r])) : 0.f;
+        }
+        contract_ring(Y, ringB, rbs[0], rbs[1], z, g, n);
+      }
+      if (o0 + n < Lr) store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
+    } else if (PASS == 1) {
       // ---- dv2_j = sum_i P22 g (owned key j across lanes, window queries in registers) ----
       const float v2o = vec(kV2)[min(o0 + n, Lr - 1)];
       float acc = 0.f;
@@ -352,8 +427,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
             z2[tt][r] = p * Gj;
           }
         }
-        contract_ring(X, ringA, rbs[0], rbs[1], z1, g, n);
-        contract_ring(Y, ringA, rbs[0], rbs[1], z2, g, n);
+        contract_ring2(X, Y, ringA, rbs[0], rbs[1], z1, z2, g, n);
       }
       const float du1 = -Bi * lane_group_sum(acc);
       const float Ci = du1 * Bi;
@@ -462,6 +536,7 @@ template <typename T, int NT, int NW>
 static void launch_nt(int pass, const VjpArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.bh * (int64_t)a.nseg)), block(NW * 64);
   switch (pass) {
+    case 0: vjp_stream_kernel<T, NT, NW, 0><<<grid, block, 0, st>>>(a); break;
     case 1: vjp_stream_kernel<T, NT, NW, 1><<<grid, block, 0, st>>>(a); break;
     case 2: vjp_stream_kernel<T, NT, NW, 2><<<grid, block, 0, st>>>(a); break;
     case 3: vjp_stream_kernel<T, NT, NW, 3><<<grid, block, 0, st>>>(a); break;
