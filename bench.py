@@ -6,10 +6,11 @@ tokens, d = 64, band W = 256, T = 15 base steps, R = 2, bf16 inputs, fp32 duals)
 resident in HBM before the timed region.  The metric is tokens of the sequence per second:
 L / (t_fwd + t_vjp) for all heads together.
 
-Prints ONE JSON line.  Besides the throughput it reports, for the dominant kernel (the
-forward Sinkhorn half-step, 2(T+R) launches per step), its average launch time measured with
-HIP events on its own stream during the timed steps and the achieved fraction of the VALU
-issue roofline, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line.  Besides the throughput it reports, for the dominant kernel (the fused
+balanced Sinkhorn step, T + R launches per step), its average launch time measured with HIP
+events on its own stream during the timed steps, the achieved fraction of the VALU issue
+roofline and, when a current rocprofv3 record exists, its HBM bytes per launch; and the fp64
+CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -23,22 +24,38 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# MI355X unit counts and clock used for the VALU roofline: 256 CUs x 4 SIMDs x 16 lanes at
-# 2.4 GHz issue 39.3e12 fp32 lane-operations per second (no packed fp32).  v_exp_f32 is a
-# quarter-rate transcendental, so one exponential occupies 4 issue slots.
-VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
+# VALU roofline of MI355X from unit counts and clock: 256 CUs x 4 SIMDs, each issuing a wave64
+# fp32 VALU instruction every 2 cycles (32 lanes per cycle, the rate behind the 157.3 TFLOP/s
+# fp32 vector peak with FMA counted as 2 flops), at 2.4 GHz: 78.6e12 lane-operations per second.
+# v_exp_f32 is quarter rate, so one exponential takes 4 issue slots.
+VALU_LANE_OPS_PER_S = 256 * 4 * 32 * 2.4e9
 EXP_SLOTS = 4
-# Minimal VALU work of one balanced log-domain half-step per band entry: form the exponent
-# (1 fma), track the running max (1 max), shift (1 sub), exponentiate (1 exp = 4 slots),
-# accumulate (1 add): 8 issue slots.
-SLOTS_PER_ENTRY_STEP = 4 + EXP_SLOTS
+# Minimal VALU work of one fused balanced Sinkhorn step per band entry: form the exponent (1 fma),
+# track the row max (1 max), shift (1 sub), exponentiate (1 exp = 4 slots), accumulate the row sum
+# (1 add), accumulate the column sum of the normalised plan (1 fma): 9 issue slots.
+SLOTS_PER_ENTRY_STEP = 5 + EXP_SLOTS
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_sinkhorn_step_kernel.json")
 
 
 def band_entries(L: int, h: int) -> int:
     """|{(i, j): 0 <= i, j < L, |i - j| <= h}|."""
     h = min(h, L - 1) if L > 0 else 0
     return L * (2 * h + 1) - h * (h + 1)
+
+
+def traffic_per_launch():
+    """HBM bytes per step-kernel launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    record, or None when there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+        from entropic_ot_attention_amd.profiling import source_sha
+        if rec.get("source_sha256") != source_sha():
+            return None
+        return round(float(rec["bytes_per_launch"]))
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def parse():
@@ -50,6 +67,8 @@ def parse():
     ap.add_argument("--schedule", default="one_reference", choices=["one_reference", "direct_four"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="one device copy of this many MiB before warmup (counter calibration)")
     return ap.parse_args()
 
 
@@ -120,6 +139,20 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    if args.calibration_copy_mib > 0:
+        # one elementwise kernel that reads and writes exactly this many bytes; the source is
+        # evicted from the last-level cache first (a fill of another buffer of the same size),
+        # so every byte it reads comes from HBM
+        n = args.calibration_copy_mib << 18
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        evict = torch.empty_like(src)
+        evict.fill_(2.0)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst, evict
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -145,20 +178,24 @@ def main():
     h = min(w.W // 2, rows) if not w.dustbin else rows
     nnz = band_entries(rows, h) * w.bh                         # band entries per launch
     avg_launch_s = (kstep_ms / max(kstep_n, 1)) / 1e3
-    achieved = SLOTS_PER_ENTRY_STEP * nnz / avg_launch_s / 1e12     # Tslot/s
+    achieved = SLOTS_PER_ENTRY_STEP * nnz / avg_launch_s / 1e12     # T lane-slots/s
     peak = VALU_LANE_OPS_PER_S / 1e12
+    traffic = traffic_per_launch()
     roofline = {
         "bound": "alu",
-        "kernel": "lse_kernel (forward Sinkhorn half-step)",
+        "kernel": "sinkhorn_step_kernel (fused balanced Sinkhorn step)",
         "achieved": round(achieved, 3),
         "peak": round(peak, 3),
-        "unit": "T VALU issue-slots/s",
+        "unit": "T VALU lane-slots/s",
         "frac": round(achieved / peak, 4),
-        "traffic": None,
+        "traffic": traffic,
         "avg_launch_us": round(avg_launch_s * 1e6, 2),
         "launches_timed": kstep_n,
         "algorithmic_work": f"{SLOTS_PER_ENTRY_STEP} slots x {nnz} band entries per launch",
     }
+    if traffic is not None:
+        roofline["hbm_gbs"] = round(traffic / avg_launch_s / 1e9, 1)
+        roofline["hbm_frac"] = round(traffic / avg_launch_s / 1e9 / HBM_PEAK_GBS, 4)
     out = {
         "metric": "fwd+R=2 VJP tokens/s at L=262144 W=256 d=64",
         "value": round(value, 1),

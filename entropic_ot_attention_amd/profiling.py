@@ -1,0 +1,100 @@
+"""Summaries of rocprofv3 output for the committed profile records.
+
+    python -m entropic_ot_attention_amd.profiling stats <kernel_stats.csv> <out.md> "<command>"
+    python -m entropic_ot_attention_amd.profiling traffic <fetch.csv> <write.csv> <out.json> \
+        <kernel substring> <calibration kernel substring> <calibration bytes> "<command>"
+
+`stats` writes a short markdown table (calls, average and total duration per kernel) from a
+`--kernel-trace --stats --output-format csv` run.  `traffic` turns two `--pmc FETCH_SIZE` and
+`--pmc WRITE_SIZE` runs into HBM bytes per launch of one kernel, each counter scaled by what it
+reads for the calibration kernel in the same run (an elementwise kernel that reads and writes a
+known number of bytes, bench.py --calibration-copy-mib), and records the SHA-256 of the kernel's source
+file so a reader can tell when the record no longer describes the code.
+"""
+
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+STEP_KERNEL_SOURCE = os.path.join(PKG, "csrc", "ska_fused.hip")
+
+
+def source_sha(path: str = STEP_KERNEL_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stats_markdown(csv_path: str, out_md: str, command: str, top: int = 14) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [
+        "# rocprofv3 kernel statistics",
+        "",
+        "Command:",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| kernel | calls | avg us | total ms | % |",
+        "|---|---:|---:|---:|---:|",
+    ]
+    for r in rows[:top]:
+        lines.append(f"| `{r['Name'][:96]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(csv_path: str, counter: str):
+    """{dispatch id: (kernel name, summed counter value)} for one counter."""
+    out = collections.defaultdict(lambda: ["", 0.0])
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = out[r["Dispatch_Id"]]
+        d[0] = r["Kernel_Name"]
+        d[1] += float(r["Counter_Value"])
+    return out
+
+
+def traffic_record(fetch_csv: str, write_csv: str, kernel: str, calib_kernel: str, calib_bytes: int,
+                   command: str):
+    rec = {"kernel": kernel, "source_sha256": source_sha(), "command": command,
+           "calibration_kernel": calib_kernel, "calibration_bytes": calib_bytes}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        disp = _per_dispatch(path, counter)
+        copies = [v for k, (n, v) in disp.items() if calib_kernel in n]
+        kvals = [v for k, (n, v) in disp.items() if kernel in n]
+        if not copies or not kvals:
+            raise RuntimeError(f"{counter}: calibration copy or kernel '{kernel}' not found")
+        copy_kib = max(copies)
+        scale = calib_bytes / (copy_kib * 1024.0)        # true bytes per counted byte
+        rec[f"{name}_kib_per_launch_raw"] = sum(kvals) / len(kvals)
+        rec[f"{name}_calibration_kib"] = copy_kib
+        rec[f"{name}_scale"] = scale
+        rec[f"{name}_bytes_per_launch"] = sum(kvals) / len(kvals) * 1024.0 * scale
+        rec[f"{name}_launches"] = len(kvals)
+    rec["bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    return rec
+
+
+def main(argv):
+    if argv[1] == "stats":
+        stats_markdown(argv[2], argv[3], argv[4])
+    elif argv[1] == "traffic":
+        rec = traffic_record(argv[2], argv[3], argv[5], argv[6], int(argv[7]), argv[8])
+        with open(argv[4], "w") as f:
+            json.dump(rec, f, indent=1)
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv)
