@@ -59,15 +59,17 @@ __device__ __forceinline__ void load_frag(Frag<float>& f, const float* row, bool
   }
 }
 
-__device__ __forceinline__ f32x4 dot_tile(const Frag<bf16>& w, const Frag<bf16>& o) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w.a, o.a, acc, 0, 0, 0);
+// init + w.o over d = 64 for a 16 x 16 tile (init enters the matrix-core accumulator)
+__device__ __forceinline__ f32x4 dot_tile(const Frag<bf16>& w, const Frag<bf16>& o,
+                                          f32x4 init = f32x4{0.f, 0.f, 0.f, 0.f}) {
+  f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w.a, o.a, init, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w.b, o.b, acc, 0, 0, 0);
   return acc;
 }
 
-__device__ __forceinline__ f32x4 dot_tile(const Frag<float>& w, const Frag<float>& o) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ f32x4 dot_tile(const Frag<float>& w, const Frag<float>& o,
+                                          f32x4 init = f32x4{0.f, 0.f, 0.f, 0.f}) {
+  f32x4 acc = init;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -292,6 +294,18 @@ struct RowStage {
       const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)tc * kD + col);
       const bool ok = (t >= 0) & (t < Lr) & (row < ROWS);
       x[i] = uint4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
+    }
+  }
+  // the same when every row lies inside the sequence: no clamping or selection, and the
+  // per-thread offset from the (wave-uniform) first row is loop-invariant
+  __device__ __forceinline__ void load_inside(const T* base, int r0) {
+    const T* rb = base + (int64_t)r0 * kD;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * NTHR + (int)threadIdx.x;
+      const int row = c / kChunksPerRow, col = (c % kChunksPerRow) * (16 / (int)sizeof(T));
+      if (ROWS * kChunksPerRow % NTHR == 0 || row < ROWS)
+        x[i] = *reinterpret_cast<const uint4*>(rb + (unsigned)(row * kD + col));
     }
   }
   template <int RING>

@@ -5,7 +5,7 @@
 //
 //   1. finish the previous column update for the block's key window:
 //        v_j <- v_j - log sum_i exp(S_ij + u_i + v_j)      (column sums from the previous launch)
-//   2. row update for the 64 owned queries:  u_i = -log sum_j exp(S_ij + v_j)   (exact max shift)
+//   2. row update for the 64 owned queries:  u_i = -log sum_j exp(S_ij + v_j)
 //   3. column sums of the new plan exp(S + u + v) restricted to the owned rows, written as one
 //      partial row per block; the next launch (or the finishing kernel) completes step 1.
 //
@@ -17,10 +17,16 @@
 // order (no atomics, bitwise reproducible).  K's window for the block is staged in LDS once and
 // shared by the four waves.
 //
+// After the first step the row log-sum-exp is shifted by the previous step's row dual, which
+// enters the matrix-core accumulator, instead of by the row maximum.  Each shifted term is then
+// an entry of the previous plan after its column normalisation, hence at most 1, and each row
+// sum lies in [1 / (2h + 1), 2h + 1]: the max pass disappears with no loss of range.  The first
+// step (from u = 0) subtracts the exact row maximum.
+//
 // Column sums can underflow only when a column's mass under the current plan falls below
-// 2^-100 (scores spanning more than ~70 nats inside one band); such a column is finished by an
+// 2^-60 (scores spanning more than ~40 nats inside one band); such a column is finished by an
 // exact log-sum-exp over its band instead, so the result never depends on that threshold beyond
-// rounding.
+// rounding.  (A plan entry lost to underflow is below 2^-118.)
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -93,7 +99,7 @@ template <typename T>
 __device__ __forceinline__ float column_combine(int j, const ColIn& in, const float* u_h, const T* Qh,
                                                 const T* Kh, const StepArgs& a) {
   const float s = in.p0 + in.p1;
-  if (s >= 0x1p-100f) return in.vp - fast_log2(s);
+  if (s >= 0x1p-60f) return in.vp - fast_log2(s);
   return exact_column<T>(j, u_h, Qh, Kh, a.Lr, a.h, a.c2);
 }
 
@@ -110,16 +116,19 @@ struct StepSmem {
   static constexpr int kRingBytes = kRing * Lds<T>::stride * (int)sizeof(T);
 };
 
-// One full Sinkhorn step for one segment of consecutive 64-row blocks of one problem.
-template <typename T, int NT>
+// One full Sinkhorn step for one segment of consecutive 64-row blocks of one problem.  SHIFT:
+// the row log-sum-exp is shifted by the previous step's row duals (every launch after the first);
+// otherwise by the exact row maximum.
+template <typename T, int NT, bool SHIFT>
 __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   constexpr int H16 = (NT - 1) / 2;
   constexpr int RING = StepSmem<T, NT>::kRing;
+  constexpr int LS = Lds<T>::stride;
   static_assert(H16 % 2 == 0, "ring rows must be a multiple of 64");
-  __shared__ __attribute__((aligned(16))) T kring[RING * Lds<T>::stride];
+  __shared__ __attribute__((aligned(16))) T kring[RING * LS];
   __shared__ float vring[RING];            // finished column duals, by key mod RING
   __shared__ float pring[RING];            // this segment's column sums, by key mod RING
-  __shared__ float cpart[kWaves * RING];          // [wave][RING] block column sums
+  __shared__ float cpart[kWaves * RING];   // [wave][RING] block column sums
 
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -129,16 +138,18 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   const int c_lo = 64 * blk0 - 16 * H16;    // first column this segment touches
   const int own_lo = 64 * blk0, own_hi = 64 * blk1;
   const int Lr = a.Lr, h = a.h;
+  const float c2 = a.c2, inv_c2 = 1.f / a.c2;
   const T* Qh = static_cast<const T*>(a.Q) + head * (int64_t)Lr * kD;
   const T* Kh = static_cast<const T*>(a.K) + head * (int64_t)Lr * kD;
   const int64_t vo = head * (int64_t)a.Lpad;
+  const float* u_prev_h = a.u_prev + vo;
   const float* part_prev_h = a.part_prev ? a.part_prev + head * (int64_t)a.nseg * a.pstride : nullptr;
   float* part_out_h = a.part_out + (head * (int64_t)a.nseg + seg) * a.pstride;
 
   // finished column dual of key j (log2 units) from its loads, and its owner-side copies
   auto finish_from = [&](int j, const ColIn& in) -> float {
     if (j < 0 || j >= Lr) return 0.f;
-    const float v = part_prev_h ? column_combine<T>(j, in, a.u_prev + vo, Qh, Kh, a) : in.vp;
+    const float v = part_prev_h ? column_combine<T>(j, in, u_prev_h, Qh, Kh, a) : in.vp;
     if (j >= own_lo && j < own_hi) {
       a.v_next[vo + j] = v;
       if (a.save_v) a.save_v[head * a.save_v_stride + j] = v * kLn2;
@@ -149,15 +160,22 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     if (part_prev_h) return column_loads(j, a.v_prev + vo, part_prev_h, a);
     return ColIn{0.f, 0.f, a.v_prev[vo + min(max(j, 0), Lr - 1)]};
   };
+  // previous row duals of rows o, .., o + 3 (log2 units); the dual buffers are padded to Lpad,
+  // a multiple of 64, and hold 0 past Lr
+  auto shift_rows = [&](int o) -> f32x4 {
+    if constexpr (SHIFT) return load4(u_prev_h + o);
+    return f32x4{0.f, 0.f, 0.f, 0.f};
+  };
 
   const bool exact_h = (h == 16 * H16);
   // per-wave column sums live at columns [16 wave, 16 wave + 16 NT) of a RING-wide row; the
   // other columns stay zero so the block sum below needs no coverage tests
   for (int c = threadIdx.x; c < kWaves * RING; c += 256) cpart[c] = 0.f;
 
-  // prologue: the first block's whole window and query fragment
+  // prologue: the first block's whole window, query fragment and row shifts
   Frag<T> fq;
   load_frag(fq, Qh + (int64_t)(64 * blk0 + 16 * wave + n) * kD, 64 * blk0 + 16 * wave + n < Lr, g);
+  f32x4 ush = shift_rows(64 * blk0 + 16 * wave + 4 * g);
   {
     RowStage<T, RING, 256> first;
     first.load(Kh, c_lo, Lr);
@@ -175,114 +193,165 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     const int cb = b0 - 16 * H16;             // block window [cb, cb + RING)
     const bool more = blk + 1 < blk1;
     // prefetch the 64 key rows the next block adds: [cb + RING, cb + RING + 64)
-    // (and the next block's query fragment and new column loads), all in flight during compute
+    // (and the next block's query fragment, row shifts and new column loads), all in flight
+    // during compute
     RowStage<T, 64, 256> nr;
     ColIn nc{0.f, 0.f, 0.f};
     Frag<T> fq_next;
+    f32x4 ush_next;
     if (more) {
-      nr.load(Kh, cb + RING, Lr);
+      if (cb + RING >= 0 && cb + RING + 64 <= Lr) nr.load_inside(Kh, cb + RING);
+      else nr.load(Kh, cb + RING, Lr);
       const int on = b0 + 64 + 16 * wave + n;
       load_frag(fq_next, Qh + (int64_t)on * kD, on < Lr, g);
+      ush_next = shift_rows(b0 + 64 + 16 * wave + 4 * g);
       if (threadIdx.x < 64) nc = loads_for(cb + RING + (int)threadIdx.x);
     }
 
-    // score strip in registers (wave rows o0 .. o0 + 15), exact row log-sum-exp
+    // score strip in registers (wave rows o0 .. o0 + 15), row shift in the accumulator:
+    // x = c2 (ush / c2 + q.k) + v_j  ~  log2(e) S + v_j + u_prev  on the band, -inf elsewhere
     const int o0 = b0 + 16 * wave;
     const int cw = o0 - 16 * H16;
     const bool rows_in = (o0 + 15 < Lr);
-    // Tile t covers keys cw + 16t .. cw + 16t + 15; over its entries i - j spans
-    // [16 H16 - 16 t - 15, 16 H16 - 16 t + 15].  Wave-uniform classes: "dead" tiles (no entry on
-    // the band or inside the sequence) skip the MFMA; "clean" tiles skip the per-entry masks.
-    // All MFMAs are issued first, each into its own accumulator, so LDS reads and matrix-core
-    // latency overlap across tiles; the vector pass follows.
-    auto dead_tile = [&](int t) -> bool {
-      const int j0 = cw + 16 * t;
-      const int dlo = 16 * H16 - 16 * t - 15, dhi = 16 * H16 - 16 * t + 15;
-      return (dlo > h) | (dhi < -h) | (j0 >= Lr) | (j0 + 15 < 0) | (o0 >= Lr);
-    };
-    auto tile_row = [&](int t) -> int { return (cw + 16 * t + 4 * RING) % RING; };  // no straddling
-    // x = log2(e) S + v_j on the band, -inf elsewhere (in place on the MFMA result)
-    auto transform = [&](f32x4& xt, int t, float vjt) {
-      const int j0 = cw + 16 * t;
-      const int dlo = 16 * H16 - 16 * t - 15, dhi = 16 * H16 - 16 * t + 15;
-      const bool clean = rows_in & (j0 >= 0) & (j0 + 15 < Lr) & (dhi <= h) & (dlo >= -h);
-      if (clean) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xt[r] = fmaf(xt[r], a.c2, vjt);
-      } else {
-        const int j = j0 + n;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = o0 + 4 * g + r;
-          const bool ok = (i < Lr) & (j >= 0) & (j < Lr) & (abs(i - j) <= h);
-          xt[r] = ok ? fmaf(xt[r], a.c2, vjt) : -INFINITY;
-        }
-      }
-    };
-    f32x4 x[NT];
+    const f32x4 shc = {ush[0] * inv_c2, ush[1] * inv_c2, ush[2] * inv_c2, ush[3] * inv_c2};
     // Interior blocks of a band whose half-width fills its halo class (h = 16 H16): every tile is
     // on the band and inside the sequence; only the first and last tiles cross the band edge,
     // along a fixed per-lane pattern (i - j <= h  <=>  4g + r <= n on tile 0, i - j >= -h  <=>
     // 4g + r >= n on tile NT - 1).  No per-tile tests.
     const bool interior = exact_h & (cb >= 0) & (cb + RING <= Lr) & (b0 + 64 <= Lr);
-    if (interior) {
-      int row = (cw + 4 * RING) % RING;
-      Frag<T> fk[2];
-      lds_frag(fk[0], kring, row + n, g);
+    const int row0 = (cw + 4 * RING) % RING;
+    auto strip = [&](f32x4 (&x)[NT]) {
+      if (interior) {
+        // per-lane bases plus a wave-uniform row offset per tile: one address add per read
+        const T* klane = kring + n * LS + 16 * g;
+        const float* vlane = vring + n;
+        auto tile_row = [&](int t) { return (row0 + 16 * t < RING) ? row0 + 16 * t : row0 + 16 * t - RING; };
+        auto kfrag = [&](Frag<T>& f, int rt) {
+          const f32x4* p = reinterpret_cast<const f32x4*>(klane + rt * LS);
+          if constexpr (sizeof(T) == 2) {
+            f.a = __builtin_bit_cast(bf16x8, p[0]);
+            f.b = __builtin_bit_cast(bf16x8, p[1]);
+          } else {
+            lds_frag(f, kring, rt + n, g);
+          }
+        };
+        Frag<T> fk[2];
+        kfrag(fk[0], tile_row(0));
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int rnext = (row + 16 >= RING) ? row + 16 - RING : row + 16;
-        if (t + 1 < NT) lds_frag(fk[(t + 1) & 1], kring, rnext + n, g);
-        const float vjt = vring[row + n];
-        x[t] = dot_tile(fq, fk[t & 1]);
+        for (int t = 0; t < NT; ++t) {
+          const int rt = tile_row(t);
+          if (t + 1 < NT) kfrag(fk[(t + 1) & 1], tile_row(t + 1));
+          const float vjt = vlane[rt];
+          x[t] = dot_tile(fq, fk[t & 1], shc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[t][r] = fmaf(x[t][r], a.c2, vjt);
-        if (t == 0) {
+          for (int r = 0; r < 4; ++r) x[t][r] = fmaf(x[t][r], c2, vjt);
+          if (t == 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[0][r] = (4 * g + r <= n) ? x[0][r] : -INFINITY;
+            for (int r = 0; r < 4; ++r) x[0][r] = (4 * g + r <= n) ? x[0][r] : -INFINITY;
+          }
+          if (t == NT - 1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[t][r] = (4 * g + r >= n) ? x[t][r] : -INFINITY;
+          }
         }
-        if (t == NT - 1) {
+      } else {
+        // Tile t covers keys cw + 16t .. cw + 16t + 15; over its entries i - j spans
+        // [16 H16 - 16 t - 15, 16 H16 - 16 t + 15].  Wave-uniform classes: "dead" tiles (no entry
+        // on the band or inside the sequence) skip the MFMA; "clean" tiles skip the masks.
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[t][r] = (4 * g + r >= n) ? x[t][r] : -INFINITY;
+        for (int t = 0; t < NT; ++t) {
+          const int j0 = cw + 16 * t;
+          const int dlo = 16 * H16 - 16 * t - 15, dhi = 16 * H16 - 16 * t + 15;
+          const bool dead = (dlo > h) | (dhi < -h) | (j0 >= Lr) | (j0 + 15 < 0) | (o0 >= Lr);
+          if (dead) {
+            x[t] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            continue;
+          }
+          const int rt = (row0 + 16 * t) % RING;
+          Frag<T> fk;
+          lds_frag(fk, kring, rt + n, g);
+          const float vjt = vring[rt + n];
+          x[t] = dot_tile(fq, fk, shc);
+          const bool clean = rows_in & (j0 >= 0) & (j0 + 15 < Lr) & (dhi <= h) & (dlo >= -h);
+          if (clean) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[t][r] = fmaf(x[t][r], c2, vjt);
+          } else {
+            const int j = j0 + n;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = o0 + 4 * g + r;
+              const bool ok = (i < Lr) & (j >= 0) & (j < Lr) & (abs(i - j) <= h);
+              x[t][r] = ok ? fmaf(x[t][r], c2, vjt) : -INFINITY;
+            }
+          }
         }
-        row = rnext;
       }
-    } else {
+    };
+
+    // column sums of the new plan over the wave's 16 rows: in-lane over the 4 rows, then over the
+    // four lane groups (lanes n, n + 16, n + 32, n + 48 hold the same key).  gfx950 lane swaps
+    // reduce four tiles at once: v_permlane32_swap(cp_a, cp_b) leaves a's and b's half sums in the
+    // low and high 32 lanes, v_permlane16_swap of two such pairs leaves the full sums of tiles
+    // a, c, b, d in lane groups 0..3; each lane then stores one tile's sum for its key.
+    // Lane group g of a reduced quad (tiles q, q+1, q+2, q+3) holds tile q + {0, 2, 1, 3}[g].
+    const int gsel = (g == 1) ? 2 : (g == 2) ? 1 : g;
+    // cp[t]: this lane's key of tile t summed over its 4 rows of the new plan
+    auto emit_columns = [&](float (&cp)[NT + 3]) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (dead_tile(t)) {
-          x[t] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-          continue;
+      for (int t = NT; t < NT + 3; ++t) cp[t] = 0.f;
+#pragma unroll
+      for (int q = 0; q < NT; q += 4) {
+        const float s4 = swap16_sum(swap32_sum(cp[q], cp[q + 1]), swap32_sum(cp[q + 2], cp[q + 3]));
+        const int t = q + gsel;
+        if (t < NT) cpart[wave * RING + 16 * wave + 16 * t + n] = s4;
+      }
+    };
+
+    // Row log-sum-exp.  With SHIFT the previous row duals are already in x, and then 2^x is an
+    // entry of the previous plan after its column normalisation (x = log2 P_prev - log2 colsum),
+    // so every term is at most 1 and every row sum lies in [1 / (2h + 1), 2h + 1]: no max pass
+    // is needed.  Without SHIFT (the first step, from u = 0) the exact row maximum is subtracted.
+    // u = -log2 sum_j 2^(c2 S_ij + v_j) either way.
+    float u[4];
+    float cp[NT + 3];
+    {
+      f32x4 x[NT];
+      strip(x);
+      float mx[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!SHIFT) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float mm = x[0][r];
+#pragma unroll
+          for (int t = 1; t < NT; ++t) mm = fmaxf(mm, x[t][r]);
+          mm = row16_max(mm);
+          mx[r] = (mm == -INFINITY) ? 0.f : mm;     // empty rows (past the sequence) stay 0
+#pragma unroll
+          for (int t = 0; t < NT; ++t) x[t][r] -= mx[r];
         }
-        Frag<T> fk;
-        lds_frag(fk, kring, tile_row(t) + n, g);
-        const float vjt = vring[tile_row(t) + n];
-        x[t] = dot_tile(fq, fk);
-        transform(x[t], t, vjt);
       }
-    }
-    float m[4], rinv[4], u[4];
+      float ll[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float mm = x[0][r];
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int t = 1; t < NT; ++t) mm = fmaxf(mm, x[t][r]);
-      m[r] = row16_max(mm);
-    }
+        for (int r = 0; r < 4; ++r) {
+          x[t][r] = fast_exp2(x[t][r]);
+          ll[r] += x[t][r];
+        }
+      float rinv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ms = (m[r] == -INFINITY) ? 0.f : m[r];
-      float ll = 0.f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        x[t][r] = fast_exp2(x[t][r] - ms);
-        ll += x[t][r];
+      for (int r = 0; r < 4; ++r) {
+        ll[r] = row16_sum(ll[r]);
+        const bool empty = (ll[r] == 0.f);          // no terms: rows past the sequence
+        u[r] = empty ? 0.f : fmaf(shc[r], c2, -(mx[r] + fast_log2(ll[r])));
+        rinv[r] = empty ? 0.f : __builtin_amdgcn_rcpf(ll[r]);
       }
-      const float l = row16_sum(ll);
-      const bool empty = (m[r] == -INFINITY);
-      u[r] = empty ? 0.f : -(m[r] + fast_log2(l));
-      rinv[r] = empty ? 0.f : __builtin_amdgcn_rcpf(l);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        cp[t] = x[t][0] * rinv[0] + x[t][1] * rinv[1] + x[t][2] * rinv[2] + x[t][3] * rinv[3];
     }
+    emit_columns(cp);
     if (n < 4) {
       const int i = o0 + 4 * g + n;
       const float ui = (n == 0) ? u[0] : (n == 1) ? u[1] : (n == 2) ? u[2] : u[3];
@@ -291,59 +360,29 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
         if (a.save_u) a.save_u[head * a.save_u_stride + i] = ui * kLn2;
       }
     }
-    // column sums of the new plan over the wave's 16 rows: in-lane over the 4 rows, then over the
-    // four lane groups (lanes n, n + 16, n + 32, n + 48 hold the same key).  gfx950 lane swaps
-    // reduce four tiles at once: v_permlane32_swap(cp_a, cp_b) leaves a's and b's half sums in the
-    // low and high 32 lanes, v_permlane16_swap of two such pairs leaves the full sums of tiles
-    // a, c, b, d in lane groups 0..3; each lane then stores one tile's sum for its key.
-    float cp[NT + 3];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      cp[t] = x[t][0] * rinv[0] + x[t][1] * rinv[1] + x[t][2] * rinv[2] + x[t][3] * rinv[3];
-#pragma unroll
-    for (int t = NT; t < NT + 3; ++t) cp[t] = 0.f;
-    auto swap32 = [](float a, float b) {
-      const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-      return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    };
-    auto swap16 = [](float a, float b) {
-      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-      return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    };
-    // lane group g of a reduced quad (tiles q, q+1, q+2, q+3) holds tile q + {0, 2, 1, 3}[g]
-    const int gsel = (g == 1) ? 2 : (g == 2) ? 1 : g;
-#pragma unroll
-    for (int q = 0; q < NT; q += 4) {
-      const float ab = swap32(cp[q], cp[q + 1]);
-      const float cd = swap32(cp[q + 2], cp[q + 3]);
-      const float s4 = swap16(ab, cd);
-      const int t = q + gsel;
-      if (t < NT) cpart[wave * RING + 16 * wave + 16 * t + n] = s4;
-    }
     __syncthreads();
-    // block column sums (fixed wave order) into the segment accumulator
+    // Block column sums (fixed wave order) into the segment accumulator.  Columns [cb, cb + 64)
+    // leave the window with this block: their sums are written out and their ring slots take the
+    // next block's new keys [cb + RING, cb + RING + 64) (every wave is past its reads of kring
+    // and vring for this block).
     for (int c = threadIdx.x; c < RING; c += 256) {
       const float sacc = ((cpart[c] + cpart[RING + c]) + cpart[2 * RING + c]) + cpart[3 * RING + c];
-      pring[(cb + c + 4 * RING) % RING] += sacc;
-    }
-    __syncthreads();
-    if (more) {
-      // columns [cb, cb + 64) leave the window: write them out, then reuse their ring slots
-      // for the next block's new keys [cb + RING, cb + RING + 64)
-      if (threadIdx.x < 64) {
-        const int j = cb + threadIdx.x, slot = (j + 4 * RING) % RING;
-        part_out_h[j - c_lo] = pring[slot];
+      const int j = cb + c, slot = (j + 4 * RING) % RING;
+      if (!more) {
+        part_out_h[j - c_lo] = pring[slot] + sacc;
+      } else if (c < 64) {
+        part_out_h[j - c_lo] = pring[slot] + sacc;
         pring[slot] = 0.f;
         vring[slot] = finish_from(j + RING, nc);
+      } else {
+        pring[slot] += sacc;
       }
+    }
+    if (more) {
       nr.template store<RING>(kring, cb + RING);
       fq = fq_next;
+      ush = ush_next;
       __syncthreads();
-    } else {
-      for (int c = threadIdx.x; c < RING; c += 256) {
-        const int j = cb + c;
-        part_out_h[j - c_lo] = pring[(j + 4 * RING) % RING];
-      }
     }
   }
 }
@@ -389,7 +428,9 @@ void fused_segments(int64_t bh, int Lr, int nt, int* seg_len, int* nseg) {
 template <typename T, int NT>
 static void launch_step_t(const StepArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.bh * (int64_t)a.nseg);
-  sinkhorn_step_kernel<T, NT><<<dim3(blocks), dim3(256), 0, st>>>(a);
+  // the first step (no column partials yet, u = 0) has no previous plan to shift by
+  if (a.part_prev) sinkhorn_step_kernel<T, NT, true><<<dim3(blocks), dim3(256), 0, st>>>(a);
+  else sinkhorn_step_kernel<T, NT, false><<<dim3(blocks), dim3(256), 0, st>>>(a);
 }
 
 hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, hipStream_t st) {
