@@ -308,6 +308,21 @@ struct RowStage {
         x[i] = *reinterpret_cast<const uint4*>(rb + (unsigned)(row * kD + col));
     }
   }
+  // store into ring slots slot0, slot0 + 1, .. (slot0 a wave-uniform multiple of 16), wrapping
+  // at RING
+  template <int RING>
+  __device__ __forceinline__ void store_slots(T* ring, int slot0) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * NTHR + (int)threadIdx.x;
+      const int row = c / kChunksPerRow, col = (c % kChunksPerRow) * (16 / (int)sizeof(T));
+      if (ROWS * kChunksPerRow % NTHR == 0 || row < ROWS) {
+        int rr = slot0 + row;
+        if (RING % 64 != 0 || ROWS > 64 || rr >= RING) rr = (rr >= RING) ? rr - RING : rr;
+        *reinterpret_cast<uint4*>(ring + rr * Lds<T>::stride + col) = x[i];
+      }
+    }
+  }
   template <int RING>
   __device__ __forceinline__ void store(T* ring, int r0) const {
 #pragma unroll

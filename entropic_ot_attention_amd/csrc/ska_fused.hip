@@ -70,8 +70,10 @@ __device__ float exact_column(int j, const float* u_h, const T* Qh, const T* Kh,
 // columns [S k - 16 H16, S (k + 1) + 16 H16) with S = 64 seg_len, so at most two segments hold a
 // partial for j (seg_len >= H16 / 2); they are added in ascending segment order.
 // Loads of the column finish for key j: the (at most two) segment partials and the previous dual.
+// The column sum is p0 w0 + p1 w1 with weights 0 or 1 (partials are finite), applied where the
+// values are used, so that issuing the loads never waits on them.
 struct ColIn {
-  float p0, p1, vp;
+  float p0, p1, vp, w0, w1;
 };
 __device__ __forceinline__ ColIn column_loads(int j, const float* vprev_h, const float* part_h,
                                               const StepArgs& a) {
@@ -86,9 +88,9 @@ __device__ __forceinline__ ColIn column_loads(int j, const float* vprev_h, const
     const bool ok = (k <= k1) & (c >= 0) & (c < a.pstride);
     const int kc = min(k, a.nseg - 1), cc = min(max(c, 0), a.pstride - 1);
     const float x = part_h[(int64_t)kc * a.pstride + cc];
-    p[q] = ok ? x : 0.f;
+    p[q] = ok ? x : 0.f;     // an unused slot may hold anything, even non-finite values
   }
-  return ColIn{p[0], p[1], vprev_h[jc]};
+  return ColIn{p[0], p[1], vprev_h[jc], 1.f, 1.f};
 }
 
 // Finished column dual (log2 units) of key j from the previous dual and the column sums of
@@ -98,7 +100,7 @@ __device__ __forceinline__ ColIn column_loads(int j, const float* vprev_h, const
 template <typename T>
 __device__ __forceinline__ float column_combine(int j, const ColIn& in, const float* u_h, const T* Qh,
                                                 const T* Kh, const StepArgs& a) {
-  const float s = in.p0 + in.p1;
+  const float s = in.p0 * in.w0 + in.p1 * in.w1;
   if (s >= 0x1p-60f) return in.vp - fast_log2(s);
   return exact_column<T>(j, u_h, Qh, Kh, a.Lr, a.h, a.c2);
 }
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   };
   auto loads_for = [&](int j) -> ColIn {
     if (part_prev_h) return column_loads(j, a.v_prev + vo, part_prev_h, a);
-    return ColIn{0.f, 0.f, a.v_prev[vo + min(max(j, 0), Lr - 1)]};
+    return ColIn{0.f, 0.f, a.v_prev[vo + min(max(j, 0), Lr - 1)], 0.f, 0.f};
   };
   // previous row duals of rows o, .., o + 3 (log2 units); the dual buffers are padded to Lpad,
   // a multiple of 64, and hold 0 past Lr
@@ -175,7 +177,11 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   // prologue: the first block's whole window, query fragment and row shifts
   Frag<T> fq;
   load_frag(fq, Qh + (int64_t)(64 * blk0 + 16 * wave + n) * kD, 64 * blk0 + 16 * wave + n < Lr, g);
-  f32x4 ush = shift_rows(64 * blk0 + 16 * wave + 4 * g);
+  // row shifts / c2 for the matrix-core accumulator, carried from block to block
+  auto shift_acc = [&](f32x4 us) {
+    return f32x4{us[0] * inv_c2, us[1] * inv_c2, us[2] * inv_c2, us[3] * inv_c2};
+  };
+  f32x4 shc = shift_acc(shift_rows(64 * blk0 + 16 * wave + 4 * g));
   {
     RowStage<T, RING, 256> first;
     first.load(Kh, c_lo, Lr);
@@ -192,20 +198,42 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     const int b0 = 64 * blk;
     const int cb = b0 - 16 * H16;             // block window [cb, cb + RING)
     const bool more = blk + 1 < blk1;
+    // ring slot of the window's first key (a multiple of 16; the 64 keys [cb, cb + 64) occupy
+    // consecutive slots unless the ring is not a multiple of 64 keys past it)
+    const int s_cb = (cb + RING) % RING;
+    // the wave that finishes the columns leaving with this block rotates, so that extra work
+    // spreads over the four SIMDs
+    const int dw = blk & 3;
     // prefetch the 64 key rows the next block adds: [cb + RING, cb + RING + 64)
     // (and the next block's query fragment, row shifts and new column loads), all in flight
     // during compute
     RowStage<T, 64, 256> nr;
-    ColIn nc{0.f, 0.f, 0.f};
+    ColIn nc{0.f, 0.f, 0.f, 0.f, 0.f};
     Frag<T> fq_next;
     f32x4 ush_next;
     if (more) {
       if (cb + RING >= 0 && cb + RING + 64 <= Lr) nr.load_inside(Kh, cb + RING);
       else nr.load(Kh, cb + RING, Lr);
       const int on = b0 + 64 + 16 * wave + n;
-      load_frag(fq_next, Qh + (int64_t)on * kD, on < Lr, g);
+      load_frag(fq_next, Qh + (int64_t)on * kD, (b0 + 128 <= Lr) || (on < Lr), g);
       ush_next = shift_rows(b0 + 64 + 16 * wave + 4 * g);
-      if (threadIdx.x < 64) nc = loads_for(cb + RING + (int)threadIdx.x);
+      if (wave == dw) {
+        // Keys j = cb + RING + lane enter with the next block.  Inside a segment their first
+        // column partial is the segment's own (at offset j - c_lo of its row) and a second one
+        // comes from the next segment once j - c_lo reaches S = 64 seg_len (the same loads and
+        // order as column_loads, without its divisions).
+        const int j = cb + RING + lane;
+        const float vp = a.v_prev[vo + min(j, Lr - 1)];
+        if (part_prev_h) {
+          const int c0 = j - c_lo, c1 = c0 - 64 * a.seg_len;
+          const bool two = (c1 >= 0) & (seg + 1 < a.nseg);
+          const float p0 = part_prev_h[(int64_t)seg * a.pstride + c0];
+          const float p1 = part_prev_h[(int64_t)(two ? seg + 1 : seg) * a.pstride + (two ? c1 : c0)];
+          nc = ColIn{p0, p1, vp, 1.f, two ? 1.f : 0.f};
+        } else {
+          nc = ColIn{0.f, 0.f, vp, 0.f, 0.f};
+        }
+      }
     }
 
     // score strip in registers (wave rows o0 .. o0 + 15), row shift in the accumulator:
@@ -213,7 +241,6 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     const int o0 = b0 + 16 * wave;
     const int cw = o0 - 16 * H16;
     const bool rows_in = (o0 + 15 < Lr);
-    const f32x4 shc = {ush[0] * inv_c2, ush[1] * inv_c2, ush[2] * inv_c2, ush[3] * inv_c2};
     // Interior blocks of a band whose half-width fills its halo class (h = 16 H16): every tile is
     // on the band and inside the sequence; only the first and last tiles cross the band edge,
     // along a fixed per-lane pattern (i - j <= h  <=>  4g + r <= n on tile 0, i - j >= -h  <=>
@@ -362,26 +389,34 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     }
     __syncthreads();
     // Block column sums (fixed wave order) into the segment accumulator.  Columns [cb, cb + 64)
-    // leave the window with this block: their sums are written out and their ring slots take the
+    // leave the window with this block: wave dw writes their sums out and its slots take the
     // next block's new keys [cb + RING, cb + RING + 64) (every wave is past its reads of kring
     // and vring for this block).
-    for (int c = threadIdx.x; c < RING; c += 256) {
-      const float sacc = ((cpart[c] + cpart[RING + c]) + cpart[2 * RING + c]) + cpart[3 * RING + c];
-      const int j = cb + c, slot = (j + 4 * RING) % RING;
-      if (!more) {
-        part_out_h[j - c_lo] = pring[slot] + sacc;
-      } else if (c < 64) {
-        part_out_h[j - c_lo] = pring[slot] + sacc;
+    auto slot_of = [&](int c) {
+      const int sl = s_cb + c;
+      return (sl >= RING) ? sl - RING : sl;
+    };
+    auto block_sum = [&](int c) {
+      return ((cpart[c] + cpart[RING + c]) + cpart[2 * RING + c]) + cpart[3 * RING + c];
+    };
+    for (int c = 64 + (int)threadIdx.x; c < RING; c += 256) {
+      const float sacc = block_sum(c);
+      const int slot = slot_of(c);
+      if (more) pring[slot] += sacc;
+      else part_out_h[cb + c - c_lo] = pring[slot] + sacc;
+    }
+    if (wave == dw) {
+      const int c = lane, slot = slot_of(c);
+      part_out_h[cb + c - c_lo] = pring[slot] + block_sum(c);
+      if (more) {
         pring[slot] = 0.f;
-        vring[slot] = finish_from(j + RING, nc);
-      } else {
-        pring[slot] += sacc;
+        vring[slot] = finish_from(cb + RING + c, nc);
       }
     }
     if (more) {
-      nr.template store<RING>(kring, cb + RING);
+      nr.template store_slots<RING>(kring, s_cb);
       fq = fq_next;
-      ush = ush_next;
+      shc = shift_acc(ush_next);
       __syncthreads();
     }
   }
