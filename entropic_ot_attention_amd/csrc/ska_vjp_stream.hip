@@ -20,16 +20,22 @@
 // Work decomposition as in the fused forward step: a workgroup of NW waves walks a segment of
 // consecutive blocks of 16 NW owned tokens; the band window of the block (16 NW + 32 H16
 // tokens) of the two window-side tensors lives in LDS rings, each block brings in only its 16 NW
-// new rows (loaded one block ahead), and the window-side vectors live in rings alongside.
-// Pass 2 keeps its 16 x (16 + 32 H16) reference-plan strip in registers (owned rows in lane
-// registers, keys across lanes) so the column sums need du2, known only after the sweep; passes
-// 1, 3 and 4 put the window in lane registers and the owned tokens across lanes, so sums over
-// the window stay in-lane and contractions over the window feed the matrix cores directly, the
-// other operand read transposed from its LDS ring.
+// new rows (loaded one block ahead, together with the next block's owned operands and owned-side
+// vectors; no load is waited on where it is issued), and the window-side vectors live in rings
+// alongside.  Pass 2 keeps its 16 x (16 + 32 H16) reference-plan strip in registers (owned rows
+// in lane registers, keys across lanes) so the column sums need du2, known only after the sweep;
+// passes 0, 1, 3 and 4 put the window in lane registers and the owned tokens across lanes, so
+// sums over the window stay in-lane and contractions over the window feed the matrix cores
+// directly, the other operand read transposed from its LDS ring.  The owned-side dual enters the
+// matrix-core accumulator, so each reference-plan entry costs one fma and one exponential.
+// Interior blocks of a band that fills its halo class (h = 16 H16) run a straight-line path whose
+// only masks are fixed per-lane patterns on the first and last tiles.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "ska_device.h"
 #include "ska_internal.h"
@@ -42,21 +48,11 @@ namespace ska {
 // rb + 4 g + e (e = 0..3) of column c0 + n: one half of a bf16 MFMA A operand of the
 // transposed ring rows.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ s16x4 tr_read(const bf16* ring, int row, int col) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (s16x4 __attribute__((address_space(3)))*)(ring + row * Lds<bf16>::stride + col));
-}
-__device__ __forceinline__ bf16x8 tr_operand(const bf16* ring, int rb0, int rb1, int b, int g, int n) {
-  const int r = 4 * g + (n >> 2), c = 16 * b + 4 * (n & 3);
-  const s16x4 lo = tr_read(ring, rb0 + r, c), hi = tr_read(ring, rb1 + r, c);
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
+__device__ __forceinline__ s16x4 tr_read(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p));
 }
 
-// acc[b][r] (lane l) += sum over the 32 window rows of tiles (rb0, rb1) of
-//   Op[row][16 b + 4 g + r] * Z[row][n]    (Op rows read transposed from the LDS ring)
-// z[tt][r] holds Z for row rb_tt + 4 g + r at owned token n.
+// z[tt][r] -> bf16 B operand (rows 4 g + r of tile tt of the pair)
 __device__ __forceinline__ bf16x8 pack_z(const float (&z)[2][4]) {
   bf16x8 zb;
 #pragma unroll
@@ -66,47 +62,62 @@ __device__ __forceinline__ bf16x8 pack_z(const float (&z)[2][4]) {
   }
   return zb;
 }
-__device__ __forceinline__ void contract_ring(f32x4 (&acc)[4], const bf16* ring, int rb0, int rb1,
-                                              const float (&z)[2][4], int g, int n) {
+
+// Contractions over the 32 window rows of a tile pair (ring slots rt0, rt1):
+//   acc[b][r] (lane (g, n)) += sum_rows Op[row][16 b + 4 g + r] * Z[row][n]
+// with Op read transposed from the ring and z[tt][r] = Z[rt_tt + 4 g + r][n].
+struct TrLane {   // per-lane part of the transposed-read address (bf16 rings)
+  int off;
+  __device__ TrLane(int g, int n) : off((4 * g + (n >> 2)) * Lds<bf16>::stride + 4 * (n & 3)) {}
+};
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* ring, const TrLane& tl, int rt0, int rt1, int b) {
+  const s16x4 lo = tr_read(ring + tl.off + rt0 * Lds<bf16>::stride + 16 * b);
+  const s16x4 hi = tr_read(ring + tl.off + rt1 * Lds<bf16>::stride + 16 * b);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ void contract_pair(f32x4 (&acc)[4], const bf16* ring, const TrLane& tl,
+                                              int rt0, int rt1, const float (&z)[2][4], int, int) {
   const bf16x8 zb = pack_z(z);
 #pragma unroll
   for (int b = 0; b < 4; ++b)
-    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(ring, rb0, rb1, b, g, n), zb, acc[b], 0, 0, 0);
+    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(ring, tl, rt0, rt1, b), zb, acc[b], 0, 0, 0);
 }
-// Two contractions against the same ring rows (shares the transposed reads).
-__device__ __forceinline__ void contract_ring2(f32x4 (&x)[4], f32x4 (&y)[4], const bf16* ring, int rb0,
-                                               int rb1, const float (&z1)[2][4],
-                                               const float (&z2)[2][4], int g, int n) {
+__device__ __forceinline__ void contract_pair2(f32x4 (&x)[4], f32x4 (&y)[4], const bf16* ring,
+                                               const TrLane& tl, int rt0, int rt1,
+                                               const float (&z1)[2][4], const float (&z2)[2][4], int,
+                                               int) {
   const bf16x8 zb1 = pack_z(z1), zb2 = pack_z(z2);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const bf16x8 av = tr_operand(ring, rb0, rb1, b, g, n);
+    const bf16x8 av = tr_operand(ring, tl, rt0, rt1, b);
     x[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, zb1, x[b], 0, 0, 0);
     y[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, zb2, y[b], 0, 0, 0);
   }
 }
-__device__ __forceinline__ void contract_ring(f32x4 (&acc)[4], const float* ring, int rb0, int rb1,
-                                              const float (&z)[2][4], int g, int n) {
+__device__ __forceinline__ void contract_pair(f32x4 (&acc)[4], const float* ring, const TrLane&,
+                                              int rt0, int rt1, const float (&z)[2][4], int g, int n) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = (tt == 0 ? rb0 : rb1) + 4 * g + r;
+      const int row = (tt == 0 ? rt0 : rt1) + 4 * g + r;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(ring[row * Lds<float>::stride + 16 * b + n],
                                                       z[tt][r], acc[b], 0, 0, 0);
     }
 }
-
-__device__ __forceinline__ void contract_ring2(f32x4 (&x)[4], f32x4 (&y)[4], const float* ring,
-                                               int rb0, int rb1, const float (&z1)[2][4],
-                                               const float (&z2)[2][4], int g, int n) {
+__device__ __forceinline__ void contract_pair2(f32x4 (&x)[4], f32x4 (&y)[4], const float* ring,
+                                               const TrLane&, int rt0, int rt1,
+                                               const float (&z1)[2][4], const float (&z2)[2][4],
+                                               int g, int n) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = (tt == 0 ? rb0 : rb1) + 4 * g + r;
+      const int row = (tt == 0 ? rt0 : rt1) + 4 * g + r;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const float av = ring[row * Lds<float>::stride + 16 * b + n];
@@ -116,17 +127,25 @@ __device__ __forceinline__ void contract_ring2(f32x4 (&x)[4], f32x4 (&y)[4], con
     }
 }
 
+// Window-tile operand fragment at ring slot rt (rows rt + n, d-slice of lane group g): bf16 reads
+// from a per-lane base plus a wave-uniform row offset; fp32 through lds_frag.
+__device__ __forceinline__ void ring_frag(Frag<bf16>& f, const bf16* ring, const bf16* lane_base, int rt,
+                                          int, int) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(lane_base + rt * Lds<bf16>::stride);
+  f.a = __builtin_bit_cast(bf16x8, p[0]);
+  f.b = __builtin_bit_cast(bf16x8, p[1]);
+}
+__device__ __forceinline__ void ring_frag(Frag<float>& f, const float* ring, const float*, int rt, int g,
+                                          int n) {
+  lds_frag(f, ring, rt + n, g);
+}
+
 template <int PASS> struct VjpPass {
   static constexpr bool owns_keys = (PASS == 1 || PASS == 4);
   // window-side vectors kept in LDS rings
   static constexpr int nvec = PASS <= 1 ? 1 : PASS == 2 ? 2 : PASS == 3 ? 5 : 4;
-};
-
-template <typename T, int NT, int NW, int PASS>
-struct VjpSmem {
-  static constexpr int kH16 = (NT - 1) / 2;
-  static constexpr int kBR = 16 * NW;
-  static constexpr int kRing = kBR + 32 * kH16;
+  // owned-side values per lane (pass 2: the dual of each of the lane's 4 owned rows)
+  static constexpr int nown = PASS <= 1 ? 1 : PASS == 2 ? 4 : PASS == 3 ? 3 : 5;
 };
 
 template <typename T, int NT, int NW, int PASS>
@@ -136,11 +155,12 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   constexpr int BR = 16 * NW;                  // owned tokens per block
   constexpr int RING = BR + 32 * H16;          // block window
   constexpr int NTHR = NW * 64;
-  constexpr int NV = P::nvec;
+  constexpr int NV = P::nvec, NO = P::nown;
   constexpr int NP = (NT + 1) / 2;             // tile pairs of a contraction
-  __shared__ __attribute__((aligned(16))) T ringA[RING * Lds<T>::stride];  // S window operand
-  __shared__ __attribute__((aligned(16))) T ringB[RING * Lds<T>::stride];  // g window operand
-  __shared__ float wv[NV][RING];                                          // window vectors
+  constexpr int LS = Lds<T>::stride;
+  __shared__ __attribute__((aligned(16))) T ringA[RING * LS];  // S window operand
+  __shared__ __attribute__((aligned(16))) T ringB[RING * LS];  // g window operand
+  __shared__ __attribute__((aligned(16))) float wv[NV][RING];  // window vectors
   __shared__ float pring[PASS == 2 ? RING : 1];
   __shared__ float cpart[PASS == 2 ? NW * RING : 1];
 
@@ -149,9 +169,11 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   const int64_t head = blockIdx.x / a.nseg;
   const int seg = blockIdx.x % a.nseg;
   const int blk0 = seg * a.seg_len, blk1 = min(blk0 + a.seg_len, a.nblk);
-  const int c_lo = BR * blk0 - 16 * H16;
+  const int halo = 16 * H16;
+  const int c_lo = BR * blk0 - halo;
   const int own_lo = BR * blk0, own_hi = BR * blk1;
   const int Lr = a.Lr, h = a.h;
+  const float c2 = a.c2, inv_c2 = 1.f / a.c2;
   const int64_t tb = head * (int64_t)Lr * kD;
   const T* winA = static_cast<const T*>(P::owns_keys ? a.Q : a.K) + tb;
   const T* winB = static_cast<const T*>(P::owns_keys ? a.dO : a.V) + tb;
@@ -160,70 +182,125 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   const int64_t vo = head * (int64_t)a.Lpad;
   auto vec = [&](int which) -> float* { return a.ws + which * a.vec_stride + vo; };
   const bool exact_h = (h == 16 * H16);
-
-  // window-side vector entry k of token j (0 outside the sequence)
-  auto window_vec = [&](int k, int j) -> float {
-    const int jc = min(max(j, 0), Lr - 1);
-    float x;
-    if (PASS == 0) x = a.fv[vo + jc];
-    else if (PASS == 1) x = vec(kU2)[jc];
-    else if (PASS == 2) x = (k == 0) ? vec(kV2)[jc] : vec(kDV2)[jc];
-    else if (PASS == 3) {
-      const int src[5] = {kV2, kDV2, kEE, kFF, kEG};
-      x = vec(src[k])[jc];
-    } else {
-      const int src[4] = {kU2, kDU2, kEB, kCC};
-      x = vec(src[k])[jc];
-    }
-    return (j >= 0 && j < Lr) ? x : 0.f;
-  };
-  // pass 3: finished dv1 of key j from the pass-2 segment column sums; the owner stores dv1, F
   const float* part_h = a.part + head * (int64_t)a.nseg * a.pstride;
-  auto dv1_loads = [&](int j, float& p0, float& p1, float& e) {
-    const int S = BR * a.seg_len, halo = 16 * H16;
-    const int jc = min(max(j, 0), Lr - 1);
-    const int k0 = max(0, floor_div(jc - halo, S)), k1 = min(a.nseg - 1, floor_div(jc + halo, S));
-    float pp[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int k = k0 + q, c = jc - (S * k - halo);
-      const bool ok = (k <= k1) & (c >= 0) & (c < a.pstride);
-      const float x = part_h[(int64_t)min(k, a.nseg - 1) * a.pstride + min(max(c, 0), a.pstride - 1)];
-      pp[q] = ok ? x : 0.f;
-    }
-    p0 = pp[0];
-    p1 = pp[1];
-    e = vec(kEE)[jc];
-  };
-  // loads of the NV window vectors of token j (pass 3 computes F from the dv1 partials)
+
+  // ---- window-side vectors of token j: raw loads and a 0/1 weight applied when stored ----
   struct VecIn {
     float v[NV];
-    float p0, p1;
+    float w;               // token inside the sequence
+    float p0, p1, w0, w1;  // pass 3: dv1 column partials of the pass-2 segments and weights
   };
-  auto vec_loads = [&](int j) -> VecIn {
+  auto vec_raw = [&](int jc, VecIn& r) {
+    if constexpr (PASS == 0) {
+      r.v[0] = a.fv[vo + jc];
+    } else if constexpr (PASS == 1) {
+      r.v[0] = vec(kU2)[jc];
+    } else if constexpr (PASS == 2) {
+      r.v[0] = vec(kV2)[jc];
+      r.v[1] = vec(kDV2)[jc];
+    } else if constexpr (PASS == 3) {
+      r.v[0] = vec(kV2)[jc];
+      r.v[1] = vec(kDV2)[jc];
+      r.v[2] = vec(kEE)[jc];
+      r.v[3] = 0.f;                  // F: computed from the dv1 partials when stored
+      r.v[4] = vec(kEG)[jc];
+    } else {
+      r.v[0] = vec(kU2)[jc];
+      r.v[1] = vec(kDU2)[jc];
+      r.v[2] = vec(kEB)[jc];
+      r.v[3] = vec(kCC)[jc];
+    }
+  };
+  // any token j (window of the first block): clamped loads, partials found by segment division
+  auto vec_loads_any = [&](int j) -> VecIn {
     VecIn r;
+    const int jc = min(max(j, 0), Lr - 1);
+    vec_raw(jc, r);
+    r.w = (j >= 0 && j < Lr) ? 1.f : 0.f;
+    r.p0 = r.p1 = r.w0 = r.w1 = 0.f;
+    if constexpr (PASS == 3) {
+      const int S = BR * a.seg_len;
+      const int k0 = max(0, floor_div(jc - halo, S)), k1 = min(a.nseg - 1, floor_div(jc + halo, S));
+      float pp[2];
 #pragma unroll
-    for (int k = 0; k < NV; ++k) r.v[k] = window_vec(k, j);
-    r.p0 = r.p1 = 0.f;
-    if (PASS == 3) {
-      float e;
-      dv1_loads(j, r.p0, r.p1, e);
+      for (int q = 0; q < 2; ++q) {
+        const int k = k0 + q, c = jc - (S * k - halo);
+        const bool ok = (k <= k1) & (c >= 0) & (c < a.pstride);
+        const float x = part_h[(int64_t)min(k, a.nseg - 1) * a.pstride + min(max(c, 0), a.pstride - 1)];
+        pp[q] = ok ? x : 0.f;   // an unused slot may hold anything
+      }
+      r.p0 = pp[0];
+      r.p1 = pp[1];
+      r.w0 = r.w1 = 1.f;
     }
     return r;
   };
-  auto vec_store = [&](int j, const VecIn& in) {
-    const int slot = (j + 4 * RING) % RING;
+  // token j = cb + RING + t entering with the next block (j > 0).  Inside a segment its first
+  // dv1 partial is the segment's own, at offset j - c_lo of its row, and a second one comes from
+  // the next segment once j - c_lo reaches S = BR seg_len (no division; the loads never wait).
+  auto vec_loads_next = [&](int j) -> VecIn {
+    VecIn r;
+    const bool in = j < Lr;
+    vec_raw(in ? j : Lr - 1, r);
+    r.w = in ? 1.f : 0.f;
+    r.p0 = r.p1 = r.w0 = r.w1 = 0.f;
+    if constexpr (PASS == 3) {
+      const int c0 = j - c_lo, c1 = c0 - BR * a.seg_len;
+      const bool two = in & (c1 >= 0) & (seg + 1 < a.nseg);
+      const int c0i = in ? c0 : 0;      // offset 0 of a segment row is always written
+      r.p0 = part_h[(int64_t)seg * a.pstride + c0i];
+      r.p1 = part_h[(int64_t)(two ? seg + 1 : seg) * a.pstride + (two ? c1 : c0i)];
+      r.w0 = r.w;
+      r.w1 = two ? 1.f : 0.f;
+    }
+    return r;
+  };
+  auto vec_store = [&](int j, int slot, const VecIn& in) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) wv[k][slot] = in.v[k];
-    if (PASS == 3) {
-      const bool ok = (j >= 0 && j < Lr);
-      const float E = in.v[2];
-      const float dv1 = ok ? -E * (in.p0 + in.p1) : 0.f;
+    for (int k = 0; k < NV; ++k) wv[k][slot] = in.v[k] * in.w;
+    if constexpr (PASS == 3) {
+      const float E = in.v[2] * in.w;
+      const float dv1 = -E * (in.p0 * in.w0 + in.p1 * in.w1);
       wv[3][slot] = dv1 * E;                         // F = dv1 e^{dv1}
-      if (ok && j >= own_lo && j < own_hi) {
+      if (in.w != 0.f && j >= own_lo && j < own_hi) {
         vec(kDV1)[j] = dv1;
         vec(kFF)[j] = dv1 * E;
       }
+    }
+  };
+
+  // ---- owned-side values of the block rows o0 .. o0 + 15 (raw loads), and their prepared
+  // form: own[0] (pass 2: own[0..3]) becomes the owned dual / c2 for the accumulator ----
+  auto own_loads = [&](int o0, float (&o)[NO]) {
+    if constexpr (PASS == 2) {
+      const f32x4 u = load4(vec(kU2) + min(o0 + 4 * g, a.Lpad - 4));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = u[r];
+    } else {
+      const int oc = min(o0 + n, Lr - 1);
+      if constexpr (PASS == 0) {
+        o[0] = a.fu[vo + oc];
+      } else if constexpr (PASS == 1) {
+        o[0] = vec(kV2)[oc];
+      } else if constexpr (PASS == 3) {
+        o[0] = vec(kU2)[oc];
+        o[1] = vec(kDU2)[oc];
+        o[2] = vec(kEB)[oc];
+      } else {
+        o[0] = vec(kV2)[oc];
+        o[1] = vec(kDV2)[oc];
+        o[2] = vec(kEE)[oc];
+        o[3] = vec(kFF)[oc];
+        o[4] = vec(kEG)[oc];
+      }
+    }
+  };
+  auto own_prep = [&](float (&o)[NO]) {
+    if constexpr (PASS == 2) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] *= inv_c2;
+    } else {
+      o[0] *= inv_c2;
     }
   };
 
@@ -235,275 +312,339 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     ra.template store<RING>(ringA, c_lo);
     rb.template store<RING>(ringB, c_lo);
   }
-  for (int c = threadIdx.x; c < RING; c += NTHR) vec_store(c_lo + c, vec_loads(c_lo + c));
-  if (PASS == 2) {
+  for (int c = threadIdx.x; c < RING; c += NTHR)
+    vec_store(c_lo + c, (c_lo + c + 4 * RING) % RING, vec_loads_any(c_lo + c));
+  if constexpr (PASS == 2) {
     for (int c = threadIdx.x; c < RING; c += NTHR) pring[c] = 0.f;
     for (int c = threadIdx.x; c < NW * RING; c += NTHR) cpart[c] = 0.f;
   }
   Frag<T> fA, fB;   // owned operands of the score and value-score products
+  float own[NO];
   {
     const int o = BR * blk0 + 16 * wave + n;
     load_frag(fA, ownA + (int64_t)o * kD, o < Lr, g);
     if (PASS != 0) load_frag(fB, ownB + (int64_t)o * kD, o < Lr, g);
+    own_loads(BR * blk0 + 16 * wave, own);
+    own_prep(own);
   }
   __syncthreads();
 
+  // per-lane parts of the LDS addresses
+  const T* laneA = ringA + n * LS + 16 * g;
+  const T* laneB = ringB + n * LS + 16 * g;
+  const TrLane trl(g, n);
+
   for (int blk = blk0; blk < blk1; ++blk) {
     const int b0 = BR * blk;
-    const int cb = b0 - 16 * H16;              // block window [cb, cb + RING)
+    const int cb = b0 - halo;                  // block window [cb, cb + RING)
     const bool more = blk + 1 < blk1;
-    // prefetch the next block: its BR new window rows, vectors and owned operands
+    const int s_cb = (cb + RING) % RING;       // ring slot of the window's first token
+    auto slot_of = [&](int c) {                // ring slot of window token cb + c, 0 <= c < RING
+      const int sl = s_cb + c;
+      return (sl >= RING) ? sl - RING : sl;
+    };
+    // prefetch the next block: its BR new window rows, vectors, owned operands and values
     RowStage<T, BR, NTHR> na, nb;
     VecIn nv;
     Frag<T> fA_next, fB_next;
+    float own_next[NO];
     if (more) {
-      na.load(winA, cb + RING, Lr);
-      nb.load(winB, cb + RING, Lr);
-      if ((int)threadIdx.x < BR) nv = vec_loads(cb + RING + (int)threadIdx.x);
+      if (cb + RING + BR <= Lr) {
+        na.load_inside(winA, cb + RING);
+        nb.load_inside(winB, cb + RING);
+      } else {
+        na.load(winA, cb + RING, Lr);
+        nb.load(winB, cb + RING, Lr);
+      }
+      if ((int)threadIdx.x < BR) nv = vec_loads_next(cb + RING + (int)threadIdx.x);
       const int on = b0 + BR + 16 * wave + n;
-      load_frag(fA_next, ownA + (int64_t)on * kD, on < Lr, g);
-      if (PASS != 0) load_frag(fB_next, ownB + (int64_t)on * kD, on < Lr, g);
+      const bool next_in = (b0 + 2 * BR <= Lr) || (on < Lr);
+      load_frag(fA_next, ownA + (int64_t)on * kD, next_in, g);
+      if (PASS != 0) load_frag(fB_next, ownB + (int64_t)on * kD, next_in, g);
+      own_loads(b0 + BR + 16 * wave, own_next);
     }
 
     const int o0 = b0 + 16 * wave;             // owned tokens o0 .. o0 + 15
-    const int cw = o0 - 16 * H16;              // window tiles cw + 16 t
+    const int cw = o0 - halo;                  // window tiles cw + 16 t
+    const int s_cw = slot_of(16 * wave);       // ring slot of tile 0
+    auto tile_slot = [&](int t) {
+      const int sl = s_cw + 16 * t;
+      return (sl >= RING) ? sl - RING : sl;
+    };
     const bool interior = exact_h & (cb >= 0) & (cb + RING <= Lr) & (b0 + BR <= Lr);
-    auto tile_row = [&](int t) -> int { return (cw + 16 * t + 4 * RING) % RING; };
-    auto dead_tile = [&](int t) -> bool {
-      const int j0 = cw + 16 * t;
-      const int dlo = 16 * H16 - 16 * t - 15, dhi = 16 * H16 - 16 * t + 15;
-      return (dlo > h) | (dhi < -h) | (j0 >= Lr) | (j0 + 15 < 0) | (o0 >= Lr);
-    };
-    // band/sequence mask of a window-in-registers entry (window token w = cw + 16t + 4g + r,
-    // owned token o0 + n) and of an owned-in-registers entry (owned o0 + 4g + r, window
-    // cw + 16t + n); on interior blocks only tiles 0 and NT - 1 are partial, along fixed lanes
-    auto keep_w = [&](int t, int r) -> bool {
-      if (interior) return (t == 0) ? (4 * g + r >= n) : (t == NT - 1) ? (4 * g + r <= n) : true;
-      const int w = cw + 16 * t + 4 * g + r, o = o0 + n;
-      return (w >= 0) & (w < Lr) & (o < Lr) & (abs(w - o) <= h);
-    };
-    auto keep_o = [&](int t, int r) -> bool {
-      if (interior) return (t == 0) ? (4 * g + r <= n) : (t == NT - 1) ? (4 * g + r >= n) : true;
-      const int i = o0 + 4 * g + r, j = cw + 16 * t + n;
-      return (i < Lr) & (j >= 0) & (j < Lr) & (abs(i - j) <= h);
-    };
+    // window vector k of the lane's 4 window tokens 4 g + r of the tile at slot rt
+    auto wvec4 = [&](int k, int rt) -> f32x4 { return *reinterpret_cast<const f32x4*>(&wv[k][rt + 4 * g]); };
 
-    if (PASS == 0) {
-      // ---- O_i = sum_j P22_ij V_j (owned query i across lanes, window keys in registers) ----
-      const float u2o = a.fu[vo + min(o0 + n, Lr - 1)];
-      f32x4 Y[4];
+    // Score tile t with the owned dual in the accumulator: the exponent of P22 is
+    // c2 * sc + (window dual).  Masks: I (interior) needs them only on tiles 0 and NT - 1, along
+    // fixed lane patterns; otherwise per entry, and tiles off the band or the sequence are dead.
+    auto body = [&](auto interior_c) {
+      constexpr bool I = decltype(interior_c)::value;
+      auto dead = [&](int t) -> bool {
+        if constexpr (I) return false;
+        const int j0 = cw + 16 * t;
+        const int dlo = 16 * H16 - 16 * t - 15, dhi = 16 * H16 - 16 * t + 15;
+        return (dlo > h) | (dhi < -h) | (j0 >= Lr) | (j0 + 15 < 0) | (o0 >= Lr);
+      };
+      // window in registers (rows 4 g + r of the tile), owned token o0 + n across lanes
+      auto keep_w = [&](int t, int r) -> bool {
+        if constexpr (I) return (t == 0) ? (4 * g + r >= n) : (t == NT - 1) ? (4 * g + r <= n) : true;
+        const int w = cw + 16 * t + 4 * g + r, o = o0 + n;
+        return (w >= 0) & (w < Lr) & (o < Lr) & (abs(w - o) <= h);
+      };
+      // owned rows o0 + 4 g + r in registers, window token cw + 16 t + n across lanes
+      auto keep_o = [&](int t, int r) -> bool {
+        if constexpr (I) return (t == 0) ? (4 * g + r <= n) : (t == NT - 1) ? (4 * g + r >= n) : true;
+        const int i = o0 + 4 * g + r, j = cw + 16 * t + n;
+        return (i < Lr) & (j >= 0) & (j < Lr) & (abs(i - j) <= h);
+      };
+
+      // Software pipeline over the strip (kDepth 2: window fragments two tiles ahead and
+      // matrix-core products one tile ahead; 1: fragments one tile ahead; 0: none, where the
+      // strip itself fills the registers), vector work on the current tile; a scheduling fence
+      // per tile keeps the compiler from hoisting every tile's reads (and registers) up front.
+#ifndef SKA_VJP_DEPTH
+#define SKA_VJP_DEPTH ((PASS == 2) ? 0 : (PASS <= 1) ? 2 : 1)
+#endif
+      constexpr int kDepth = SKA_VJP_DEPTH;
+      Frag<T> fw[2], fwg[2];
+      f32x4 sc[2], gv[2];
+      const f32x4 ci = (PASS == 2) ? f32x4{own[0], own[1 % NO], own[2 % NO], own[3 % NO]}
+                                   : f32x4{own[0], own[0], own[0], own[0]};
+      auto load = [&](int t) {
+        const int rt = tile_slot(t);
+        ring_frag(fw[t & 1], ringA, laneA, rt, g, n);
+        if constexpr (PASS != 0) ring_frag(fwg[t & 1], ringB, laneB, rt, g, n);
+      };
+      auto mma = [&](int t) {
+        if constexpr (PASS == 2) {
+          sc[t & 1] = dot_tile(fA, fw[t & 1], ci);
+          gv[t & 1] = dot_tile(fB, fwg[t & 1]);
+        } else {
+          sc[t & 1] = dot_tile(fw[t & 1], fA, ci);
+          if constexpr (PASS != 0) gv[t & 1] = dot_tile(fwg[t & 1], fB);
+        }
+      };
+      auto pipeline = [&](auto&& valu) {
+        if constexpr (kDepth == 2) {
+          load(0);
+          mma(0);
+          if (NT > 1) load(1);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int t = 0; t < NT; ++t) {
+            if (t + 1 < NT) mma(t + 1);
+            if (t + 2 < NT) load(t + 2);
+            valu(t, sc[t & 1], gv[t & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if constexpr (kDepth == 1) {
+          load(0);
 #pragma unroll
-      for (int pq = 0; pq < NP; ++pq) {
+          for (int t = 0; t < NT; ++t) {
+            if (t + 1 < NT) load(t + 1);
+            mma(t);
+            valu(t, sc[t & 1], gv[t & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            load(t);
+            mma(t);
+            valu(t, sc[t & 1], gv[t & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      };
+
+      if constexpr (PASS == 0) {
+        // ---- O_i = sum_j P22_ij V_j (owned query i across lanes, window keys in registers) ----
+        f32x4 Y[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z[2][4];
-        int rbs[2];
+        pipeline([&](int t, const f32x4& s, const f32x4&) {
+          const int rt = tile_slot(t), tt = t & 1;
+          const f32x4 vw = wvec4(0, rt);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int t = 2 * pq + tt;
-          rbs[tt] = (t < NT) ? tile_row(t) : tile_row(2 * pq);
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(fmaf(s[r], c2, vw[r]));
+            z[tt][r] = (keep_w(t, r) && !dead(t)) ? p : 0.f;
+          }
+          if (tt == 1 || t == NT - 1) {
+            if (tt == 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) z[tt][r] = 0.f;
-          if (t >= NT || dead_tile(t)) continue;
-          const int rr = rbs[tt];
-          Frag<T> fw;
-          lds_frag(fw, ringA, rr + n, g);
-          const f32x4 sc = dot_tile(fw, fA);
+              for (int r = 0; r < 4; ++r) z[1][r] = 0.f;
+            }
+            contract_pair(Y, ringB, trl, tile_slot(t - tt), tt ? rt : tile_slot(t), z, g, n);
+          }
+        });
+        if (o0 + n < Lr) store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
+      } else if constexpr (PASS == 1) {
+        // ---- dv2_j = sum_i P22 g (owned key j across lanes, window queries in registers) ----
+        float acc = 0.f;
+        pipeline([&](int t, const f32x4& s, const f32x4& gg) {
+          if (dead(t)) return;
+          const f32x4 uw = wvec4(0, tile_slot(t));
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            z[tt][r] = keep_w(t, r) ? fast_exp2(fmaf(sc[r], a.c2, u2o + wv[0][rr + 4 * g + r])) : 0.f;
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(fmaf(s[r], c2, uw[r]));
+            acc = keep_w(t, r) ? fmaf(p, gg[r], acc) : acc;
+          }
+        });
+        const float dv2 = lane_group_sum(acc);
+        if (g == 0 && o0 + n < Lr) vec(kDV2)[o0 + n] = dv2;
+      } else if constexpr (PASS == 2) {
+        // ---- du2_i = sum_j P22 (g - dv2_j); column sums of P22 du2 (owned rows in registers) ----
+        f32x4 x[NT];
+        float racc[4] = {0.f, 0.f, 0.f, 0.f};
+        pipeline([&](int t, const f32x4& s, const f32x4& gg) {
+          if (dead(t)) {
+            x[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            return;
+          }
+          const int rt = tile_slot(t);
+          const float v2j = wv[0][rt + n], dj = wv[1][rt + n];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(fmaf(s[r], c2, v2j));
+            const float p = keep_o(t, r) ? e : 0.f;
+            x[t][r] = p;
+            racc[r] = fmaf(p, gg[r] - dj, racc[r]);
+          }
+        });
+        float du2[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) du2[r] = row16_sum(racc[r]);
+        if (n < 4) {
+          const int i = o0 + 4 * g + n;
+          const float di = (n == 0) ? du2[0] : (n == 1) ? du2[1] : (n == 2) ? du2[2] : du2[3];
+          if (i < Lr) vec(kDU2)[i] = di;
         }
-        contract_ring(Y, ringB, rbs[0], rbs[1], z, g, n);
-      }
-      if (o0 + n < Lr) store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
-    } else if (PASS == 1) {
-      // ---- dv2_j = sum_i P22 g (owned key j across lanes, window queries in registers) ----
-      const float v2o = vec(kV2)[min(o0 + n, Lr - 1)];
-      float acc = 0.f;
+        float cp[NT + 3];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (dead_tile(t)) continue;
-        const int rr = tile_row(t);
-        Frag<T> fw, fwg;
-        lds_frag(fw, ringA, rr + n, g);
-        lds_frag(fwg, ringB, rr + n, g);
-        const f32x4 sc = dot_tile(fw, fA);
-        const f32x4 gv = dot_tile(fwg, fB);
+        for (int t = 0; t < NT; ++t)
+          cp[t] = x[t][0] * du2[0] + x[t][1] * du2[1] + x[t][2] * du2[2] + x[t][3] * du2[3];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(fmaf(sc[r], a.c2, wv[0][rr + 4 * g + r] + v2o));
-          acc = keep_w(t, r) ? fmaf(p, gv[r], acc) : acc;
+        for (int t = NT; t < NT + 3; ++t) cp[t] = 0.f;
+        // lane group g of a reduced quad (tiles q..q+3) holds tile q + {0, 2, 1, 3}[g]
+        const int gsel = (g == 1) ? 2 : (g == 2) ? 1 : g;
+#pragma unroll
+        for (int q = 0; q < NT; q += 4) {
+          const float s4 = swap16_sum(swap32_sum(cp[q], cp[q + 1]), swap32_sum(cp[q + 2], cp[q + 3]));
+          const int t = q + gsel;
+          if (t < NT) cpart[wave * RING + 16 * wave + 16 * t + n] = s4;
+        }
+      } else if constexpr (PASS == 3) {
+        // ---- du1, dQ (owned query i across lanes, window keys in registers) ----
+        const float Ai = own[1 % NO], Bi = own[2 % NO];
+        float acc = 0.f;
+        f32x4 X[4], Y[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float z1[2][4], z2[2][4];
+        pipeline([&](int t, const f32x4& s, const f32x4& gg) {
+          const int rt = tile_slot(t), tt = t & 1;
+          const f32x4 vw = wvec4(0, rt), Dw = wvec4(1, rt), Ew = wvec4(2, rt), Fw = wvec4(3, rt),
+                      Gw = wvec4(4, rt);
+          const bool live = !dead(t);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(fmaf(s[r], c2, vw[r]));
+            const float p = (keep_w(t, r) && live) ? e : 0.f;
+            acc = fmaf(p, Fw[r], acc);
+            z1[tt][r] = p * (gg[r] - fmaf(Bi, Fw[r], fmaf(Ai, Ew[r], Dw[r])));
+            z2[tt][r] = p * Gw[r];
+          }
+          if (tt == 1 || t == NT - 1) {
+            if (tt == 0) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) z1[1][r] = z2[1][r] = 0.f;
+            }
+            contract_pair2(X, Y, ringA, trl, tile_slot(t - tt), tt ? rt : tile_slot(t), z1, z2, g, n);
+          }
+        });
+        const float du1 = -Bi * lane_group_sum(acc);
+        const float Ci = du1 * Bi;
+        if (o0 + n < Lr) {
+          if (g == 0) {
+            vec(kDU1)[o0 + n] = du1;
+            vec(kCC)[o0 + n] = Ci;
+          }
+          f32x4 r4[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) r4[b][r] = X[b][r] - Ci * Y[b][r];
+          store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, r4, a.s, g);
+        }
+      } else {
+        // ---- dK, dV (owned key j across lanes, window queries in registers) ----
+        const float Dj = own[1 % NO], Ej = own[2 % NO], Fj = own[3 % NO], Gj = own[4 % NO];
+        f32x4 X[4], Y[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float z1[2][4], z2[2][4];
+        pipeline([&](int t, const f32x4& s, const f32x4& gg) {
+          const int rt = tile_slot(t), tt = t & 1;
+          const f32x4 uw = wvec4(0, rt), Aw = wvec4(1, rt), Bw = wvec4(2, rt), Cw = wvec4(3, rt);
+          const bool live = !dead(t);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(fmaf(s[r], c2, uw[r]));
+            const float p = (keep_w(t, r) && live) ? e : 0.f;
+            z1[tt][r] = p * (gg[r] - fmaf(Cw[r], Gj, fmaf(Bw[r], Fj, fmaf(Aw[r], Ej, Dj))));
+            z2[tt][r] = p;
+          }
+          if (tt == 1 || t == NT - 1) {
+            if (tt == 0) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) z1[1][r] = z2[1][r] = 0.f;
+            }
+            const int r0 = tile_slot(t - tt), r1 = tt ? rt : tile_slot(t);
+            contract_pair(X, ringA, trl, r0, r1, z1, g, n);
+            contract_pair(Y, ringB, trl, r0, r1, z2, g, n);
+          }
+        });
+        if (o0 + n < Lr) {
+          store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, X, a.s, g);
+          store_row(static_cast<T*>(a.out1) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
         }
       }
-      const float dv2 = lane_group_sum(acc);
-      if (g == 0 && o0 + n < Lr) vec(kDV2)[o0 + n] = dv2;
-    } else if (PASS == 2) {
-      // ---- du2_i = sum_j P22 (g - dv2_j); column sums of P22 du2 (owned rows in registers) ----
-      float u2o[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) u2o[r] = vec(kU2)[min(o0 + 4 * g + r, Lr - 1)];
-      f32x4 x[NT];
-      float racc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (dead_tile(t)) {
-          x[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          continue;
-        }
-        const int rr = tile_row(t);
-        Frag<T> fw, fwg;
-        lds_frag(fw, ringA, rr + n, g);
-        lds_frag(fwg, ringB, rr + n, g);
-        const f32x4 sc = dot_tile(fA, fw);
-        const f32x4 gv = dot_tile(fB, fwg);
-        const float v2j = wv[0][rr + n], dj = wv[1][rr + n];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = keep_o(t, r) ? fast_exp2(fmaf(sc[r], a.c2, u2o[r] + v2j)) : 0.f;
-          x[t][r] = p;
-          racc[r] = fmaf(p, gv[r] - dj, racc[r]);
-        }
-      }
-      float du2[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) du2[r] = row16_sum(racc[r]);
-      if (n < 4) {
-        const int i = o0 + 4 * g + n;
-        const float di = (n == 0) ? du2[0] : (n == 1) ? du2[1] : (n == 2) ? du2[2] : du2[3];
-        if (i < Lr) vec(kDU2)[i] = di;
-      }
-      float cp[NT + 3];
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        cp[t] = x[t][0] * du2[0] + x[t][1] * du2[1] + x[t][2] * du2[2] + x[t][3] * du2[3];
-#pragma unroll
-      for (int t = NT; t < NT + 3; ++t) cp[t] = 0.f;
-      const int gsel = (g == 1) ? 2 : (g == 2) ? 1 : g;
-#pragma unroll
-      for (int q = 0; q < NT; q += 4) {
-        const float s4 = swap16_sum(swap32_sum(cp[q], cp[q + 1]), swap32_sum(cp[q + 2], cp[q + 3]));
-        const int t = q + gsel;
-        if (t < NT) cpart[wave * RING + 16 * wave + 16 * t + n] = s4;
-      }
-      __syncthreads();
+    };
+    if (interior) body(std::true_type{});
+    else body(std::false_type{});
+
+    __syncthreads();   // every wave is done with this block's window
+    if constexpr (PASS == 2) {
+      // block column sums (fixed wave order) into the segment accumulator; columns [cb, cb + BR)
+      // leave the window with this block and are written out
+      float* out = a.part + (head * (int64_t)a.nseg + seg) * a.pstride + (cb - c_lo);
       for (int c = threadIdx.x; c < RING; c += NTHR) {
         float sacc = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) sacc += cpart[w * RING + c];
-        pring[(cb + c + 4 * RING) % RING] += sacc;
-      }
-    } else if (PASS == 3) {
-      // ---- du1, dQ (owned query i across lanes, window keys in registers) ----
-      const int oi = min(o0 + n, Lr - 1);
-      const float u2o = vec(kU2)[oi], Ai = vec(kDU2)[oi], Bi = vec(kEB)[oi];
-      float acc = 0.f;
-      f32x4 X[4], Y[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int pq = 0; pq < NP; ++pq) {
-        float z1[2][4], z2[2][4];
-        int rbs[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int t = 2 * pq + tt;
-          rbs[tt] = (t < NT) ? tile_row(t) : tile_row(2 * pq);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) z1[tt][r] = z2[tt][r] = 0.f;
-          if (t >= NT || dead_tile(t)) continue;
-          const int rr = rbs[tt];
-          Frag<T> fw, fwg;
-          lds_frag(fw, ringA, rr + n, g);
-          lds_frag(fwg, ringB, rr + n, g);
-          const f32x4 sc = dot_tile(fw, fA);
-          const f32x4 gv = dot_tile(fwg, fB);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int k = rr + 4 * g + r;
-            const float v2j = wv[0][k], Dj = wv[1][k], Ej = wv[2][k], Fj = wv[3][k], Gj = wv[4][k];
-            const float p = keep_w(t, r) ? fast_exp2(fmaf(sc[r], a.c2, u2o + v2j)) : 0.f;
-            acc = fmaf(p, Fj, acc);
-            z1[tt][r] = p * (gv[r] - Dj - Ai * Ej - Bi * Fj);
-            z2[tt][r] = p * Gj;
-          }
+        const int slot = slot_of(c);
+        if (!more) {
+          out[c] = pring[slot] + sacc;
+        } else if (c < BR) {
+          out[c] = pring[slot] + sacc;
+          pring[slot] = 0.f;
+        } else {
+          pring[slot] += sacc;
         }
-        contract_ring2(X, Y, ringA, rbs[0], rbs[1], z1, z2, g, n);
-      }
-      const float du1 = -Bi * lane_group_sum(acc);
-      const float Ci = du1 * Bi;
-      if (o0 + n < Lr) {
-        if (g == 0) {
-          vec(kDU1)[o0 + n] = du1;
-          vec(kCC)[o0 + n] = Ci;
-        }
-        f32x4 r4[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) r4[b][r] = X[b][r] - Ci * Y[b][r];
-        store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, r4, a.s, g);
-      }
-    } else {
-      // ---- dK, dV (owned key j across lanes, window queries in registers) ----
-      const int oj = min(o0 + n, Lr - 1);
-      const float v2o = vec(kV2)[oj], Dj = vec(kDV2)[oj], Ej = vec(kEE)[oj], Fj = vec(kFF)[oj],
-                  Gj = vec(kEG)[oj];
-      f32x4 X[4], Y[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int pq = 0; pq < NP; ++pq) {
-        float z1[2][4], z2[2][4];
-        int rbs[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int t = 2 * pq + tt;
-          rbs[tt] = (t < NT) ? tile_row(t) : tile_row(2 * pq);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) z1[tt][r] = z2[tt][r] = 0.f;
-          if (t >= NT || dead_tile(t)) continue;
-          const int rr = rbs[tt];
-          Frag<T> fw, fwg;
-          lds_frag(fw, ringA, rr + n, g);
-          lds_frag(fwg, ringB, rr + n, g);
-          const f32x4 sc = dot_tile(fw, fA);
-          const f32x4 gv = dot_tile(fwg, fB);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int k = rr + 4 * g + r;
-            const float u2i = wv[0][k], Ai = wv[1][k], Bi = wv[2][k], Ci = wv[3][k];
-            const float p = keep_w(t, r) ? fast_exp2(fmaf(sc[r], a.c2, u2i + v2o)) : 0.f;
-            z1[tt][r] = p * (gv[r] - Dj - Ai * Ej - Bi * Fj - Ci * Gj);
-            z2[tt][r] = p;
-          }
-        }
-        contract_ring(X, ringA, rbs[0], rbs[1], z1, g, n);
-        contract_ring(Y, ringB, rbs[0], rbs[1], z2, g, n);
-      }
-      if (o0 + n < Lr) {
-        store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, X, a.s, g);
-        store_row(static_cast<T*>(a.out1) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
       }
     }
-
-    __syncthreads();   // every wave is done with this block's window
     if (more) {
-      if (PASS == 2 && (int)threadIdx.x < BR) {
-        // columns [cb, cb + BR) leave the window: write this segment's sums out
-        const int j = cb + threadIdx.x, slot = (j + 4 * RING) % RING;
-        a.part[(head * (int64_t)a.nseg + seg) * a.pstride + (j - c_lo)] = pring[slot];
-        pring[slot] = 0.f;
-      }
-      if ((int)threadIdx.x < BR) vec_store(cb + RING + (int)threadIdx.x, nv);
-      na.template store<RING>(ringA, cb + RING);
-      nb.template store<RING>(ringB, cb + RING);
+      if ((int)threadIdx.x < BR) vec_store(cb + RING + (int)threadIdx.x, slot_of(threadIdx.x), nv);
+      na.template store_slots<RING>(ringA, s_cb);
+      nb.template store_slots<RING>(ringB, s_cb);
       fA = fA_next;
       fB = fB_next;
+      own_prep(own_next);
+#pragma unroll
+      for (int k = 0; k < NO; ++k) own[k] = own_next[k];
       __syncthreads();
-    } else if (PASS == 2) {
-      for (int c = threadIdx.x; c < RING; c += NTHR)
-        a.part[(head * (int64_t)a.nseg + seg) * a.pstride + (cb + c - c_lo)] =
-            pring[(cb + c + 4 * RING) % RING];
     }
   }
 }
