@@ -404,7 +404,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       // strip itself fills the registers), vector work on the current tile; a scheduling fence
       // per tile keeps the compiler from hoisting every tile's reads (and registers) up front.
 #ifndef SKA_VJP_DEPTH
-#define SKA_VJP_DEPTH ((PASS == 2) ? 0 : (PASS <= 1) ? 2 : 1)
+#define SKA_VJP_DEPTH 2
 #endif
       constexpr int kDepth = SKA_VJP_DEPTH;
       Frag<T> fw[2], fwg[2];
@@ -649,15 +649,19 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   }
 }
 
-// Waves per workgroup of the streaming passes: bf16 uses 12 waves (192-token blocks) with two
-// window rings of 192 + 32 H16 rows, fp32 4 waves; both up to the halo LDS holds.
+#ifndef SKA_BF16_NW
+#define SKA_BF16_NW 8
+#endif
+// Waves per workgroup of the streaming passes: bf16 uses 8 waves (128-token blocks, two waves per
+// SIMD with room for the pipelined strips' registers) with two window rings of 128 + 32 H16 rows,
+// fp32 4 waves; both up to the halo LDS holds (one workgroup per CU).
 int vjp_stream_waves(int elt, int h, int* nt) {
   const int h16 = (h + 15) / 16;
   const int H16 = (h16 <= 2) ? 2 : (h16 <= 4) ? 4 : (h16 <= 8) ? 8 : 0;
   if (H16 == 0) return 0;
   if (elt == 0 && H16 > 4) return 0;
   *nt = 1 + 2 * H16;
-  return (elt == 1) ? 12 : 4;
+  return (elt == 1) ? SKA_BF16_NW : 4;
 }
 
 void vjp_stream_segments(int64_t bh, int Lr, int nw, int nt, int* seg_len, int* nseg) {
@@ -687,10 +691,10 @@ static void launch_nt(int pass, const VjpArgs& a, hipStream_t st) {
 
 hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, const VjpArgs& a,
                                   hipStream_t st) {
-  if (elt == 1 && nw == 12) {
-    if (nt == 5) launch_nt<bf16, 5, 12>(pass, a, st);
-    else if (nt == 9) launch_nt<bf16, 9, 12>(pass, a, st);
-    else launch_nt<bf16, 17, 12>(pass, a, st);
+  if (elt == 1) {
+    if (nt == 5) launch_nt<bf16, 5, SKA_BF16_NW>(pass, a, st);
+    else if (nt == 9) launch_nt<bf16, 9, SKA_BF16_NW>(pass, a, st);
+    else launch_nt<bf16, 17, SKA_BF16_NW>(pass, a, st);
   } else {
     if (nt == 5) launch_nt<float, 5, 4>(pass, a, st);
     else launch_nt<float, 9, 4>(pass, a, st);

@@ -91,7 +91,7 @@ def _fused_fwd_bytes(bh, L, W):
 
 def _vjp_bytes(bh, L, W, bf16=False):
     """VJP workspace: 14 vectors [bh][Lpad], plus dv1 column partials [bh][nseg][pstride] when
-    the streaming passes cover the band (bf16: h <= 128 with 12-wave / 192-token blocks; fp32:
+    the streaming passes cover the band (bf16: h <= 128 with 8-wave / 128-token blocks; fp32:
     h <= 64 with 4-wave / 64-token blocks)."""
     Lpad = -(-L // 64) * 64
     base = 14 * bh * Lpad
@@ -100,7 +100,7 @@ def _vjp_bytes(bh, L, W, bf16=False):
     H16 = next((c for c in (2, 4, 8) if h16 <= c), 0)   # 0: chunked passes, no partials
     if H16 == 0 or (not bf16 and H16 > 4):
         return base * 4
-    nw = 12 if bf16 else 4
+    nw = 8 if bf16 else 4
     br = 16 * nw
     nblk = -(-L // br)
     sl = min(max(-(-bh * nblk // 256), -(-(32 * H16) // br), 1), nblk)
