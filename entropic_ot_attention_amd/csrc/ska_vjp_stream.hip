@@ -127,6 +127,49 @@ __device__ __forceinline__ void contract_pair2(f32x4 (&x)[4], f32x4 (&y)[4], con
     }
 }
 
+// Contraction operands of a tile pair, fetched ahead of their use: bf16 holds the four
+// transposed A operands; fp32 keeps the slots and reads the ring inside the contraction.
+template <typename T> struct PairOps;
+template <> struct PairOps<bf16> {
+  bf16x8 v[4];
+  __device__ __forceinline__ void fetch(const bf16* ring, const TrLane& tl, int rt0, int rt1) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[b] = tr_operand(ring, tl, rt0, rt1, b);
+  }
+  __device__ __forceinline__ void contract(f32x4 (&acc)[4], const bf16*, const TrLane&,
+                                           const float (&z)[2][4], int, int) const {
+    const bf16x8 zb = pack_z(z);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[b], zb, acc[b], 0, 0, 0);
+  }
+  __device__ __forceinline__ void contract2(f32x4 (&x)[4], f32x4 (&y)[4], const bf16*, const TrLane&,
+                                            const float (&z1)[2][4], const float (&z2)[2][4], int,
+                                            int) const {
+    const bf16x8 zb1 = pack_z(z1), zb2 = pack_z(z2);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      x[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[b], zb1, x[b], 0, 0, 0);
+      y[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[b], zb2, y[b], 0, 0, 0);
+    }
+  }
+};
+template <> struct PairOps<float> {
+  int rt0, rt1;
+  __device__ __forceinline__ void fetch(const float*, const TrLane&, int r0, int r1) {
+    rt0 = r0;
+    rt1 = r1;
+  }
+  __device__ __forceinline__ void contract(f32x4 (&acc)[4], const float* ring, const TrLane& tl,
+                                           const float (&z)[2][4], int g, int n) const {
+    contract_pair(acc, ring, tl, rt0, rt1, z, g, n);
+  }
+  __device__ __forceinline__ void contract2(f32x4 (&x)[4], f32x4 (&y)[4], const float* ring,
+                                            const TrLane& tl, const float (&z1)[2][4],
+                                            const float (&z2)[2][4], int g, int n) const {
+    contract_pair2(x, y, ring, tl, rt0, rt1, z1, z2, g, n);
+  }
+};
+
 // Window-tile operand fragment at ring slot rt (rows rt + n, d-slice of lane group g): bf16 reads
 // from a per-lane base plus a wave-uniform row offset; fp32 through lds_frag.
 __device__ __forceinline__ void ring_frag(Frag<bf16>& f, const bf16* ring, const bf16* lane_base, int rt,
@@ -409,12 +452,36 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       constexpr int kDepth = SKA_VJP_DEPTH;
       Frag<T> fw[2], fwg[2];
       f32x4 sc[2], gv[2];
+      // window vectors of the tile, read with its fragments (pass 2: two per lane)
+      constexpr int NWV = (PASS == 2) ? 1 : NV;
+      f32x4 wb[2][NWV];
       const f32x4 ci = (PASS == 2) ? f32x4{own[0], own[1 % NO], own[2 % NO], own[3 % NO]}
                                    : f32x4{own[0], own[0], own[0], own[0]};
-      auto load = [&](int t) {
+      // (fragments of tile t + 2 are read before the vector work on tile t, its window vectors
+      // after it: wb[t & 1] still holds tile t's until then)
+      auto load_frags = [&](int t) {
         const int rt = tile_slot(t);
         ring_frag(fw[t & 1], ringA, laneA, rt, g, n);
         if constexpr (PASS != 0) ring_frag(fwg[t & 1], ringB, laneB, rt, g, n);
+      };
+      auto load_vecs = [&](int t) {
+        const int rt = tile_slot(t);
+        if constexpr (PASS == 2) {
+          wb[t & 1][0][0] = wv[0][rt + n];
+          wb[t & 1][0][1] = wv[1][rt + n];
+        } else {
+#pragma unroll
+          for (int k = 0; k < NWV; ++k) wb[t & 1][k] = wvec4(k, rt);
+        }
+      };
+      // transposed contraction operands of the pair starting at tile t (fetched at its first
+      // tile, used after its second)
+      PairOps<T> opA, opB;
+      auto pair_fetch = [&](int t) {
+        const int r0 = tile_slot(t), r1 = (t + 1 < NT) ? tile_slot(t + 1) : r0;
+        if constexpr (PASS == 0) opB.fetch(ringB, trl, r0, r1);
+        if constexpr (PASS == 3 || PASS == 4) opA.fetch(ringA, trl, r0, r1);
+        if constexpr (PASS == 4) opB.fetch(ringB, trl, r0, r1);
       };
       auto mma = [&](int t) {
         if constexpr (PASS == 2) {
@@ -427,21 +494,30 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       };
       auto pipeline = [&](auto&& valu) {
         if constexpr (kDepth == 2) {
-          load(0);
+          load_frags(0);
+          load_vecs(0);
           mma(0);
-          if (NT > 1) load(1);
+          if (NT > 1) {
+            load_frags(1);
+            load_vecs(1);
+          }
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             if (t + 1 < NT) mma(t + 1);
-            if (t + 2 < NT) load(t + 2);
+            if (t + 2 < NT) load_frags(t + 2);
             valu(t, sc[t & 1], gv[t & 1]);
+            if (t + 2 < NT) load_vecs(t + 2);
             __builtin_amdgcn_sched_barrier(0);
           }
         } else if constexpr (kDepth == 1) {
-          load(0);
+          load_frags(0);
+          load_vecs(0);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            if (t + 1 < NT) load(t + 1);
+            if (t + 1 < NT) {
+              load_frags(t + 1);
+              load_vecs(t + 1);
+            }
             mma(t);
             valu(t, sc[t & 1], gv[t & 1]);
             __builtin_amdgcn_sched_barrier(0);
@@ -449,7 +525,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         } else {
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            load(t);
+            load_frags(t);
+            load_vecs(t);
             mma(t);
             valu(t, sc[t & 1], gv[t & 1]);
             __builtin_amdgcn_sched_barrier(0);
@@ -464,8 +541,9 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         for (int b = 0; b < 4; ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4&) {
-          const int rt = tile_slot(t), tt = t & 1;
-          const f32x4 vw = wvec4(0, rt);
+          const int tt = t & 1;
+          if (tt == 0) pair_fetch(t);
+          const f32x4 vw = wb[t & 1][0];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = fast_exp2(fmaf(s[r], c2, vw[r]));
@@ -476,7 +554,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) z[1][r] = 0.f;
             }
-            contract_pair(Y, ringB, trl, tile_slot(t - tt), tt ? rt : tile_slot(t), z, g, n);
+            opB.contract(Y, ringB, trl, z, g, n);
           }
         });
         if (o0 + n < Lr) store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
@@ -485,7 +563,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         float acc = 0.f;
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
           if (dead(t)) return;
-          const f32x4 uw = wvec4(0, tile_slot(t));
+          const f32x4 uw = wb[t & 1][0];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = fast_exp2(fmaf(s[r], c2, uw[r]));
@@ -503,8 +581,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
             x[t] = f32x4{0.f, 0.f, 0.f, 0.f};
             return;
           }
-          const int rt = tile_slot(t);
-          const float v2j = wv[0][rt + n], dj = wv[1][rt + n];
+          const float v2j = wb[t & 1][0][0], dj = wb[t & 1][0][1];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float e = fast_exp2(fmaf(s[r], c2, v2j));
@@ -544,9 +621,10 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z1[2][4], z2[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
-          const int rt = tile_slot(t), tt = t & 1;
-          const f32x4 vw = wvec4(0, rt), Dw = wvec4(1, rt), Ew = wvec4(2, rt), Fw = wvec4(3, rt),
-                      Gw = wvec4(4, rt);
+          const int tt = t & 1;
+          if (tt == 0) pair_fetch(t);
+          const f32x4 vw = wb[t & 1][0], Dw = wb[t & 1][1 % NWV], Ew = wb[t & 1][2 % NWV],
+                      Fw = wb[t & 1][3 % NWV], Gw = wb[t & 1][4 % NWV];
           const bool live = !dead(t);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -561,7 +639,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) z1[1][r] = z2[1][r] = 0.f;
             }
-            contract_pair2(X, Y, ringA, trl, tile_slot(t - tt), tt ? rt : tile_slot(t), z1, z2, g, n);
+            opA.contract2(X, Y, ringA, trl, z1, z2, g, n);
           }
         });
         const float du1 = -Bi * lane_group_sum(acc);
@@ -586,8 +664,10 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z1[2][4], z2[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
-          const int rt = tile_slot(t), tt = t & 1;
-          const f32x4 uw = wvec4(0, rt), Aw = wvec4(1, rt), Bw = wvec4(2, rt), Cw = wvec4(3, rt);
+          const int tt = t & 1;
+          if (tt == 0) pair_fetch(t);
+          const f32x4 uw = wb[t & 1][0], Aw = wb[t & 1][1 % NWV], Bw = wb[t & 1][2 % NWV],
+                      Cw = wb[t & 1][3 % NWV];
           const bool live = !dead(t);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -601,9 +681,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) z1[1][r] = z2[1][r] = 0.f;
             }
-            const int r0 = tile_slot(t - tt), r1 = tt ? rt : tile_slot(t);
-            contract_pair(X, ringA, trl, r0, r1, z1, g, n);
-            contract_pair(Y, ringB, trl, r0, r1, z2, g, n);
+            opA.contract(X, ringA, trl, z1, g, n);
+            opB.contract(Y, ringB, trl, z2, g, n);
           }
         });
         if (o0 + n < Lr) {
