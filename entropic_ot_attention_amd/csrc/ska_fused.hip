@@ -149,13 +149,19 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   float* part_out_h = a.part_out + (head * (int64_t)a.nseg + seg) * a.pstride;
 
   // finished column dual of key j (log2 units) from its loads, and its owner-side copies
-  auto finish_from = [&](int j, const ColIn& in) -> float {
+  auto finish_value = [&](int j, const ColIn& in) -> float {
     if (j < 0 || j >= Lr) return 0.f;
-    const float v = part_prev_h ? column_combine<T>(j, in, u_prev_h, Qh, Kh, a) : in.vp;
-    if (j >= own_lo && j < own_hi) {
+    return part_prev_h ? column_combine<T>(j, in, u_prev_h, Qh, Kh, a) : in.vp;
+  };
+  auto store_owned_v = [&](int j, float v) {
+    if (j >= own_lo && j < own_hi && j < Lr) {
       a.v_next[vo + j] = v;
       if (a.save_v) a.save_v[head * a.save_v_stride + j] = v * kLn2;
     }
+  };
+  auto finish_from = [&](int j, const ColIn& in) -> float {
+    const float v = finish_value(j, in);
+    store_owned_v(j, v);
     return v;
   };
   auto loads_for = [&](int j) -> ColIn {
@@ -379,14 +385,13 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
         cp[t] = x[t][0] * rinv[0] + x[t][1] * rinv[1] + x[t][2] * rinv[2] + x[t][3] * rinv[3];
     }
     emit_columns(cp);
-    if (n < 4) {
-      const int i = o0 + 4 * g + n;
-      const float ui = (n == 0) ? u[0] : (n == 1) ? u[1] : (n == 2) ? u[2] : u[3];
-      if (i < Lr) {
-        a.u_out[vo + i] = ui;
-        if (a.save_u) a.save_u[head * a.save_u_stride + i] = ui * kLn2;
-      }
-    }
+    // Global stores of the block are issued after its end-of-block wait for the prefetched
+    // registers: loads and stores share one counter, so a store issued earlier would be waited
+    // for there as well.
+    const int st_i = (n < 4) ? o0 + 4 * g + n : Lr;      // row dual (lanes n < 4 of each group)
+    const float st_u = (n == 0) ? u[0] : (n == 1) ? u[1] : (n == 2) ? u[2] : u[3];
+    int st_pj = -1, st_vj = Lr;                           // column partial / finished column dual
+    float st_pv = 0.f, st_vv = 0.f;
     __syncthreads();
     // Block column sums (fixed wave order) into the segment accumulator.  Columns [cb, cb + 64)
     // leave the window with this block: wave dw writes their sums out and its slots take the
@@ -407,10 +412,13 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     }
     if (wave == dw) {
       const int c = lane, slot = slot_of(c);
-      part_out_h[cb + c - c_lo] = pring[slot] + block_sum(c);
+      st_pj = cb + c - c_lo;
+      st_pv = pring[slot] + block_sum(c);
       if (more) {
         pring[slot] = 0.f;
-        vring[slot] = finish_from(cb + RING + c, nc);
+        st_vj = cb + RING + c;
+        st_vv = finish_value(st_vj, nc);
+        vring[slot] = st_vv;
       }
     }
     if (more) {
@@ -419,6 +427,12 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
       shc = shift_acc(ush_next);
       __syncthreads();
     }
+    if (st_i < Lr) {
+      a.u_out[vo + st_i] = st_u;
+      if (a.save_u) a.save_u[head * a.save_u_stride + st_i] = st_u * kLn2;
+    }
+    if (st_pj >= 0) part_out_h[st_pj] = st_pv;
+    store_owned_v(st_vj, st_vv);
   }
 }
 
