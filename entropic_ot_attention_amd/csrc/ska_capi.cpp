@@ -207,7 +207,9 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
       a.part_out = part[k % 2];
       a.save_v = (k - 1 >= p->T) ? duals + 2 * (int64_t)(k - 1 - p->T) * g.Lr : nullptr;
       a.save_u = (k > p->T) ? duals + (2 * (int64_t)(k - p->T) - 1) * g.Lr : nullptr;
-      SKA_LAUNCH(ska::kTimedStep, st, ska::launch_fused_step(pl.elt, nt, a, st));
+      // alternate the walk direction: each step starts where the previous one ended, on data
+      // still in the last-level cache
+      SKA_LAUNCH(ska::kTimedStep, st, ska::launch_fused_step(pl.elt, nt, a, (k % 2) == 0, st));
     }
     a.v_prev = vbuf[K_steps % 2];
     a.part_prev = part[K_steps % 2];

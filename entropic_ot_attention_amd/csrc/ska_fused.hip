@@ -120,8 +120,11 @@ struct StepSmem {
 
 // One full Sinkhorn step for one segment of consecutive 64-row blocks of one problem.  SHIFT:
 // the row log-sum-exp is shifted by the previous step's row duals (every launch after the first);
-// otherwise by the exact row maximum.
-template <typename T, int NT, bool SHIFT>
+// otherwise by the exact row maximum.  REV: the segment is walked from its last block down;
+// consecutive launches alternate direction, so each starts on the keys and queries the previous
+// one touched last (still in the last-level cache when a launch reads a little more than it
+// holds).
+template <typename T, int NT, bool SHIFT, bool REV>
 __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   constexpr int H16 = (NT - 1) / 2;
   constexpr int RING = StepSmem<T, NT>::kRing;
@@ -181,36 +184,44 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   for (int c = threadIdx.x; c < kWaves * RING; c += 256) cpart[c] = 0.f;
 
   // prologue: the first block's whole window, query fragment and row shifts
+  const int blkF = REV ? blk1 - 1 : blk0;     // first block walked
+  const int cF = 64 * blkF - 16 * H16;
   Frag<T> fq;
-  load_frag(fq, Qh + (int64_t)(64 * blk0 + 16 * wave + n) * kD, 64 * blk0 + 16 * wave + n < Lr, g);
+  load_frag(fq, Qh + (int64_t)(64 * blkF + 16 * wave + n) * kD, 64 * blkF + 16 * wave + n < Lr, g);
   // row shifts / c2 for the matrix-core accumulator, carried from block to block
   auto shift_acc = [&](f32x4 us) {
     return f32x4{us[0] * inv_c2, us[1] * inv_c2, us[2] * inv_c2, us[3] * inv_c2};
   };
-  f32x4 shc = shift_acc(shift_rows(64 * blk0 + 16 * wave + 4 * g));
+  f32x4 shc = shift_acc(shift_rows(64 * blkF + 16 * wave + 4 * g));
   {
     RowStage<T, RING, 256> first;
-    first.load(Kh, c_lo, Lr);
-    first.template store<RING>(kring, c_lo);
+    first.load(Kh, cF, Lr);
+    first.template store<RING>(kring, cF);
   }
   for (int c = threadIdx.x; c < RING; c += 256) {
-    const int j = c_lo + c;
+    const int j = cF + c;
     vring[(j + 4 * RING) % RING] = finish_from(j, loads_for(j));
     pring[c] = 0.f;
   }
   __syncthreads();
 
-  for (int blk = blk0; blk < blk1; ++blk) {
+  for (int it = 0; it < blk1 - blk0; ++it) {
+    const int blk = REV ? blk1 - 1 - it : blk0 + it;
     const int b0 = 64 * blk;
     const int cb = b0 - 16 * H16;             // block window [cb, cb + RING)
-    const bool more = blk + 1 < blk1;
+    const bool more = it + 1 < blk1 - blk0;
+    const int b0n = REV ? b0 - 64 : b0 + 64;  // rows of the next block walked
+    // keys entering the window with the next block, and (window offset of) the keys leaving it
+    // with this one; both take the same ring slots
+    const int enter0 = REV ? cb - 64 : cb + RING;
+    const int leave_c = REV ? RING - 64 : 0;
     // ring slot of the window's first key (a multiple of 16; the 64 keys [cb, cb + 64) occupy
     // consecutive slots unless the ring is not a multiple of 64 keys past it)
     const int s_cb = (cb + RING) % RING;
     // the wave that finishes the columns leaving with this block rotates, so that extra work
     // spreads over the four SIMDs
     const int dw = blk & 3;
-    // prefetch the 64 key rows the next block adds: [cb + RING, cb + RING + 64)
+    // prefetch the 64 key rows the next block adds: [enter0, enter0 + 64)
     // (and the next block's query fragment, row shifts and new column loads), all in flight
     // during compute
     RowStage<T, 64, 256> nr;
@@ -218,24 +229,34 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     Frag<T> fq_next;
     f32x4 ush_next;
     if (more) {
-      if (cb + RING >= 0 && cb + RING + 64 <= Lr) nr.load_inside(Kh, cb + RING);
-      else nr.load(Kh, cb + RING, Lr);
-      const int on = b0 + 64 + 16 * wave + n;
-      load_frag(fq_next, Qh + (int64_t)on * kD, (b0 + 128 <= Lr) || (on < Lr), g);
-      ush_next = shift_rows(b0 + 64 + 16 * wave + 4 * g);
+      if (enter0 >= 0 && enter0 + 64 <= Lr) nr.load_inside(Kh, enter0);
+      else nr.load(Kh, enter0, Lr);
+      const int on = b0n + 16 * wave + n;
+      load_frag(fq_next, Qh + (int64_t)on * kD, (b0n + 64 <= Lr) || (on < Lr), g);
+      ush_next = shift_rows(b0n + 16 * wave + 4 * g);
       if (wave == dw) {
-        // Keys j = cb + RING + lane enter with the next block.  Inside a segment their first
-        // column partial is the segment's own (at offset j - c_lo of its row) and a second one
-        // comes from the next segment once j - c_lo reaches S = 64 seg_len (the same loads and
-        // order as column_loads, without its divisions).
-        const int j = cb + RING + lane;
+        // Keys j = enter0 + lane enter with the next block.  Inside a segment their column
+        // partials sit at fixed offsets (no divisions): the segment's own row at j - c_lo, and,
+        // walking up, the next segment's row once j - c_lo reaches S = 64 seg_len, or, walking
+        // down, the previous segment's row while j - c_lo < 2 halo.  Partials are summed in
+        // ascending segment order, as column_loads does.
+        const int j = enter0 + lane;
         const float vp = a.v_prev[vo + min(j, Lr - 1)];
         if (part_prev_h) {
-          const int c0 = j - c_lo, c1 = c0 - 64 * a.seg_len;
-          const bool two = (c1 >= 0) & (seg + 1 < a.nseg);
-          const float p0 = part_prev_h[(int64_t)seg * a.pstride + c0];
-          const float p1 = part_prev_h[(int64_t)(two ? seg + 1 : seg) * a.pstride + (two ? c1 : c0)];
-          nc = ColIn{p0, p1, vp, 1.f, two ? 1.f : 0.f};
+          const int S = 64 * a.seg_len, c0 = j - c_lo;
+          const float* own_row = part_prev_h + (int64_t)seg * a.pstride;
+          if constexpr (!REV) {
+            const int c1 = c0 - S;
+            const bool two = (c1 >= 0) & (seg + 1 < a.nseg);
+            const float p0 = own_row[c0];
+            const float p1 = part_prev_h[(int64_t)(two ? seg + 1 : seg) * a.pstride + (two ? c1 : c0)];
+            nc = ColIn{p0, p1, vp, 1.f, two ? 1.f : 0.f};
+          } else {
+            const bool low = (seg > 0) & (c0 < 32 * H16);
+            const float p0 = part_prev_h[(int64_t)(low ? seg - 1 : seg) * a.pstride + (low ? c0 + S : c0)];
+            const float p1 = own_row[c0];
+            nc = ColIn{p0, p1, vp, 1.f, low ? 1.f : 0.f};
+          }
         } else {
           nc = ColIn{0.f, 0.f, vp, 0.f, 0.f};
         }
@@ -393,10 +414,10 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     int st_pj = -1, st_vj = Lr;                           // column partial / finished column dual
     float st_pv = 0.f, st_vv = 0.f;
     __syncthreads();
-    // Block column sums (fixed wave order) into the segment accumulator.  Columns [cb, cb + 64)
-    // leave the window with this block: wave dw writes their sums out and its slots take the
-    // next block's new keys [cb + RING, cb + RING + 64) (every wave is past its reads of kring
-    // and vring for this block).
+    // Block column sums (fixed wave order) into the segment accumulator.  The 64 columns at
+    // window offset leave_c leave the window with this block: wave dw writes their sums out and
+    // their slots take the next block's new keys [enter0, enter0 + 64) (every wave is past its
+    // reads of kring and vring for this block).
     auto slot_of = [&](int c) {
       const int sl = s_cb + c;
       return (sl >= RING) ? sl - RING : sl;
@@ -404,25 +425,26 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     auto block_sum = [&](int c) {
       return ((cpart[c] + cpart[RING + c]) + cpart[2 * RING + c]) + cpart[3 * RING + c];
     };
-    for (int c = 64 + (int)threadIdx.x; c < RING; c += 256) {
+    for (int k = (int)threadIdx.x; k < RING - 64; k += 256) {
+      const int c = REV ? k : k + 64;                     // the columns that stay
       const float sacc = block_sum(c);
       const int slot = slot_of(c);
       if (more) pring[slot] += sacc;
       else part_out_h[cb + c - c_lo] = pring[slot] + sacc;
     }
     if (wave == dw) {
-      const int c = lane, slot = slot_of(c);
+      const int c = leave_c + lane, slot = slot_of(c);
       st_pj = cb + c - c_lo;
       st_pv = pring[slot] + block_sum(c);
       if (more) {
         pring[slot] = 0.f;
-        st_vj = cb + RING + c;
+        st_vj = enter0 + lane;
         st_vv = finish_value(st_vj, nc);
         vring[slot] = st_vv;
       }
     }
     if (more) {
-      nr.template store_slots<RING>(kring, s_cb);
+      nr.template store_slots<RING>(kring, slot_of(leave_c));
       fq = fq_next;
       shc = shift_acc(ush_next);
       __syncthreads();
@@ -475,27 +497,28 @@ void fused_segments(int64_t bh, int Lr, int nt, int* seg_len, int* nseg) {
 }
 
 template <typename T, int NT>
-static void launch_step_t(const StepArgs& a, hipStream_t st) {
+static void launch_step_t(const StepArgs& a, bool rev, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.bh * (int64_t)a.nseg);
   // the first step (no column partials yet, u = 0) has no previous plan to shift by
-  if (a.part_prev) sinkhorn_step_kernel<T, NT, true><<<dim3(blocks), dim3(256), 0, st>>>(a);
-  else sinkhorn_step_kernel<T, NT, false><<<dim3(blocks), dim3(256), 0, st>>>(a);
+  if (!a.part_prev) sinkhorn_step_kernel<T, NT, false, false><<<dim3(blocks), dim3(256), 0, st>>>(a);
+  else if (rev) sinkhorn_step_kernel<T, NT, true, true><<<dim3(blocks), dim3(256), 0, st>>>(a);
+  else sinkhorn_step_kernel<T, NT, true, false><<<dim3(blocks), dim3(256), 0, st>>>(a);
 }
 
-hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, hipStream_t st) {
+hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, bool rev, hipStream_t st) {
   if (elt == 1) {
     switch (nt) {
-      case 5: launch_step_t<bf16, 5>(a, st); break;
-      case 9: launch_step_t<bf16, 9>(a, st); break;
-      case 17: launch_step_t<bf16, 17>(a, st); break;
-      default: launch_step_t<bf16, 25>(a, st); break;
+      case 5: launch_step_t<bf16, 5>(a, rev, st); break;
+      case 9: launch_step_t<bf16, 9>(a, rev, st); break;
+      case 17: launch_step_t<bf16, 17>(a, rev, st); break;
+      default: launch_step_t<bf16, 25>(a, rev, st); break;
     }
   } else {
     switch (nt) {
-      case 5: launch_step_t<float, 5>(a, st); break;
-      case 9: launch_step_t<float, 9>(a, st); break;
-      case 17: launch_step_t<float, 17>(a, st); break;
-      default: launch_step_t<float, 25>(a, st); break;
+      case 5: launch_step_t<float, 5>(a, rev, st); break;
+      case 9: launch_step_t<float, 9>(a, rev, st); break;
+      case 17: launch_step_t<float, 17>(a, rev, st); break;
+      default: launch_step_t<float, 25>(a, rev, st); break;
     }
   }
   return hipGetLastError();

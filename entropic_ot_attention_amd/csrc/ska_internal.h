@@ -102,7 +102,8 @@ hipError_t launch_lse(int elt, const void* own, const void* win, const float* vi
                       float* vsave, int64_t save_stride, const Geometry& g, hipStream_t st);
 hipError_t launch_out(int elt, const void* Q, const void* K, const void* V, const float* u2,
                       const float* v2, void* O, const Geometry& g, hipStream_t st);
-hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, hipStream_t st);
+// rev: walk each segment from its last block down (consecutive steps alternate)
+hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, bool rev, hipStream_t st);
 hipError_t launch_finish_columns(int elt, const StepArgs& a, hipStream_t st);
 hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, const VjpArgs& a,
                                   hipStream_t st);
