@@ -8,9 +8,10 @@ L / (t_fwd + t_vjp) for all heads together.
 
 Prints ONE JSON line.  Besides the throughput it reports, for the dominant kernel (the fused
 balanced Sinkhorn step, T + R launches per step), its average launch time measured with HIP
-events on its own stream during the timed steps, the achieved fraction of the VALU issue
-roofline and, when a current rocprofv3 record exists, its HBM bytes per launch; and the fp64
-CPU oracle timed on a bounded sample of the same workload.
+events on its own stream during the timed steps, the achieved fraction of its binding roofline
+(HBM: algorithmic bytes per launch over launch time) with the VALU and matrix-core fractions
+beside it, and, when a current rocprofv3 record exists, its measured HBM bytes per launch; and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -35,6 +36,11 @@ EXP_SLOTS = 4
 # accumulate the row sum (1 add) and the column sum of the normalised plan (1 fma): 7 issue slots.
 SLOTS_PER_ENTRY_STEP = 3 + EXP_SLOTS
 HBM_PEAK_GBS = 8000.0
+# O(L) fp32 vectors one step reads and writes per token and head: previous column duals, previous
+# row duals, column partials in; row duals, column duals, column partials out
+STEP_VECTOR_BYTES_PER_TOKEN = 6 * 4
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense
+MFMA_F32_PEAK_TFLOPS = 157.3
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_sinkhorn_step_kernel.json")
 
 
@@ -178,26 +184,40 @@ def main():
     h = min(w.W // 2, rows) if not w.dustbin else rows
     nnz = band_entries(rows, h) * w.bh                         # band entries per launch
     avg_launch_s = (kstep_ms / max(kstep_n, 1)) / 1e3
-    achieved = SLOTS_PER_ENTRY_STEP * nnz / avg_launch_s / 1e12     # T lane-slots/s
-    peak = VALU_LANE_OPS_PER_S / 1e12
+    # Rooflines of the dominant kernel (one full Sinkhorn step per launch).  HBM binds: the
+    # step must stream the query and key rows once plus O(L) fp32 vectors, which takes longer at
+    # 8 TB/s than the step's minimal VALU work (7 issue slots per band entry) or matrix-core work
+    # (2 d flops per band entry) at their peaks.
+    elt = 2 if w.dtype == "bf16" else 4
+    alg_bytes = w.bh * rows * (2 * w.d * elt + STEP_VECTOR_BYTES_PER_TOKEN)
+    hbm_gbs = alg_bytes / avg_launch_s / 1e9
+    valu = SLOTS_PER_ENTRY_STEP * nnz / avg_launch_s / 1e12            # T lane-slots/s
+    mfma_tflops = 2 * w.d * nnz / avg_launch_s / 1e12
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     traffic = traffic_per_launch()
     roofline = {
-        "bound": "alu",
+        "bound": "hbm",
         "kernel": "sinkhorn_step_kernel (fused balanced Sinkhorn step)",
-        "achieved": round(achieved, 3),
-        "peak": round(peak, 3),
-        "unit": "T VALU lane-slots/s",
-        "frac": round(achieved / peak, 4),
+        "achieved": round(hbm_gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "traffic": traffic,
         "avg_launch_us": round(avg_launch_s * 1e6, 2),
         "launches_timed": kstep_n,
-        "algorithmic_work": f"{SLOTS_PER_ENTRY_STEP} slots x {nnz} band entries per launch",
+        "algorithmic_bytes": alg_bytes,
+        "algorithmic_work": f"{w.bh * rows} token rows x (2 x {w.d} x {elt} B of Q, K + "
+                            f"{STEP_VECTOR_BYTES_PER_TOKEN} B of O(L) vectors) per launch",
+        "valu": {"achieved": round(valu, 3), "peak": round(VALU_LANE_OPS_PER_S / 1e12, 3),
+                 "unit": "T VALU lane-slots/s", "frac": round(valu / (VALU_LANE_OPS_PER_S / 1e12), 4),
+                 "work": f"{SLOTS_PER_ENTRY_STEP} slots x {nnz} band entries"},
+        "mfma": {"achieved": round(mfma_tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                 "frac": round(mfma_tflops / mfma_peak, 4)},
     }
     if traffic is not None:
-        roofline["hbm_gbs"] = round(traffic / avg_launch_s / 1e9, 1)
-        roofline["hbm_frac"] = round(traffic / avg_launch_s / 1e9 / HBM_PEAK_GBS, 4)
+        roofline["traffic_gbs"] = round(traffic / avg_launch_s / 1e9, 1)
     out = {
-        "metric": "fwd+R=2 VJP tokens/s at L=262144 W=256 d=64",
+        "metric": f"fwd+R={w.R} VJP tokens/s at L={L} W={w.W} d={w.d}; % of MFMA/HBM roofline",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
