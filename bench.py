@@ -50,14 +50,15 @@ def band_entries(L: int, h: int) -> int:
     return L * (2 * h + 1) - h * (h + 1)
 
 
-def traffic_per_launch():
+def traffic_per_launch(workload: str):
     """HBM bytes per step-kernel launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    record, or None when there is none or the kernel source changed since it was taken."""
+    record, or None when there is none, it was taken on another workload, or the kernel source
+    changed since it was taken."""
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
         from entropic_ot_attention_amd.profiling import source_sha
-        if rec.get("source_sha256") != source_sha():
+        if rec.get("source_sha256") != source_sha() or rec.get("workload") != workload:
             return None
         return round(float(rec["bytes_per_launch"]))
     except (OSError, ValueError, KeyError):
@@ -194,7 +195,7 @@ def main():
     valu = SLOTS_PER_ENTRY_STEP * nnz / avg_launch_s / 1e12            # T lane-slots/s
     mfma_tflops = 2 * w.d * nnz / avg_launch_s / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    traffic = traffic_per_launch()
+    traffic = traffic_per_launch(w.name)
     roofline = {
         "bound": "hbm",
         "kernel": "sinkhorn_step_kernel (fused balanced Sinkhorn step)",

@@ -106,8 +106,7 @@ size_t workspace_for(const Plan& pl, ska_op op) {
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   const int64_t vs = pl.g.bh * (int64_t)pl.g.Lpad;
   if (vjp) {
-    // streaming passes (one-reference schedule, bands LDS holds) add dv1 column partials; the
-    // workspace covers both schedules
+    // streaming passes (both schedules, bands LDS holds) add dv1 column partials
     int nt = 0;
     const int nw = ska::vjp_stream_waves(pl.elt, pl.g.h, &nt);
     int64_t part = 0;
@@ -242,7 +241,7 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
       o.pstride = 16 * onw * o.seg_len + 16 * (ont - 1);
       o.c2 = g.c2;
       o.s = g.s;
-      SKA_LAUNCH(ska::kTimedOut, st, ska::launch_vjp_stream_pass(pl.elt, ont, onw, 0, o, st));
+      SKA_LAUNCH(ska::kTimedOut, st, ska::launch_vjp_stream_pass(pl.elt, ont, onw, 0, false, o, st));
     } else {
       SKA_LAUNCH(ska::kTimedOut, st,
                  ska::launch_out(pl.elt, Q, K, V, ubuf[K_steps % 2], vbuf[(K_steps + 1) % 2], O, g, st));
@@ -300,7 +299,7 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
   hipError_t e = ska::launch_vjp_prep(duals, ws, g, st);
   if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
   int nt = 0;
-  const int nw = d4 ? 0 : ska::vjp_stream_waves(pl.elt, g.h, &nt);
+  const int nw = ska::vjp_stream_waves(pl.elt, g.h, &nt);
   if (nw > 0) {
     // streaming passes: dv2 (owns keys), du2 + dv1 column sums (owns queries), du1 + dQ (owns
     // queries), dK + dV (owns keys)
@@ -324,7 +323,7 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
     for (int pass = 1; pass <= 4; ++pass) {
       a.out0 = (pass == 3) ? dQ : dK;
       a.out1 = dV;
-      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_pass(pl.elt, nt, nw, pass, a, st));
+      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_pass(pl.elt, nt, nw, pass, d4, a, st));
     }
     return SKA_OK;
   }

@@ -105,7 +105,7 @@ hipError_t launch_out(int elt, const void* Q, const void* K, const void* V, cons
 // rev: walk each segment from its last block down (consecutive steps alternate)
 hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, bool rev, hipStream_t st);
 hipError_t launch_finish_columns(int elt, const StepArgs& a, hipStream_t st);
-hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, const VjpArgs& a,
+hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, bool d4, const VjpArgs& a,
                                   hipStream_t st);
 hipError_t launch_vjp_prep(const float* duals, float* ws, const Geometry& g, hipStream_t st);
 hipError_t launch_vjp_pass(int elt, int pass, bool direct4, const void* Q, const void* K,

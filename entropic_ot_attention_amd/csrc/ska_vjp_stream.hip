@@ -183,23 +183,26 @@ __device__ __forceinline__ void ring_frag(Frag<float>& f, const float* ring, con
   lds_frag(f, ring, rt + n, g);
 }
 
-template <int PASS> struct VjpPass {
+template <int PASS, bool D4> struct VjpPass {
   static constexpr bool owns_keys = (PASS == 1 || PASS == 4);
-  // window-side vectors kept in LDS rings
-  static constexpr int nvec = PASS <= 1 ? 1 : PASS == 2 ? 2 : PASS == 3 ? 5 : 4;
+  // window-side vectors kept in LDS rings (direct-four pass 2 also needs v1 for P21)
+  static constexpr int nvec = PASS <= 1 ? 1 : PASS == 2 ? (D4 ? 3 : 2) : PASS == 3 ? 5 : 4;
   // owned-side values per lane (pass 2: the dual of each of the lane's 4 owned rows)
   static constexpr int nown = PASS <= 1 ? 1 : PASS == 2 ? 4 : PASS == 3 ? 3 : 5;
 };
 
-template <typename T, int NT, int NW, int PASS>
+// D4: the direct-four schedule, each staircase plan P^(2,2), P^(2,1), P^(1,1), P^(1,0) from its own
+// exponential [technical summaries §2.2: the comparison variant of the adjoint]; passes 0 and 1
+// are the same for both schedules.  Its window- and owned-side vectors are the duals and
+// cotangents themselves (v1, dv1, v0, u1, du1) instead of the orbit factors.
+template <typename T, int NT, int NW, int PASS, bool D4 = false>
 __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
-  using P = VjpPass<PASS>;
+  using P = VjpPass<PASS, D4>;
   constexpr int H16 = (NT - 1) / 2;
   constexpr int BR = 16 * NW;                  // owned tokens per block
   constexpr int RING = BR + 32 * H16;          // block window
   constexpr int NTHR = NW * 64;
   constexpr int NV = P::nvec, NO = P::nown;
-  constexpr int NP = (NT + 1) / 2;             // tile pairs of a contraction
   constexpr int LS = Lds<T>::stride;
   __shared__ __attribute__((aligned(16))) T ringA[RING * LS];  // S window operand
   __shared__ __attribute__((aligned(16))) T ringB[RING * LS];  // g window operand
@@ -241,17 +244,18 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     } else if constexpr (PASS == 2) {
       r.v[0] = vec(kV2)[jc];
       r.v[1] = vec(kDV2)[jc];
+      if constexpr (D4) r.v[2 % NV] = vec(kV1)[jc];
     } else if constexpr (PASS == 3) {
       r.v[0] = vec(kV2)[jc];
       r.v[1] = vec(kDV2)[jc];
-      r.v[2] = vec(kEE)[jc];
-      r.v[3] = 0.f;                  // F: computed from the dv1 partials when stored
-      r.v[4] = vec(kEG)[jc];
+      r.v[2] = vec(D4 ? kV1 : kEE)[jc];
+      r.v[3] = 0.f;                  // F (dv1 when direct): from the dv1 partials when stored
+      r.v[4] = vec(D4 ? kV0 : kEG)[jc];
     } else {
       r.v[0] = vec(kU2)[jc];
       r.v[1] = vec(kDU2)[jc];
-      r.v[2] = vec(kEB)[jc];
-      r.v[3] = vec(kCC)[jc];
+      r.v[2] = vec(D4 ? kU1 : kEB)[jc];
+      r.v[3] = vec(D4 ? kDU1 : kCC)[jc];
     }
   };
   // any token j (window of the first block): clamped loads, partials found by segment division
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   auto vec_store = [&](int j, int slot, const VecIn& in) {
 #pragma unroll
     for (int k = 0; k < NV; ++k) wv[k][slot] = in.v[k] * in.w;
-    if constexpr (PASS == 3) {
+    if constexpr (PASS == 3 && !D4) {
       const float E = in.v[2] * in.w;
       const float dv1 = -E * (in.p0 * in.w0 + in.p1 * in.w1);
       wv[3][slot] = dv1 * E;                         // F = dv1 e^{dv1}
@@ -309,6 +313,11 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         vec(kDV1)[j] = dv1;
         vec(kFF)[j] = dv1 * E;
       }
+    } else if constexpr (PASS == 3) {
+      // direct: the partials already hold sum_i P21 du2
+      const float dv1 = -(in.p0 * in.w0 + in.p1 * in.w1) * in.w;
+      wv[3][slot] = dv1;
+      if (in.w != 0.f && j >= own_lo && j < own_hi) vec(kDV1)[j] = dv1;
     }
   };
 
@@ -328,17 +337,18 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       } else if constexpr (PASS == 3) {
         o[0] = vec(kU2)[oc];
         o[1] = vec(kDU2)[oc];
-        o[2] = vec(kEB)[oc];
+        o[2] = vec(D4 ? kU1 : kEB)[oc];
       } else {
         o[0] = vec(kV2)[oc];
         o[1] = vec(kDV2)[oc];
-        o[2] = vec(kEE)[oc];
-        o[3] = vec(kFF)[oc];
-        o[4] = vec(kEG)[oc];
+        o[2] = vec(D4 ? kV1 : kEE)[oc];
+        o[3] = vec(D4 ? kDV1 : kFF)[oc];
+        o[4] = vec(D4 ? kV0 : kEG)[oc];
       }
     }
   };
   auto own_prep = [&](float (&o)[NO]) {
+    if constexpr (D4) return;      // direct: plain duals, added to the exponents explicitly
     if constexpr (PASS == 2) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] *= inv_c2;
@@ -455,8 +465,9 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       // window vectors of the tile, read with its fragments (pass 2: two per lane)
       constexpr int NWV = (PASS == 2) ? 1 : NV;
       f32x4 wb[2][NWV];
-      const f32x4 ci = (PASS == 2) ? f32x4{own[0], own[1 % NO], own[2 % NO], own[3 % NO]}
-                                   : f32x4{own[0], own[0], own[0], own[0]};
+      const f32x4 ci = D4 ? f32x4{0.f, 0.f, 0.f, 0.f}
+                   : (PASS == 2) ? f32x4{own[0], own[1 % NO], own[2 % NO], own[3 % NO]}
+                                 : f32x4{own[0], own[0], own[0], own[0]};
       // (fragments of tile t + 2 are read before the vector work on tile t, its window vectors
       // after it: wb[t & 1] still holds tile t's until then)
       auto load_frags = [&](int t) {
@@ -469,6 +480,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         if constexpr (PASS == 2) {
           wb[t & 1][0][0] = wv[0][rt + n];
           wb[t & 1][0][1] = wv[1][rt + n];
+          if constexpr (D4) wb[t & 1][0][2] = wv[2 % NV][rt + n];
         } else {
 #pragma unroll
           for (int k = 0; k < NWV; ++k) wb[t & 1][k] = wvec4(k, rt);
@@ -582,12 +594,25 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
             return;
           }
           const float v2j = wb[t & 1][0][0], dj = wb[t & 1][0][1];
+          if constexpr (!D4) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = fast_exp2(fmaf(s[r], c2, v2j));
-            const float p = keep_o(t, r) ? e : 0.f;
-            x[t][r] = p;
-            racc[r] = fmaf(p, gg[r] - dj, racc[r]);
+            for (int r = 0; r < 4; ++r) {
+              const float e = fast_exp2(fmaf(s[r], c2, v2j));
+              const float p = keep_o(t, r) ? e : 0.f;
+              x[t][r] = p;
+              racc[r] = fmaf(p, gg[r] - dj, racc[r]);
+            }
+          } else {
+            // direct: du2 from P22, the column sums from P21 = exp(S + u2 + v1)
+            const float v1j = wb[t & 1][0][2];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float xs = fmaf(s[r], c2, own[r]);
+              const bool keep = keep_o(t, r);
+              const float p22 = fast_exp2(xs + v2j), p21 = fast_exp2(xs + v1j);
+              x[t][r] = keep ? p21 : 0.f;
+              racc[r] = keep ? fmaf(p22, gg[r] - dj, racc[r]) : racc[r];
+            }
           }
         });
         float du2[4];
@@ -626,13 +651,28 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
           const f32x4 vw = wb[t & 1][0], Dw = wb[t & 1][1 % NWV], Ew = wb[t & 1][2 % NWV],
                       Fw = wb[t & 1][3 % NWV], Gw = wb[t & 1][4 % NWV];
           const bool live = !dead(t);
+          if constexpr (!D4) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = fast_exp2(fmaf(s[r], c2, vw[r]));
-            const float p = (keep_w(t, r) && live) ? e : 0.f;
-            acc = fmaf(p, Fw[r], acc);
-            z1[tt][r] = p * (gg[r] - fmaf(Bi, Fw[r], fmaf(Ai, Ew[r], Dw[r])));
-            z2[tt][r] = p * Gw[r];
+            for (int r = 0; r < 4; ++r) {
+              const float e = fast_exp2(fmaf(s[r], c2, vw[r]));
+              const float p = (keep_w(t, r) && live) ? e : 0.f;
+              acc = fmaf(p, Fw[r], acc);
+              z1[tt][r] = p * (gg[r] - fmaf(Bi, Fw[r], fmaf(Ai, Ew[r], Dw[r])));
+              z2[tt][r] = p * Gw[r];
+            }
+          } else {
+            // direct: Ai = du2, Bi = u1 of the owned query; window E = v1, F = dv1, G = v0
+            const float u2i = own[0];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float xs = s[r] * c2;
+              const float p22 = fast_exp2(xs + u2i + vw[r]), p21 = fast_exp2(xs + u2i + Ew[r]);
+              const float p11 = fast_exp2(xs + Bi + Ew[r]), p10 = fast_exp2(xs + Bi + Gw[r]);
+              const bool keep = keep_w(t, r) && live;
+              acc = keep ? fmaf(p11, Fw[r], acc) : acc;
+              z1[tt][r] = keep ? p22 * (gg[r] - Dw[r]) - p21 * Ai - p11 * Fw[r] : 0.f;
+              z2[tt][r] = keep ? p10 : 0.f;
+            }
           }
           if (tt == 1 || t == NT - 1) {
             if (tt == 0) {
@@ -642,12 +682,14 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
             opA.contract2(X, Y, ringA, trl, z1, z2, g, n);
           }
         });
-        const float du1 = -Bi * lane_group_sum(acc);
-        const float Ci = du1 * Bi;
+        // one-reference: du1 = -B sum P22 E F, coefficient of Z2 is C = du1 B;
+        // direct: du1 = -sum P11 dv1, coefficient du1 (C = du1 e^{du1} is not needed)
+        const float du1 = D4 ? -lane_group_sum(acc) : -Bi * lane_group_sum(acc);
+        const float Ci = D4 ? du1 : du1 * Bi;
         if (o0 + n < Lr) {
           if (g == 0) {
             vec(kDU1)[o0 + n] = du1;
-            vec(kCC)[o0 + n] = Ci;
+            if constexpr (!D4) vec(kCC)[o0 + n] = Ci;
           }
           f32x4 r4[4];
 #pragma unroll
@@ -669,12 +711,26 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
           const f32x4 uw = wb[t & 1][0], Aw = wb[t & 1][1 % NWV], Bw = wb[t & 1][2 % NWV],
                       Cw = wb[t & 1][3 % NWV];
           const bool live = !dead(t);
+          if constexpr (!D4) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = fast_exp2(fmaf(s[r], c2, uw[r]));
-            const float p = (keep_w(t, r) && live) ? e : 0.f;
-            z1[tt][r] = p * (gg[r] - fmaf(Cw[r], Gj, fmaf(Bw[r], Fj, fmaf(Aw[r], Ej, Dj))));
-            z2[tt][r] = p;
+            for (int r = 0; r < 4; ++r) {
+              const float e = fast_exp2(fmaf(s[r], c2, uw[r]));
+              const float p = (keep_w(t, r) && live) ? e : 0.f;
+              z1[tt][r] = p * (gg[r] - fmaf(Cw[r], Gj, fmaf(Bw[r], Fj, fmaf(Aw[r], Ej, Dj))));
+              z2[tt][r] = p;
+            }
+          } else {
+            // direct: owned D = dv2, E = v1, F = dv1, G = v0; window A = du2, B = u1, C = du1
+            const float v2j = own[0];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float xs = s[r] * c2;
+              const float p22 = fast_exp2(xs + uw[r] + v2j), p21 = fast_exp2(xs + uw[r] + Ej);
+              const float p11 = fast_exp2(xs + Bw[r] + Ej), p10 = fast_exp2(xs + Bw[r] + Gj);
+              const bool keep = keep_w(t, r) && live;
+              z1[tt][r] = keep ? p22 * (gg[r] - Dj) - p21 * Aw[r] - p11 * Fj - p10 * Cw[r] : 0.f;
+              z2[tt][r] = keep ? p22 : 0.f;
+            }
           }
           if (tt == 1 || t == NT - 1) {
             if (tt == 0) {
@@ -757,26 +813,35 @@ void vjp_stream_segments(int64_t bh, int Lr, int nw, int nt, int* seg_len, int* 
 }
 
 template <typename T, int NT, int NW>
-static void launch_nt(int pass, const VjpArgs& a, hipStream_t st) {
+static void launch_nt(int pass, bool d4, const VjpArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.bh * (int64_t)a.nseg)), block(NW * 64);
   switch (pass) {
     case 0: vjp_stream_kernel<T, NT, NW, 0><<<grid, block, 0, st>>>(a); break;
     case 1: vjp_stream_kernel<T, NT, NW, 1><<<grid, block, 0, st>>>(a); break;
-    case 2: vjp_stream_kernel<T, NT, NW, 2><<<grid, block, 0, st>>>(a); break;
-    case 3: vjp_stream_kernel<T, NT, NW, 3><<<grid, block, 0, st>>>(a); break;
-    default: vjp_stream_kernel<T, NT, NW, 4><<<grid, block, 0, st>>>(a); break;
+    case 2:
+      if (d4) vjp_stream_kernel<T, NT, NW, 2, true><<<grid, block, 0, st>>>(a);
+      else vjp_stream_kernel<T, NT, NW, 2><<<grid, block, 0, st>>>(a);
+      break;
+    case 3:
+      if (d4) vjp_stream_kernel<T, NT, NW, 3, true><<<grid, block, 0, st>>>(a);
+      else vjp_stream_kernel<T, NT, NW, 3><<<grid, block, 0, st>>>(a);
+      break;
+    default:
+      if (d4) vjp_stream_kernel<T, NT, NW, 4, true><<<grid, block, 0, st>>>(a);
+      else vjp_stream_kernel<T, NT, NW, 4><<<grid, block, 0, st>>>(a);
+      break;
   }
 }
 
-hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, const VjpArgs& a,
+hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, bool d4, const VjpArgs& a,
                                   hipStream_t st) {
   if (elt == 1) {
-    if (nt == 5) launch_nt<bf16, 5, SKA_BF16_NW>(pass, a, st);
-    else if (nt == 9) launch_nt<bf16, 9, SKA_BF16_NW>(pass, a, st);
-    else launch_nt<bf16, 17, SKA_BF16_NW>(pass, a, st);
+    if (nt == 5) launch_nt<bf16, 5, SKA_BF16_NW>(pass, d4, a, st);
+    else if (nt == 9) launch_nt<bf16, 9, SKA_BF16_NW>(pass, d4, a, st);
+    else launch_nt<bf16, 17, SKA_BF16_NW>(pass, d4, a, st);
   } else {
-    if (nt == 5) launch_nt<float, 5, 4>(pass, a, st);
-    else launch_nt<float, 9, 4>(pass, a, st);
+    if (nt == 5) launch_nt<float, 5, 4>(pass, d4, a, st);
+    else launch_nt<float, 9, 4>(pass, d4, a, st);
   }
   return hipGetLastError();
 }

@@ -2,14 +2,14 @@
 
     python -m entropic_ot_attention_amd.profiling stats <kernel_stats.csv> <out.md> "<command>"
     python -m entropic_ot_attention_amd.profiling traffic <fetch.csv> <write.csv> <out.json> \
-        <kernel substring> <calibration kernel substring> <calibration bytes> "<command>"
+        <kernel substring> <calibration kernel substring> <calibration bytes> "<command>" <workload>
 
 `stats` writes a short markdown table (calls, average and total duration per kernel) from a
 `--kernel-trace --stats --output-format csv` run.  `traffic` turns two `--pmc FETCH_SIZE` and
 `--pmc WRITE_SIZE` runs into HBM bytes per launch of one kernel, each counter scaled by what it
 reads for the calibration kernel in the same run (an elementwise kernel that reads and writes a
-known number of bytes, bench.py --calibration-copy-mib), and records the SHA-256 of the kernel's source
-file so a reader can tell when the record no longer describes the code.
+known number of bytes, bench.py --calibration-copy-mib), and records the workload and the SHA-256
+of the kernel's source file so a reader can tell when the record no longer describes the code.
 """
 
 from __future__ import annotations
@@ -65,8 +65,8 @@ def _per_dispatch(csv_path: str, counter: str):
 
 
 def traffic_record(fetch_csv: str, write_csv: str, kernel: str, calib_kernel: str, calib_bytes: int,
-                   command: str):
-    rec = {"kernel": kernel, "source_sha256": source_sha(), "command": command,
+                   command: str, workload: str):
+    rec = {"kernel": kernel, "workload": workload, "source_sha256": source_sha(), "command": command,
            "calibration_kernel": calib_kernel, "calibration_bytes": calib_bytes}
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         disp = _per_dispatch(path, counter)
@@ -89,7 +89,7 @@ def main(argv):
     if argv[1] == "stats":
         stats_markdown(argv[2], argv[3], argv[4])
     elif argv[1] == "traffic":
-        rec = traffic_record(argv[2], argv[3], argv[5], argv[6], int(argv[7]), argv[8])
+        rec = traffic_record(argv[2], argv[3], argv[5], argv[6], int(argv[7]), argv[8], argv[9])
         with open(argv[4], "w") as f:
             json.dump(rec, f, indent=1)
     else:
