@@ -100,7 +100,11 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
 
 // Forward workspace, fused path (bands up to half-width 192): two column-dual and two row-dual
 // buffers [bh][Lpad] plus two column-partial buffers [bh][nseg][64 seg_len + 32 H16] (about one
-// float per token); split path (wider bands): two dual buffers.  VJP: kVjpVecs vectors [bh][Lpad].  All O(bh L (1 + W/64)) floats.
+// float per token).  Wide path (wider windows up to 8 x 33 tiles, e.g. the dense dustbin
+// support): two dual buffers plus one partial row of 16 x (window tiles) floats per 16-token row
+// tile, about bh L (W + 32) / 16 floats.  Split path (wider still): two dual buffers.  VJP:
+// kVjpVecs vectors [bh][Lpad], plus the streaming passes' dv1 column partials (about one float
+// per token).
 size_t workspace_for(const Plan& pl, ska_op op) {
   if (pl.empty) return 0;
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
@@ -118,7 +122,14 @@ size_t workspace_for(const Plan& pl, ska_op op) {
     return (size_t)(ska::kVjpVecs * vs + part) * sizeof(float);
   }
   const int nt = ska::fused_tiles_for(pl.g.h);
-  if (nt == 0) return (size_t)(ska::kFwdVecs * vs) * sizeof(float);
+  if (nt == 0) {
+    // wide path: row and column duals plus one partial row per 16-token row tile; split path
+    // (windows wider than the wide step holds in registers): the two duals
+    const int64_t part = ska::wide_step_tiles(pl.g.Lr, pl.g.h) > 0
+                             ? pl.g.bh * ((pl.g.Lr + 15) / 16) * (16 * (int64_t)ska::wide_window_tiles(pl.g.Lr, pl.g.h))
+                             : 0;
+    return (size_t)(ska::kFwdVecs * vs + part) * sizeof(float);
+  }
   int seg_len = 0, nseg = 0;
   ska::fused_segments(pl.g.bh, pl.g.Lr, nt, &seg_len, &nseg);
   const int64_t ps = pl.g.bh * (int64_t)nseg * ska::fused_pstride(nt, seg_len);
@@ -145,6 +156,23 @@ ska_status check_ptr(const void* ptr, const char* name) {
     if (_e != hipSuccess)                                                            \
       return fail(SKA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(_e)); \
   } while (0)
+
+ska::WideArgs wide_args(const Plan& pl, const void* Q, const void* K, const void* V, const void* dO) {
+  ska::WideArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.dO = dO;
+  a.bh = pl.g.bh;
+  a.Lr = pl.g.Lr;
+  a.Lpad = pl.g.Lpad;
+  a.h = pl.g.h;
+  a.nrt = (pl.g.Lr + 15) / 16;
+  a.pw = 16 * ska::wide_window_tiles(pl.g.Lr, pl.g.h);
+  a.c2 = pl.g.c2;
+  a.s = pl.g.s;
+  return a;
+}
 
 ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K, const void* V,
                    void* O, float* duals, void* workspace, size_t workspace_bytes,
@@ -243,12 +271,48 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
       o.s = g.s;
       SKA_LAUNCH(ska::kTimedOut, st, ska::launch_vjp_stream_pass(pl.elt, ont, onw, 0, false, o, st));
     } else {
-      SKA_LAUNCH(ska::kTimedOut, st,
-                 ska::launch_out(pl.elt, Q, K, V, ubuf[K_steps % 2], vbuf[(K_steps + 1) % 2], O, g, st));
+      ska::WideArgs o = wide_args(pl, Q, K, V, nullptr);
+      o.out0 = O;
+      o.fu = ubuf[K_steps % 2];
+      o.fv = vbuf[(K_steps + 1) % 2];
+      SKA_LAUNCH(ska::kTimedOut, st, ska::launch_wide_pass(pl.elt, 0, false, o, st));
     }
     return SKA_OK;
   }
-  // split path (bands wider than the fused step holds, e.g. the dense dustbin support)
+  const int kt = ska::wide_step_tiles(g.Lr, g.h);
+  if (kt > 0) {
+    // wide path: one fused step launch per Sinkhorn step (row update and column partials of each
+    // 16-token row tile), then the column finish
+    float* u = wsf;
+    float* v = u + vs;
+    ska::WideArgs a = wide_args(pl, Q, K, V, nullptr);
+    a.part = v + vs;
+    a.save_stride = dstride;
+    hipError_t e = ska::launch_fill(u, 2 * vs, 0.f, st);
+    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+    const int K_steps = p->T + p->R;
+    for (int k = 1; k <= K_steps; ++k) {
+      // step k: u_k from v_{k-1}; saves u_k (k > T) and v_{k-1} (k - 1 >= T)
+      a.v_in = v;
+      a.u_out = u;
+      a.save_u = (k > p->T) ? duals + (2 * (int64_t)(k - p->T) - 1) * g.Lr : nullptr;
+      a.save_v = (k - 1 >= p->T) ? duals + 2 * (int64_t)(k - 1 - p->T) * g.Lr : nullptr;
+      SKA_LAUNCH(ska::kTimedStep, st, ska::launch_wide_step(pl.elt, kt, a, st));
+      // finish k: v_k (saved by the next step, or here after the last one)
+      a.v_out = v;
+      a.save_u = nullptr;
+      a.save_v = (k == K_steps) ? duals + 2 * (int64_t)p->R * g.Lr : nullptr;
+      e = ska::launch_wide_finish(pl.elt, a, st);
+      if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+    }
+    ska::WideArgs o = wide_args(pl, Q, K, V, nullptr);
+    o.out0 = O;
+    o.fu = u;
+    o.fv = v;
+    SKA_LAUNCH(ska::kTimedOut, st, ska::launch_wide_pass(pl.elt, 0, false, o, st));
+    return SKA_OK;
+  }
+  // split path (windows wider than the wide step holds): separate row and column half-steps
   float* u = wsf;
   float* v = u + vs;
   hipError_t e = ska::launch_fill(u, 2 * vs, 0.f, st);
@@ -267,7 +331,11 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
     SKA_LAUNCH(ska::kTimedStep, st,
                ska::launch_lse(pl.elt, K, Q, u, v, duals + (2 * a) * (int64_t)g.Lr, dstride, g, st));
   }
-  SKA_LAUNCH(ska::kTimedOut, st, ska::launch_out(pl.elt, Q, K, V, u, v, O, g, st));
+  ska::WideArgs o = wide_args(pl, Q, K, V, nullptr);
+  o.out0 = O;
+  o.fu = u;
+  o.fv = v;
+  SKA_LAUNCH(ska::kTimedOut, st, ska::launch_wide_pass(pl.elt, 0, false, o, st));
   return SKA_OK;
 }
 
@@ -327,11 +395,15 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
     }
     return SKA_OK;
   }
-  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 0, d4, Q, K, V, dO, dV, ws, g, st));
-  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 1, d4, Q, K, V, dO, nullptr, ws, g, st));
-  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 2, d4, Q, K, V, dO, nullptr, ws, g, st));
-  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 3, d4, Q, K, V, dO, dQ, ws, g, st));
-  SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_pass(pl.elt, 4, d4, Q, K, V, dO, dK, ws, g, st));
+  // wide passes A..E (bands wider than the streaming passes hold): each owns the side it reduces
+  ska::WideArgs w = wide_args(pl, Q, K, V, dO);
+  w.ws = ws;
+  w.vec_stride = g.bh * (int64_t)g.Lpad;
+  void* outs[6] = {nullptr, dV, nullptr, nullptr, dQ, dK};
+  for (int pass = 1; pass <= 5; ++pass) {
+    w.out0 = outs[pass];
+    SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_wide_pass(pl.elt, pass, d4, w, st));
+  }
   return SKA_OK;
 }
 

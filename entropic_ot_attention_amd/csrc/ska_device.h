@@ -59,6 +59,18 @@ __device__ __forceinline__ void load_frag(Frag<float>& f, const float* row, bool
   }
 }
 
+// The same without a validity test: the caller passes a readable row and masks the results.
+__device__ __forceinline__ void load_frag_raw(Frag<bf16>& f, const bf16* row, int g) {
+  const uint4* p = reinterpret_cast<const uint4*>(row + 16 * g);
+  f.a = __builtin_bit_cast(bf16x8, p[0]);
+  f.b = __builtin_bit_cast(bf16x8, p[1]);
+}
+__device__ __forceinline__ void load_frag_raw(Frag<float>& f, const float* row, int g) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(row + 16 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.v[i] = p[i];
+}
+
 // init + w.o over d = 64 for a 16 x 16 tile (init enters the matrix-core accumulator)
 __device__ __forceinline__ f32x4 dot_tile(const Frag<bf16>& w, const Frag<bf16>& o,
                                           f32x4 init = f32x4{0.f, 0.f, 0.f, 0.f}) {
@@ -263,6 +275,34 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 }
 
 __device__ __forceinline__ int floor_div(int a, int b) { return (a >= 0) ? a / b : -((-a + b - 1) / b); }
+
+__device__ __forceinline__ float dot64(const bf16* a, const bf16* b) {
+  float s = 0.f;
+  for (int d = 0; d < kD; ++d) s = fmaf((float)a[d], (float)b[d], s);
+  return s;
+}
+__device__ __forceinline__ float dot64(const float* a, const float* b) {
+  float s = 0.f;
+  for (int d = 0; d < kD; ++d) s = fmaf(a[d], b[d], s);
+  return s;
+}
+
+// Exact column update (log2 units): -log2 sum_i 2^(c2 q_i.k_j + u_i) over the band of key j.
+// Used where a column's summed mass underflows; the same arithmetic runs in every block that
+// needs column j, so all of them agree bitwise.
+template <typename T>
+__device__ float exact_column(int j, const float* u_h, const T* Qh, const T* Kh, int Lr, int h,
+                              float c2) {
+  float m = -INFINITY;
+  const int i0 = max(0, j - h), i1 = min(Lr - 1, j + h);
+  for (int i = i0; i <= i1; ++i)
+    m = fmaxf(m, fmaf(dot64(Qh + (int64_t)i * kD, Kh + (int64_t)j * kD), c2, u_h[i]));
+  if (!(m > -INFINITY)) return m == m ? 0.f : m;   // NaN propagates
+  float l = 0.f;
+  for (int i = i0; i <= i1; ++i)
+    l += fast_exp2(fmaf(dot64(Qh + (int64_t)i * kD, Kh + (int64_t)j * kD), c2, u_h[i]) - m);
+  return -(m + fast_log2(l));
+}
 
 // MFMA operand fragment of row `row` of a row-major LDS array (d-slice of lane group g).
 __device__ __forceinline__ void lds_frag(Frag<bf16>& f, const bf16* rows, int row, int g) {

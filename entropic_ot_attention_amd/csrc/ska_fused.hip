@@ -37,34 +37,6 @@
 
 namespace ska {
 
-__device__ __forceinline__ float dot64(const bf16* a, const bf16* b) {
-  float s = 0.f;
-  for (int d = 0; d < kD; ++d) s = fmaf((float)a[d], (float)b[d], s);
-  return s;
-}
-__device__ __forceinline__ float dot64(const float* a, const float* b) {
-  float s = 0.f;
-  for (int d = 0; d < kD; ++d) s = fmaf(a[d], b[d], s);
-  return s;
-}
-
-// Exact column update (log2 units): -log2 sum_i 2^(c2 q_i.k_j + u_i) over the band of key j.
-// Used where a column's summed mass underflows; the same arithmetic runs in every block that
-// needs column j, so all of them agree bitwise.
-template <typename T>
-__device__ float exact_column(int j, const float* u_h, const T* Qh, const T* Kh, int Lr, int h,
-                              float c2) {
-  float m = -INFINITY;
-  const int i0 = max(0, j - h), i1 = min(Lr - 1, j + h);
-  for (int i = i0; i <= i1; ++i)
-    m = fmaxf(m, fmaf(dot64(Qh + (int64_t)i * kD, Kh + (int64_t)j * kD), c2, u_h[i]));
-  if (!(m > -INFINITY)) return m == m ? 0.f : m;   // NaN propagates
-  float l = 0.f;
-  for (int i = i0; i <= i1; ++i)
-    l += fast_exp2(fmaf(dot64(Qh + (int64_t)i * kD, Kh + (int64_t)j * kD), c2, u_h[i]) - m);
-  return -(m + fast_log2(l));
-}
-
 // Finished column dual (log2 units) of key j from the previous dual and the column sums of
 // exp(S + u + v_prev) that the previous launch left per segment.  Segment k of a problem covers
 // columns [S k - 16 H16, S (k + 1) + 16 H16) with S = 64 seg_len, so at most two segments hold a

@@ -92,6 +92,42 @@ struct VjpArgs {
 int vjp_stream_waves(int elt, int h, int* nt);
 void vjp_stream_segments(int64_t bh, int Lr, int nw, int nt, int* seg_len, int* nseg);
 
+// Arguments of the wide-band engine (see ska_wide.hip): one workgroup per 16-token row tile
+// of one problem, its band window split over the workgroup's waves.  Column partials of the
+// fused step are [bh][nrt][pw] fp32: row tile rt (nrt = ceil(Lr / 16)) keeps the partial of key
+// j at j - 16 t0(rt), t0(rt) = max(0, 16 rt - h) / 16 its first window tile, pw = 16 x the
+// widest window in tiles.
+struct WideArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dO;
+  void* out0;              // output pass: O; pass A: dV; pass D: dQ; pass E: dK
+  const float* v_in;       // step / finish: column duals before the step (log2) [bh][Lpad]
+  float* u_out;            // step: row duals of the step (log2); finish: read by the exact fallback
+  float* v_out;            // finish: column duals after the step (may alias v_in)
+  float* part;             // step column partials
+  float* save_u;           // optional natural-unit copies (saved duals), head stride save_stride
+  float* save_v;
+  int64_t save_stride;
+  float* ws;               // VJP: kVjpVecs vectors [bh][Lpad]
+  int64_t vec_stride;
+  const float* fu;         // output pass: u^(R), v^(R) (log2) [bh][Lpad]
+  const float* fv;
+  int64_t bh;
+  int Lr, Lpad, h, nrt, pw;
+  float c2, s;
+};
+
+// Register tiles per wave of the wide fused step for half-width h (its window of at most 8 KT
+// tiles stays in registers), or 0 when the window is wider than that.
+int wide_step_tiles(int Lr, int h);
+// Widest window of a row tile in 16-token tiles.
+inline int wide_window_tiles(int Lr, int h) {
+  const int64_t all = ((int64_t)Lr + 15) / 16, band = ((2 * (int64_t)h + 15) >> 4) + 2;
+  return (int)(all < band ? all : band);
+}
+
 enum TimedKernel : int { kTimedStep = 0, kTimedOut = 1, kTimedVjp = 2, kTimedKinds = 3 };
 
 // Launchers (return the hipGetLastError() of their launches).  `elt` is 0 for fp32, 1 for bf16.
@@ -100,16 +136,14 @@ hipError_t launch_save_duals(const float* vec_log2, float* duals, int64_t dual_s
                              const Geometry& g, hipStream_t st);
 hipError_t launch_lse(int elt, const void* own, const void* win, const float* vin, float* vout,
                       float* vsave, int64_t save_stride, const Geometry& g, hipStream_t st);
-hipError_t launch_out(int elt, const void* Q, const void* K, const void* V, const float* u2,
-                      const float* v2, void* O, const Geometry& g, hipStream_t st);
 // rev: walk each segment from its last block down (consecutive steps alternate)
 hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, bool rev, hipStream_t st);
 hipError_t launch_finish_columns(int elt, const StepArgs& a, hipStream_t st);
 hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, bool d4, const VjpArgs& a,
                                   hipStream_t st);
+hipError_t launch_wide_step(int elt, int kt, const WideArgs& a, hipStream_t st);
+hipError_t launch_wide_finish(int elt, const WideArgs& a, hipStream_t st);
+// pass: 0 output, 1..5 the VJP passes A..E
+hipError_t launch_wide_pass(int elt, int pass, bool d4, const WideArgs& a, hipStream_t st);
 hipError_t launch_vjp_prep(const float* duals, float* ws, const Geometry& g, hipStream_t st);
-hipError_t launch_vjp_pass(int elt, int pass, bool direct4, const void* Q, const void* K,
-                           const void* V, const void* dO, void* out, float* ws, const Geometry& g,
-                           hipStream_t st);
-
 }  // namespace ska

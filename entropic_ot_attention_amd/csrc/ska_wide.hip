@@ -1,0 +1,647 @@
+// Wide-band engine (gfx950): bands too wide for the register-resident streaming kernels, up to
+// the dense support of the dustbin-block variant [technical summaries §2.3: the dustbin token
+// joins a support widened to every active pair; cost O(L max(W, L))].
+//
+// Decomposition.  One workgroup of 8 waves per 16-token row tile of one problem.  The row tile's
+// window (its band: every token of a dense problem) is cut into 8 contiguous runs of 16-token
+// tiles, one per wave, so a problem of a few thousand tokens still gives each SIMD two waves and
+// the matrix cores a long independent MFMA stream per wave.  Per-wave partial results (row maxima
+// and sums, vector cotangent sums, 16 x 64 contraction accumulators) are combined across the
+// workgroup through LDS in fixed wave order, so results do not depend on timing.
+//
+// Forward step [technical summaries §2.1: log-domain row update, then column update, on the
+// fixed support]: wide_step_kernel keeps the row tile's scores against its whole window in
+// registers (up to 8 x 33 tiles per workgroup), so one score evaluation and one exponential per
+// entry give the exact row update (workgroup max and sum) and the row tile's column sums of the
+// row-normalised plan; wide_finish_kernel adds each column's partials in a fixed order and
+// finishes the column update, exactly where a column's mass underflows.
+//
+// Output and VJP [spec output P^(2,2) V; abstract and technical summaries §2.2: the R = 2
+// score cotangent as the reference plan tile times a modifier field]: wide_pass_kernel runs the
+// output and five VJP passes, each owning the side it reduces over, so no pass needs partial sums
+// across workgroups:
+//   out (owns queries)  O_i = sum_j P22_ij V_j
+//   A   (owns keys)     dv2_j = sum_i P22 g,  dV_j = sum_i P22_ij dO_i
+//   B   (owns queries)  du2_i = sum_j P22 (g - dv2_j)
+//   C   (owns keys)     dv1_j = -e^{dv1_j} sum_i P22 du2_i          (direct: -sum_i P21 du2_i)
+//   D   (owns queries)  du1_i = -e^{du1_i} sum_j P22 E_j dv1_j      (direct: -sum_j P11 dv1_j)
+//                       dQ_i = s sum_j dS_ij k_j with dS = Z1 - C_i Z2, so du1_i (known only at
+//                       the end of the row) multiplies a second accumulator
+//   E   (owns keys)     dK_j = s sum_i dS_ij q_i
+// with P22 = exp(S + u2 + v2), g_ij = dO_i . V_j, A = du2, B = e^{u1 - u2}, C = du1 B, D = dv2,
+// E = e^{v1 - v2}, F = dv1 E, G = e^{v0 - v2} (one reference tile), or each staircase plan from
+// its own exponential (direct four).
+//
+// Tile layout: a score tile has the window tokens in lane registers (4 g + r) and the owned tokens
+// across lanes (n) in the passes, so sums over the window stay in-lane and the contraction over
+// the window takes the plan values straight from the result registers as its B operand, the
+// window rows of the other tensor read transposed from LDS.  The fused step swaps the roles
+// (owned rows in registers, window across lanes): its row sums stay in-lane and its column sums
+// reduce over the four lane groups with lane swaps.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "ska_device.h"
+#include "ska_internal.h"
+
+namespace ska {
+
+constexpr int kWideWaves = 8;
+constexpr int kWideThreads = 64 * kWideWaves;
+
+// Window of row tile rt: tiles t0 .. t0 + nt - 1; wave w takes tiles wt0 .. wt0 + wnt - 1.
+struct WideTile {
+  int o0, t0, nt, wt0, wnt;
+};
+__device__ __forceinline__ WideTile wide_tile(int rt, int Lr, int h, int wave) {
+  WideTile w;
+  w.o0 = 16 * rt;
+  const int lo = max(0, w.o0 - h), hi = min(Lr - 1, w.o0 + 15 + h);
+  w.t0 = lo >> 4;
+  w.nt = (hi >> 4) - w.t0 + 1;
+  w.wt0 = w.t0 + (w.nt * wave) / kWideWaves;
+  w.wnt = w.t0 + (w.nt * (wave + 1)) / kWideWaves - w.wt0;
+  return w;
+}
+
+// Workgroup -> (problem, row tile).  Workgroups are dispatched round-robin over the 8 XCDs
+// (XCD = id mod 8); each XCD is given a contiguous run of the row tiles in (problem, tile) order,
+// so the workgroups sharing an XCD's L2 mostly read the window tensors of one problem.  Ids past
+// the last tile return at once.
+__device__ __forceinline__ bool wide_work(int64_t nwork, int nrt, int64_t* head, int* rt) {
+  const int64_t id = blockIdx.x, per = (nwork + 7) / 8;
+  const int64_t w = (id % 8) * per + id / 8;
+  if (w >= nwork) return false;
+  *head = w / nrt;
+  *rt = (int)(w % nrt);
+  return true;
+}
+
+__device__ __forceinline__ float pick4(const float (&v)[4], int k) {
+  return (k == 0) ? v[0] : (k == 1) ? v[1] : (k == 2) ? v[2] : v[3];
+}
+
+// =============================================================================================
+// Fused step: row update of the row tile against its window, plus the tile's column partials.
+// =============================================================================================
+template <typename T, int KT>
+__global__ __launch_bounds__(kWideThreads) void wide_step_kernel(WideArgs a) {
+  __shared__ float red[2][kWideWaves][16];
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t head;
+  int rt;
+  if (!wide_work(a.bh * a.nrt, a.nrt, &head, &rt)) return;
+  const int Lr = a.Lr, h = a.h;
+  const float c2 = a.c2;
+  const WideTile wt = wide_tile(rt, Lr, h, wave);
+  const int o0 = wt.o0;
+  const int64_t tb = head * (int64_t)Lr * kD;
+  const T* Qh = static_cast<const T*>(a.Q) + tb;
+  const T* Kh = static_cast<const T*>(a.K) + tb;
+  const int64_t vo = head * (int64_t)a.Lpad;
+  const float* vin = a.v_in + vo;
+
+  // Owned query rows o0 + n (A operand: result rows 4 g + r), window keys across lanes.  Loads
+  // are never conditional (rows clamped into the sequence, tiles past the wave's run clamped to
+  // its last tile) and validity is applied to the results, so a load is waited on only where its
+  // data is used and the prefetch stays in flight.
+  Frag<T> fq;
+  load_frag_raw(fq, Qh + (int64_t)min(o0 + n, Lr - 1) * kD, g);
+  Frag<T> fk[3];
+  float vj[3];
+  auto load_tile = [&](int t, int b) {
+    const int tc = min(t, wt.wnt - 1);
+    const int j = min(max(16 * (wt.wt0 + tc) + n, 0), Lr - 1);
+    load_frag_raw(fk[b], Kh + (int64_t)j * kD, g);
+    vj[b] = vin[j];
+  };
+
+  // exponents x = log2(e) S + v_j of the wave's strip, masked to -inf off the support
+  float x[KT][4];
+  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  // window fragments two tiles ahead of the matrix cores
+  load_tile(0, 0);
+  if (KT > 1) load_tile(1, 1);
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    if (t + 2 < KT) load_tile(t + 2, (t + 2) % 3);
+    if (t < wt.wnt) {
+      const f32x4 sc = dot_tile(fq, fk[t % 3]);
+      const int j0 = 16 * (wt.wt0 + t), j = j0 + n;
+      // a tile inside the sequence and the band on every entry needs no mask
+      const bool inner = (o0 + 15 < Lr) & (j0 + 15 < Lr) & (o0 + 15 - j0 <= h) & (j0 + 15 - o0 <= h);
+      if (inner) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[t][r] = fmaf(sc[r], c2, vj[t % 3]);
+          m[r] = fmaxf(m[r], x[t][r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = o0 + 4 * g + r;
+          const bool ok = (i < Lr) & (j < Lr) & (abs(i - j) <= h);
+          x[t][r] = ok ? fmaf(sc[r], c2, vj[t % 3]) : -INFINITY;
+          m[r] = fmaxf(m[r], x[t][r]);
+        }
+      }
+    }
+  }
+
+  // exact row maximum over the workgroup
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = row16_max(m[r]);
+  if (n < 4) red[0][wave][4 * g + n] = pick4(m, n);
+  __syncthreads();
+  float M[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float mm = red[0][0][4 * g + r];
+#pragma unroll
+    for (int w = 1; w < kWideWaves; ++w) mm = fmaxf(mm, red[0][w][4 * g + r]);
+    M[r] = (mm > -INFINITY) ? mm : 0.f;   // a row with no support entries
+  }
+  float l[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    if (t < wt.wnt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(x[t][r] - M[r]);
+        x[t][r] = p;
+        l[r] += p;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[t][r] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) l[r] = row16_sum(l[r]);
+  if (n < 4) red[1][wave][4 * g + n] = pick4(l, n);
+  __syncthreads();
+  float rinv[4], uu[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float ll = red[1][0][4 * g + r];
+#pragma unroll
+    for (int w = 1; w < kWideWaves; ++w) ll += red[1][w][4 * g + r];
+    const bool live = ll > 0.f;
+    uu[r] = live ? -(M[r] + fast_log2(ll)) : 0.f;
+    rinv[r] = live ? __builtin_amdgcn_rcpf(ll) : 0.f;
+  }
+
+  // column partials of the row-normalised plan: in-lane over the 4 rows, then over the 4 lane
+  // groups; a reduced quad of tiles q .. q + 3 leaves tile q + {0, 2, 1, 3}[g] in lane group g
+  float* prow = a.part + ((int64_t)head * a.nrt + rt) * a.pw + 16 * (wt.wt0 - wt.t0);
+  const int gsel = (g == 1) ? 2 : (g == 2) ? 1 : g;
+#pragma unroll
+  for (int q = 0; q < KT; q += 4) {
+    if (q < wt.wnt) {
+      float c[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = q + k;
+        c[k] = (t < KT) ? fmaf(x[t][3], rinv[3], fmaf(x[t][2], rinv[2], fmaf(x[t][1], rinv[1], x[t][0] * rinv[0])))
+                        : 0.f;
+      }
+      const float s4 = swap16_sum(swap32_sum(c[0], c[1]), swap32_sum(c[2], c[3]));
+      const int t = q + gsel;
+      if (t < wt.wnt) prow[16 * t + n] = s4;
+    }
+  }
+
+  if (wave == 0 && n < 4) {
+    const int i = o0 + 4 * g + n;
+    if (i < Lr) {
+      const float ui = pick4(uu, n);
+      a.u_out[vo + i] = ui;
+      if (a.save_u) a.save_u[head * a.save_stride + i] = ui * kLn2;
+    }
+  }
+  // the column duals this step started from, for the owned tokens (saved duals)
+  if (a.save_v && wave == 1 && lane < 16 && o0 + lane < Lr)
+    a.save_v[head * a.save_stride + o0 + lane] = vin[o0 + lane] * kLn2;
+}
+
+// =============================================================================================
+// Column finish: v_j <- v_j - log2(sum of the row tiles' partials, added in a fixed order); exact
+// log-sum-exp over the column's support where the summed mass underflows.
+// =============================================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void wide_finish_kernel(WideArgs a) {
+  // 64 columns per workgroup; thread group q (of 4) adds a contiguous quarter of each column's
+  // row tiles, the quarters are then added in order
+  __shared__ float quarter[4][64];
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t head = blockIdx.y;
+  const int j = blockIdx.x * 64 + c;
+  const int h = a.h, jc = min(j, a.Lr - 1);
+  // row tiles with a row in the band of key j
+  const int rlo = max(0, floor_div(jc - h, 16)), rhi = min(a.nrt - 1, (jc + h) / 16);
+  const int nr = rhi - rlo + 1, r0 = rlo + (nr * q) / 4, r1 = rlo + (nr * (q + 1)) / 4;
+  const float* ph = a.part + head * (int64_t)a.nrt * a.pw;
+  float s = 0.f;
+#pragma unroll 8
+  for (int rt = r0; rt < r1; ++rt) s += ph[(int64_t)rt * a.pw + jc - 16 * (max(0, 16 * rt - h) >> 4)];
+  quarter[q][c] = s;
+  __syncthreads();
+  if (q != 0 || j >= a.Lr) return;
+  s = ((quarter[0][c] + quarter[1][c]) + quarter[2][c]) + quarter[3][c];
+  const int64_t vo = head * (int64_t)a.Lpad;
+  float v;
+  if (s >= 0x1p-60f) {
+    v = a.v_in[vo + j] - fast_log2(s);
+  } else {
+    const int64_t tb = head * (int64_t)a.Lr * kD;
+    v = exact_column<T>(j, a.u_out + vo, static_cast<const T*>(a.Q) + tb,
+                        static_cast<const T*>(a.K) + tb, a.Lr, h, a.c2);
+  }
+  a.v_out[vo + j] = v;
+  if (a.save_v) a.save_v[head * a.save_stride + j] = v * kLn2;
+}
+
+// =============================================================================================
+// Output and VJP passes.
+// =============================================================================================
+enum WidePass : int { kWOut = 0, kWA, kWB, kWC, kWD, kWE };
+
+template <int P> struct WideTraits {
+  static constexpr bool owns_keys = (P == kWA || P == kWC || P == kWE);
+  static constexpr bool needs_g = (P == kWA || P == kWB || P == kWD || P == kWE);
+  static constexpr int nstage = (P == kWC) ? 1 : 2;   // window tensors staged per wave
+  // staged tensor the contraction reads: 0 = the score operand, 1 = the second tensor, -1 none
+  static constexpr int csrc = (P == kWOut || P == kWA) ? 1 : (P == kWD || P == kWE) ? 0 : -1;
+  static constexpr int nacc = (P == kWD) ? 2 : (csrc >= 0) ? 1 : 0;   // 16 x 64 accumulators
+  static constexpr bool has_red = (P != kWOut && P != kWE);
+};
+
+// 32 window rows of a [L][64] tensor held per lane between their global load and their LDS store
+// (rows outside the sequence become zeros when stored).
+template <typename T>
+struct WaveStage {
+  static constexpr int kCPR = 64 * (int)sizeof(T) / 16;   // 16-byte chunks per row
+  static constexpr int kPer = 32 * kCPR / 64;
+  uint4 x[kPer];
+  __device__ __forceinline__ void load(const T* base, int r0, int Lr, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * 64 + lane, row = c / kCPR, col = (c % kCPR) * (16 / (int)sizeof(T));
+      const int t = min(r0 + row, Lr - 1);
+      x[i] = *reinterpret_cast<const uint4*>(base + (int64_t)t * kD + col);
+    }
+  }
+  __device__ __forceinline__ void store(T* lds, int r0, int Lr, int lane) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * 64 + lane, row = c / kCPR, col = (c % kCPR) * (16 / (int)sizeof(T));
+      const bool ok = r0 + row < Lr;
+      *reinterpret_cast<uint4*>(lds + row * Lds<T>::stride + col) =
+          uint4{ok ? x[i].x : 0u, ok ? x[i].y : 0u, ok ? x[i].z : 0u, ok ? x[i].w : 0u};
+    }
+  }
+};
+
+template <typename T, int P>
+struct WideSmem {
+  using TR = WideTraits<P>;
+  static constexpr int kStageElems = 32 * Lds<T>::stride;   // one staged tensor of one wave
+  static constexpr int kStageBytes = kWideWaves * TR::nstage * kStageElems * (int)sizeof(T);
+  static constexpr int kRedFloats = (TR::nacc * 16 + 1) * 64;   // one wave's partials
+  static constexpr int kRedBytes = kWideWaves * kRedFloats * 4;
+  static constexpr int kBytes = kStageBytes > kRedBytes ? kStageBytes : kRedBytes;
+};
+
+template <typename T, int P, bool D4>
+__global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
+  using TR = WideTraits<P>;
+  using SM = WideSmem<T, P>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SM::kBytes];
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t head;
+  int rt;
+  if (!wide_work(a.bh * a.nrt, a.nrt, &head, &rt)) return;
+  const int Lr = a.Lr, h = a.h;
+  const float c2 = a.c2;
+  const WideTile wt = wide_tile(rt, Lr, h, wave);
+  const int o0 = wt.o0, o = o0 + n;
+  const int64_t tb = head * (int64_t)Lr * kD;
+  const T* Qp = static_cast<const T*>(a.Q) + tb;
+  const T* Kp = static_cast<const T*>(a.K) + tb;
+  const T* Vp = static_cast<const T*>(a.V) + tb;
+  const T* dOp = static_cast<const T*>(a.dO) + tb;
+  const T* own_s = TR::owns_keys ? Kp : Qp;
+  const T* own_g = TR::owns_keys ? Vp : dOp;
+  const T* winA = TR::owns_keys ? Qp : Kp;                         // score operand
+  const T* winB = (P == kWOut) ? Vp : (TR::owns_keys ? dOp : Vp);   // value-score / value operand
+  const int64_t vo = head * (int64_t)a.Lpad;
+  auto vec = [&](int which) -> const float* { return a.ws + which * a.vec_stride + vo; };
+
+  T* sA = reinterpret_cast<T*>(smem) + wave * TR::nstage * SM::kStageElems;
+  T* sB = sA + SM::kStageElems;
+
+  // (loads are never conditional: rows clamped into the sequence, results masked where used)
+  Frag<T> fo, fog;
+  const int oc = min(o, Lr - 1);
+  load_frag_raw(fo, own_s + (int64_t)oc * kD, g);
+  if (TR::needs_g) load_frag_raw(fog, own_g + (int64_t)oc * kD, g);
+
+  // owned-token vectors (o < Lpad always; padding entries are zero)
+  float own_u2 = 0.f, own_v2 = 0.f, ox0 = 0.f, ox1 = 0.f, ox2 = 0.f, ox3 = 0.f;
+  if constexpr (P == kWOut) {
+    own_u2 = a.fu[vo + o];
+  } else if constexpr (TR::owns_keys) {
+    own_v2 = vec(kV2)[o];
+    if constexpr (P == kWC) {
+      ox0 = D4 ? vec(kV1)[o] : vec(kEE)[o];                 // v1 (direct) or E
+    } else if constexpr (P == kWE) {
+      ox0 = vec(kDV2)[o];                                   // D
+      ox1 = D4 ? vec(kV1)[o] : vec(kEE)[o];                 // v1 or E
+      ox2 = D4 ? vec(kDV1)[o] : vec(kFF)[o];                // dv1 or F
+      ox3 = D4 ? vec(kV0)[o] : vec(kEG)[o];                 // v0 or G
+    }
+  } else {
+    own_u2 = vec(kU2)[o];
+    if constexpr (P == kWD) {
+      ox0 = vec(kDU2)[o];                                   // A = du2
+      ox1 = D4 ? vec(kU1)[o] : vec(kEB)[o];                 // u1 (direct) or B
+    }
+  }
+  const float* fv = (P == kWOut) ? a.fv + vo : nullptr;
+
+  float red = 0.f;
+  f32x4 acc[4], acc2[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = acc2[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // window-side vectors of a tile: 4 consecutive tokens per lane (clamped into the padding)
+  constexpr int NWV = (P == kWOut || P == kWA) ? 1 : (P == kWB || P == kWC) ? 2 : (P == kWD) ? 5 : 4;
+  auto load_vecs = [&](int wb, f32x4 (&v)[NWV]) {
+    const int wc = min(wb, a.Lpad - 4);
+    if constexpr (P == kWOut) {
+      v[0] = load4(fv + wc);
+    } else if constexpr (TR::owns_keys) {
+      v[0] = load4(vec(kU2) + wc);
+      if constexpr (P == kWC) v[1 % NWV] = load4(vec(kDU2) + wc);
+      if constexpr (P == kWE) {
+        v[1 % NWV] = load4(vec(kDU2) + wc);                          // A = du2
+        v[2 % NWV] = load4(vec(D4 ? kU1 : kEB) + wc);                // u1 or B
+        v[3 % NWV] = load4(vec(D4 ? kDU1 : kCC) + wc);               // du1 or C
+      }
+    } else {
+      v[0] = load4(vec(kV2) + wc);
+      if constexpr (P == kWB) v[1 % NWV] = load4(vec(kDV2) + wc);
+      if constexpr (P == kWD) {
+        v[1 % NWV] = load4(vec(kDV2) + wc);                          // D
+        v[2 % NWV] = load4(vec(D4 ? kV1 : kEE) + wc);                // v1 or E
+        v[3 % NWV] = load4(vec(D4 ? kDV1 : kFF) + wc);               // dv1 or F
+        v[4 % NWV] = load4(vec(D4 ? kV0 : kEG) + wc);                // v0 or G
+      }
+    }
+  };
+
+  WaveStage<T> na, nb;
+  const int nch = (wt.wnt + 1) >> 1;     // chunks of two tiles
+  int w0 = 16 * wt.wt0;
+  na.load(winA, w0, Lr, lane);
+  if (TR::nstage == 2) nb.load(winB, w0, Lr, lane);
+  na.store(sA, w0, Lr, lane);
+  if (TR::nstage == 2) nb.store(sB, w0, Lr, lane);
+  __builtin_amdgcn_wave_barrier();
+  for (int c = 0; c < nch; ++c, w0 += 32) {
+    // this chunk's window vectors, then the next chunk's rows (issued unconditionally, past the
+    // run they read rows clamped into the sequence): waiting for the vectors leaves the rows in
+    // flight
+    f32x4 wvv[2][NWV];
+    load_vecs(w0 + 4 * g, wvv[0]);
+    load_vecs(w0 + 16 + 4 * g, wvv[1]);
+    na.load(winA, w0 + 32, Lr, lane);
+    if (TR::nstage == 2) nb.load(winB, w0 + 32, Lr, lane);
+    float z1[2][4], z2[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z1[tt][r] = z2[tt][r] = 0.f;
+      if (2 * c + tt >= wt.wnt) continue;
+      const int wb = w0 + 16 * tt + 4 * g;          // this lane's window tokens wb + r
+      const f32x4 (&wv)[NWV] = wvv[tt];
+      Frag<T> fw;
+      lds_frag(fw, sA, 16 * tt + n, g);
+      const f32x4 sc = dot_tile(fw, fo);
+      f32x4 gv = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (TR::needs_g) {
+        Frag<T> fwg;
+        lds_frag(fwg, sB, 16 * tt + n, g);
+        gv = dot_tile(fwg, fog);
+      }
+      if constexpr (P == kWOut) {
+        const f32x4 wv2 = wv[0];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(sc[r], c2, own_u2 + wv2[r]));
+          z1[tt][r] = in_band(wb + r, o, h, Lr) ? p : 0.f;
+        }
+      } else if constexpr (TR::owns_keys) {
+        const f32x4 wu2 = wv[0], wa = wv[1 % NWV], wbv = wv[2 % NWV], wc = wv[3 % NWV];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool keep = in_band(wb + r, o, h, Lr);
+          const float xq = fmaf(sc[r], c2, wu2[r]);                 // log2(e) S + u2_i
+          const float p22 = fast_exp2(xq + own_v2);
+          if constexpr (P == kWA) {
+            red = keep ? fmaf(p22, gv[r], red) : red;
+            z1[tt][r] = keep ? p22 : 0.f;
+          } else if constexpr (P == kWC) {
+            const float pw = D4 ? fast_exp2(xq + ox0) : p22;        // P21 (direct) or P22
+            red = keep ? fmaf(pw, wa[r], red) : red;
+          } else {  // E
+            float ds;
+            if constexpr (D4) {
+              const float xs = sc[r] * c2;
+              const float p21 = fast_exp2(xq + ox1);
+              const float p11 = fast_exp2(xs + wbv[r] + ox1);
+              const float p10 = fast_exp2(xs + wbv[r] + ox3);
+              ds = p22 * (gv[r] - ox0) - p21 * wa[r] - p11 * ox2 - p10 * wc[r];
+            } else {
+              ds = p22 * (gv[r] - ox0 - wa[r] * ox1 - wbv[r] * ox2 - wc[r] * ox3);
+            }
+            z1[tt][r] = keep ? ds : 0.f;
+          }
+        }
+      } else {
+        const f32x4 wv2 = wv[0], wd = wv[1 % NWV], we = wv[2 % NWV], wf = wv[3 % NWV], wg = wv[4 % NWV];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool keep = in_band(wb + r, o, h, Lr);
+          const float xs = sc[r] * c2;
+          const float p22 = fast_exp2(xs + own_u2 + wv2[r]);
+          if constexpr (P == kWB) {
+            red = keep ? fmaf(p22, gv[r] - wd[r], red) : red;
+          } else {  // D
+            if constexpr (D4) {
+              const float p21 = fast_exp2(xs + own_u2 + we[r]);
+              const float p11 = fast_exp2(xs + ox1 + we[r]);
+              const float p10 = fast_exp2(xs + ox1 + wg[r]);
+              red = keep ? fmaf(p11, wf[r], red) : red;
+              z1[tt][r] = keep ? p22 * (gv[r] - wd[r]) - p21 * ox0 - p11 * wf[r] : 0.f;
+              z2[tt][r] = keep ? p10 : 0.f;
+            } else {
+              red = keep ? fmaf(p22, wf[r], red) : red;
+              z1[tt][r] = keep ? p22 * (gv[r] - wd[r] - ox0 * we[r] - ox1 * wf[r]) : 0.f;
+              z2[tt][r] = keep ? p22 * wg[r] : 0.f;
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
+    }
+    if constexpr (TR::csrc >= 0) {
+      const T* src = (TR::csrc == 0) ? sA : sB;
+      if constexpr (P == kWD) contract2(acc, acc2, src, z1, z2, g, n);
+      else contract(acc, src, z1, g, n);
+    }
+    __builtin_amdgcn_wave_barrier();
+    na.store(sA, w0 + 32, Lr, lane);
+    if (TR::nstage == 2) nb.store(sB, w0 + 32, Lr, lane);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- combine the waves' partials (fixed order) in wave 0 ----
+  if constexpr (TR::has_red) red = group_sum(red);
+  __syncthreads();                      // every wave is done with its staging area
+  float* rbuf = reinterpret_cast<float*>(smem);
+  if (wave != 0) {
+    float* mine = rbuf + wave * SM::kRedFloats;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (TR::nacc >= 1) mine[(4 * b + r) * 64 + lane] = acc[b][r];
+        if constexpr (TR::nacc >= 2) mine[(16 + 4 * b + r) * 64 + lane] = acc2[b][r];
+      }
+    if constexpr (TR::has_red) mine[TR::nacc * 16 * 64 + lane] = red;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll 1
+  for (int w = 1; w < kWideWaves; ++w) {
+    const float* theirs = rbuf + w * SM::kRedFloats;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (TR::nacc >= 1) acc[b][r] += theirs[(4 * b + r) * 64 + lane];
+        if constexpr (TR::nacc >= 2) acc2[b][r] += theirs[(16 + 4 * b + r) * 64 + lane];
+      }
+    if constexpr (TR::has_red) red += theirs[TR::nacc * 16 * 64 + lane];
+  }
+
+  const bool valid = o < Lr;
+  if (!valid) return;
+  float* ws = a.ws;
+  const int64_t ob = vo + o;
+  T* out_row = static_cast<T*>(a.out0) + tb + (int64_t)o * kD;
+  if constexpr (P == kWOut) {
+    store_row(out_row, acc, 1.f, g);
+  } else if constexpr (P == kWA) {
+    if (g == 0) ws[kDV2 * a.vec_stride + ob] = red;
+    store_row(out_row, acc, 1.f, g);
+  } else if constexpr (P == kWB) {
+    if (g == 0) ws[kDU2 * a.vec_stride + ob] = red;
+  } else if constexpr (P == kWC) {
+    const float dv1 = D4 ? -red : -ox0 * red;
+    if (g == 0) {
+      ws[kDV1 * a.vec_stride + ob] = dv1;
+      ws[kFF * a.vec_stride + ob] = dv1 * ws[kEE * a.vec_stride + ob];
+    }
+  } else if constexpr (P == kWD) {
+    const float eb = ws[kEB * a.vec_stride + ob];
+    const float du1 = D4 ? -red : -eb * red;
+    const float cc = D4 ? du1 : du1 * eb;            // coefficient of Z2 in dS
+    if (g == 0) {
+      ws[kDU1 * a.vec_stride + ob] = du1;
+      ws[kCC * a.vec_stride + ob] = du1 * eb;
+    }
+    f32x4 r4[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) r4[b][r] = acc[b][r] - cc * acc2[b][r];
+    store_row(out_row, r4, a.s, g);
+  } else {  // E
+    store_row(out_row, acc, a.s, g);
+  }
+}
+
+// =============================================================================================
+// launchers
+// =============================================================================================
+int wide_step_tiles(int Lr, int h) {
+  const int per_wave = (wide_window_tiles(Lr, h) + kWideWaves - 1) / kWideWaves;
+  if (per_wave <= 4) return 4;
+  if (per_wave <= 8) return 8;
+  if (per_wave <= 16) return 16;
+  if (per_wave <= 33) return 33;
+  return 0;
+}
+
+static dim3 wide_grid(const WideArgs& a) {
+  const int64_t nwork = a.bh * (int64_t)a.nrt;
+  return dim3((unsigned)(8 * ((nwork + 7) / 8)), 1, 1);
+}
+
+template <typename T>
+static void wide_step_t(int kt, const WideArgs& a, hipStream_t st) {
+  const dim3 grid = wide_grid(a), block(kWideThreads);
+  switch (kt) {
+    case 4: wide_step_kernel<T, 4><<<grid, block, 0, st>>>(a); break;
+    case 8: wide_step_kernel<T, 8><<<grid, block, 0, st>>>(a); break;
+    case 16: wide_step_kernel<T, 16><<<grid, block, 0, st>>>(a); break;
+    default: wide_step_kernel<T, 33><<<grid, block, 0, st>>>(a); break;
+  }
+}
+
+hipError_t launch_wide_step(int elt, int kt, const WideArgs& a, hipStream_t st) {
+  if (kt != 4 && kt != 8 && kt != 16 && kt != 33) return hipErrorInvalidValue;
+  if (elt == 1) wide_step_t<bf16>(kt, a, st);
+  else wide_step_t<float>(kt, a, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_wide_finish(int elt, const WideArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.Lr + 63) / 64), (unsigned)a.bh);
+  if (elt == 1) wide_finish_kernel<bf16><<<grid, dim3(256), 0, st>>>(a);
+  else wide_finish_kernel<float><<<grid, dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, bool D4>
+static void wide_pass_t(int pass, const WideArgs& a, hipStream_t st) {
+  const dim3 grid = wide_grid(a), block(kWideThreads);
+  switch (pass) {
+    case kWOut: wide_pass_kernel<T, kWOut, false><<<grid, block, 0, st>>>(a); break;
+    case kWA: wide_pass_kernel<T, kWA, false><<<grid, block, 0, st>>>(a); break;
+    case kWB: wide_pass_kernel<T, kWB, false><<<grid, block, 0, st>>>(a); break;
+    case kWC: wide_pass_kernel<T, kWC, D4><<<grid, block, 0, st>>>(a); break;
+    case kWD: wide_pass_kernel<T, kWD, D4><<<grid, block, 0, st>>>(a); break;
+    default: wide_pass_kernel<T, kWE, D4><<<grid, block, 0, st>>>(a); break;
+  }
+}
+
+hipError_t launch_wide_pass(int elt, int pass, bool d4, const WideArgs& a, hipStream_t st) {
+  if (pass < kWOut || pass > kWE) return hipErrorInvalidValue;
+  if (elt == 1) {
+    if (d4) wide_pass_t<bf16, true>(pass, a, st);
+    else wide_pass_t<bf16, false>(pass, a, st);
+  } else {
+    if (d4) wide_pass_t<float, true>(pass, a, st);
+    else wide_pass_t<float, false>(pass, a, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ska

@@ -38,6 +38,10 @@ SMALL = [
     ("L900_W128_bf16", 2, 900, 128, 6, 1.0, BF16),
     ("L1500_W256_eps05_bf16", 1, 1500, 256, 4, 0.5, BF16),
     ("L600_W128_T4", 2, 600, 128, 4, 1.0, F32),
+    # wide engine: register-strip fused step (windows up to 8 x 33 tiles) and window-split passes
+    ("L900_W600_bf16_wide", 2, 900, 600, 5, 1.0, BF16),
+    ("L700_W2000_dense", 1, 700, 2000, 4, 1.0, F32),
+    ("L1300_W700_eps05_wide", 1, 1300, 700, 3, 0.5, F32),
 ]
 
 
@@ -83,6 +87,39 @@ def test_tiny_epsilon_exact_column_fallback():
     err = float(np.abs(got["duals"][0] - ref["duals"]).max())
     say(f"tiny epsilon: |S|max={smax:.1f} tol={tol:.2e} duals maxabs={err:.2e}")
     assert err <= tol, (err, tol)
+
+
+def test_tiny_epsilon_wide_exact_column_fallback():
+    """The same epsilon = 0.01 regime on a dense support (W > 2 L): the wide step's column finish
+    takes the exact log-sum-exp for columns whose mass falls below 2^-60; tolerances as in the
+    banded case."""
+    import oracle
+    w, x = _inputs(1, 150, 400, 3, 0.01, F32, seed=8)
+    say("[gpu] tiny epsilon wide column fallback")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 400, 3, 2, 0.01)
+    Q, K, V, dO = (as64(x[k][0]) for k in ("Q", "K", "V", "dO"))
+    ref = oracle_head(Q, K, V, dO, 400, 3, 2, 0.01)
+    S = oracle.band_scores(Q, K, 150, 0.01)
+    smax = float(np.abs(S[np.isfinite(S)]).max())
+    tol = 64 * smax * 2.0 ** -24
+    for name in ("O", "dQ", "dK", "dV"):
+        g, r = got[name][0], ref[name]
+        rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+        assert np.all(np.isfinite(g)) and rel <= tol, (name, rel, tol)
+    err = float(np.abs(got["duals"][0] - ref["duals"]).max())
+    say(f"tiny epsilon wide: |S|max={smax:.1f} tol={tol:.2e} duals maxabs={err:.2e}")
+    assert err <= tol, (err, tol)
+
+
+def test_split_half_steps_beyond_register_window():
+    """A window of 271 tiles (L = 4400, h = 2150) is wider than the wide step holds in registers
+    (8 waves x 33 tiles): the forward runs separate row and column half-steps."""
+    w, x = _inputs(1, 4400, 4300, 1, 1.0, F32, seed=9)
+    say("[gpu] split half-steps L=4400 W=4300 T=1")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 4300, 1)
+    ref = {k: [v] for k, v in oracle_head(*(as64(x[k][0]) for k in ("Q", "K", "V", "dO")),
+                                          4300, 1, 2, 1.0).items()}
+    compare(got, ref, torch.float32, "split L4400 W4300")
 
 
 @pytest.mark.parametrize("R", [1, 3, 4])
