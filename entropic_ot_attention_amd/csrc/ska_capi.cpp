@@ -297,7 +297,7 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
       a.u_out = u;
       a.save_u = (k > p->T) ? duals + (2 * (int64_t)(k - p->T) - 1) * g.Lr : nullptr;
       a.save_v = (k - 1 >= p->T) ? duals + 2 * (int64_t)(k - 1 - p->T) * g.Lr : nullptr;
-      SKA_LAUNCH(ska::kTimedStep, st, ska::launch_wide_step(pl.elt, kt, a, st));
+      SKA_LAUNCH(ska::kTimedStep, st, ska::launch_wide_step(pl.elt, kt, k == 1, a, st));
       // finish k: v_k (saved by the next step, or here after the last one)
       a.v_out = v;
       a.save_u = nullptr;

@@ -71,6 +71,20 @@ __device__ __forceinline__ void load_frag_raw(Frag<float>& f, const float* row, 
   for (int i = 0; i < 4; ++i) f.v[i] = p[i];
 }
 
+// Fragment loads with the lane groups' d-slices interleaved along the row (fp32: MFMA (i, e)
+// takes d = 16 i + 4 g + e; bf16: the two MFMAs take d = 8 g + e and d = 32 + 8 g + e), so the
+// four lane groups of a row read one contiguous piece of it per load instruction instead of four
+// pieces of separate cache lines.  The sum over d is unchanged when both operands of a
+// contraction use this layout (and only then).
+__device__ __forceinline__ void load_frag_il(Frag<bf16>& f, const bf16* row, int g) {
+  f.a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + 8 * g));
+  f.b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + 32 + 8 * g));
+}
+__device__ __forceinline__ void load_frag_il(Frag<float>& f, const float* row, int g) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.v[i] = *reinterpret_cast<const f32x4*>(row + 16 * i + 4 * g);
+}
+
 // init + w.o over d = 64 for a 16 x 16 tile (init enters the matrix-core accumulator)
 __device__ __forceinline__ f32x4 dot_tile(const Frag<bf16>& w, const Frag<bf16>& o,
                                           f32x4 init = f32x4{0.f, 0.f, 0.f, 0.f}) {

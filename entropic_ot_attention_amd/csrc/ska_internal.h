@@ -141,7 +141,9 @@ hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, bool rev, hipSt
 hipError_t launch_finish_columns(int elt, const StepArgs& a, hipStream_t st);
 hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, bool d4, const VjpArgs& a,
                                   hipStream_t st);
-hipError_t launch_wide_step(int elt, int kt, const WideArgs& a, hipStream_t st);
+// first: the first step of the iteration (u = v = 0), which takes the exact row maximum; later
+// steps shift the row log-sum-exp by the previous row duals (read from u_out before it is rewritten)
+hipError_t launch_wide_step(int elt, int kt, bool first, const WideArgs& a, hipStream_t st);
 hipError_t launch_wide_finish(int elt, const WideArgs& a, hipStream_t st);
 // pass: 0 output, 1..5 the VJP passes A..E
 hipError_t launch_wide_pass(int elt, int pass, bool d4, const WideArgs& a, hipStream_t st);

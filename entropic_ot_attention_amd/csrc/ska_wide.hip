@@ -83,10 +83,36 @@ __device__ __forceinline__ float pick4(const float (&v)[4], int k) {
   return (k == 0) ? v[0] : (k == 1) ? v[1] : (k == 2) ? v[2] : v[3];
 }
 
+// 32 window rows of a [L][64] tensor held per lane between their global load and their LDS store
+// (rows outside the sequence become zeros when stored).
+template <typename T>
+struct WaveStage {
+  static constexpr int kCPR = 64 * (int)sizeof(T) / 16;   // 16-byte chunks per row
+  static constexpr int kPer = 32 * kCPR / 64;
+  uint4 x[kPer];
+  __device__ __forceinline__ void load(const T* base, int r0, int Lr, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * 64 + lane, row = c / kCPR, col = (c % kCPR) * (16 / (int)sizeof(T));
+      const int t = min(r0 + row, Lr - 1);
+      x[i] = *reinterpret_cast<const uint4*>(base + (int64_t)t * kD + col);
+    }
+  }
+  __device__ __forceinline__ void store(T* lds, int r0, int Lr, int lane) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * 64 + lane, row = c / kCPR, col = (c % kCPR) * (16 / (int)sizeof(T));
+      const bool ok = r0 + row < Lr;
+      *reinterpret_cast<uint4*>(lds + row * Lds<T>::stride + col) =
+          uint4{ok ? x[i].x : 0u, ok ? x[i].y : 0u, ok ? x[i].z : 0u, ok ? x[i].w : 0u};
+    }
+  }
+};
+
 // =============================================================================================
 // Fused step: row update of the row tile against its window, plus the tile's column partials.
 // =============================================================================================
-template <typename T, int KT>
+template <typename T, int KT, bool SHIFT>
 __global__ __launch_bounds__(kWideThreads) void wide_step_kernel(WideArgs a) {
   __shared__ float red[2][kWideWaves][16];
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
@@ -104,79 +130,130 @@ __global__ __launch_bounds__(kWideThreads) void wide_step_kernel(WideArgs a) {
   const int64_t vo = head * (int64_t)a.Lpad;
   const float* vin = a.v_in + vo;
 
-  // Owned query rows o0 + n (A operand: result rows 4 g + r), window keys across lanes.  Loads
-  // are never conditional (rows clamped into the sequence, tiles past the wave's run clamped to
-  // its last tile) and validity is applied to the results, so a load is waited on only where its
-  // data is used and the prefetch stays in flight.
+  // Owned query rows o0 + n (A operand: result rows 4 g + r), window keys across lanes.  The
+  // window keys reach the wave two tiles at a time through its own LDS buffer: coalesced row
+  // loads (adjacent lanes, adjacent addresses) cost the vector L1 a quarter of the accesses of
+  // per-lane fragment loads.  Loads are never conditional (rows clamped into the sequence, chunks
+  // past the wave's run re-read its rows) and validity is applied to the results, so a load is
+  // waited on only where its data is used and the next chunk stays in flight.
+  __shared__ __attribute__((aligned(16))) T kstage[kWideWaves][32 * Lds<T>::stride];
+  T* sK = kstage[wave];
   Frag<T> fq;
   load_frag_raw(fq, Qh + (int64_t)min(o0 + n, Lr - 1) * kD, g);
-  Frag<T> fk[3];
-  float vj[3];
-  auto load_tile = [&](int t, int b) {
-    const int tc = min(t, wt.wnt - 1);
-    const int j = min(max(16 * (wt.wt0 + tc) + n, 0), Lr - 1);
-    load_frag_raw(fk[b], Kh + (int64_t)j * kD, g);
-    vj[b] = vin[j];
+  constexpr int NC = (KT + 1) / 2;         // chunks of two tiles
+  WaveStage<T> ns;
+  float vj[3][2];                          // v of key n of each tile of a chunk, chunk c in slot c % 3
+  auto chunk_row0 = [&](int c) { return 16 * (wt.wt0 + min(2 * c, max(wt.wnt - 1, 0))); };
+  auto load_vj = [&](int c) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) vj[c % 3][tt] = vin[min(chunk_row0(c) + 16 * tt + n, Lr - 1)];
   };
+  load_vj(0);
+  ns.load(Kh, chunk_row0(0), Lr, lane);
+  ns.store(sK, chunk_row0(0), Lr, lane);
+  if (NC > 1) {
+    load_vj(1);
+    ns.load(Kh, chunk_row0(1), Lr, lane);
+  }
+  __builtin_amdgcn_wave_barrier();
 
-  // exponents x = log2(e) S + v_j of the wave's strip, masked to -inf off the support
+  // Strip of the wave: x[t][r] holds the plan entry 2^(log2(e) S + v_j - shift_i) of row
+  // 4 g + r, key n of tile t (0 off the support).  SHIFT (every step after the first): the shift
+  // is the previous step's row dual, which enters the matrix-core accumulator; after a column
+  // update every column of the previous plan sums to one, so each entry is at most 1 and each
+  // row sum lies in [1 / n, n] (n = window length): the exponentials are taken as the tiles
+  // arrive, with no maximum pass.  The first step shifts by the exact row maximum instead.
   float x[KT][4];
+  float up[4] = {0.f, 0.f, 0.f, 0.f};      // previous row duals of rows 4 g + r
+  f32x4 ci = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (SHIFT) {
+    const f32x4 u4 = load4(a.u_out + vo + min(o0 + 4 * g, a.Lpad - 4));
+    const float inv_c2 = 1.f / c2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      up[r] = u4[r];
+      ci[r] = u4[r] * inv_c2;
+    }
+  }
+  // rows 4 g + r: inside the sequence, and their band limits
+  bool iv[4];
+  int ilo[4], ihi[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = o0 + 4 * g + r;
+    iv[r] = i < Lr;
+    ilo[r] = i - h;
+    ihi[r] = i + h;
+  }
   float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  // window fragments two tiles ahead of the matrix cores
-  load_tile(0, 0);
-  if (KT > 1) load_tile(1, 1);
+  float l[4] = {0.f, 0.f, 0.f, 0.f};
+  // Every one of the KT tiles is computed (tiles past the wave's run, at most one per wave for a
+  // dense support, are masked), so the strip is one branch-free block: the matrix-core chain of
+  // tile t + 1 is issued ahead of the vector work on tile t and the two interleave within the
+  // wave, instead of the two waves of a SIMD alternating between whole MFMA and VALU phases.
+  auto mma = [&](int t) -> f32x4 {
+    Frag<T> fk;
+    lds_frag(fk, sK, 16 * (t & 1) + n, g);
+    return dot_tile(fq, fk, ci);
+  };
+  f32x4 sc[2];
+  sc[0] = mma(0);
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
-    if (t + 2 < KT) load_tile(t + 2, (t + 2) % 3);
-    if (t < wt.wnt) {
-      const f32x4 sc = dot_tile(fq, fk[t % 3]);
-      const int j0 = 16 * (wt.wt0 + t), j = j0 + n;
-      // a tile inside the sequence and the band on every entry needs no mask
-      const bool inner = (o0 + 15 < Lr) & (j0 + 15 < Lr) & (o0 + 15 - j0 <= h) & (j0 + 15 - o0 <= h);
-      if (inner) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[t][r] = fmaf(sc[r], c2, vj[t % 3]);
-          m[r] = fmaxf(m[r], x[t][r]);
+    if (t + 1 < KT) {
+      if (t & 1) {
+        // tile t + 1 opens chunk c + 1: into the buffer, and chunk c + 2 into registers
+        const int c1 = (t + 1) >> 1;
+        __builtin_amdgcn_wave_barrier();
+        ns.store(sK, chunk_row0(c1), Lr, lane);
+        __builtin_amdgcn_wave_barrier();
+        if (c1 + 1 < NC) {
+          load_vj(c1 + 1);
+          ns.load(Kh, chunk_row0(c1 + 1), Lr, lane);
         }
+      }
+      sc[(t + 1) & 1] = mma(t + 1);
+    }
+    const f32x4 s = sc[t & 1];
+    const float vjt = vj[(t >> 1) % 3][t & 1];
+    const int j = 16 * (wt.wt0 + t) + n;
+    const bool jv = (j < Lr) & (t < wt.wnt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float xv = fmaf(s[r], c2, vjt);
+      const bool ok = jv & iv[r] & (j >= ilo[r]) & (j <= ihi[r]);
+      if constexpr (SHIFT) {
+        x[t][r] = ok ? fast_exp2(xv) : 0.f;
+        l[r] += x[t][r];
       } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = o0 + 4 * g + r;
-          const bool ok = (i < Lr) & (j < Lr) & (abs(i - j) <= h);
-          x[t][r] = ok ? fmaf(sc[r], c2, vj[t % 3]) : -INFINITY;
-          m[r] = fmaxf(m[r], x[t][r]);
-        }
+        x[t][r] = ok ? xv : -INFINITY;
+        m[r] = fmaxf(m[r], x[t][r]);
       }
     }
   }
 
-  // exact row maximum over the workgroup
+  float M[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!SHIFT) {
+    // exact row maximum over the workgroup, then the exponentials
 #pragma unroll
-  for (int r = 0; r < 4; ++r) m[r] = row16_max(m[r]);
-  if (n < 4) red[0][wave][4 * g + n] = pick4(m, n);
-  __syncthreads();
-  float M[4];
+    for (int r = 0; r < 4; ++r) m[r] = row16_max(m[r]);
+    if (n < 4) red[0][wave][4 * g + n] = pick4(m, n);
+    __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float mm = red[0][0][4 * g + r];
+    for (int r = 0; r < 4; ++r) {
+      float mm = red[0][0][4 * g + r];
 #pragma unroll
-    for (int w = 1; w < kWideWaves; ++w) mm = fmaxf(mm, red[0][w][4 * g + r]);
-    M[r] = (mm > -INFINITY) ? mm : 0.f;   // a row with no support entries
-  }
-  float l[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int w = 1; w < kWideWaves; ++w) mm = fmaxf(mm, red[0][w][4 * g + r]);
+      M[r] = (mm > -INFINITY) ? mm : 0.f;   // a row with no support entries
+    }
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    if (t < wt.wnt) {
+    for (int t = 0; t < KT; ++t) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(x[t][r] - M[r]);
+        const float p = fast_exp2(x[t][r] - M[r]);   // 0 off the support and past the run
         x[t][r] = p;
         l[r] += p;
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[t][r] = 0.f;
     }
   }
 #pragma unroll
@@ -190,7 +267,8 @@ __global__ __launch_bounds__(kWideThreads) void wide_step_kernel(WideArgs a) {
 #pragma unroll
     for (int w = 1; w < kWideWaves; ++w) ll += red[1][w][4 * g + r];
     const bool live = ll > 0.f;
-    uu[r] = live ? -(M[r] + fast_log2(ll)) : 0.f;
+    // new row dual: shift - log2(row sum of the shifted plan)
+    uu[r] = live ? (SHIFT ? up[r] - fast_log2(ll) : -(M[r] + fast_log2(ll))) : 0.f;
     rinv[r] = live ? __builtin_amdgcn_rcpf(ll) : 0.f;
   }
 
@@ -277,32 +355,6 @@ template <int P> struct WideTraits {
   static constexpr int csrc = (P == kWOut || P == kWA) ? 1 : (P == kWD || P == kWE) ? 0 : -1;
   static constexpr int nacc = (P == kWD) ? 2 : (csrc >= 0) ? 1 : 0;   // 16 x 64 accumulators
   static constexpr bool has_red = (P != kWOut && P != kWE);
-};
-
-// 32 window rows of a [L][64] tensor held per lane between their global load and their LDS store
-// (rows outside the sequence become zeros when stored).
-template <typename T>
-struct WaveStage {
-  static constexpr int kCPR = 64 * (int)sizeof(T) / 16;   // 16-byte chunks per row
-  static constexpr int kPer = 32 * kCPR / 64;
-  uint4 x[kPer];
-  __device__ __forceinline__ void load(const T* base, int r0, int Lr, int lane) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = i * 64 + lane, row = c / kCPR, col = (c % kCPR) * (16 / (int)sizeof(T));
-      const int t = min(r0 + row, Lr - 1);
-      x[i] = *reinterpret_cast<const uint4*>(base + (int64_t)t * kD + col);
-    }
-  }
-  __device__ __forceinline__ void store(T* lds, int r0, int Lr, int lane) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = i * 64 + lane, row = c / kCPR, col = (c % kCPR) * (16 / (int)sizeof(T));
-      const bool ok = r0 + row < Lr;
-      *reinterpret_cast<uint4*>(lds + row * Lds<T>::stride + col) =
-          uint4{ok ? x[i].x : 0u, ok ? x[i].y : 0u, ok ? x[i].z : 0u, ok ? x[i].w : 0u};
-    }
-  }
 };
 
 template <typename T, int P>
@@ -582,10 +634,8 @@ __global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
 // =============================================================================================
 int wide_step_tiles(int Lr, int h) {
   const int per_wave = (wide_window_tiles(Lr, h) + kWideWaves - 1) / kWideWaves;
-  if (per_wave <= 4) return 4;
-  if (per_wave <= 8) return 8;
-  if (per_wave <= 16) return 16;
-  if (per_wave <= 33) return 33;
+  for (int kt : {4, 8, 12, 16, 24, 33})
+    if (per_wave <= kt) return kt;
   return 0;
 }
 
@@ -594,21 +644,28 @@ static dim3 wide_grid(const WideArgs& a) {
   return dim3((unsigned)(8 * ((nwork + 7) / 8)), 1, 1);
 }
 
-template <typename T>
+template <typename T, bool SHIFT>
 static void wide_step_t(int kt, const WideArgs& a, hipStream_t st) {
   const dim3 grid = wide_grid(a), block(kWideThreads);
   switch (kt) {
-    case 4: wide_step_kernel<T, 4><<<grid, block, 0, st>>>(a); break;
-    case 8: wide_step_kernel<T, 8><<<grid, block, 0, st>>>(a); break;
-    case 16: wide_step_kernel<T, 16><<<grid, block, 0, st>>>(a); break;
-    default: wide_step_kernel<T, 33><<<grid, block, 0, st>>>(a); break;
+    case 4: wide_step_kernel<T, 4, SHIFT><<<grid, block, 0, st>>>(a); break;
+    case 8: wide_step_kernel<T, 8, SHIFT><<<grid, block, 0, st>>>(a); break;
+    case 12: wide_step_kernel<T, 12, SHIFT><<<grid, block, 0, st>>>(a); break;
+    case 16: wide_step_kernel<T, 16, SHIFT><<<grid, block, 0, st>>>(a); break;
+    case 24: wide_step_kernel<T, 24, SHIFT><<<grid, block, 0, st>>>(a); break;
+    default: wide_step_kernel<T, 33, SHIFT><<<grid, block, 0, st>>>(a); break;
   }
 }
 
-hipError_t launch_wide_step(int elt, int kt, const WideArgs& a, hipStream_t st) {
-  if (kt != 4 && kt != 8 && kt != 16 && kt != 33) return hipErrorInvalidValue;
-  if (elt == 1) wide_step_t<bf16>(kt, a, st);
-  else wide_step_t<float>(kt, a, st);
+hipError_t launch_wide_step(int elt, int kt, bool first, const WideArgs& a, hipStream_t st) {
+  if (kt != 4 && kt != 8 && kt != 12 && kt != 16 && kt != 24 && kt != 33) return hipErrorInvalidValue;
+  if (elt == 1) {
+    if (first) wide_step_t<bf16, false>(kt, a, st);
+    else wide_step_t<bf16, true>(kt, a, st);
+  } else {
+    if (first) wide_step_t<float, false>(kt, a, st);
+    else wide_step_t<float, true>(kt, a, st);
+  }
   return hipGetLastError();
 }
 
