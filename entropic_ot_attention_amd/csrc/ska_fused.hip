@@ -246,7 +246,11 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     // 4g + r >= n on tile NT - 1).  No per-tile tests.
     const bool interior = exact_h & (cb >= 0) & (cb + RING <= Lr) & (b0 + 64 <= Lr);
     const int row0 = (cw + 4 * RING) % RING;
-    auto strip = [&](f32x4 (&x)[NT]) {
+    // Interior blocks of a shifted step take the exponentials (and row sums) as the tiles arrive,
+    // which overlaps them with the key-fragment reads and the matrix-core work of later tiles;
+    // their x then holds 2^x (0 off the band).
+    const bool exp_in_strip = SHIFT && interior;
+    auto strip = [&](f32x4 (&x)[NT], float (&ll)[4]) {
       if (interior) {
         // per-lane bases plus a wave-uniform row offset per tile: one address add per read
         const T* klane = kring + n * LS + 16 * g;
@@ -261,23 +265,31 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
             lds_frag(f, kring, rt + n, g);
           }
         };
-        Frag<T> fk[2];
-        kfrag(fk[0], tile_row(0));
+        // key fragments KA tiles ahead of the matrix cores (an LDS read takes longer than the
+        // work on one tile)
+        constexpr int KA = 2;
+        Frag<T> fk[KA + 1];
+#pragma unroll
+        for (int t = 0; t < KA && t < NT; ++t) kfrag(fk[t], tile_row(t));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int rt = tile_row(t);
-          if (t + 1 < NT) kfrag(fk[(t + 1) & 1], tile_row(t + 1));
+          if (t + KA < NT) kfrag(fk[(t + KA) % (KA + 1)], tile_row(t + KA));
           const float vjt = vlane[rt];
-          x[t] = dot_tile(fq, fk[t & 1], shc);
+          x[t] = dot_tile(fq, fk[t % (KA + 1)], shc);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[t][r] = fmaf(x[t][r], c2, vjt);
-          if (t == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[0][r] = (4 * g + r <= n) ? x[0][r] : -INFINITY;
-          }
-          if (t == NT - 1) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[t][r] = (4 * g + r >= n) ? x[t][r] : -INFINITY;
+          for (int r = 0; r < 4; ++r) {
+            float xv = fmaf(x[t][r], c2, vjt);
+            bool keep = true;
+            if (t == 0) keep = (4 * g + r <= n);
+            if (t == NT - 1) keep = (4 * g + r >= n);
+            if constexpr (SHIFT) {
+              xv = keep ? fast_exp2(xv) : 0.f;
+              ll[r] += xv;
+            } else {
+              xv = keep ? xv : -INFINITY;
+            }
+            x[t][r] = xv;
           }
         }
       } else {
@@ -343,7 +355,8 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     float cp[NT + 3];
     {
       f32x4 x[NT];
-      strip(x);
+      float ll[4] = {0.f, 0.f, 0.f, 0.f};
+      strip(x, ll);
       float mx[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (!SHIFT) {
 #pragma unroll
@@ -357,14 +370,15 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
           for (int t = 0; t < NT; ++t) x[t][r] -= mx[r];
         }
       }
-      float ll[4] = {0.f, 0.f, 0.f, 0.f};
+      if (!exp_in_strip) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[t][r] = fast_exp2(x[t][r]);
-          ll[r] += x[t][r];
-        }
+          for (int r = 0; r < 4; ++r) {
+            x[t][r] = fast_exp2(x[t][r]);
+            ll[r] += x[t][r];
+          }
+      }
       float rinv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
