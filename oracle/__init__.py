@@ -30,6 +30,8 @@ from .sinkhorn_band import (  # noqa: F401
     forward_from_base,
     vjp_one_reference,
     vjp_direct_four,
+    vjp_tail,
+    vjp_tail_one_reference,
     staircase_plan,
     dustbin_block_forward,
     dustbin_block_vjp,

@@ -375,6 +375,110 @@ def vjp_one_reference(Q, K, V, dO, duals, prob: BandProblem, active=None, want_p
 
 
 # --------------------------------------------------------------------------------------
+# VJP, any tail depth R >= 1
+# --------------------------------------------------------------------------------------
+
+def _tail_duals(duals, R):
+    """duals = [v0, u1, v1, ..., uR, vR] -> (us, vs) with us[a] = u^(a) (a >= 1), vs[b] = v^(b)."""
+    if len(duals) != 2 * R + 1:
+        raise ValueError("expected 2 R + 1 saved duals")
+    us = [None] + [duals[2 * a - 1] for a in range(1, R + 1)]
+    vs = [duals[2 * b] for b in range(R + 1)]
+    return us, vs
+
+
+def vjp_tail(Q, K, V, dO, duals, prob: BandProblem, active=None, want_parts=False):
+    """Exact VJP of O = P^(R,R) V through an R-step tail (any R >= 1) with v^(0) stopped:
+    reverse-mode differentiation of the tail steps in turn, last step first, every
+    staircase plan P^(a,b) = exp(S + u^(a) + v^(b)) from its own exponential.
+
+      O = P^(R,R) V:            dV = P^(R,R)^T dO,  g_ij = dO_i . V_j
+      P^(R,R):                  dS = P g,  du^(R) = rowsum(P g),  dv^(R) = colsum(P g)
+      for a = R, R-1, ..., 1:
+        v^(a) = -LSE_col(S + u^(a))     (weights P^(a,a), columns sum to one)
+            dS -= P^(a,a) dv^(a)_j,  du^(a) -= rowsum(P^(a,a) dv^(a)_j)
+        u^(a) = -LSE_row(S + v^(a-1))   (weights P^(a,a-1), rows sum to one)
+            dS -= P^(a,a-1) du^(a)_i,  dv^(a-1) -= colsum(P^(a,a-1) du^(a)_i)   (a > 1;
+            v^(0) is stopped)
+      dQ = s dS K,  dK = s dS^T Q
+    R = 2 is the four-plan adjoint of vjp_direct_four.
+    [technical summaries §2.1: R differentiable tail steps from the stopped base state;
+    §2.2: the exact tail adjoint through the staircase plans]"""
+    R = prob.R
+    h = prob.h
+    d = np.asarray(Q).shape[1]
+    s = 1.0 / (np.sqrt(d) * prob.eps)
+    S = band_scores(Q, K, h, prob.eps, active)
+    us, vs = _tail_duals(duals, R)
+    L = S.shape[1]
+    P = staircase_plan(S, us[R], vs[R], h)
+    g = _value_scores(dO, V, h, active)
+    dS = P * g
+    du = [None] + [np.zeros(L) for _ in range(R)]
+    dv = [np.zeros(L) for _ in range(R + 1)]
+    du[R] = du[R] + _row_sum(P * g)
+    dv[R] = dv[R] + _col_sum(P * g, h)
+    for a in range(R, 0, -1):
+        Paa = staircase_plan(S, us[a], vs[a], h)
+        dS = dS - Paa * _row_vec(dv[a], h)
+        du[a] = du[a] - _row_sum(Paa * _row_vec(dv[a], h))
+        Pab = staircase_plan(S, us[a], vs[a - 1], h)
+        dS = dS - Pab * du[a][None, :]
+        if a > 1:
+            dv[a - 1] = dv[a - 1] - _col_sum(Pab * du[a][None, :], h)
+    dQ, dK, dV = _score_contractions(dS, Q, K, P, dO, h, s)
+    if want_parts:
+        return dQ, dK, dV, dict(dS=dS, du=du, dv=dv, P=P, g=g, S=S)
+    return dQ, dK, dV
+
+
+def vjp_tail_one_reference(Q, K, V, dO, duals, prob: BandProblem, active=None,
+                           want_parts=False):
+    """The same VJP (any R >= 1) with one reference tile: only P = P^(R,R) is
+    exponentiated; every other staircase plan is P * eu_a(i) * ev_b(j) with
+    eu_a = exp(u^(a) - u^(R)), ev_b = exp(v^(b) - v^(R)) (the orbit equation).
+
+    Vector cotangents, each a reduction of the reference tile:
+      dv^(R)_j = sum_i P_ij g_ij
+      du^(R)_i = sum_j P_ij (g_ij - dv^(R)_j)
+      for a = R-1, ..., 1:
+        dv^(a)_j = -ev_a(j) sum_i P_ij eu_{a+1}(i) du^(a+1)_i
+        du^(a)_i = -eu_a(i) sum_j P_ij ev_a(j) dv^(a)_j
+    Modifier field (2 R rank-one terms) and score cotangent:
+      M_ij = g_ij - sum_a eu_a(i) ev_a(j) dv^(a)_j - sum_a eu_a(i) du^(a)_i ev_{a-1}(j),
+      dS = P * M.
+    R = 2 is vjp_one_reference.
+    [abstract: one reference plan tile times a modifier field of vector cotangents and dual
+    differences; technical summaries §2.2: orbit equation P^(a,b) = P^(R,R) exp(du) exp(dv)]"""
+    R = prob.R
+    h = prob.h
+    d = np.asarray(Q).shape[1]
+    s = 1.0 / (np.sqrt(d) * prob.eps)
+    S = band_scores(Q, K, h, prob.eps, active)
+    us, vs = _tail_duals(duals, R)
+    P = staircase_plan(S, us[R], vs[R], h)
+    g = _value_scores(dO, V, h, active)
+    eu = [None] + [np.exp(us[a] - us[R]) for a in range(1, R + 1)]
+    ev = [np.exp(vs[b] - vs[R]) for b in range(R + 1)]
+    du = [None] * (R + 1)
+    dv = [None] * (R + 1)
+    dv[R] = _col_sum(P * g, h)
+    du[R] = _row_sum(P * (g - _row_vec(dv[R], h)))
+    for a in range(R - 1, 0, -1):
+        dv[a] = -ev[a] * _col_sum(P * (eu[a + 1] * du[a + 1])[None, :], h)
+        du[a] = -eu[a] * _row_sum(P * _row_vec(ev[a] * dv[a], h))
+    M = g.copy()
+    for a in range(1, R + 1):
+        M = M - eu[a][None, :] * _row_vec(ev[a] * dv[a], h)
+        M = M - (eu[a] * du[a])[None, :] * _row_vec(ev[a - 1], h)
+    dS = P * M
+    dQ, dK, dV = _score_contractions(dS, Q, K, P, dO, h, s)
+    if want_parts:
+        return dQ, dK, dV, dict(dS=dS, M=M, du=du, dv=dv, P=P, g=g, S=S)
+    return dQ, dK, dV
+
+
+# --------------------------------------------------------------------------------------
 # dustbin_block: same surrogate on an augmented support
 # --------------------------------------------------------------------------------------
 

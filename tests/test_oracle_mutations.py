@@ -1,4 +1,5 @@
-"""The pins in test_oracle.py must fail for plausible mistakes in the oracle.
+"""The pins in test_oracle.py and test_oracle_tail.py must fail for plausible mistakes in
+the oracle.
 
 Each case plants one mistake (an update order swapped, a dropped modifier term, a
 flipped sign, a wrong dual in a factor, a transposed contraction, a missing scale,
@@ -34,10 +35,31 @@ MUTATIONS = {
     "output_uses_P21": ("    uR, vR = duals[-2], duals[-1]", "    uR, vR = duals[-2], duals[-3]"),
 }
 
+# mistakes in the general-R adjoint forms, caught by the pins in test_oracle_tail.py
+TAIL_MUTATIONS = {
+    "tail_drop_column_modifier_term": (
+        "        M = M - eu[a][None, :] * _row_vec(ev[a] * dv[a], h)\n", ""),
+    "tail_wrong_level_in_dv": (
+        "dv[a] = -ev[a] * _col_sum(P * (eu[a + 1] * du[a + 1])[None, :], h)",
+        "dv[a] = -ev[a] * _col_sum(P * (eu[a] * du[a + 1])[None, :], h)"),
+    "tail_wrong_column_factor_in_row_term": (
+        "(eu[a] * du[a])[None, :] * _row_vec(ev[a - 1], h)",
+        "(eu[a] * du[a])[None, :] * _row_vec(ev[a], h)"),
+    "tail_sign_of_du": ("du[a] = -eu[a] * _row_sum(", "du[a] = eu[a] * _row_sum("),
+    "tail_step_form_wrong_row_plan": (
+        "Pab = staircase_plan(S, us[a], vs[a - 1], h)", "Pab = staircase_plan(S, us[a], vs[a], h)"),
+    "tail_step_form_skips_column_term": (
+        "        dS = dS - Paa * _row_vec(dv[a], h)\n", ""),
+}
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_pins_catch_planted_mistake(name):
-    before, after = MUTATIONS[name]
+
+CASES = [(n, "tests/test_oracle.py") for n in sorted(MUTATIONS)] + \
+        [(n, "tests/test_oracle_tail.py") for n in sorted(TAIL_MUTATIONS)]
+
+
+@pytest.mark.parametrize("name,pins", CASES, ids=[c[0] for c in CASES])
+def test_pins_catch_planted_mistake(name, pins):
+    before, after = {**MUTATIONS, **TAIL_MUTATIONS}[name]
     src = open(SRC).read()
     assert before in src, f"mutation anchor for {name} no longer present"
     with tempfile.TemporaryDirectory() as d:
@@ -47,7 +69,7 @@ def test_pins_catch_planted_mistake(name):
                         ignore=shutil.ignore_patterns("__pycache__", "golden"))
         with open(os.path.join(d, "oracle", "sinkhorn_band.py"), "w") as f:
             f.write(src.replace(before, after))
-        r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle.py", "-q", "-x",
+        r = subprocess.run([sys.executable, "-m", "pytest", pins, "-q", "-x",
                             "-p", "no:cacheprovider"], cwd=d, capture_output=True, text=True,
                            timeout=300)
     assert r.returncode != 0, f"planted mistake {name} passed every pin:\n{r.stdout[-2000:]}"

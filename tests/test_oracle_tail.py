@@ -1,0 +1,130 @@
+"""Pins of the oracle's adjoint for a general tail depth R (CPU only).
+
+The two general-R forms (step-by-step reverse mode with every staircase plan from its own
+exponential, and the one-reference-tile orbit form) are pinned against dense torch fp64
+autograd through the same surrogate (tests/independent.py), against central finite
+differences with the stopped base held fixed, against the invariants that fix row and column
+sums of the score cotangent, and, at R = 2, against the four-plan and one-reference functions.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import sinkhorn_band as sb
+from tests.independent import dense_autograd
+
+
+def _qkv(L, d=8, seed=0):
+    r = np.random.default_rng(seed)
+    return [r.standard_normal((L, d)) for _ in range(4)]
+
+
+def _dense_from_band(X, h):
+    L = X.shape[1]
+    D = np.zeros((L, L))
+    for k, o in enumerate(range(-h, h + 1)):
+        for i in range(L):
+            j = i + o
+            if 0 <= j < L:
+                D[i, j] = X[k, i]
+    return D
+
+
+CASES = [
+    # L, W, T, R, eps
+    (21, 8, 3, 1, 1.0),
+    (30, 12, 0, 1, 0.7),
+    (27, 10, 4, 3, 1.0),
+    (40, 80, 5, 3, 1.2),
+    (33, 14, 2, 4, 0.8),
+    (18, 0, 1, 4, 1.0),
+]
+
+
+@pytest.mark.parametrize("L,W,T,R,eps", CASES)
+def test_tail_vjp_matches_dense_autograd(L, W, T, R, eps):
+    """Both general-R forms == dense torch-fp64 autograd through the same surrogate."""
+    Q, K, V, dO = _qkv(L, seed=L * 7 + R)
+    prob = sb.BandProblem(W=W, T=T, R=R, eps=eps)
+    O, duals = oracle.forward(Q, K, V, prob)
+    Or, dQr, dKr, dVr, dualsr = dense_autograd(Q, K, V, dO, W, T, R, eps)
+    np.testing.assert_allclose(O, Or, atol=1e-12)
+    np.testing.assert_allclose(duals, dualsr, atol=1e-11)
+    for fn in (oracle.vjp_tail, oracle.vjp_tail_one_reference):
+        dQ, dK, dV = fn(Q, K, V, dO, duals, prob)
+        np.testing.assert_allclose(dQ, dQr, atol=1e-10)
+        np.testing.assert_allclose(dK, dKr, atol=1e-10)
+        np.testing.assert_allclose(dV, dVr, atol=1e-11)
+
+
+def test_tail_forms_reduce_to_the_r2_adjoints():
+    """At R = 2 the step-by-step form is the four-plan adjoint and the orbit form is the
+    one-reference adjoint, entry by entry."""
+    L, W = 35, 12
+    Q, K, V, dO = _qkv(L, seed=5)
+    prob = sb.BandProblem(W=W, T=3, R=2, eps=0.9)
+    _, duals = oracle.forward(Q, K, V, prob)
+    a = oracle.vjp_tail(Q, K, V, dO, duals, prob, want_parts=True)
+    b = oracle.vjp_direct_four(Q, K, V, dO, duals, prob, want_parts=True)
+    c = oracle.vjp_tail_one_reference(Q, K, V, dO, duals, prob, want_parts=True)
+    e = oracle.vjp_one_reference(Q, K, V, dO, duals, prob, want_parts=True)
+    np.testing.assert_allclose(a[3]["dS"], b[3]["dS"], atol=1e-13)
+    np.testing.assert_allclose(c[3]["dS"], e[3]["dS"], atol=1e-13)
+    np.testing.assert_allclose(a[3]["du"][1], b[3]["du1"], atol=1e-13)
+    np.testing.assert_allclose(c[3]["dv"][1], e[3]["dv1"], atol=1e-13)
+
+
+@pytest.mark.parametrize("R", [1, 3, 4])
+def test_tail_orbit_form_equals_step_form_entrywise(R):
+    """Orbit identity: every staircase plan is the reference tile times row and column
+    factors, so the two forms give the same score cotangent entry by entry."""
+    L, W = 44, 14
+    Q, K, V, dO = _qkv(L, seed=20 + R)
+    prob = sb.BandProblem(W=W, T=2, R=R, eps=0.6)
+    _, duals = oracle.forward(Q, K, V, prob)
+    a = oracle.vjp_tail(Q, K, V, dO, duals, prob, want_parts=True)
+    b = oracle.vjp_tail_one_reference(Q, K, V, dO, duals, prob, want_parts=True)
+    np.testing.assert_allclose(a[3]["dS"], b[3]["dS"], atol=1e-13)
+    for a_ in range(1, R + 1):
+        np.testing.assert_allclose(a[3]["du"][a_], b[3]["du"][a_], atol=1e-13)
+        np.testing.assert_allclose(a[3]["dv"][a_], b[3]["dv"][a_], atol=1e-13)
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_tail_invariants(R):
+    """Row sums of dS vanish (the tail starts with a row update, which absorbs a per-row
+    shift of S); column sums equal -sum_i P^(1,0)_ij du^(1)_i, the cotangent of the stopped
+    v^(0); dV = P^(R,R)^T dO."""
+    L, W = 31, 10
+    h = W // 2
+    Q, K, V, dO = _qkv(L, seed=40 + R)
+    prob = sb.BandProblem(W=W, T=3, R=R)
+    _, duals = oracle.forward(Q, K, V, prob)
+    _, _, dV, parts = oracle.vjp_tail(Q, K, V, dO, duals, prob, want_parts=True)
+    dS = _dense_from_band(parts["dS"], h)
+    np.testing.assert_allclose(dS.sum(1), 0, atol=1e-13)
+    P10 = _dense_from_band(sb.staircase_plan(parts["S"], duals[1], duals[0], h), h)
+    np.testing.assert_allclose(dS.sum(0), -(P10 * parts["du"][1][:, None]).sum(0), atol=1e-13)
+    P = _dense_from_band(parts["P"], h)
+    np.testing.assert_allclose(dV, P.T @ dO, atol=1e-13)
+
+
+def test_tail_vjp_central_finite_differences():
+    """R = 4: <dQ, e_Q> + <dK, e_K> + <dV, e_V> equals the directional derivative of
+    <O, dO> with v^(0) frozen (central differences)."""
+    L, W = 24, 8
+    Q, K, V, dO = _qkv(L, seed=3)
+    prob = sb.BandProblem(W=W, T=3, R=4, eps=0.9)
+    _, duals = oracle.forward(Q, K, V, prob)
+    v0 = duals[0]
+    dQ, dK, dV = oracle.vjp_tail_one_reference(Q, K, V, dO, duals, prob)
+    r = np.random.default_rng(4)
+    for _ in range(3):
+        eQ, eK, eV = (r.standard_normal(Q.shape) for _ in range(3))
+        delta = 1e-5
+        f = lambda t: float(np.sum(oracle.forward_from_base(  # noqa: E731
+            Q + t * eQ, K + t * eK, V + t * eV, v0, prob) * dO))
+        fd = (f(delta) - f(-delta)) / (2 * delta)
+        an = float(np.sum(dQ * eQ) + np.sum(dK * eK) + np.sum(dV * eV))
+        assert abs(fd - an) < 1e-7 * max(1.0, abs(an)), (fd, an)
