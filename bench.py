@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="seq1x4_L262144_W256_bf16")
     ap.add_argument("--schedule", default="one_reference", choices=["one_reference", "direct_four"])
+    ap.add_argument("--tail-depth", type=int, default=0,
+                    help="run the named workload with this tail depth R (1..4) instead of its own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -95,7 +97,10 @@ def cpu_baseline(w, sample_tokens: int):
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         O, duals = oracle.forward(Q, K, V, p)
-        oracle.vjp_one_reference(Q, K, V, dO, duals, p)
+        if w.R == 2:
+            oracle.vjp_one_reference(Q, K, V, dO, duals, p)
+        else:
+            oracle.vjp_tail_one_reference(Q, K, V, dO, duals, p)
         dt = time.perf_counter() - t0
     # one token of the workload spans all heads: scale the single-head sample accordingly
     value = n / (w.bh * dt)
@@ -118,6 +123,8 @@ def main():
     from entropic_ot_attention_amd.workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.tail_depth:
+        w = w.with_(R=args.tail_depth)
     dev = torch.device("cuda:0")
     x = make_inputs(w)
     Q, K, V, dO = (x[k].to(dev) for k in ("Q", "K", "V", "dO"))

@@ -60,6 +60,7 @@ void timing_end(int kind, std::pair<hipEvent_t, hipEvent_t> ev, hipStream_t st) 
 struct Plan {
   ska::Geometry g;
   int elt;
+  int R;
   bool empty;
 };
 
@@ -78,7 +79,7 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
   const bool dustbin = (op == SKA_OP_DUSTBIN_BLOCK_FWD || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   if (op < SKA_OP_FWD || op > SKA_OP_DUSTBIN_BLOCK_VJP) return fail(SKA_ERR_INVALID, "unknown op");
   if (p->R < 1) return fail(SKA_ERR_INVALID, "R must be >= 1");
-  if (vjp && p->R != 2) return fail(SKA_ERR_UNSUPPORTED, "the VJP is built for R == 2");
+  if (vjp && p->R > ska::kTailMaxR) return fail(SKA_ERR_UNSUPPORTED, "the VJP is built for R <= 4");
   if (p->d != ska::kD) return fail(SKA_ERR_UNSUPPORTED, "head dimension d must be 64");
   const int64_t Lr = p->L + (dustbin ? 1 : 0);
   if (Lr > (int64_t(1) << 30)) return fail(SKA_ERR_UNSUPPORTED, "L above 2^30 tokens");
@@ -87,6 +88,7 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
   if (dustbin && h < p->L) h = p->L;  // widened band: every token reaches the dustbin
   if (h > Lr) h = Lr;                 // wider than the sequence changes nothing
   out->elt = p->dtype;
+  out->R = p->R;
   out->empty = (p->bh == 0 || Lr == 0);
   out->g.bh = p->bh;
   out->g.Lr = (int)Lr;
@@ -109,6 +111,7 @@ size_t workspace_for(const Plan& pl, ska_op op) {
   if (pl.empty) return 0;
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   const int64_t vs = pl.g.bh * (int64_t)pl.g.Lpad;
+  if (vjp && pl.R != 2) return (size_t)(ska::tail_vecs(pl.R) * vs) * sizeof(float);
   if (vjp) {
     // streaming passes (both schedules, bands LDS holds) add dv1 column partials
     int nt = 0;
@@ -346,6 +349,8 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
   SKA_TRY(check_problem(p, op, &pl));
   if (sched != SKA_ONE_REFERENCE && sched != SKA_DIRECT_FOUR)
     return fail(SKA_ERR_INVALID, "unknown schedule");
+  if (sched == SKA_DIRECT_FOUR && p->R != 2)
+    return fail(SKA_ERR_UNSUPPORTED, "the direct-four schedule is the R == 2 adjoint");
   if (pl.empty) return SKA_OK;
   SKA_TRY(check_ptr(Q, "Q"));
   SKA_TRY(check_ptr(K, "K"));
@@ -364,6 +369,29 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
   const ska::Geometry& g = pl.g;
   float* ws = static_cast<float*>(workspace);
   const bool d4 = (sched == SKA_DIRECT_FOUR);
+  if (p->R != 2) {
+    // general tail depth: one-reference-tile adjoint, 2R + 2 passes on the wide decomposition
+    // (A: dv^(R) and dV; B: du^(R); C, D for each level a = R-1 .. 1; then dQ and dK)
+    hipError_t e = ska::launch_tail_prep(duals, ws, p->R, g, st);
+    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+    ska::WideArgs w = wide_args(pl, Q, K, V, dO);
+    w.ws = ws;
+    w.vec_stride = g.bh * (int64_t)g.Lpad;
+    w.R = p->R;
+    w.out0 = dV;
+    SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 0, w, st));
+    SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 1, w, st));
+    for (int lev = p->R - 1; lev >= 1; --lev) {
+      w.level = lev;
+      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 2, w, st));
+      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 3, w, st));
+    }
+    w.out0 = dQ;
+    SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 4, w, st));
+    w.out0 = dK;
+    SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 5, w, st));
+    return SKA_OK;
+  }
   hipError_t e = ska::launch_vjp_prep(duals, ws, g, st);
   if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
   int nt = 0;

@@ -117,7 +117,14 @@ struct WideArgs {
   int64_t bh;
   int Lr, Lpad, h, nrt, pw;
   float c2, s;
+  int R, level;            // general tail depth passes: the depth, and the level a of passes C/D
 };
+
+// VJP workspace of a general tail depth R (any band), each [bh][Lpad] fp32: u^(R), v^(R) (log2
+// units), the orbit factors EU_a = exp(u^(a) - u^(R)) (a = 1..R) and EV_b = exp(v^(b) - v^(R))
+// (b = 0..R), and the scaled cotangents F_a = dv^(a) EV_a and C_a = du^(a) EU_a (a = 1..R).
+inline int tail_vecs(int R) { return 3 + 4 * R; }
+constexpr int kTailMaxR = 4;
 
 // Register tiles per wave of the wide fused step for half-width h (its window of at most 8 KT
 // tiles stays in registers), or 0 when the window is wider than that.
@@ -148,4 +155,9 @@ hipError_t launch_wide_finish(int elt, const WideArgs& a, hipStream_t st);
 // pass: 0 output, 1..5 the VJP passes A..E
 hipError_t launch_wide_pass(int elt, int pass, bool d4, const WideArgs& a, hipStream_t st);
 hipError_t launch_vjp_prep(const float* duals, float* ws, const Geometry& g, hipStream_t st);
+// General tail depth (1 <= R <= kTailMaxR), one-reference-tile adjoint on the wide decomposition:
+// the vector preparation, then passes 0 (A: dv^(R), dV), 1 (B: du^(R)), 2 (C: dv^(a)),
+// 3 (D: du^(a)), 4 (dQ), 5 (dK).
+hipError_t launch_tail_prep(const float* duals, float* ws, int R, const Geometry& g, hipStream_t st);
+hipError_t launch_tail_pass(int elt, int pass, const WideArgs& a, hipStream_t st);
 }  // namespace ska

@@ -630,6 +630,243 @@ __global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
 }
 
 // =============================================================================================
+// General tail depth R: the exact one-reference-tile adjoint through an R-step tail.
+// [technical summaries §2.1: R differentiable tail steps from the stopped base state; §2.2 and
+// abstract: every staircase plan is the reference tile P = P^(R,R) times row and column factors]
+// With EU_a = exp(u^(a) - u^(R)), EV_b = exp(v^(b) - v^(R)), the vector cotangents are reductions
+// of the reference tile, level by level (F_a = dv^(a) EV_a, C_a = du^(a) EU_a):
+//   A (owns keys)     dv^(R)_j = sum_i P g                          F_R = dv^(R);  dV = P^T dO
+//   B (owns queries)  du^(R)_i = sum_j P (g - F_R(j))               C_R = du^(R)
+//   for a = R-1 .. 1:
+//   C (owns keys)     dv^(a)_j = -EV_a(j) sum_i P C_{a+1}(i)        F_a = dv^(a) EV_a
+//   D (owns queries)  du^(a)_i = -EU_a(i) sum_j P F_a(j)            C_a = du^(a) EU_a
+//   Q (owns queries)  dQ_i = s sum_j P M k_j,  E (owns keys) dK_j = s sum_i P M q_i, with the
+//                     modifier M = g - sum_a [EU_a(i) F_a(j) + C_a(i) EV_{a-1}(j)] (2 R terms).
+// (R = 2 gives A = du2, B, C, D, E, F, G of the two-level passes.)
+// =============================================================================================
+struct TailVec {
+  int R;
+  __device__ int u() const { return 0; }
+  __device__ int v() const { return 1; }
+  __device__ int eu(int a) const { return 2 + (a - 1); }        // a = 1..R
+  __device__ int ev(int b) const { return 2 + R + b; }          // b = 0..R
+  __device__ int f(int a) const { return 3 + 2 * R + (a - 1); }
+  __device__ int c(int a) const { return 3 + 3 * R + (a - 1); }
+};
+
+// duals (natural units, [bh][2R+1][Lr]: v0, u1, v1, .., uR, vR) -> the tail vectors
+__global__ void tail_prep_kernel(const float* __restrict__ duals, float* __restrict__ ws, int R,
+                                 int Lr, int Lpad, int64_t vec_stride) {
+  const int64_t head = blockIdx.y;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= Lpad) return;
+  const TailVec tv{R};
+  const int64_t ob = head * Lpad + t;
+  auto at = [&](int k) -> float& { return ws[k * vec_stride + ob]; };
+  const bool ok = t < Lr;
+  const float* dh = duals + head * (2 * (int64_t)R + 1) * Lr;
+  auto dual = [&](int slot) { return ok ? dh[(int64_t)slot * Lr + t] : 0.f; };
+  const float uR = dual(2 * R - 1), vR = dual(2 * R);
+  at(tv.u()) = uR * kLog2e;
+  at(tv.v()) = vR * kLog2e;
+  for (int a = 1; a <= R; ++a) {
+    at(tv.eu(a)) = ok ? expf(dual(2 * a - 1) - uR) : 0.f;
+    at(tv.f(a)) = 0.f;
+    at(tv.c(a)) = 0.f;
+  }
+  for (int b = 0; b <= R; ++b) at(tv.ev(b)) = ok ? expf(dual(2 * b) - vR) : 0.f;
+}
+
+enum TailPass : int { kTA = 0, kTB, kTC, kTD, kTQ, kTE };
+
+template <int GP> struct TailTraits {
+  static constexpr bool owns_keys = (GP == kTA || GP == kTC || GP == kTE);
+  static constexpr bool needs_g = (GP != kTC && GP != kTD);
+  static constexpr int nstage = needs_g ? 2 : 1;
+  // staged tensor the contraction reads: 0 = the score operand, 1 = the second tensor, -1 none
+  static constexpr int csrc = (GP == kTA) ? 1 : (GP == kTQ || GP == kTE) ? 0 : -1;
+  static constexpr bool has_red = (GP <= kTD);
+};
+
+// RT: the tail depth for the dQ and dK passes (compile time: their 2 RT modifier terms stay in
+// registers); 0 for the level passes, which take R and the level at run time.
+template <typename T, int GP, int RT>
+__global__ __launch_bounds__(kWideThreads) void tail_pass_kernel(WideArgs a) {
+  using TR = TailTraits<GP>;
+  constexpr int kStageElems = 32 * Lds<T>::stride;
+  constexpr int kStageBytes = kWideWaves * TR::nstage * kStageElems * (int)sizeof(T);
+  constexpr int kRedFloats = ((TR::csrc >= 0 ? 16 : 0) + 1) * 64;
+  constexpr int kRedBytes = kWideWaves * kRedFloats * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStageBytes > kRedBytes ? kStageBytes : kRedBytes];
+  constexpr int NM = (GP == kTQ || GP == kTE) ? RT : 0;     // modifier levels
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t head;
+  int rt;
+  if (!wide_work(a.bh * a.nrt, a.nrt, &head, &rt)) return;
+  const int Lr = a.Lr, h = a.h;
+  const float c2 = a.c2;
+  const TailVec tv{a.R};
+  const int lev = a.level;
+  const WideTile wt = wide_tile(rt, Lr, h, wave);
+  const int o0 = wt.o0, o = o0 + n;
+  const int64_t tb = head * (int64_t)Lr * kD;
+  const T* Qp = static_cast<const T*>(a.Q) + tb;
+  const T* Kp = static_cast<const T*>(a.K) + tb;
+  const T* Vp = static_cast<const T*>(a.V) + tb;
+  const T* dOp = static_cast<const T*>(a.dO) + tb;
+  const T* own_s = TR::owns_keys ? Kp : Qp;
+  const T* own_g = TR::owns_keys ? Vp : dOp;
+  const T* winA = TR::owns_keys ? Qp : Kp;
+  const T* winB = TR::owns_keys ? dOp : Vp;
+  const int64_t vo = head * (int64_t)a.Lpad;
+  auto vec = [&](int which) -> float* { return a.ws + which * a.vec_stride + vo; };
+
+  T* sA = reinterpret_cast<T*>(smem) + wave * TR::nstage * kStageElems;
+  T* sB = sA + kStageElems;
+  Frag<T> fo, fog;
+  const int oc = min(o, Lr - 1);
+  load_frag_raw(fo, own_s + (int64_t)oc * kD, g);
+  if constexpr (TR::needs_g) load_frag_raw(fog, own_g + (int64_t)oc * kD, g);
+
+  // owned-token values: its dual of the reference tile, and the modifier factors
+  const float own_d = vec(TR::owns_keys ? tv.v() : tv.u())[o];
+  float own_x[NM > 0 ? NM : 1], own_y[NM > 0 ? NM : 1];
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    if constexpr (GP == kTQ) {
+      own_x[k] = vec(tv.eu(k + 1))[o];          // EU_a(i)
+      own_y[k] = vec(tv.c(k + 1))[o];           // C_a(i)
+    } else {
+      own_x[k] = vec(tv.f(k + 1))[o];           // F_a(j)
+      own_y[k] = vec(tv.ev(k))[o];              // EV_{a-1}(j)
+    }
+  }
+  // window vector of the level passes
+  const int wsel = (GP == kTB) ? tv.f(a.R) : (GP == kTC) ? tv.c(lev + 1) : (GP == kTD) ? tv.f(lev) : 0;
+
+  float red = 0.f;
+  f32x4 acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  WaveStage<T> na, nb;
+  const int nch = (wt.wnt + 1) >> 1;
+  int w0 = 16 * wt.wt0;
+  na.load(winA, w0, Lr, lane);
+  if (TR::nstage == 2) nb.load(winB, w0, Lr, lane);
+  na.store(sA, w0, Lr, lane);
+  if (TR::nstage == 2) nb.store(sB, w0, Lr, lane);
+  __builtin_amdgcn_wave_barrier();
+  for (int c = 0; c < nch; ++c, w0 += 32) {
+    na.load(winA, w0 + 32, Lr, lane);
+    if (TR::nstage == 2) nb.load(winB, w0 + 32, Lr, lane);
+    float z[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[tt][r] = 0.f;
+      if (2 * c + tt >= wt.wnt) continue;
+      const int wb = w0 + 16 * tt + 4 * g;        // this lane's window tokens wb + r
+      const int wc = min(wb, a.Lpad - 4);
+      Frag<T> fw;
+      lds_frag(fw, sA, 16 * tt + n, g);
+      const f32x4 sc = dot_tile(fw, fo);
+      f32x4 gv = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (TR::needs_g) {
+        Frag<T> fwg;
+        lds_frag(fwg, sB, 16 * tt + n, g);
+        gv = dot_tile(fwg, fog);
+      }
+      const f32x4 wd = load4(vec(TR::owns_keys ? tv.u() : tv.v()) + wc);
+      f32x4 wsv = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (GP == kTB || GP == kTC || GP == kTD) wsv = load4(vec(wsel) + wc);
+      f32x4 wx[NM > 0 ? NM : 1], wy[NM > 0 ? NM : 1];
+#pragma unroll
+      for (int k = 0; k < NM; ++k) {
+        if constexpr (GP == kTQ) {
+          wx[k] = load4(vec(tv.f(k + 1)) + wc);   // F_a(j)
+          wy[k] = load4(vec(tv.ev(k)) + wc);      // EV_{a-1}(j)
+        } else {
+          wx[k] = load4(vec(tv.eu(k + 1)) + wc);  // EU_a(i)
+          wy[k] = load4(vec(tv.c(k + 1)) + wc);   // C_a(i)
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = in_band(wb + r, o, h, Lr);
+        const float p = fast_exp2(fmaf(sc[r], c2, own_d + wd[r]));
+        if constexpr (GP == kTA) {
+          red = keep ? fmaf(p, gv[r], red) : red;
+          z[tt][r] = keep ? p : 0.f;
+        } else if constexpr (GP == kTB) {
+          red = keep ? fmaf(p, gv[r] - wsv[r], red) : red;
+        } else if constexpr (GP == kTC || GP == kTD) {
+          red = keep ? fmaf(p, wsv[r], red) : red;
+        } else {
+          float m = gv[r];
+#pragma unroll
+          for (int k = 0; k < NM; ++k) {
+            if constexpr (GP == kTQ) m -= own_x[k] * wx[k][r] + own_y[k] * wy[k][r];
+            else m -= wx[k][r] * own_x[k] + wy[k][r] * own_y[k];
+          }
+          z[tt][r] = keep ? p * m : 0.f;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
+    }
+    if constexpr (TR::csrc >= 0) contract(acc, (TR::csrc == 0) ? sA : sB, z, g, n);
+    __builtin_amdgcn_wave_barrier();
+    na.store(sA, w0 + 32, Lr, lane);
+    if (TR::nstage == 2) nb.store(sB, w0 + 32, Lr, lane);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- combine the waves' partials (fixed order) in wave 0 ----
+  if constexpr (TR::has_red) red = group_sum(red);
+  __syncthreads();
+  float* rbuf = reinterpret_cast<float*>(smem);
+  constexpr int NA = (TR::csrc >= 0) ? 16 : 0;
+  if (wave != 0) {
+    float* mine = rbuf + wave * kRedFloats;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if constexpr (NA > 0) mine[(4 * b + r) * 64 + lane] = acc[b][r];
+    if constexpr (TR::has_red) mine[NA * 64 + lane] = red;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll 1
+  for (int w = 1; w < kWideWaves; ++w) {
+    const float* theirs = rbuf + w * kRedFloats;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if constexpr (NA > 0) acc[b][r] += theirs[(4 * b + r) * 64 + lane];
+    if constexpr (TR::has_red) red += theirs[NA * 64 + lane];
+  }
+  if (o >= Lr) return;
+  T* out_row = static_cast<T*>(a.out0) + tb + (int64_t)o * kD;
+  if constexpr (GP == kTA) {
+    if (g == 0) vec(tv.f(a.R))[o] = red;                    // dv^(R) (EV_R = 1)
+    store_row(out_row, acc, 1.f, g);                        // dV
+  } else if constexpr (GP == kTB) {
+    if (g == 0) vec(tv.c(a.R))[o] = red;                    // du^(R) (EU_R = 1)
+  } else if constexpr (GP == kTC) {
+    const float e = vec(tv.ev(lev))[o];
+    if (g == 0) vec(tv.f(lev))[o] = -e * e * red;           // dv^(a) = -EV_a red, F_a = dv^(a) EV_a
+  } else if constexpr (GP == kTD) {
+    const float e = vec(tv.eu(lev))[o];
+    if (g == 0) vec(tv.c(lev))[o] = -e * e * red;           // du^(a) = -EU_a red, C_a = du^(a) EU_a
+  } else {
+    store_row(out_row, acc, a.s, g);                        // dQ or dK
+  }
+}
+
+// =============================================================================================
 // launchers
 // =============================================================================================
 int wide_step_tiles(int Lr, int h) {
@@ -687,6 +924,45 @@ static void wide_pass_t(int pass, const WideArgs& a, hipStream_t st) {
     case kWD: wide_pass_kernel<T, kWD, D4><<<grid, block, 0, st>>>(a); break;
     default: wide_pass_kernel<T, kWE, D4><<<grid, block, 0, st>>>(a); break;
   }
+}
+
+hipError_t launch_tail_prep(const float* duals, float* ws, int R, const Geometry& g, hipStream_t st) {
+  const int64_t vs = g.bh * (int64_t)g.Lpad;
+  tail_prep_kernel<<<dim3((unsigned)((g.Lpad + 255) / 256), (unsigned)g.bh), dim3(256), 0, st>>>(
+      duals, ws, R, g.Lr, g.Lpad, vs);
+  return hipGetLastError();
+}
+
+template <typename T, int GP>
+static void tail_pass_r(const WideArgs& a, hipStream_t st) {
+  const dim3 grid = wide_grid(a), block(kWideThreads);
+  switch (a.R) {
+    case 1: tail_pass_kernel<T, GP, 1><<<grid, block, 0, st>>>(a); break;
+    case 2: tail_pass_kernel<T, GP, 2><<<grid, block, 0, st>>>(a); break;
+    case 3: tail_pass_kernel<T, GP, 3><<<grid, block, 0, st>>>(a); break;
+    default: tail_pass_kernel<T, GP, 4><<<grid, block, 0, st>>>(a); break;
+  }
+}
+
+template <typename T>
+static void tail_pass_t(int pass, const WideArgs& a, hipStream_t st) {
+  const dim3 grid = wide_grid(a), block(kWideThreads);
+  switch (pass) {
+    case kTA: tail_pass_kernel<T, kTA, 0><<<grid, block, 0, st>>>(a); break;
+    case kTB: tail_pass_kernel<T, kTB, 0><<<grid, block, 0, st>>>(a); break;
+    case kTC: tail_pass_kernel<T, kTC, 0><<<grid, block, 0, st>>>(a); break;
+    case kTD: tail_pass_kernel<T, kTD, 0><<<grid, block, 0, st>>>(a); break;
+    case kTQ: tail_pass_r<T, kTQ>(a, st); break;
+    default: tail_pass_r<T, kTE>(a, st); break;
+  }
+}
+
+hipError_t launch_tail_pass(int elt, int pass, const WideArgs& a, hipStream_t st) {
+  if (pass < kTA || pass > kTE || a.R < 1 || a.R > kTailMaxR) return hipErrorInvalidValue;
+  if ((pass == kTC || pass == kTD) && (a.level < 1 || a.level >= a.R)) return hipErrorInvalidValue;
+  if (elt == 1) tail_pass_t<bf16>(pass, a, st);
+  else tail_pass_t<float>(pass, a, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_wide_pass(int elt, int pass, bool d4, const WideArgs& a, hipStream_t st) {

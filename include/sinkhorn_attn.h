@@ -16,8 +16,8 @@
  *                                     v_j = -log sum_i exp(S_ij + u_i);   v^(0) := v (stopped).
  *   Tail: for a = 1..R:  u^(a) from v^(a-1), then v^(a) from u^(a) (same two updates).
  *   Output: O = P V with P_ij = exp(S_ij + u^(R)_i + v^(R)_j) on Omega.
- *   VJP (R = 2): exact gradient of <O, dO> with respect to Q, K, V through the tail, with
- *   v^(0) held fixed (stop-gradient on the base).
+ *   VJP (1 <= R <= 4): exact gradient of <O, dO> with respect to Q, K, V through the tail,
+ *   with v^(0) held fixed (stop-gradient on the base).
  *
  * Tensor layout: Q, K, V, O, dO, dQ, dK, dV are [bh][Lr][d] row-major (d contiguous), element
  * type given by ska_problem.dtype.  Duals are fp32 [bh][2R+1][Lr] in natural-log units, in the
@@ -48,19 +48,19 @@ extern "C" {
 
 typedef enum { SKA_F32 = 0, SKA_BF16 = 1 } ska_dtype;
 
-/* Adjoint schedule for the R = 2 VJP.
- * SKA_ONE_REFERENCE: only the reference plan P^(2,2) is exponentiated; the other staircase
- *   plans enter through the orbit factors exp(u^(a)-u^(2)), exp(v^(b)-v^(2)) (abstract;
- *   technical summaries §2.2, orbit equation).
- * SKA_DIRECT_FOUR: every staircase plan P^(2,2), P^(2,1), P^(1,1), P^(1,0) is exponentiated
- *   on its own (the direct four-plan adjoint, atlas.scime.ai Key results); kept for
- *   comparison. */
+/* Adjoint schedule of the VJP.
+ * SKA_ONE_REFERENCE: only the reference plan P^(R,R) is exponentiated; the other staircase
+ *   plans enter through the orbit factors exp(u^(a)-u^(R)), exp(v^(b)-v^(R)) (abstract;
+ *   technical summaries §2.2, orbit equation).  Any R from 1 to 4.
+ * SKA_DIRECT_FOUR: R = 2 only; every staircase plan P^(2,2), P^(2,1), P^(1,1), P^(1,0) is
+ *   exponentiated on its own (the direct four-plan adjoint, atlas.scime.ai Key results); kept
+ *   for comparison.  Other R return SKA_ERR_UNSUPPORTED. */
 typedef enum { SKA_ONE_REFERENCE = 0, SKA_DIRECT_FOUR = 1 } ska_schedule;
 
 typedef enum {
   SKA_OK = 0,
   SKA_ERR_INVALID = -1,     /* malformed argument (null/misaligned pointer, W odd, eps <= 0, ...) */
-  SKA_ERR_UNSUPPORTED = -2, /* well-formed but not built: d != 64, VJP with R != 2, huge L      */
+  SKA_ERR_UNSUPPORTED = -2, /* well-formed but not built: d != 64, VJP with R > 4, huge L       */
   SKA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than ska_workspace_bytes()          */
   SKA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed                        */
 } ska_status;
@@ -78,7 +78,7 @@ typedef struct {
   int64_t d;       /* head dimension; 64 is built                                               */
   int64_t W;       /* band width, even, >= 0; support |i - j| <= W / 2                          */
   int32_t T;       /* stopped base steps, >= 0                                                  */
-  int32_t R;       /* tail steps: forward >= 1, VJP == 2                                        */
+  int32_t R;       /* tail steps: forward >= 1, VJP 1..4 (direct-four schedule: 2)              */
   float epsilon;   /* entropic temperature, finite and > 0                                      */
   int32_t dtype;   /* ska_dtype of Q, K, V, O, dO, dQ, dK, dV (duals are always fp32)           */
 } ska_problem;
@@ -96,8 +96,11 @@ ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K,
                              void* O, float* duals, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
-/* Exact R = 2 tail VJP: given the forward's duals and an arbitrary cotangent dO, writes dQ, dK,
- * dV [bh][L][d].  Scores are recomputed per band tile; extra memory is O(L) vectors.
+/* Exact tail VJP (1 <= R <= 4): given the forward's duals and an arbitrary cotangent dO, writes
+ * dQ, dK, dV [bh][L][d].  Scores are recomputed per band tile; extra memory is O(L) vectors
+ * (3 + 4 R of them for R != 2).  R = 2 runs the two-level passes (both schedules); other R run
+ * 2 R + 2 passes of the one-reference adjoint, the modifier field then holding 2 R terms
+ * (technical summaries §2.1: R differentiable tail steps).
  * (abstract: one-reference-tile schedule, score cotangent = reference tile times a modifier
  * field of vector cotangents and dual differences; atlas.scime.ai Key results: complete
  * arbitrary-cotangent Q/K/V VJP.) */

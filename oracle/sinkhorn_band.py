@@ -521,8 +521,9 @@ def dustbin_block_forward(Qa, Ka, Va, prob: BandProblem, block: int = 64):
 
 def dustbin_block_vjp(Qa, Ka, Va, dOa, duals, prob: BandProblem, block: int = 64,
                       schedule: str = "one_reference"):
-    """dustbin_block VJP: the same R = 2 adjoint on the augmented support; returns
-    gradients for all L + 1 tokens including the dustbin.
+    """dustbin_block VJP: the same tail adjoint on the augmented support; returns
+    gradients for all L + 1 tokens including the dustbin.  R = 2: the one-reference or
+    four-plan adjoint; other R: the general-depth orbit form ("one_reference") or step form.
     [technical summaries §2.3: the exact R = 2 adjoint and the one-reference schedule
     carry over to the augmented state space unchanged]"""
     n = np.asarray(Qa).shape[0]
@@ -530,7 +531,10 @@ def dustbin_block_vjp(Qa, Ka, Va, dOa, duals, prob: BandProblem, block: int = 64
     Lp = active.shape[0]
     dfull = np.zeros((duals.shape[0], Lp))
     dfull[:, :n] = duals
-    fn = vjp_one_reference if schedule == "one_reference" else vjp_direct_four
+    if prob.R == 2:
+        fn = vjp_one_reference if schedule == "one_reference" else vjp_direct_four
+    else:
+        fn = vjp_tail_one_reference if schedule == "one_reference" else vjp_tail
     dQ, dK, dV = fn(_augment(np.asarray(Qa, np.float64), block),
                     _augment(np.asarray(Ka, np.float64), block),
                     _augment(np.asarray(Va, np.float64), block),
@@ -547,11 +551,12 @@ def dependency_radius(prob: BandProblem) -> int:
 
     On the band each half-step couples only tokens within h of each other, so a
     window cut changes values at most h further inward per half-step.  The forward
-    takes 2(T+R) half-steps plus the output contraction; the R = 2 VJP adds the
-    chain dv2 -> du2 -> dv1 -> du1 -> dS -> dQ/dK (five more hops).  Rows farther
-    than (2(T+R) + 6) h from an artificial cut are therefore computed exactly;
-    the radius below adds two hops and 16 tokens of margin."""
-    return (2 * (prob.T + prob.R) + 8) * prob.h + 16
+    takes 2(T+R) half-steps plus the output contraction; the VJP adds the chain
+    dv^(R) -> du^(R) -> ... -> dv^(1) -> du^(1) -> dS -> dQ/dK (2 R + 1 more hops;
+    five at R = 2).  Rows farther than (2(T+R) + 2R + 2) h from an artificial cut
+    are therefore computed exactly; the radius below adds two hops and 16 tokens
+    of margin (at R = 2 it is (2(T+R) + 8) h + 16)."""
+    return (2 * (prob.T + prob.R) + 2 * prob.R + 4) * prob.h + 16
 
 
 def sampled_rows(Q, K, V, dO, prob: BandProblem, rows, schedule: str = "one_reference"):
@@ -562,7 +567,10 @@ def sampled_rows(Q, K, V, dO, prob: BandProblem, rows, schedule: str = "one_refe
     H = dependency_radius(prob)
     rows = np.asarray(rows, dtype=np.int64)
     out = {k: np.zeros((rows.shape[0], Q.shape[1])) for k in ("O", "dQ", "dK", "dV")}
-    fn = vjp_one_reference if schedule == "one_reference" else vjp_direct_four
+    if prob.R == 2:
+        fn = vjp_one_reference if schedule == "one_reference" else vjp_direct_four
+    else:
+        fn = vjp_tail_one_reference if schedule == "one_reference" else vjp_tail
     for n, r in enumerate(rows):
         a, b = max(0, int(r) - H), min(L, int(r) + H + 1)
         sl = slice(a, b)

@@ -30,7 +30,7 @@ def gpu_run(Q, K, V, dO, W, T, R=2, eps=1.0, schedule="one_reference", dustbin=F
     Qd, Kd, Vd, dOd = (x.to(dev) for x in (Q, K, V, dO))
     O, duals = B.forward(Qd, Kd, Vd, W, T, R, eps, dustbin=dustbin)
     out = dict(O=O, duals=duals)
-    if R == 2:
+    if R <= 4:
         dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=schedule, dustbin=dustbin)
         out.update(dQ=dQ, dK=dK, dV=dV)
     torch.cuda.synchronize()
@@ -43,7 +43,7 @@ def oracle_head(Q, K, V, dO, W, T, R=2, eps=1.0, schedule="one_reference", dustb
     if dustbin:
         O, duals = oracle.dustbin_block_forward(Q, K, V, p)
         out = dict(O=O, duals=duals)
-        if R == 2:
+        if R <= 4:
             dQ, dK, dV = oracle.dustbin_block_vjp(Q, K, V, dO, duals, p, schedule=schedule)
             out.update(dQ=dQ, dK=dK, dV=dV)
         return out
@@ -51,6 +51,11 @@ def oracle_head(Q, K, V, dO, W, T, R=2, eps=1.0, schedule="one_reference", dustb
     out = dict(O=O, duals=duals)
     if R == 2:
         fn = oracle.vjp_one_reference if schedule == "one_reference" else oracle.vjp_direct_four
+    elif R <= 4:
+        fn = oracle.vjp_tail_one_reference     # general tail depth (one-reference schedule)
+    else:
+        fn = None
+    if fn is not None:
         dQ, dK, dV = fn(Q, K, V, dO, duals, p)
         out.update(dQ=dQ, dK=dK, dV=dV)
     return out

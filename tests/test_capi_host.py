@@ -155,8 +155,8 @@ def test_workspace_sizes():
     (dict(W=-2), B.SKA_OP_FWD, -1),
     (dict(T=-1), B.SKA_OP_FWD, -1),
     (dict(R=0), B.SKA_OP_FWD, -1),
-    (dict(R=3), B.SKA_OP_VJP, -2),
-    (dict(R=1), B.SKA_OP_DUSTBIN_BLOCK_VJP, -2),
+    (dict(R=5), B.SKA_OP_VJP, -2),
+    (dict(R=9), B.SKA_OP_DUSTBIN_BLOCK_VJP, -2),
     (dict(epsilon=0.0), B.SKA_OP_FWD, -1),
     (dict(epsilon=float("nan")), B.SKA_OP_VJP, -1),
     (dict(dtype=7), B.SKA_OP_FWD, -1),
@@ -187,8 +187,24 @@ def test_entry_points_reject_bad_arguments_before_launch():
     _, needv = _ws_bytes(prob, B.SKA_OP_VJP)
     args = [V(FAKE)] * 8
     assert g(ctypes.byref(prob), *args, 5, V(FAKE), needv, None) == -1      # unknown schedule
+    prob3 = _prob(R=3)
+    _, need3 = _ws_bytes(prob3, B.SKA_OP_VJP)
+    assert g(ctypes.byref(prob3), *args, 1, V(FAKE), need3, None) == -2     # direct-four needs R = 2
+    assert "R == 2" in B.ska_last_error()
     assert g(ctypes.byref(prob), *args, 0, V(FAKE), needv - 1, None) == -3
     assert g(ctypes.byref(prob), *(args[:5] + [None] + args[6:]), 0, V(FAKE), needv, None) == -1
+
+
+@pytest.mark.parametrize("R", [1, 3, 4])
+def test_general_tail_depth_workspace(R):
+    """VJP of a tail depth other than 2: 3 + 4 R vectors [bh][Lpad] (u^(R), v^(R), R row and
+    R + 1 column orbit factors, R + R scaled cotangents), whatever the band and dtype; the
+    dustbin entry point sizes its L + 1 rows the same way."""
+    for kw in (dict(L=1000, bh=3, W=16), dict(L=1000, bh=3, W=600, dtype=B.SKA_BF16)):
+        st, n = _ws_bytes(_prob(R=R, **kw), B.SKA_OP_VJP)
+        assert st == 0 and n == (3 + 4 * R) * 3 * 1024 * 4
+    st, n = _ws_bytes(_prob(R=R, L=4096, bh=4), B.SKA_OP_DUSTBIN_BLOCK_VJP)
+    assert st == 0 and n == (3 + 4 * R) * 4 * 4160 * 4
 
 
 def test_empty_problems_enqueue_nothing():
