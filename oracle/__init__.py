@@ -32,6 +32,9 @@ from .sinkhorn_band import (  # noqa: F401
     vjp_direct_four,
     vjp_tail,
     vjp_tail_one_reference,
+    vjp_full,
+    tail_remainder,
+    select_tail_depth,
     staircase_plan,
     dustbin_block_forward,
     dustbin_block_vjp,

@@ -479,6 +479,53 @@ def vjp_tail_one_reference(Q, K, V, dO, duals, prob: BandProblem, active=None,
 
 
 # --------------------------------------------------------------------------------------
+# full backpropagation and the a posteriori bias certificate
+# --------------------------------------------------------------------------------------
+
+def vjp_full(Q, K, V, dO, prob: BandProblem, active=None):
+    """Exact gradient of <O, dO> through all T + R steps from u = v = 0, with no stop-gradient
+    on the base: the same iteration read as a tail of depth T + R whose stopped base is the
+    constant initial v = 0, differentiated step by step (vjp_tail).
+    [technical summaries §2.4 and Key results: the stop-gradient surrogate compared with full
+    backpropagation through time]"""
+    pf = BandProblem(W=prob.W, T=0, R=prob.T + prob.R, eps=prob.eps)
+    _, duals = forward(Q, K, V, pf, active)
+    return vjp_tail(Q, K, V, dO, duals, pf, active)
+
+
+def tail_remainder(Q, K, V, dO, prob: BandProblem, active=None) -> dict:
+    """A posteriori bias certificate: the gradient remainder the stopped base drops at tail
+    depth R, r = grad_full - grad_R, as squared norms summed over the tensor, and
+    eta_R = ||(r_dQ, r_dK)|| / ||(dQ_full, dK_full)||.  dV has no remainder (V enters only the
+    output), which the result reports as rem_dV2.
+    [technical summaries §2.4: an operational measurement of the gradient remainder eta_R,
+    certified against a user tolerance tau, selecting the tail depth R]"""
+    _, duals = forward(Q, K, V, prob, active)
+    fn = vjp_one_reference if prob.R == 2 else vjp_tail_one_reference
+    dQr, dKr, dVr = fn(Q, K, V, dO, duals, prob, active)
+    dQf, dKf, dVf = vjp_full(Q, K, V, dO, prob, active)
+    out = {"rem_dQ2": float(np.sum((dQf - dQr) ** 2)), "full_dQ2": float(np.sum(dQf ** 2)),
+           "rem_dK2": float(np.sum((dKf - dKr) ** 2)), "full_dK2": float(np.sum(dKf ** 2)),
+           "rem_dV2": float(np.sum((dVf - dVr) ** 2))}
+    den = out["full_dQ2"] + out["full_dK2"]
+    out["eta"] = float(np.sqrt((out["rem_dQ2"] + out["rem_dK2"]) / den)) if den > 0 else 0.0
+    return out
+
+
+def select_tail_depth(Q, K, V, dO, W: int, T: int, eps: float = 1.0, tau: float = 1e-5,
+                      R_max: int = 4):
+    """Smallest R in 1..R_max with eta_R <= tau (None if none), and the eta_R computed.
+    [technical summaries §2.4: dynamic choice of the tail depth; Key results: R = 2 is the
+    smallest depth meeting tau = 1e-5 on the pages' problems]"""
+    etas = {}
+    for R in range(1, R_max + 1):
+        etas[R] = tail_remainder(Q, K, V, dO, BandProblem(W=W, T=T, R=R, eps=eps))["eta"]
+        if etas[R] <= tau:
+            return R, etas
+    return None, etas
+
+
+# --------------------------------------------------------------------------------------
 # dustbin_block: same surrogate on an augmented support
 # --------------------------------------------------------------------------------------
 

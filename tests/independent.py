@@ -5,6 +5,8 @@
 * ``dense_autograd``: the stopped-base tail surrogate written with dense [L, L]
   torch float64 tensors and differentiated by torch autograd on the CPU
   ("exact autodiff through the surrogate", the pages' validation baseline).
+* ``dense_autograd_full``: the same iteration with gradients flowing through the base steps
+  as well (full backpropagation through time).
 """
 
 from __future__ import annotations
@@ -67,3 +69,26 @@ def dense_autograd(Q, K, V, dO, W, T, R, eps):
     (O * dOt).sum().backward()
     return (O.detach().numpy(), Qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy(),
             np.stack([x.detach().numpy() for x in duals]))
+
+
+def dense_autograd_full(Q, K, V, dO, W, T, R, eps):
+    """Dense-matrix iteration with no stop-gradient: T base steps and R tail steps, all
+    differentiated.  Returns (O, dQ, dK, dV)."""
+    Qt = torch.tensor(np.asarray(Q, np.float64), requires_grad=True)
+    Kt = torch.tensor(np.asarray(K, np.float64), requires_grad=True)
+    Vt = torch.tensor(np.asarray(V, np.float64), requires_grad=True)
+    dOt = torch.tensor(np.asarray(dO, np.float64))
+    L, d = Qt.shape
+    idx = torch.arange(L)
+    mask = (idx[:, None] - idx[None, :]).abs() <= W // 2
+    S = (Qt @ Kt.T) / (math.sqrt(d) * eps)
+    S = S.masked_fill(~mask, float("-inf"))
+    u = torch.zeros(L, dtype=torch.float64)
+    v = torch.zeros(L, dtype=torch.float64)
+    for _ in range(T + R):
+        u = -torch.logsumexp(S + v[None, :], dim=1)
+        v = -torch.logsumexp(S + u[:, None], dim=0)
+    P = torch.exp(S + u[:, None] + v[None, :])
+    O = P @ Vt
+    (O * dOt).sum().backward()
+    return O.detach().numpy(), Qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy()

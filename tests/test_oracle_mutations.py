@@ -50,6 +50,9 @@ TAIL_MUTATIONS = {
         "Pab = staircase_plan(S, us[a], vs[a - 1], h)", "Pab = staircase_plan(S, us[a], vs[a], h)"),
     "tail_step_form_skips_column_term": (
         "        dS = dS - Paa * _row_vec(dv[a], h)\n", ""),
+    "full_backprop_one_step_short": (
+        "pf = BandProblem(W=prob.W, T=0, R=prob.T + prob.R, eps=prob.eps)",
+        "pf = BandProblem(W=prob.W, T=0, R=prob.T + prob.R - 1, eps=prob.eps)"),
 }
 
 
