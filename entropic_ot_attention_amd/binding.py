@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "lib
 SKA_F32, SKA_BF16 = 0, 1
 SKA_ONE_REFERENCE, SKA_DIRECT_FOUR = 0, 1
 SKA_OP_FWD, SKA_OP_VJP, SKA_OP_DUSTBIN_BLOCK_FWD, SKA_OP_DUSTBIN_BLOCK_VJP = 0, 1, 2, 3
+SKA_OP_TAIL_REMAINDER = 4
 SKA_OK = 0
 TIMED_STEP, TIMED_OUT, TIMED_VJP = 0, 1, 2
 
@@ -27,7 +28,7 @@ SCHEDULES = {"one_reference": SKA_ONE_REFERENCE, "direct_four": SKA_DIRECT_FOUR}
 EXPORTS = (
     "ska_workspace_bytes", "sinkhorn_attn_fwd", "sinkhorn_attn_vjp",
     "sinkhorn_attn_dustbin_block_fwd", "sinkhorn_attn_dustbin_block_vjp",
-    "ska_status_string", "ska_last_error", "ska_timing_enable", "ska_timing_read",
+    "sinkhorn_attn_tail_remainder", "ska_status_string", "ska_last_error", "ska_timing_enable", "ska_timing_read",
 )
 
 
@@ -54,9 +55,10 @@ def _load():
     lib.sinkhorn_attn_dustbin_block_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sinkhorn_attn_vjp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, st, vp, sz, vp]
     lib.sinkhorn_attn_dustbin_block_vjp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, st, vp, sz, vp]
+    lib.sinkhorn_attn_tail_remainder.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     for name in ("ska_workspace_bytes", "sinkhorn_attn_fwd", "sinkhorn_attn_dustbin_block_fwd",
-                 "sinkhorn_attn_vjp", "sinkhorn_attn_dustbin_block_vjp", "ska_timing_enable",
-                 "ska_timing_read"):
+                 "sinkhorn_attn_vjp", "sinkhorn_attn_dustbin_block_vjp",
+                 "sinkhorn_attn_tail_remainder", "ska_timing_enable", "ska_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ska_status_string.argtypes = [ctypes.c_int]
     lib.ska_status_string.restype = ctypes.c_char_p
@@ -153,6 +155,14 @@ def sinkhorn_attn_dustbin_block_vjp(problem, Q, K, V, duals, dO, dQ, dK, dV, sch
            "sinkhorn_attn_dustbin_block_vjp")
 
 
+def sinkhorn_attn_tail_remainder(problem, Q, K, V, dO, sums, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check(lib.sinkhorn_attn_tail_remainder(ctypes.byref(problem), _ptr(Q, "Q"), _ptr(K, "K"),
+                                            _ptr(V, "V"), _ptr(dO, "dO"), _ptr(sums, "sums"),
+                                            ws, nb, _stream(stream)),
+           "sinkhorn_attn_tail_remainder")
+
+
 def ska_timing_enable(on: bool):
     _check(lib.ska_timing_enable(1 if on else 0), "ska_timing_enable")
 
@@ -217,3 +227,34 @@ def vjp(Q, K, V, duals, dO, W: int, T: int, R: int = 2, epsilon: float = 1.0,
     fn = sinkhorn_attn_dustbin_block_vjp if dustbin else sinkhorn_attn_vjp
     fn(prob, Q, K, V, duals, dO, dQ, dK, dV, SCHEDULES[schedule], workspace, stream)
     return dQ, dK, dV
+
+
+def tail_remainder(Q, K, V, dO, W: int, T: int, R: int = 2, epsilon: float = 1.0,
+                   workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """A posteriori bias certificate: squared norms of the gradient remainder dropped by the
+    stopped base at tail depth R and of the full (all T + R steps) gradient, summed over all
+    problems, as computed by sinkhorn_attn_tail_remainder; eta_R is their relative l2 ratio
+    over dQ and dK."""
+    bh, rows, d, L = _shape_check(Q, K, V, False)
+    if dO.shape != Q.shape or dO.dtype != Q.dtype:
+        raise ValueError("dO must match Q in shape and dtype")
+    prob = make_problem(bh, L, d, W, T, R, epsilon, Q.dtype)
+    if workspace is None:
+        workspace = workspace_for(prob, SKA_OP_TAIL_REMAINDER, Q.device)
+    sums = torch.zeros(4, dtype=torch.float64, device=Q.device)
+    sinkhorn_attn_tail_remainder(prob, Q, K, V, dO, sums, workspace, stream)
+    rq, fq, rk, fk = (float(x) for x in sums.cpu())
+    return {"rem_dQ2": rq, "full_dQ2": fq, "rem_dK2": rk, "full_dK2": fk,
+            "eta": ((rq + rk) / (fq + fk)) ** 0.5 if fq + fk > 0 else 0.0}
+
+
+def select_tail_depth(Q, K, V, dO, W: int, T: int, epsilon: float = 1.0, tau: float = 1e-5,
+                      R_max: int = 4) -> tuple:
+    """The smallest tail depth R in 1..R_max whose certified remainder eta_R is at most tau
+    (None if none is), and every eta_R computed on the way."""
+    etas = {}
+    for R in range(1, R_max + 1):
+        etas[R] = tail_remainder(Q, K, V, dO, W, T, R, epsilon)["eta"]
+        if etas[R] <= tau:
+            return R, etas
+    return None, etas

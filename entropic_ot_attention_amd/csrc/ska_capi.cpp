@@ -60,7 +60,7 @@ void timing_end(int kind, std::pair<hipEvent_t, hipEvent_t> ev, hipStream_t st) 
 struct Plan {
   ska::Geometry g;
   int elt;
-  int R;
+  int R, T;
   bool empty;
 };
 
@@ -77,9 +77,11 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
   if (p->dtype != SKA_F32 && p->dtype != SKA_BF16) return fail(SKA_ERR_INVALID, "unknown dtype");
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   const bool dustbin = (op == SKA_OP_DUSTBIN_BLOCK_FWD || op == SKA_OP_DUSTBIN_BLOCK_VJP);
-  if (op < SKA_OP_FWD || op > SKA_OP_DUSTBIN_BLOCK_VJP) return fail(SKA_ERR_INVALID, "unknown op");
+  if (op < SKA_OP_FWD || op > SKA_OP_TAIL_REMAINDER) return fail(SKA_ERR_INVALID, "unknown op");
   if (p->R < 1) return fail(SKA_ERR_INVALID, "R must be >= 1");
-  if (vjp && p->R > ska::kTailMaxR) return fail(SKA_ERR_UNSUPPORTED, "the VJP is built for R <= 4");
+  if (vjp && p->R > ska::kTailMaxR) return fail(SKA_ERR_UNSUPPORTED, "the VJP is built for R <= 256");
+  if (op == SKA_OP_TAIL_REMAINDER && (int64_t)p->T + p->R > ska::kTailMaxR)
+    return fail(SKA_ERR_UNSUPPORTED, "the tail remainder runs the adjoint at depth T + R <= 256");
   if (p->d != ska::kD) return fail(SKA_ERR_UNSUPPORTED, "head dimension d must be 64");
   const int64_t Lr = p->L + (dustbin ? 1 : 0);
   if (Lr > (int64_t(1) << 30)) return fail(SKA_ERR_UNSUPPORTED, "L above 2^30 tokens");
@@ -89,6 +91,7 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
   if (h > Lr) h = Lr;                 // wider than the sequence changes nothing
   out->elt = p->dtype;
   out->R = p->R;
+  out->T = p->T;
   out->empty = (p->bh == 0 || Lr == 0);
   out->g.bh = p->bh;
   out->g.Lr = (int)Lr;
@@ -107,8 +110,14 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
 // tile, about bh L (W + 32) / 16 floats.  Split path (wider still): two dual buffers.  VJP:
 // kVjpVecs vectors [bh][Lpad], plus the streaming passes' dv1 column partials (about one float
 // per token).
+struct RemLayout {
+  size_t o, dq_r, dk_r, dv_r, dq_f, dk_f, dv_f, duals_r, duals_f, part, inner, inner_bytes, total;
+};
+RemLayout rem_layout(const Plan& pl);
+
 size_t workspace_for(const Plan& pl, ska_op op) {
   if (pl.empty) return 0;
+  if (op == SKA_OP_TAIL_REMAINDER) return rem_layout(pl).total;
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   const int64_t vs = pl.g.bh * (int64_t)pl.g.Lpad;
   if (vjp && pl.R != 2) return (size_t)(ska::tail_vecs(pl.R) * vs) * sizeof(float);
@@ -137,6 +146,36 @@ size_t workspace_for(const Plan& pl, ska_op op) {
   ska::fused_segments(pl.g.bh, pl.g.Lr, nt, &seg_len, &nseg);
   const int64_t ps = pl.g.bh * (int64_t)nseg * ska::fused_pstride(nt, seg_len);
   return (size_t)(4 * vs + 2 * ps) * sizeof(float);
+}
+
+// Tail-remainder workspace: O, the two gradient sets (tail at depth R, full at depth T + R),
+// both dual sets, the reduction's block sums, then the larger inner workspace of the forward and
+// VJP calls; every piece 256-byte aligned.
+RemLayout rem_layout(const Plan& pl) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t elems = (size_t)pl.g.bh * pl.g.Lr * ska::kD;
+  const size_t tb = up(elems * (pl.elt == 1 ? 2 : 4));
+  RemLayout L{};
+  size_t at = 0;
+  L.o = at; at += tb;
+  L.dq_r = at; at += tb;
+  L.dk_r = at; at += tb;
+  L.dv_r = at; at += tb;
+  L.dq_f = at; at += tb;
+  L.dk_f = at; at += tb;
+  L.dv_f = at; at += tb;
+  L.duals_r = at; at += up((size_t)(2 * pl.R + 1) * pl.g.bh * pl.g.Lr * sizeof(float));
+  L.duals_f = at; at += up((size_t)(2 * (pl.T + pl.R) + 1) * pl.g.bh * pl.g.Lr * sizeof(float));
+  L.part = at; at += up(2 * ska::kSqPartials * sizeof(double));
+  Plan a = pl, b = pl;
+  b.R = pl.T + pl.R;
+  size_t inner = workspace_for(a, SKA_OP_FWD);
+  for (size_t x : {workspace_for(b, SKA_OP_FWD), workspace_for(a, SKA_OP_VJP), workspace_for(b, SKA_OP_VJP)})
+    inner = x > inner ? x : inner;
+  L.inner = at;
+  L.inner_bytes = up(inner);
+  L.total = at + L.inner_bytes;
+  return L;
 }
 
 ska_status check_ptr(const void* ptr, const char* name) {
@@ -479,6 +518,46 @@ ska_status sinkhorn_attn_dustbin_block_vjp(const ska_problem* p, const void* Q, 
   g_err.clear();
   return run_vjp(p, SKA_OP_DUSTBIN_BLOCK_VJP, Q, K, V, duals, dO, dQ, dK, dV, schedule,
                  workspace, workspace_bytes, stream);
+}
+
+ska_status sinkhorn_attn_tail_remainder(const ska_problem* p, const void* Q, const void* K,
+                                        const void* V, const void* dO, double* sums,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  g_err.clear();
+  Plan pl;
+  SKA_TRY(check_problem(p, SKA_OP_TAIL_REMAINDER, &pl));
+  if (pl.empty) return SKA_OK;
+  SKA_TRY(check_ptr(Q, "Q"));
+  SKA_TRY(check_ptr(K, "K"));
+  SKA_TRY(check_ptr(V, "V"));
+  SKA_TRY(check_ptr(dO, "dO"));
+  if (!sums || (reinterpret_cast<uintptr_t>(sums) & 7u) != 0)
+    return fail(SKA_ERR_INVALID, "sums must be an 8-byte aligned device pointer");
+  const RemLayout L = rem_layout(pl);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(SKA_ERR_WORKSPACE, "workspace smaller than ska_workspace_bytes()");
+  if (!aligned16(workspace)) return fail(SKA_ERR_INVALID, "workspace is not 16-byte aligned");
+  char* w = static_cast<char*>(workspace);
+  void* inner = w + L.inner;
+  // the stopped-base surrogate at depth R, then full backpropagation: depth T + R from u = v = 0
+  ska_problem pr = *p, pf = *p;
+  pf.T = 0;
+  pf.R = p->T + p->R;
+  float* dr = reinterpret_cast<float*>(w + L.duals_r);
+  float* df = reinterpret_cast<float*>(w + L.duals_f);
+  SKA_TRY(run_fwd(&pr, SKA_OP_FWD, Q, K, V, w + L.o, dr, inner, L.inner_bytes, stream));
+  SKA_TRY(run_vjp(&pr, SKA_OP_VJP, Q, K, V, dr, dO, w + L.dq_r, w + L.dk_r, w + L.dv_r,
+                  SKA_ONE_REFERENCE, inner, L.inner_bytes, stream));
+  SKA_TRY(run_fwd(&pf, SKA_OP_FWD, Q, K, V, w + L.o, df, inner, L.inner_bytes, stream));
+  SKA_TRY(run_vjp(&pf, SKA_OP_VJP, Q, K, V, df, dO, w + L.dq_f, w + L.dk_f, w + L.dv_f,
+                  SKA_ONE_REFERENCE, inner, L.inner_bytes, stream));
+  const int64_t n = pl.g.bh * (int64_t)pl.g.Lr * ska::kD;
+  double* part = reinterpret_cast<double*>(w + L.part);
+  hipError_t e = ska::launch_sq_diff(pl.elt, w + L.dq_f, w + L.dq_r, n, part, sums, stream);
+  if (e == hipSuccess) e = ska::launch_sq_diff(pl.elt, w + L.dk_f, w + L.dk_r, n, part, sums + 2, stream);
+  if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+  return SKA_OK;
 }
 
 const char* ska_status_string(ska_status s) {

@@ -124,7 +124,9 @@ struct WideArgs {
 // units), the orbit factors EU_a = exp(u^(a) - u^(R)) (a = 1..R) and EV_b = exp(v^(b) - v^(R))
 // (b = 0..R), and the scaled cotangents F_a = dv^(a) EV_a and C_a = du^(a) EU_a (a = 1..R).
 inline int tail_vecs(int R) { return 3 + 4 * R; }
-constexpr int kTailMaxR = 4;
+// Deepest tail the general passes run (a full backpropagation through T + R steps from u = v = 0
+// is the general adjoint at depth T + R): the workspace holds 3 + 4 R vectors.
+constexpr int kTailMaxR = 256;
 
 // Register tiles per wave of the wide fused step for half-width h (its window of at most 8 KT
 // tiles stays in registers), or 0 when the window is wider than that.
@@ -155,6 +157,11 @@ hipError_t launch_wide_finish(int elt, const WideArgs& a, hipStream_t st);
 // pass: 0 output, 1..5 the VJP passes A..E
 hipError_t launch_wide_pass(int elt, int pass, bool d4, const WideArgs& a, hipStream_t st);
 hipError_t launch_vjp_prep(const float* duals, float* ws, const Geometry& g, hipStream_t st);
+// out2[0] = sum (a - b)^2, out2[1] = sum a^2 over n elements (double, fixed order); part holds
+// 2 x kSqPartials doubles of block sums
+constexpr int kSqPartials = 256;
+hipError_t launch_sq_diff(int elt, const void* a, const void* b, int64_t n, double* part,
+                          double* out2, hipStream_t st);
 // General tail depth (1 <= R <= kTailMaxR), one-reference-tile adjoint on the wide decomposition:
 // the vector preparation, then passes 0 (A: dv^(R), dV), 1 (B: du^(R)), 2 (C: dv^(a)),
 // 3 (D: du^(a)), 4 (dQ), 5 (dK).

@@ -125,6 +125,57 @@ __global__ void vjp_prep_kernel(const float* __restrict__ duals, float* __restri
 }
 
 // =============================================================================================
+// Squared-norm reductions of the tail-remainder certificate: sum (a - b)^2 and sum a^2 over n
+// elements, in double, in a fixed order (per-block tree, then one block over the block sums).
+// =============================================================================================
+constexpr int kSqBlocks = kSqPartials;
+
+template <typename T>
+__global__ __launch_bounds__(256) void sqdiff_partial_kernel(const T* __restrict__ a, const T* __restrict__ b,
+                                                             int64_t n, double* __restrict__ part) {
+  __shared__ double sd[256], sa[256];
+  double d2 = 0.0, a2 = 0.0;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const double x = (double)(float)a[i], y = (double)(float)b[i];
+    d2 += (x - y) * (x - y);
+    a2 += x * x;
+  }
+  sd[threadIdx.x] = d2;
+  sa[threadIdx.x] = a2;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) {
+      sd[threadIdx.x] += sd[threadIdx.x + off];
+      sa[threadIdx.x] += sa[threadIdx.x + off];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    part[2 * blockIdx.x] = sd[0];
+    part[2 * blockIdx.x + 1] = sa[0];
+  }
+}
+
+__global__ __launch_bounds__(256) void sum_pairs_kernel(const double* __restrict__ part, int nblk,
+                                                        double* __restrict__ out) {
+  __shared__ double sd[256], sa[256];
+  sd[threadIdx.x] = ((int)threadIdx.x < nblk) ? part[2 * threadIdx.x] : 0.0;
+  sa[threadIdx.x] = ((int)threadIdx.x < nblk) ? part[2 * threadIdx.x + 1] : 0.0;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) {
+      sd[threadIdx.x] += sd[threadIdx.x + off];
+      sa[threadIdx.x] += sa[threadIdx.x + off];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[0] = sd[0];
+    out[1] = sa[0];
+  }
+}
+
+// =============================================================================================
 // launchers
 // =============================================================================================
 static dim3 pass_grid(const Geometry& g) {
@@ -154,6 +205,16 @@ hipError_t launch_lse(int elt, const void* own, const void* win, const float* vi
   else
     lse_kernel<float><<<pass_grid(g), dim3(256), 0, st>>>(
         (const float*)own, (const float*)win, vin, vout, vsave, save_stride, g.Lr, g.Lpad, g.h, g.c2);
+  return hipGetLastError();
+}
+
+hipError_t launch_sq_diff(int elt, const void* a, const void* b, int64_t n, double* part,
+                          double* out2, hipStream_t st) {
+  if (elt == 1)
+    sqdiff_partial_kernel<bf16><<<dim3(kSqBlocks), dim3(256), 0, st>>>((const bf16*)a, (const bf16*)b, n, part);
+  else
+    sqdiff_partial_kernel<float><<<dim3(kSqBlocks), dim3(256), 0, st>>>((const float*)a, (const float*)b, n, part);
+  sum_pairs_kernel<<<dim3(1), dim3(256), 0, st>>>(part, kSqBlocks, out2);
   return hipGetLastError();
 }
 

@@ -688,8 +688,10 @@ template <int GP> struct TailTraits {
   static constexpr bool has_red = (GP <= kTD);
 };
 
-// RT: the tail depth for the dQ and dK passes (compile time: their 2 RT modifier terms stay in
-// registers); 0 for the level passes, which take R and the level at run time.
+// RT: the tail depth for the dQ and dK passes (1..4 at compile time: their 2 RT modifier terms
+// and owned factors stay in registers); RT = -1: any depth, the modifier accumulated level by
+// level with its factors read per tile; 0 for the level passes, which take R and the level at
+// run time.
 template <typename T, int GP, int RT>
 __global__ __launch_bounds__(kWideThreads) void tail_pass_kernel(WideArgs a) {
   using TR = TailTraits<GP>;
@@ -698,7 +700,8 @@ __global__ __launch_bounds__(kWideThreads) void tail_pass_kernel(WideArgs a) {
   constexpr int kRedFloats = ((TR::csrc >= 0 ? 16 : 0) + 1) * 64;
   constexpr int kRedBytes = kWideWaves * kRedFloats * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStageBytes > kRedBytes ? kStageBytes : kRedBytes];
-  constexpr int NM = (GP == kTQ || GP == kTE) ? RT : 0;     // modifier levels
+  constexpr int NM = (GP == kTQ || GP == kTE) && RT > 0 ? RT : 0;   // register-held modifier levels
+  constexpr bool kLoopM = (GP == kTQ || GP == kTE) && RT < 0;        // modifier levels at run time
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t head;
@@ -810,7 +813,30 @@ __global__ __launch_bounds__(kWideThreads) void tail_pass_kernel(WideArgs a) {
             if constexpr (GP == kTQ) m -= own_x[k] * wx[k][r] + own_y[k] * wy[k][r];
             else m -= wx[k][r] * own_x[k] + wy[k][r] * own_y[k];
           }
-          z[tt][r] = keep ? p * m : 0.f;
+          z[tt][r] = keep ? p * m : 0.f;     // (kLoopM: the modifier is applied below)
+        }
+      }
+      if constexpr (kLoopM) {
+        // z = p g so far: subtract p sum_a [EU_a(i) F_a(j) + C_a(i) EV_{a-1}(j)], level by level
+        f32x4 msub = {0.f, 0.f, 0.f, 0.f};
+        for (int lv = 1; lv <= a.R; ++lv) {
+          if constexpr (GP == kTQ) {
+            const float ox = vec(tv.eu(lv))[o], oy = vec(tv.c(lv))[o];
+            const f32x4 fx = load4(vec(tv.f(lv)) + wc), fy = load4(vec(tv.ev(lv - 1)) + wc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) msub[r] += ox * fx[r] + oy * fy[r];
+          } else {
+            const float ox = vec(tv.f(lv))[o], oy = vec(tv.ev(lv - 1))[o];
+            const f32x4 fx = load4(vec(tv.eu(lv)) + wc), fy = load4(vec(tv.c(lv)) + wc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) msub[r] += fx[r] * ox + fy[r] * oy;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool keep = in_band(wb + r, o, h, Lr);
+          const float p = fast_exp2(fmaf(sc[r], c2, own_d + wd[r]));
+          z[tt][r] = keep ? p * (gv[r] - msub[r]) : 0.f;
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
@@ -940,7 +966,8 @@ static void tail_pass_r(const WideArgs& a, hipStream_t st) {
     case 1: tail_pass_kernel<T, GP, 1><<<grid, block, 0, st>>>(a); break;
     case 2: tail_pass_kernel<T, GP, 2><<<grid, block, 0, st>>>(a); break;
     case 3: tail_pass_kernel<T, GP, 3><<<grid, block, 0, st>>>(a); break;
-    default: tail_pass_kernel<T, GP, 4><<<grid, block, 0, st>>>(a); break;
+    case 4: tail_pass_kernel<T, GP, 4><<<grid, block, 0, st>>>(a); break;
+    default: tail_pass_kernel<T, GP, -1><<<grid, block, 0, st>>>(a); break;
   }
 }
 

@@ -16,7 +16,7 @@
  *                                     v_j = -log sum_i exp(S_ij + u_i);   v^(0) := v (stopped).
  *   Tail: for a = 1..R:  u^(a) from v^(a-1), then v^(a) from u^(a) (same two updates).
  *   Output: O = P V with P_ij = exp(S_ij + u^(R)_i + v^(R)_j) on Omega.
- *   VJP (1 <= R <= 4): exact gradient of <O, dO> with respect to Q, K, V through the tail,
+ *   VJP (1 <= R <= 256): exact gradient of <O, dO> with respect to Q, K, V through the tail,
  *   with v^(0) held fixed (stop-gradient on the base).
  *
  * Tensor layout: Q, K, V, O, dO, dQ, dK, dV are [bh][Lr][d] row-major (d contiguous), element
@@ -51,7 +51,7 @@ typedef enum { SKA_F32 = 0, SKA_BF16 = 1 } ska_dtype;
 /* Adjoint schedule of the VJP.
  * SKA_ONE_REFERENCE: only the reference plan P^(R,R) is exponentiated; the other staircase
  *   plans enter through the orbit factors exp(u^(a)-u^(R)), exp(v^(b)-v^(R)) (abstract;
- *   technical summaries §2.2, orbit equation).  Any R from 1 to 4.
+ *   technical summaries §2.2, orbit equation).  Any R from 1 to 256.
  * SKA_DIRECT_FOUR: R = 2 only; every staircase plan P^(2,2), P^(2,1), P^(1,1), P^(1,0) is
  *   exponentiated on its own (the direct four-plan adjoint, atlas.scime.ai Key results); kept
  *   for comparison.  Other R return SKA_ERR_UNSUPPORTED. */
@@ -60,7 +60,7 @@ typedef enum { SKA_ONE_REFERENCE = 0, SKA_DIRECT_FOUR = 1 } ska_schedule;
 typedef enum {
   SKA_OK = 0,
   SKA_ERR_INVALID = -1,     /* malformed argument (null/misaligned pointer, W odd, eps <= 0, ...) */
-  SKA_ERR_UNSUPPORTED = -2, /* well-formed but not built: d != 64, VJP with R > 4, huge L       */
+  SKA_ERR_UNSUPPORTED = -2, /* well-formed but not built: d != 64, VJP with R > 256, huge L     */
   SKA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than ska_workspace_bytes()          */
   SKA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed                        */
 } ska_status;
@@ -69,7 +69,8 @@ typedef enum {
   SKA_OP_FWD = 0,
   SKA_OP_VJP = 1,
   SKA_OP_DUSTBIN_BLOCK_FWD = 2,
-  SKA_OP_DUSTBIN_BLOCK_VJP = 3
+  SKA_OP_DUSTBIN_BLOCK_VJP = 3,
+  SKA_OP_TAIL_REMAINDER = 4
 } ska_op;
 
 typedef struct {
@@ -78,7 +79,7 @@ typedef struct {
   int64_t d;       /* head dimension; 64 is built                                               */
   int64_t W;       /* band width, even, >= 0; support |i - j| <= W / 2                          */
   int32_t T;       /* stopped base steps, >= 0                                                  */
-  int32_t R;       /* tail steps: forward >= 1, VJP 1..4 (direct-four schedule: 2)              */
+  int32_t R;       /* tail steps: forward >= 1, VJP 1..256 (direct-four schedule: 2)            */
   float epsilon;   /* entropic temperature, finite and > 0                                      */
   int32_t dtype;   /* ska_dtype of Q, K, V, O, dO, dQ, dK, dV (duals are always fp32)           */
 } ska_problem;
@@ -96,7 +97,7 @@ ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K,
                              void* O, float* duals, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
-/* Exact tail VJP (1 <= R <= 4): given the forward's duals and an arbitrary cotangent dO, writes
+/* Exact tail VJP (1 <= R <= 256): given the forward's duals and an arbitrary cotangent dO, writes
  * dQ, dK, dV [bh][L][d].  Scores are recomputed per band tile; extra memory is O(L) vectors
  * (3 + 4 R of them for R != 2).  R = 2 runs the two-level passes (both schedules); other R run
  * 2 R + 2 passes of the one-reference adjoint, the modifier field then holding 2 R terms
@@ -127,6 +128,28 @@ ska_status sinkhorn_attn_dustbin_block_vjp(const ska_problem* p, const void* Q, 
                                            void* dQ, void* dK, void* dV, ska_schedule schedule,
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
+
+/* A posteriori bias certificate of the stopped base (technical summaries §2.4: a measurement of
+ * the gradient remainder eta_R that the stop-gradient on the base drops, certified against a
+ * tolerance tau, which selects the tail depth R; Key results: it reconstructs the full remainder
+ * to numerical precision and selects R = 2 at tau = 1e-5).
+ * Full backpropagation through all T + R steps from u = v = 0 is exactly the tail adjoint at
+ * depth T + R with no stopped base (T' = 0: the initial v = 0 is a constant), so this entry runs
+ * the forward and the one-reference VJP twice on the caller's workspace, at (T, R) and at
+ * (0, T + R), and writes the remainder and full-gradient squared norms summed over all problems:
+ *   sums[0] = ||dQ_full - dQ_R||^2,  sums[1] = ||dQ_full||^2,
+ *   sums[2] = ||dK_full - dK_R||^2,  sums[3] = ||dK_full||^2
+ * (dV has no remainder: V enters only the output).  eta_R = sqrt((sums[0] + sums[2]) /
+ * (sums[1] + sums[3])).  `sums` is a device pointer to 4 doubles; the sums are taken in double in
+ * a fixed order.  Requires 1 <= R and T + R <= 256; workspace from
+ * ska_workspace_bytes(p, SKA_OP_TAIL_REMAINDER): O(bh L (T + R)) floats of duals and cotangent
+ * vectors plus seven [bh][L][d] tensors.  Gradients are formed in the input dtype, so with bf16
+ * inputs remainders below the bf16 rounding of the gradients (about 4e-3 relative) are not
+ * resolved: certify with fp32 inputs.  An empty problem writes nothing. */
+ska_status sinkhorn_attn_tail_remainder(const ska_problem* p, const void* Q, const void* K,
+                                        const void* V, const void* dO, double* sums,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
 
 /* Static string for a status code. */
 const char* ska_status_string(ska_status s);

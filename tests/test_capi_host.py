@@ -155,8 +155,8 @@ def test_workspace_sizes():
     (dict(W=-2), B.SKA_OP_FWD, -1),
     (dict(T=-1), B.SKA_OP_FWD, -1),
     (dict(R=0), B.SKA_OP_FWD, -1),
-    (dict(R=5), B.SKA_OP_VJP, -2),
-    (dict(R=9), B.SKA_OP_DUSTBIN_BLOCK_VJP, -2),
+    (dict(R=300), B.SKA_OP_VJP, -2),
+    (dict(R=257), B.SKA_OP_DUSTBIN_BLOCK_VJP, -2),
     (dict(epsilon=0.0), B.SKA_OP_FWD, -1),
     (dict(epsilon=float("nan")), B.SKA_OP_VJP, -1),
     (dict(dtype=7), B.SKA_OP_FWD, -1),
@@ -205,6 +205,31 @@ def test_general_tail_depth_workspace(R):
         assert st == 0 and n == (3 + 4 * R) * 3 * 1024 * 4
     st, n = _ws_bytes(_prob(R=R, L=4096, bh=4), B.SKA_OP_DUSTBIN_BLOCK_VJP)
     assert st == 0 and n == (3 + 4 * R) * 4 * 4160 * 4
+
+
+def test_tail_remainder_workspace_and_checks():
+    """The certificate's workspace holds O and two gradient sets [bh][L][d] (input dtype), both
+    dual sets (2R + 1 and 2(T + R) + 1 vectors), 256 x 2 doubles of block sums and the largest
+    inner forward/VJP workspace, each piece rounded to 256 bytes; T + R above 256 is rejected."""
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for dtype, esz in ((B.SKA_F32, 4), (B.SKA_BF16, 2)):
+        prob = _prob(L=1000, bh=3, W=16, T=5, R=2, dtype=dtype)
+        st, n = _ws_bytes(prob, B.SKA_OP_TAIL_REMAINDER)
+        inner = max(_ws_bytes(prob, B.SKA_OP_FWD)[1], _ws_bytes(prob, B.SKA_OP_VJP)[1],
+                    _ws_bytes(_prob(L=1000, bh=3, W=16, T=0, R=7, dtype=dtype), B.SKA_OP_FWD)[1],
+                    _ws_bytes(_prob(L=1000, bh=3, W=16, T=0, R=7, dtype=dtype), B.SKA_OP_VJP)[1])
+        want = (7 * up(3 * 1000 * 64 * esz) + up(5 * 3 * 1000 * 4) + up(15 * 3 * 1000 * 4)
+                + up(512 * 8) + up(inner))
+        assert st == 0 and n == want
+    st, _ = _ws_bytes(_prob(T=250, R=7), B.SKA_OP_TAIL_REMAINDER)
+    assert st == -2 and "T + R" in B.ska_last_error()
+    prob = _prob()
+    _, need = _ws_bytes(prob, B.SKA_OP_TAIL_REMAINDER)
+    V = ctypes.c_void_p
+    f = B.lib.sinkhorn_attn_tail_remainder
+    assert f(ctypes.byref(prob), V(FAKE), V(FAKE), V(FAKE), V(FAKE), None, V(FAKE), need, None) == -1
+    assert f(ctypes.byref(prob), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE + 4), V(FAKE), need, None) == -1
+    assert f(ctypes.byref(prob), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), need - 8, None) == -3
 
 
 def test_empty_problems_enqueue_nothing():
