@@ -44,12 +44,20 @@ NEG_INF = -np.inf
 @dataclass(frozen=True)
 class BandProblem:
     """Problem constants: band width W (support |i-j| <= W//2), T base steps,
-    R tail steps, temperature epsilon (scores are q.k / (sqrt(d) * epsilon))."""
+    R tail steps, temperature epsilon (scores are q.k / (sqrt(d) * epsilon)).
+    R = 0 (no differentiable tail) takes the plan of the stopped base itself, whose duals
+    (u^(0), v^(0)) the base must have produced: it needs T >= 1."""
 
     W: int
     T: int
     R: int
     eps: float = 1.0
+
+    def __post_init__(self):
+        if self.R < 0 or self.T < 0:
+            raise ValueError("T and R must be >= 0")
+        if self.R == 0 and self.T == 0:
+            raise ValueError("R = 0 needs T >= 1: the plan's duals come from the base")
 
     @property
     def h(self) -> int:
@@ -176,13 +184,19 @@ def _forward_duals(S: np.ndarray, h: int, T: int, R: int):
     v^(0) is under stop-gradient.  Tail: for a = 1..R, u^(a) from v^(a-1), then
     v^(a) from u^(a).  Returns [v^(0), u^(1), v^(1), ..., u^(R), v^(R)].
     [technical summaries §2.1: stopped T-step base solve producing (u^(0), v^(0)),
-    then R differentiable steps starting from the stopped base state]"""
+    then R differentiable steps starting from the stopped base state]
+
+    With R = 0 the output plan is the base's own, P^(0,0) = exp(S + u^(0) + v^(0)), and both
+    of its duals are returned: [u^(0), v^(0)].  In every case the last two entries are the
+    duals of the output plan."""
     L = S.shape[1]
     u = np.zeros(L)
     v = np.zeros(L)
     for _ in range(T):
         u = row_update(S, v, h)
         v = col_update(S, u, h)
+    if R == 0:
+        return [u.copy(), v.copy()]
     duals = [v.copy()]
     for _ in range(R):
         u = row_update(S, v, h)
@@ -205,15 +219,18 @@ def forward(Q, K, V, prob: BandProblem, active=None):
     return O, np.stack(duals)
 
 
-def forward_from_base(Q, K, V, v0, prob: BandProblem, active=None):
+def forward_from_base(Q, K, V, v0, prob: BandProblem, active=None, u0=None):
     """Tail and output with the stopped base dual v^(0) supplied and held fixed:
     this is the function the tail VJP differentiates (v^(0) carries no gradient).
+    R = 0 outputs with the base plan itself, so u^(0) is supplied and held fixed as well.
     [technical summaries §2.1: the tail refines the potentials starting from the
     stopped base state]"""
     h = prob.h
     S = band_scores(Q, K, h, prob.eps, active)
     v = np.asarray(v0, dtype=np.float64)
-    u = None
+    if prob.R == 0 and u0 is None:
+        raise ValueError("R = 0 differentiates with both base duals fixed: pass u0")
+    u = None if u0 is None else np.asarray(u0, dtype=np.float64)
     for _ in range(prob.R):
         u = row_update(S, v, h)
         v = col_update(S, u, h)
@@ -375,11 +392,16 @@ def vjp_one_reference(Q, K, V, dO, duals, prob: BandProblem, active=None, want_p
 
 
 # --------------------------------------------------------------------------------------
-# VJP, any tail depth R >= 1
+# VJP, any tail depth R >= 0
 # --------------------------------------------------------------------------------------
 
 def _tail_duals(duals, R):
-    """duals = [v0, u1, v1, ..., uR, vR] -> (us, vs) with us[a] = u^(a) (a >= 1), vs[b] = v^(b)."""
+    """duals = [v0, u1, v1, ..., uR, vR] -> (us, vs) with us[a] = u^(a) (a >= 1), vs[b] = v^(b);
+    for R = 0, duals = [u0, v0] -> ([u0], [v0])."""
+    if R == 0:
+        if len(duals) != 2:
+            raise ValueError("expected the 2 base duals (u^(0), v^(0)) for R = 0")
+        return [duals[0]], [duals[1]]
     if len(duals) != 2 * R + 1:
         raise ValueError("expected 2 R + 1 saved duals")
     us = [None] + [duals[2 * a - 1] for a in range(1, R + 1)]
@@ -388,7 +410,7 @@ def _tail_duals(duals, R):
 
 
 def vjp_tail(Q, K, V, dO, duals, prob: BandProblem, active=None, want_parts=False):
-    """Exact VJP of O = P^(R,R) V through an R-step tail (any R >= 1) with v^(0) stopped:
+    """Exact VJP of O = P^(R,R) V through an R-step tail (any R >= 0) with v^(0) stopped:
     reverse-mode differentiation of the tail steps in turn, last step first, every
     staircase plan P^(a,b) = exp(S + u^(a) + v^(b)) from its own exponential.
 
@@ -401,7 +423,8 @@ def vjp_tail(Q, K, V, dO, duals, prob: BandProblem, active=None, want_parts=Fals
             dS -= P^(a,a-1) du^(a)_i,  dv^(a-1) -= colsum(P^(a,a-1) du^(a)_i)   (a > 1;
             v^(0) is stopped)
       dQ = s dS K,  dK = s dS^T Q
-    R = 2 is the four-plan adjoint of vjp_direct_four.
+    R = 2 is the four-plan adjoint of vjp_direct_four.  R = 0: both duals of P = P^(0,0) are
+    stopped, so no dual carries a cotangent and dS = P g.
     [technical summaries §2.1: R differentiable tail steps from the stopped base state;
     §2.2: the exact tail adjoint through the staircase plans]"""
     R = prob.R
@@ -416,8 +439,9 @@ def vjp_tail(Q, K, V, dO, duals, prob: BandProblem, active=None, want_parts=Fals
     dS = P * g
     du = [None] + [np.zeros(L) for _ in range(R)]
     dv = [np.zeros(L) for _ in range(R + 1)]
-    du[R] = du[R] + _row_sum(P * g)
-    dv[R] = dv[R] + _col_sum(P * g, h)
+    if R >= 1:
+        du[R] = du[R] + _row_sum(P * g)
+        dv[R] = dv[R] + _col_sum(P * g, h)
     for a in range(R, 0, -1):
         Paa = staircase_plan(S, us[a], vs[a], h)
         dS = dS - Paa * _row_vec(dv[a], h)
@@ -434,7 +458,7 @@ def vjp_tail(Q, K, V, dO, duals, prob: BandProblem, active=None, want_parts=Fals
 
 def vjp_tail_one_reference(Q, K, V, dO, duals, prob: BandProblem, active=None,
                            want_parts=False):
-    """The same VJP (any R >= 1) with one reference tile: only P = P^(R,R) is
+    """The same VJP (any R >= 0) with one reference tile: only P = P^(R,R) is
     exponentiated; every other staircase plan is P * eu_a(i) * ev_b(j) with
     eu_a = exp(u^(a) - u^(R)), ev_b = exp(v^(b) - v^(R)) (the orbit equation).
 
@@ -447,7 +471,7 @@ def vjp_tail_one_reference(Q, K, V, dO, duals, prob: BandProblem, active=None,
     Modifier field (2 R rank-one terms) and score cotangent:
       M_ij = g_ij - sum_a eu_a(i) ev_a(j) dv^(a)_j - sum_a eu_a(i) du^(a)_i ev_{a-1}(j),
       dS = P * M.
-    R = 2 is vjp_one_reference.
+    R = 2 is vjp_one_reference; R = 0 has no levels, so M = g.
     [abstract: one reference plan tile times a modifier field of vector cotangents and dual
     differences; technical summaries §2.2: orbit equation P^(a,b) = P^(R,R) exp(du) exp(dv)]"""
     R = prob.R
@@ -513,12 +537,12 @@ def tail_remainder(Q, K, V, dO, prob: BandProblem, active=None) -> dict:
 
 
 def select_tail_depth(Q, K, V, dO, W: int, T: int, eps: float = 1.0, tau: float = 1e-5,
-                      R_max: int = 4):
-    """Smallest R in 1..R_max with eta_R <= tau (None if none), and the eta_R computed.
+                      R_max: int = 4, R_min: int = 0):
+    """Smallest R in R_min..R_max with eta_R <= tau (None if none), and the eta_R computed.
     [technical summaries §2.4: dynamic choice of the tail depth; Key results: R = 2 is the
     smallest depth meeting tau = 1e-5 on the pages' problems]"""
     etas = {}
-    for R in range(1, R_max + 1):
+    for R in range(R_min, R_max + 1):
         etas[R] = tail_remainder(Q, K, V, dO, BandProblem(W=W, T=T, R=R, eps=eps))["eta"]
         if etas[R] <= tau:
             return R, etas

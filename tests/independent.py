@@ -41,7 +41,8 @@ def textbook_sinkhorn(A: np.ndarray, steps: int):
 
 def dense_autograd(Q, K, V, dO, W, T, R, eps):
     """Dense-matrix surrogate: stopped T-step base, R-step tail, O = P^(R,R) V.
-    Returns (O, dQ, dK, dV, duals) with duals = [v0, u1, v1, ..., uR, vR]."""
+    Returns (O, dQ, dK, dV, duals) with duals = [v0, u1, v1, ..., uR, vR] ([u0, v0] for
+    R = 0, when the output plan is the stopped base's own)."""
     Qt = torch.tensor(np.asarray(Q, np.float64), requires_grad=True)
     Kt = torch.tensor(np.asarray(K, np.float64), requires_grad=True)
     Vt = torch.tensor(np.asarray(V, np.float64), requires_grad=True)
@@ -59,7 +60,7 @@ def dense_autograd(Q, K, V, dO, W, T, R, eps):
             u = -torch.logsumexp(Sd + v[None, :], dim=1)
             v = -torch.logsumexp(Sd + u[:, None], dim=0)
     v = v.detach()
-    duals = [v]
+    duals = [u.detach(), v] if R == 0 else [v]
     for _ in range(R):
         u = -torch.logsumexp(S + v[None, :], dim=1)
         v = -torch.logsumexp(S + u[:, None], dim=0)

@@ -20,8 +20,8 @@ SRC = os.path.join(ROOT, "oracle", "sinkhorn_band.py")
 
 MUTATIONS = {
     "update_order_column_first": (
-        "        u = row_update(S, v, h)\n        v = col_update(S, u, h)\n    duals = [v.copy()]",
-        "        v = col_update(S, u, h)\n        u = row_update(S, v, h)\n    duals = [v.copy()]"),
+        "        u = row_update(S, v, h)\n        v = col_update(S, u, h)\n    if R == 0:",
+        "        v = col_update(S, u, h)\n        u = row_update(S, v, h)\n    if R == 0:"),
     "drop_modifier_C_term": ("- C[None, :] * _row_vec(G, h))", ")"),
     "sign_of_dv1": ("dv1 = -ev1 * _col_sum", "dv1 = ev1 * _col_sum"),
     "wrong_dual_in_G": ("ev0 = np.exp(v0 - v2)", "ev0 = np.exp(v1 - v2)"),
@@ -50,6 +50,8 @@ TAIL_MUTATIONS = {
         "Pab = staircase_plan(S, us[a], vs[a - 1], h)", "Pab = staircase_plan(S, us[a], vs[a], h)"),
     "tail_step_form_skips_column_term": (
         "        dS = dS - Paa * _row_vec(dv[a], h)\n", ""),
+    "r0_base_duals_swapped": (
+        "        return [u.copy(), v.copy()]\n", "        return [v.copy(), u.copy()]\n"),
     "full_backprop_one_step_short": (
         "pf = BandProblem(W=prob.W, T=0, R=prob.T + prob.R, eps=prob.eps)",
         "pf = BandProblem(W=prob.W, T=0, R=prob.T + prob.R - 1, eps=prob.eps)"),

@@ -39,6 +39,8 @@ CASES = [
     (40, 80, 5, 3, 1.2),
     (33, 14, 2, 4, 0.8),
     (18, 0, 1, 4, 1.0),
+    (25, 10, 3, 0, 1.0),
+    (20, 40, 1, 0, 0.8),
 ]
 
 
@@ -110,6 +112,47 @@ def test_tail_invariants(R):
     np.testing.assert_allclose(dV, P.T @ dO, atol=1e-13)
 
 
+def test_r0_is_the_stopped_base_plan():
+    """R = 0 outputs with the base's own plan: the same iterates as one tail step after T - 1
+    base steps, so O and the plan's duals agree with (T - 1, R = 1); with both duals stopped,
+    dS = P g and dV = P^T dO."""
+    L, W, T = 29, 10, 4
+    h = W // 2
+    Q, K, V, dO = _qkv(L, seed=90)
+    p0 = sb.BandProblem(W=W, T=T, R=0, eps=0.9)
+    p1 = sb.BandProblem(W=W, T=T - 1, R=1, eps=0.9)
+    O0, d0 = oracle.forward(Q, K, V, p0)
+    O1, d1 = oracle.forward(Q, K, V, p1)
+    assert d0.shape == (2, L)
+    np.testing.assert_allclose(O0, O1, atol=1e-14)
+    np.testing.assert_allclose(d0, d1[1:], atol=1e-14)
+    _, _, dV, parts = oracle.vjp_tail(Q, K, V, dO, d0, p0, want_parts=True)
+    P = _dense_from_band(parts["P"], h)
+    G = dO @ V.T
+    np.testing.assert_allclose(_dense_from_band(parts["dS"], h), P * G, atol=1e-13)
+    np.testing.assert_allclose(dV, P.T @ dO, atol=1e-13)
+    with pytest.raises(ValueError):
+        sb.BandProblem(W=W, T=0, R=0)
+
+
+def test_r0_central_finite_differences():
+    """R = 0: the VJP is the derivative of <O, dO> with u^(0) and v^(0) both frozen."""
+    L, W = 22, 8
+    Q, K, V, dO = _qkv(L, seed=91)
+    prob = sb.BandProblem(W=W, T=3, R=0, eps=0.8)
+    _, duals = oracle.forward(Q, K, V, prob)
+    dQ, dK, dV = oracle.vjp_tail_one_reference(Q, K, V, dO, duals, prob)
+    r = np.random.default_rng(5)
+    for _ in range(3):
+        eQ, eK, eV = (r.standard_normal(Q.shape) for _ in range(3))
+        delta = 1e-5
+        f = lambda t: float(np.sum(oracle.forward_from_base(  # noqa: E731
+            Q + t * eQ, K + t * eK, V + t * eV, duals[1], prob, u0=duals[0]) * dO))
+        fd = (f(delta) - f(-delta)) / (2 * delta)
+        an = float(np.sum(dQ * eQ) + np.sum(dK * eK) + np.sum(dV * eV))
+        assert abs(fd - an) < 1e-7 * max(1.0, abs(an)), (fd, an)
+
+
 def test_tail_vjp_central_finite_differences():
     """R = 4: <dQ, e_Q> + <dK, e_K> + <dV, e_V> equals the directional derivative of
     <O, dO> with v^(0) frozen (central differences)."""
@@ -134,7 +177,8 @@ def test_tail_vjp_central_finite_differences():
 # full backpropagation and the a posteriori bias certificate
 # --------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("L,W,T,R,eps", [(22, 8, 3, 2, 1.0), (30, 12, 5, 1, 0.8), (26, 60, 4, 3, 1.1)])
+@pytest.mark.parametrize("L,W,T,R,eps", [(22, 8, 3, 2, 1.0), (30, 12, 5, 1, 0.8), (26, 60, 4, 3, 1.1),
+                                         (24, 10, 3, 0, 0.9)])
 def test_full_backprop_matches_dense_autograd_through_the_base(L, W, T, R, eps):
     """vjp_full == dense autograd with gradients flowing through every base step."""
     from tests.independent import dense_autograd_full
@@ -162,12 +206,12 @@ def test_remainder_invariants():
 
 def test_remainder_decays_with_tail_depth():
     """The bias of the stopped base shrinks as the tail deepens (the refinement map contracts,
-    technical summaries §2.4): eta_R decreases strictly from R = 1 to 4 on a base far from
-    converged."""
+    technical summaries §2.4; Key results, bias decay from R = 0 through 1 and 2): eta_R
+    decreases strictly from R = 0 to 4 on a base far from converged."""
     L, W = 40, 12
     Q, K, V, dO = _qkv(L, seed=71)
     etas = [oracle.tail_remainder(Q, K, V, dO, sb.BandProblem(W=W, T=2, R=R, eps=1.0))["eta"]
-            for R in (1, 2, 3, 4)]
+            for R in (0, 1, 2, 3, 4)]
     assert all(b < a for a, b in zip(etas, etas[1:])), etas
 
 
@@ -180,4 +224,4 @@ def test_select_tail_depth_returns_the_smallest_certified_depth():
     Q, K = 0.3 * Q, 0.3 * K
     R, etas = oracle.select_tail_depth(Q, K, V, dO, W=128, T=15, eps=1.0, tau=1e-5, R_max=4)
     assert R == 2, etas
-    assert etas[1] > 1e-5 >= etas[2] and 3 not in etas
+    assert etas[0] > etas[1] > 1e-5 >= etas[2] and 3 not in etas
