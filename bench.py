@@ -136,7 +136,7 @@ def main():
     ws = B.workspace_for(prob, max(fwd_op, vjp_op), dev)
     ws_f = B.workspace_for(prob, fwd_op, dev)
     O = torch.empty_like(Q)
-    duals = torch.empty(w.bh, 2 * w.R + 1, rows, dtype=torch.float32, device=dev)
+    duals = torch.empty(w.bh, B.n_duals(w.R), rows, dtype=torch.float32, device=dev)
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
     sched = B.SCHEDULES[args.schedule]
     fwd = B.sinkhorn_attn_dustbin_block_fwd if w.dustbin else B.sinkhorn_attn_fwd

@@ -195,16 +195,21 @@ def workspace_for(problem: SkaProblem, op: int, device) -> torch.Tensor:
     return torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
 
 
+def n_duals(R: int) -> int:
+    """Saved dual rows per problem: v0, u1, v1, .., uR, vR (2R + 1), or u0, v0 when R = 0."""
+    return 2 if R == 0 else 2 * R + 1
+
+
 def forward(Q, K, V, W: int, T: int, R: int = 2, epsilon: float = 1.0, dustbin: bool = False,
             workspace: torch.Tensor | None = None, stream=None):
-    """O and duals [bh, 2R+1, tokens] (fp32, natural-log units)."""
+    """O and duals [bh, n_duals(R), tokens] (fp32, natural-log units)."""
     bh, rows, d, L = _shape_check(Q, K, V, dustbin)
     prob = make_problem(bh, L, d, W, T, R, epsilon, Q.dtype)
     op = SKA_OP_DUSTBIN_BLOCK_FWD if dustbin else SKA_OP_FWD
     if workspace is None:
         workspace = workspace_for(prob, op, Q.device)
     O = torch.empty_like(Q)
-    duals = torch.empty(bh, 2 * R + 1, rows, dtype=torch.float32, device=Q.device)
+    duals = torch.empty(bh, n_duals(R), rows, dtype=torch.float32, device=Q.device)
     fn = sinkhorn_attn_dustbin_block_fwd if dustbin else sinkhorn_attn_fwd
     fn(prob, Q, K, V, O, duals, workspace, stream)
     return O, duals
@@ -217,8 +222,8 @@ def vjp(Q, K, V, duals, dO, W: int, T: int, R: int = 2, epsilon: float = 1.0,
     bh, rows, d, L = _shape_check(Q, K, V, dustbin)
     if dO.shape != Q.shape or dO.dtype != Q.dtype:
         raise ValueError("dO must match Q in shape and dtype")
-    if duals.shape != (bh, 2 * R + 1, rows) or duals.dtype != torch.float32:
-        raise ValueError("duals must be fp32 [bh, 2R+1, tokens]")
+    if duals.shape != (bh, n_duals(R), rows) or duals.dtype != torch.float32:
+        raise ValueError("duals must be fp32 [bh, n_duals(R), tokens]")
     prob = make_problem(bh, L, d, W, T, R, epsilon, Q.dtype)
     op = SKA_OP_DUSTBIN_BLOCK_VJP if dustbin else SKA_OP_VJP
     if workspace is None:
@@ -249,11 +254,11 @@ def tail_remainder(Q, K, V, dO, W: int, T: int, R: int = 2, epsilon: float = 1.0
 
 
 def select_tail_depth(Q, K, V, dO, W: int, T: int, epsilon: float = 1.0, tau: float = 1e-5,
-                      R_max: int = 4) -> tuple:
-    """The smallest tail depth R in 1..R_max whose certified remainder eta_R is at most tau
+                      R_max: int = 4, R_min: int = 0) -> tuple:
+    """The smallest tail depth R in R_min..R_max whose certified remainder eta_R is at most tau
     (None if none is), and every eta_R computed on the way."""
     etas = {}
-    for R in range(1, R_max + 1):
+    for R in range(R_min, R_max + 1):
         etas[R] = tail_remainder(Q, K, V, dO, W, T, R, epsilon)["eta"]
         if etas[R] <= tau:
             return R, etas

@@ -78,7 +78,9 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   const bool dustbin = (op == SKA_OP_DUSTBIN_BLOCK_FWD || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   if (op < SKA_OP_FWD || op > SKA_OP_TAIL_REMAINDER) return fail(SKA_ERR_INVALID, "unknown op");
-  if (p->R < 1) return fail(SKA_ERR_INVALID, "R must be >= 1");
+  if (p->R < 0) return fail(SKA_ERR_INVALID, "R must be >= 0");
+  if (p->R == 0 && p->T < 1)
+    return fail(SKA_ERR_INVALID, "R = 0 needs T >= 1: the output plan's duals come from the base");
   if (vjp && p->R > ska::kTailMaxR) return fail(SKA_ERR_UNSUPPORTED, "the VJP is built for R <= 256");
   if (op == SKA_OP_TAIL_REMAINDER && (int64_t)p->T + p->R > ska::kTailMaxR)
     return fail(SKA_ERR_UNSUPPORTED, "the tail remainder runs the adjoint at depth T + R <= 256");
@@ -164,8 +166,8 @@ RemLayout rem_layout(const Plan& pl) {
   L.dq_f = at; at += tb;
   L.dk_f = at; at += tb;
   L.dv_f = at; at += tb;
-  L.duals_r = at; at += up((size_t)(2 * pl.R + 1) * pl.g.bh * pl.g.Lr * sizeof(float));
-  L.duals_f = at; at += up((size_t)(2 * (pl.T + pl.R) + 1) * pl.g.bh * pl.g.Lr * sizeof(float));
+  L.duals_r = at; at += up((size_t)ska::n_duals(pl.R) * pl.g.bh * pl.g.Lr * sizeof(float));
+  L.duals_f = at; at += up((size_t)ska::n_duals(pl.T + pl.R) * pl.g.bh * pl.g.Lr * sizeof(float));
   L.part = at; at += up(2 * ska::kSqPartials * sizeof(double));
   Plan a = pl, b = pl;
   b.R = pl.T + pl.R;
@@ -235,8 +237,10 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
 
   const ska::Geometry& g = pl.g;
   const int64_t vs = g.bh * (int64_t)g.Lpad;
-  const int64_t nd = 2 * (int64_t)p->R + 1;
+  const int64_t nd = ska::n_duals(p->R);
   const int64_t dstride = nd * g.Lr;
+  // the saved row of u_k / v_k, or none
+  auto save_at = [&](int slot) -> float* { return slot >= 0 ? duals + slot * (int64_t)g.Lr : nullptr; };
   float* wsf = static_cast<float*>(workspace);
   const int nt = ska::fused_tiles_for(g.h);
   if (nt > 0) {
@@ -274,8 +278,8 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
       a.v_next = vbuf[k % 2];
       a.u_out = ubuf[k % 2];
       a.part_out = part[k % 2];
-      a.save_v = (k - 1 >= p->T) ? duals + 2 * (int64_t)(k - 1 - p->T) * g.Lr : nullptr;
-      a.save_u = (k > p->T) ? duals + (2 * (int64_t)(k - p->T) - 1) * g.Lr : nullptr;
+      a.save_v = save_at(ska::dual_slot_v(k - 1, p->T, p->R));
+      a.save_u = save_at(ska::dual_slot_u(k, p->T, p->R));
       // alternate the walk direction: each step starts where the previous one ended, on data
       // still in the last-level cache
       SKA_LAUNCH(ska::kTimedStep, st, ska::launch_fused_step(pl.elt, nt, a, (k % 2) == 0, st));
@@ -286,7 +290,7 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
     a.v_next = vbuf[(K_steps + 1) % 2];
     a.u_out = nullptr;
     a.part_out = nullptr;
-    a.save_v = duals + 2 * (int64_t)p->R * g.Lr;
+    a.save_v = save_at(ska::dual_slot_v(K_steps, p->T, p->R));
     a.save_u = nullptr;
     e = ska::launch_finish_columns(pl.elt, a, st);
     if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
@@ -334,16 +338,16 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
     if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
     const int K_steps = p->T + p->R;
     for (int k = 1; k <= K_steps; ++k) {
-      // step k: u_k from v_{k-1}; saves u_k (k > T) and v_{k-1} (k - 1 >= T)
+      // step k: u_k from v_{k-1}; saves u_k and v_{k-1} where the layout keeps them
       a.v_in = v;
       a.u_out = u;
-      a.save_u = (k > p->T) ? duals + (2 * (int64_t)(k - p->T) - 1) * g.Lr : nullptr;
-      a.save_v = (k - 1 >= p->T) ? duals + 2 * (int64_t)(k - 1 - p->T) * g.Lr : nullptr;
+      a.save_u = save_at(ska::dual_slot_u(k, p->T, p->R));
+      a.save_v = save_at(ska::dual_slot_v(k - 1, p->T, p->R));
       SKA_LAUNCH(ska::kTimedStep, st, ska::launch_wide_step(pl.elt, kt, k == 1, a, st));
       // finish k: v_k (saved by the next step, or here after the last one)
       a.v_out = v;
       a.save_u = nullptr;
-      a.save_v = (k == K_steps) ? duals + 2 * (int64_t)p->R * g.Lr : nullptr;
+      a.save_v = (k == K_steps) ? save_at(ska::dual_slot_v(k, p->T, p->R)) : nullptr;
       e = ska::launch_wide_finish(pl.elt, a, st);
       if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
     }
@@ -364,7 +368,11 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
     SKA_LAUNCH(ska::kTimedStep, st, ska::launch_lse(pl.elt, Q, K, v, u, nullptr, 0, g, st));
     SKA_LAUNCH(ska::kTimedStep, st, ska::launch_lse(pl.elt, K, Q, u, v, nullptr, 0, g, st));
   }
-  e = ska::launch_save_duals(v, duals, dstride, g, st);
+  if (p->R == 0) {
+    e = ska::launch_save_duals(u, save_at(ska::dual_slot_u(p->T, p->T, 0)), dstride, g, st);
+    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+  }
+  e = ska::launch_save_duals(v, save_at(ska::dual_slot_v(p->T, p->T, p->R)), dstride, g, st);
   if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
   // tail: u^(a) from v^(a-1), v^(a) from u^(a); saved as slots 2a-1, 2a
   for (int a = 1; a <= p->R; ++a) {
@@ -410,7 +418,8 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
   const bool d4 = (sched == SKA_DIRECT_FOUR);
   if (p->R != 2) {
     // general tail depth: one-reference-tile adjoint, 2R + 2 passes on the wide decomposition
-    // (A: dv^(R) and dV; B: du^(R); C, D for each level a = R-1 .. 1; then dQ and dK)
+    // (A: dv^(R) and dV; B: du^(R); C, D for each level a = R-1 .. 1; then dQ and dK); R = 0
+    // differentiates the stopped base plan alone: A (dV), then dQ and dK with M = g
     hipError_t e = ska::launch_tail_prep(duals, ws, p->R, g, st);
     if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
     ska::WideArgs w = wide_args(pl, Q, K, V, dO);
@@ -419,7 +428,7 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
     w.R = p->R;
     w.out0 = dV;
     SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 0, w, st));
-    SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 1, w, st));
+    if (p->R > 0) SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 1, w, st));
     for (int lev = p->R - 1; lev >= 1; --lev) {
       w.level = lev;
       SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 2, w, st));

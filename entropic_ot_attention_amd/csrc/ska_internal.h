@@ -124,6 +124,19 @@ struct WideArgs {
 // units), the orbit factors EU_a = exp(u^(a) - u^(R)) (a = 1..R) and EV_b = exp(v^(b) - v^(R))
 // (b = 0..R), and the scaled cotangents F_a = dv^(a) EV_a and C_a = du^(a) EU_a (a = 1..R).
 inline int tail_vecs(int R) { return 3 + 4 * R; }
+// Saved duals per head, [n_duals(R)][Lr]: v^(0), u^(1), v^(1), .., u^(R), v^(R) for R >= 1; the
+// stopped base pair u^(0), v^(0) for R = 0.  The last two rows are the output plan's duals.
+inline int n_duals(int R) { return R == 0 ? 2 : 2 * R + 1; }
+// Row of u_k and of v_k (the duals after Sinkhorn step k = 1 .. T + R, counted from u = v = 0),
+// or -1 when that dual is not saved.
+inline int dual_slot_u(int k, int T, int R) {
+  const int off = (R == 0);
+  return (k - T >= 1 - off) ? 2 * (k - T) - 1 + off : -1;
+}
+inline int dual_slot_v(int k, int T, int R) {
+  const int off = (R == 0);
+  return (k >= T) ? 2 * (k - T) + off : -1;
+}
 // Deepest tail the general passes run (a full backpropagation through T + R steps from u = v = 0
 // is the general adjoint at depth T + R): the workspace holds 3 + 4 R vectors.
 constexpr int kTailMaxR = 256;
@@ -162,9 +175,9 @@ hipError_t launch_vjp_prep(const float* duals, float* ws, const Geometry& g, hip
 constexpr int kSqPartials = 256;
 hipError_t launch_sq_diff(int elt, const void* a, const void* b, int64_t n, double* part,
                           double* out2, hipStream_t st);
-// General tail depth (1 <= R <= kTailMaxR), one-reference-tile adjoint on the wide decomposition:
+// General tail depth (0 <= R <= kTailMaxR), one-reference-tile adjoint on the wide decomposition:
 // the vector preparation, then passes 0 (A: dv^(R), dV), 1 (B: du^(R)), 2 (C: dv^(a)),
-// 3 (D: du^(a)), 4 (dQ), 5 (dK).
+// 3 (D: du^(a)), 4 (dQ), 5 (dK).  R = 0 runs A (dV only), dQ and dK.
 hipError_t launch_tail_prep(const float* duals, float* ws, int R, const Geometry& g, hipStream_t st);
 hipError_t launch_tail_pass(int elt, int pass, const WideArgs& a, hipStream_t st);
 }  // namespace ska

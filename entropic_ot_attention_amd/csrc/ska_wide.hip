@@ -654,7 +654,8 @@ struct TailVec {
   __device__ int c(int a) const { return 3 + 3 * R + (a - 1); }
 };
 
-// duals (natural units, [bh][2R+1][Lr]: v0, u1, v1, .., uR, vR) -> the tail vectors
+// duals (natural units, [bh][n_duals(R)][Lr]: v0, u1, v1, .., uR, vR, or u0, v0 for R = 0) -> the
+// tail vectors
 __global__ void tail_prep_kernel(const float* __restrict__ duals, float* __restrict__ ws, int R,
                                  int Lr, int Lpad, int64_t vec_stride) {
   const int64_t head = blockIdx.y;
@@ -664,9 +665,10 @@ __global__ void tail_prep_kernel(const float* __restrict__ duals, float* __restr
   const int64_t ob = head * Lpad + t;
   auto at = [&](int k) -> float& { return ws[k * vec_stride + ob]; };
   const bool ok = t < Lr;
-  const float* dh = duals + head * (2 * (int64_t)R + 1) * Lr;
+  const int nd = (R == 0) ? 2 : 2 * R + 1;   // n_duals(R)
+  const float* dh = duals + head * nd * (int64_t)Lr;
   auto dual = [&](int slot) { return ok ? dh[(int64_t)slot * Lr + t] : 0.f; };
-  const float uR = dual(2 * R - 1), vR = dual(2 * R);
+  const float uR = dual(nd - 2), vR = dual(nd - 1);
   at(tv.u()) = uR * kLog2e;
   at(tv.v()) = vR * kLog2e;
   for (int a = 1; a <= R; ++a) {
@@ -674,6 +676,7 @@ __global__ void tail_prep_kernel(const float* __restrict__ duals, float* __restr
     at(tv.f(a)) = 0.f;
     at(tv.c(a)) = 0.f;
   }
+  if (R == 0) return;   // no levels: the modifier is g itself
   for (int b = 0; b <= R; ++b) at(tv.ev(b)) = ok ? expf(dual(2 * b) - vR) : 0.f;
 }
 
@@ -688,10 +691,10 @@ template <int GP> struct TailTraits {
   static constexpr bool has_red = (GP <= kTD);
 };
 
-// RT: the tail depth for the dQ and dK passes (1..4 at compile time: their 2 RT modifier terms
-// and owned factors stay in registers); RT = -1: any depth, the modifier accumulated level by
-// level with its factors read per tile; 0 for the level passes, which take R and the level at
-// run time.
+// RT: the tail depth for the dQ and dK passes (0..4 at compile time: their 2 RT modifier terms
+// and owned factors stay in registers, none at depth 0, where M = g); RT = -1: any depth, the
+// modifier accumulated level by level with its factors read per tile; 0 for the level passes,
+// which take R and the level at run time.
 template <typename T, int GP, int RT>
 __global__ __launch_bounds__(kWideThreads) void tail_pass_kernel(WideArgs a) {
   using TR = TailTraits<GP>;
@@ -877,7 +880,7 @@ __global__ __launch_bounds__(kWideThreads) void tail_pass_kernel(WideArgs a) {
   if (o >= Lr) return;
   T* out_row = static_cast<T*>(a.out0) + tb + (int64_t)o * kD;
   if constexpr (GP == kTA) {
-    if (g == 0) vec(tv.f(a.R))[o] = red;                    // dv^(R) (EV_R = 1)
+    if (g == 0 && a.R > 0) vec(tv.f(a.R))[o] = red;         // dv^(R) (EV_R = 1)
     store_row(out_row, acc, 1.f, g);                        // dV
   } else if constexpr (GP == kTB) {
     if (g == 0) vec(tv.c(a.R))[o] = red;                    // du^(R) (EU_R = 1)
@@ -963,6 +966,7 @@ template <typename T, int GP>
 static void tail_pass_r(const WideArgs& a, hipStream_t st) {
   const dim3 grid = wide_grid(a), block(kWideThreads);
   switch (a.R) {
+    case 0: tail_pass_kernel<T, GP, 0><<<grid, block, 0, st>>>(a); break;    // M = g
     case 1: tail_pass_kernel<T, GP, 1><<<grid, block, 0, st>>>(a); break;
     case 2: tail_pass_kernel<T, GP, 2><<<grid, block, 0, st>>>(a); break;
     case 3: tail_pass_kernel<T, GP, 3><<<grid, block, 0, st>>>(a); break;
@@ -985,7 +989,8 @@ static void tail_pass_t(int pass, const WideArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tail_pass(int elt, int pass, const WideArgs& a, hipStream_t st) {
-  if (pass < kTA || pass > kTE || a.R < 1 || a.R > kTailMaxR) return hipErrorInvalidValue;
+  if (pass < kTA || pass > kTE || a.R < 0 || a.R > kTailMaxR) return hipErrorInvalidValue;
+  if (a.R == 0 && (pass == kTB || pass == kTC || pass == kTD)) return hipErrorInvalidValue;
   if ((pass == kTC || pass == kTD) && (a.level < 1 || a.level >= a.R)) return hipErrorInvalidValue;
   if (elt == 1) tail_pass_t<bf16>(pass, a, st);
   else tail_pass_t<float>(pass, a, st);

@@ -16,12 +16,15 @@
  *                                     v_j = -log sum_i exp(S_ij + u_i);   v^(0) := v (stopped).
  *   Tail: for a = 1..R:  u^(a) from v^(a-1), then v^(a) from u^(a) (same two updates).
  *   Output: O = P V with P_ij = exp(S_ij + u^(R)_i + v^(R)_j) on Omega.
- *   VJP (1 <= R <= 256): exact gradient of <O, dO> with respect to Q, K, V through the tail,
- *   with v^(0) held fixed (stop-gradient on the base).
+ *   R = 0 (no tail, T >= 1): the output plan is the base's own, with u^(0), v^(0) the duals of
+ *   the last base step, both under stop-gradient.
+ *   VJP (0 <= R <= 256): exact gradient of <O, dO> with respect to Q, K, V through the tail,
+ *   with v^(0) held fixed (stop-gradient on the base), and u^(0) too when R = 0.
  *
  * Tensor layout: Q, K, V, O, dO, dQ, dK, dV are [bh][Lr][d] row-major (d contiguous), element
- * type given by ska_problem.dtype.  Duals are fp32 [bh][2R+1][Lr] in natural-log units, in the
- * order v^(0), u^(1), v^(1), ..., u^(R), v^(R).
+ * type given by ska_problem.dtype.  Duals are fp32 [bh][n_d][Lr] in natural-log units: for
+ * R >= 1, n_d = 2R+1 rows in the order v^(0), u^(1), v^(1), ..., u^(R), v^(R); for R = 0,
+ * n_d = 2 rows u^(0), v^(0).  The last two rows are always the output plan's duals.
  *
  * Ownership and memory: every pointer is a device pointer owned by the caller, including the
  * workspace (size from ska_workspace_bytes).  The library allocates and frees nothing, keeps no
@@ -90,18 +93,19 @@ typedef struct {
 ska_status ska_workspace_bytes(const ska_problem* p, ska_op op, size_t* bytes);
 
 /* Forward pass: stopped T-step balanced Sinkhorn base, R-step tail, O = P^(R,R) V.
- * Writes O [bh][L][d] and duals [bh][2R+1][L].
+ * Writes O [bh][L][d] and duals [bh][n_d][L] (n_d = 2R+1, or 2 when R = 0).
  * (technical summaries §2.1: fixed band support, epsilon absorbed into S, stopped base solve
  * then differentiable tail; abstract: block-wise cost O((T+R) L W), O(L) extra HBM.) */
 ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K, const void* V,
                              void* O, float* duals, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
-/* Exact tail VJP (1 <= R <= 256): given the forward's duals and an arbitrary cotangent dO, writes
+/* Exact tail VJP (0 <= R <= 256): given the forward's duals and an arbitrary cotangent dO, writes
  * dQ, dK, dV [bh][L][d].  Scores are recomputed per band tile; extra memory is O(L) vectors
  * (3 + 4 R of them for R != 2).  R = 2 runs the two-level passes (both schedules); other R run
- * 2 R + 2 passes of the one-reference adjoint, the modifier field then holding 2 R terms
- * (technical summaries §2.1: R differentiable tail steps).
+ * 2 R + 2 passes of the one-reference adjoint, the modifier field then holding 2 R terms; R = 0
+ * runs dV, dQ and dK of the base plan with both duals fixed (score cotangent P * g)
+ * (technical summaries §2.1: R differentiable tail steps; §4.1: tail gradients from R = 0 up).
  * (abstract: one-reference-tile schedule, score cotangent = reference tile times a modifier
  * field of vector cotangents and dual differences; atlas.scime.ai Key results: complete
  * arbitrary-cotangent Q/K/V VJP.) */
@@ -111,7 +115,7 @@ ska_status sinkhorn_attn_vjp(const ska_problem* p, const void* Q, const void* K,
                              hipStream_t stream);
 
 /* dustbin_block forward: tensors hold L real tokens followed by the learned dustbin token at
- * row L ([bh][L+1][d]); duals are [bh][2R+1][L+1].  Tile padding beyond row L acts as the
+ * row L ([bh][L+1][d]); duals are [bh][n_d][L+1].  Tile padding beyond row L acts as the
  * inactive fill tokens (no support, zero target).  The support is every pair of the L+1 active
  * tokens within the widened half-width max(W/2, L), so the dustbin row and column connect to
  * every token; all active tokens, the dustbin included, have unit row and column targets.  The
@@ -141,7 +145,7 @@ ska_status sinkhorn_attn_dustbin_block_vjp(const ska_problem* p, const void* Q, 
  *   sums[2] = ||dK_full - dK_R||^2,  sums[3] = ||dK_full||^2
  * (dV has no remainder: V enters only the output).  eta_R = sqrt((sums[0] + sums[2]) /
  * (sums[1] + sums[3])).  `sums` is a device pointer to 4 doubles; the sums are taken in double in
- * a fixed order.  Requires 1 <= R and T + R <= 256; workspace from
+ * a fixed order.  Requires T + R <= 256 (and T >= 1 when R = 0); workspace from
  * ska_workspace_bytes(p, SKA_OP_TAIL_REMAINDER): O(bh L (T + R)) floats of duals and cotangent
  * vectors plus seven [bh][L][d] tensors.  Gradients are formed in the input dtype, so with bf16
  * inputs remainders below the bf16 rounding of the gradients (about 4e-3 relative) are not

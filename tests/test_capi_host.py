@@ -154,7 +154,9 @@ def test_workspace_sizes():
     (dict(W=7), B.SKA_OP_FWD, -1),
     (dict(W=-2), B.SKA_OP_FWD, -1),
     (dict(T=-1), B.SKA_OP_FWD, -1),
-    (dict(R=0), B.SKA_OP_FWD, -1),
+    (dict(R=-1), B.SKA_OP_FWD, -1),
+    (dict(R=0, T=0), B.SKA_OP_FWD, -1),
+    (dict(R=0, T=0), B.SKA_OP_TAIL_REMAINDER, -1),
     (dict(R=300), B.SKA_OP_VJP, -2),
     (dict(R=257), B.SKA_OP_DUSTBIN_BLOCK_VJP, -2),
     (dict(epsilon=0.0), B.SKA_OP_FWD, -1),
@@ -195,7 +197,7 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert g(ctypes.byref(prob), *(args[:5] + [None] + args[6:]), 0, V(FAKE), needv, None) == -1
 
 
-@pytest.mark.parametrize("R", [1, 3, 4])
+@pytest.mark.parametrize("R", [0, 1, 3, 4])
 def test_general_tail_depth_workspace(R):
     """VJP of a tail depth other than 2: 3 + 4 R vectors [bh][Lpad] (u^(R), v^(R), R row and
     R + 1 column orbit factors, R + R scaled cotangents), whatever the band and dtype; the
@@ -221,6 +223,14 @@ def test_tail_remainder_workspace_and_checks():
         want = (7 * up(3 * 1000 * 64 * esz) + up(5 * 3 * 1000 * 4) + up(15 * 3 * 1000 * 4)
                 + up(512 * 8) + up(inner))
         assert st == 0 and n == want
+    # R = 0: the base pair (u^(0), v^(0)) beside the 2 T + 1 duals of full backpropagation
+    prob0 = _prob(L=1000, bh=3, W=16, T=5, R=0)
+    st, n = _ws_bytes(prob0, B.SKA_OP_TAIL_REMAINDER)
+    inner = max(_ws_bytes(prob0, B.SKA_OP_FWD)[1], _ws_bytes(prob0, B.SKA_OP_VJP)[1],
+                _ws_bytes(_prob(L=1000, bh=3, W=16, T=0, R=5), B.SKA_OP_FWD)[1],
+                _ws_bytes(_prob(L=1000, bh=3, W=16, T=0, R=5), B.SKA_OP_VJP)[1])
+    assert st == 0 and n == (7 * up(3 * 1000 * 64 * 4) + up(2 * 3 * 1000 * 4) + up(11 * 3 * 1000 * 4)
+                             + up(512 * 8) + up(inner))
     st, _ = _ws_bytes(_prob(T=250, R=7), B.SKA_OP_TAIL_REMAINDER)
     assert st == -2 and "T + R" in B.ska_last_error()
     prob = _prob()

@@ -111,18 +111,20 @@ def test_tiny_epsilon_wide_exact_column_fallback():
     assert err <= tol, (err, tol)
 
 
-def test_split_half_steps_beyond_register_window():
+@pytest.mark.parametrize("R", [2, 0])
+def test_split_half_steps_beyond_register_window(R):
     """A window of 271 tiles (L = 4400, h = 2150) is wider than the wide step holds in registers
-    (8 waves x 33 tiles): the forward runs separate row and column half-steps."""
+    (8 waves x 33 tiles): the forward runs separate row and column half-steps (R = 0: the base
+    pair u^(0), v^(0) saved after the last base step)."""
     w, x = _inputs(1, 4400, 4300, 1, 1.0, F32, seed=9)
-    say("[gpu] split half-steps L=4400 W=4300 T=1")
-    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 4300, 1)
+    say(f"[gpu] split half-steps L=4400 W=4300 T=1 R={R}")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 4300, 1, R)
     ref = {k: [v] for k, v in oracle_head(*(as64(x[k][0]) for k in ("Q", "K", "V", "dO")),
-                                          4300, 1, 2, 1.0).items()}
-    compare(got, ref, torch.float32, "split L4400 W4300")
+                                          4300, 1, R, 1.0).items()}
+    compare(got, ref, torch.float32, f"split L4400 W4300 R={R}")
 
 
-@pytest.mark.parametrize("R", [1, 3, 4])
+@pytest.mark.parametrize("R", [0, 1, 3, 4])
 def test_forward_general_tail_depth(R):
     w, x = _inputs(2, 150, 40, 5, 1.0, F32, seed=77 + R)
     say(f"[gpu] forward R={R}")

@@ -1,5 +1,6 @@
-"""GPU parity of the general tail depth (R = 1, 3, 4): forward duals and output, and the exact
-one-reference adjoint with 2 R + 2 passes, against the fp64 oracle's general-depth orbit form
+"""GPU parity of the general tail depth (R = 0, 1, 3, 4): forward duals and output, and the exact
+one-reference adjoint with 2 R + 2 passes (R = 0: the base plan with both duals stopped, dV, dQ
+and dK with the score cotangent P g), against the fp64 oracle's general-depth orbit form
 (itself pinned to dense autograd, finite differences and the step form in test_oracle_tail.py).
 Small cases compare every element over narrow, wide and dense supports, both dtypes; the heads8
 workload at R = 4 is checked on sampled rows."""
@@ -24,6 +25,10 @@ CASES = [
     ("R4_L700_W64_bf16", 2, 700, 64, 6, 1.0, BF16, 4),
     ("R4_L900_W600_eps07_wide", 1, 900, 600, 3, 0.7, F32, 4),
     ("R4_L260_W1000_dense", 1, 260, 1000, 2, 1.0, F32, 4),
+    ("R0_L300_W40", 2, 300, 40, 5, 1.0, F32, 0),
+    ("R0_L600_W256_bf16", 2, 600, 256, 4, 1.0, BF16, 0),
+    ("R0_L900_W600_wide", 1, 900, 600, 3, 0.8, F32, 0),
+    ("R0_L20_W0_T1", 1, 20, 0, 1, 1.0, F32, 0),
 ]
 
 
@@ -46,19 +51,20 @@ def test_general_tail_depth_elementwise(case):
     compare(got, ref, w.torch_dtype, name)
 
 
-def test_dustbin_block_general_tail_depth():
-    """The dustbin-block entry points at R = 3: the same general adjoint on the augmented
+@pytest.mark.parametrize("R", [3, 0])
+def test_dustbin_block_general_tail_depth(R):
+    """The dustbin-block entry points at R = 3 and 0: the same general adjoint on the augmented
     (dense) support, gradients for every row including the dustbin token."""
-    w, x = _inputs(2, 200, 64, 4, 1.0, F32, 330, 3, dustbin=True)
-    say("[gpu] dustbin tail R=3 L=200+1")
-    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 64, 4, 3, 1.0, dustbin=True)
+    w, x = _inputs(2, 200, 64, 4, 1.0, F32, 330, R, dustbin=True)
+    say(f"[gpu] dustbin tail R={R} L=200+1")
+    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 64, 4, R, 1.0, dustbin=True)
     ref = {k: [] for k in ("O", "duals", "dQ", "dK", "dV")}
     for b in range(2):
-        r = oracle_head(*(as64(x[k][b]) for k in ("Q", "K", "V", "dO")), 64, 4, 3, 1.0,
+        r = oracle_head(*(as64(x[k][b]) for k in ("Q", "K", "V", "dO")), 64, 4, R, 1.0,
                         dustbin=True)
         for k in ref:
             ref[k].append(r[k])
-    compare(got, ref, torch.float32, "dustbin R=3")
+    compare(got, ref, torch.float32, f"dustbin R={R}")
 
 
 def test_direct_four_needs_r2():
