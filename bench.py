@@ -78,7 +78,142 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="one device copy of this many MiB before warmup (counter calibration)")
+    ap.add_argument("--certificate", action="store_true",
+                    help="time the a posteriori bias certificate eta_R (fp32 inputs) for "
+                         "R = 0..--r-max on the workload instead of the forward + VJP step")
+    ap.add_argument("--r-max", type=int, default=4)
+    ap.add_argument("--tau", type=float, default=1e-5)
     return ap.parse_args()
+
+
+def tail_pass_flops_per_entry(R: int, d: int) -> int:
+    """Matrix-core flops per band entry of the general-depth adjoint at tail depth R >= 1: the
+    passes recompute the score tile (2 d) in each of their 2 R + 2 passes, the value scores
+    g = dO . V (2 d) in the two vector passes that need them and in the dQ and dK passes, and
+    contract one tile (2 d) in the dV, dQ and dK passes: (18 + 4 R) d."""
+    return (18 + 4 * R) * d
+
+
+def certificate_main(args):
+    """A posteriori bias certificate on the GPU: for R = 0..r_max, eta_R of the workload's
+    inputs in fp32 (each call runs the forward and VJP at (T, R) and full backpropagation, the
+    adjoint at depth T + R, then the fixed-order norm reductions), the smallest R with
+    eta_R <= tau, and the matrix-core roofline of full backpropagation at depth T + 2, its
+    dominant part.  The oracle's certificate runs beside it on head 0."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from entropic_ot_attention_amd import binding as B
+    from entropic_ot_attention_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.dustbin:
+        raise SystemExit("the certificate runs on the banded entry points (no dustbin workload)")
+    w = w.with_(dtype="f32")               # remainders are resolved in fp32 only
+    dev = torch.device("cuda:0")
+    x = make_inputs(w)
+    Q, K, V, dO = (x[k].to(dev) for k in ("Q", "K", "V", "dO"))
+    L, rows = w.L, w.tokens
+    stream = torch.cuda.current_stream()
+    sums = torch.zeros(4, dtype=torch.float64, device=dev)
+    per_r = {}
+    selected = None
+    for R in range(0, args.r_max + 1):
+        if R == 0 and w.T == 0:
+            continue
+        prob = B.make_problem(w.bh, L, w.d, w.W, w.T, R, w.eps, torch.float32)
+        ws = B.workspace_for(prob, B.SKA_OP_TAIL_REMAINDER, dev)
+        for _ in range(args.warmup):
+            B.sinkhorn_attn_tail_remainder(prob, Q, K, V, dO, sums, ws, stream)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            B.sinkhorn_attn_tail_remainder(prob, Q, K, V, dO, sums, ws, stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        rq, fq, rk, fk = (float(v) for v in sums.cpu())
+        eta = ((rq + rk) / (fq + fk)) ** 0.5 if fq + fk > 0 else 0.0
+        per_r[R] = {"eta": eta, "ms": round(ms, 4)}
+        if selected is None and eta <= args.tau:
+            selected = R
+        del ws
+
+    # full backpropagation at depth T + 2 alone, timed kernel by kernel
+    Rf = w.T + 2
+    pf = B.make_problem(w.bh, L, w.d, w.W, 0, Rf, w.eps, torch.float32)
+    wsf = B.workspace_for(pf, B.SKA_OP_VJP, dev)
+    O = torch.empty_like(Q)
+    duals = torch.empty(w.bh, B.n_duals(Rf), rows, dtype=torch.float32, device=dev)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    B.sinkhorn_attn_fwd(pf, Q, K, V, O, duals, B.workspace_for(pf, B.SKA_OP_FWD, dev))
+    for _ in range(args.warmup):
+        B.sinkhorn_attn_vjp(pf, Q, K, V, duals, dO, dQ, dK, dV, B.SCHEDULES["one_reference"], wsf)
+    torch.cuda.synchronize()
+    B.ska_timing_enable(True)
+    for _ in range(args.steps):
+        B.sinkhorn_attn_vjp(pf, Q, K, V, duals, dO, dQ, dK, dV, B.SCHEDULES["one_reference"], wsf)
+    torch.cuda.synchronize()
+    kvjp_ms, kvjp_n = B.ska_timing_read(B.TIMED_VJP)
+    B.ska_timing_enable(False)
+    nnz = band_entries(rows, min(w.W // 2, rows)) * w.bh
+    vjp_s = kvjp_ms / args.steps / 1e3
+    flops = tail_pass_flops_per_entry(Rf, w.d) * nnz
+    tflops = flops / vjp_s / 1e12
+    roofline = {
+        "bound": "mfma",
+        "kernel": f"tail_pass_kernel, full backpropagation = adjoint at depth T + 2 = {Rf} "
+                  f"({2 * Rf + 2} passes)",
+        "achieved": round(tflops, 2),
+        "peak": MFMA_F32_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
+        "traffic": None,
+        "avg_launch_us": round(kvjp_ms / max(kvjp_n, 1) * 1e3, 2),
+        "launches_timed": kvjp_n,
+        "algorithmic_flops": flops,
+        "algorithmic_work": f"(18 + 4 x {Rf}) x {w.d} flops x {nnz} band entries per VJP",
+    }
+    out = {
+        "metric": f"bias certificate eta_R tokens/s at L={L} W={w.W} d={w.d} T={w.T}, R=2; "
+                  f"% of MFMA roofline of full backpropagation",
+        "value": round(w.batch * L / (per_r[2]["ms"] / 1e3), 1) if 2 in per_r else None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": per_r.get(2, {}).get("ms"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO)",
+        "config": {"workload": w.name + " (certified in fp32)", "batch": w.batch,
+                   "heads": w.heads, "L": L, "d": w.d, "W": w.W, "T": w.T, "epsilon": w.eps,
+                   "tau": args.tau},
+        "certificate": {"eta": {str(R): v["eta"] for R, v in per_r.items()},
+                        "ms": {str(R): v["ms"] for R, v in per_r.items()},
+                        "selected_R": selected},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(args.cpu_sample_tokens, rows)
+        Qh, Kh, Vh, dOh = (x[k][0, :n].double().numpy() for k in ("Q", "K", "V", "dO"))
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            ro = oracle.tail_remainder(Qh, Kh, Vh, dOh,
+                                       oracle.BandProblem(W=w.W, T=w.T, R=2, eps=w.eps))
+            dt = time.perf_counter() - t0
+        g = B.tail_remainder(*(t[0:1, :n].contiguous() for t in (Q, K, V, dO)), w.W, w.T, 2, w.eps)
+        out["cpu_baseline"] = {
+            "value": round(n / (w.bh * dt), 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"head 0 of {w.bh}, tokens 0..{n - 1}, R = 2 certificate (forward, tail "
+                      f"VJP and full backpropagation) in fp64 numpy, {dt:.2f} s; eta_2 oracle "
+                      f"{ro['eta']:.6e}, GPU on the same sample {g['eta']:.6e}"}
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(w, sample_tokens: int):
@@ -116,6 +251,10 @@ def main():
               "(every problem is independent; sharding over batch*heads is a design note only). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.certificate:
+        certificate_main(args)
+        return
 
     import torch
 
