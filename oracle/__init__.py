@@ -13,7 +13,7 @@ Attention: Tail-Refinement Gradients with a Gap-Aware Dustbin Bridge"
 * technical summary, German (gist.science/de), "Technische Zusammenfassung" §1-§5
 * technical summary, French (gist.science/fr), "Résumé Technique" §1-§5
 * AI-extracted summary (atlas.scime.ai), sections Approach / Key results /
-  Limitations
+  Limitations / Builds on
 
 Parity status: every function here is pinned by a CPU test against something
 other than itself (closed forms, an independent multiplicative Sinkhorn, dense
@@ -41,4 +41,9 @@ from .sinkhorn_band import (  # noqa: F401
     dependency_radius,
     sampled_rows,
     BandProblem,
+)
+from .contraction import (  # noqa: F401
+    block_layout,
+    block_diameters,
+    contraction_coefficients,
 )

@@ -7,6 +7,8 @@
   ("exact autodiff through the surrogate", the pages' validation baseline).
 * ``dense_autograd_full``: the same iteration with gradients flowing through the base steps
   as well (full backpropagation through time).
+* ``cross_ratio_diameter``: the projective diameter of a positive matrix by enumerating every
+  2 x 2 minor's log cross ratio of the exponentiated matrix (Birkhoff's definition).
 """
 
 from __future__ import annotations
@@ -93,3 +95,17 @@ def dense_autograd_full(Q, K, V, dO, W, T, R, eps):
     O = P @ Vt
     (O * dOt).sum().backward()
     return O.detach().numpy(), Qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy()
+
+
+def cross_ratio_diameter(A):
+    """max over i, i', j, j' of log(A_ij A_i'j' / (A_ij' A_i'j)) for a strictly positive A,
+    every quadruple enumerated."""
+    A = np.asarray(A, dtype=np.float64)
+    n, m = A.shape
+    best = 0.0
+    for i in range(n):
+        for i2 in range(n):
+            for j in range(m):
+                for j2 in range(m):
+                    best = max(best, math.log((A[i, j] * A[i2, j2]) / (A[i, j2] * A[i2, j])))
+    return best

@@ -58,21 +58,42 @@ TAIL_MUTATIONS = {
 }
 
 
+# mistakes in the projective contraction certificate, caught by test_oracle_contraction.py
+CONTRACTION_MUTATIONS = {
+    "diameter_with_unpaired_columns": (
+        "delta[rb, o + m] = float(np.max(diff.max(axis=2) - diff.min(axis=2)))",
+        "delta[rb, o + m] = float(np.max(S.max(axis=1)[:, None] - S.min(axis=1)[None, :]))"),
+    "block_active_one_token_too_far": (
+        "if max(r1 - 1 - c0, c1 - 1 - r0) > h:", "if max(r1 - 1 - c0, c1 - 1 - r0) > h + 1:"),
+    "coefficient_tanh_of_half": ("np.tanh(np.maximum(delta, 0.0) / 4.0)",
+                                 "np.tanh(np.maximum(delta, 0.0) / 2.0)"),
+    "diameter_misses_temperature": ("scale = 1.0 / (np.sqrt(d) * prob.eps)",
+                                    "scale = 1.0 / np.sqrt(d)"),
+}
+
+CONTRACTION_SRC = os.path.join(ROOT, "oracle", "contraction.py")
+
 CASES = [(n, "tests/test_oracle.py") for n in sorted(MUTATIONS)] + \
-        [(n, "tests/test_oracle_tail.py") for n in sorted(TAIL_MUTATIONS)]
+        [(n, "tests/test_oracle_tail.py") for n in sorted(TAIL_MUTATIONS)] + \
+        [(n, "tests/test_oracle_contraction.py") for n in sorted(CONTRACTION_MUTATIONS)]
 
 
 @pytest.mark.parametrize("name,pins", CASES, ids=[c[0] for c in CASES])
 def test_pins_catch_planted_mistake(name, pins):
-    before, after = {**MUTATIONS, **TAIL_MUTATIONS}[name]
-    src = open(SRC).read()
+    if name in CONTRACTION_MUTATIONS:
+        before, after = CONTRACTION_MUTATIONS[name]
+        path = CONTRACTION_SRC
+    else:
+        before, after = {**MUTATIONS, **TAIL_MUTATIONS}[name]
+        path = SRC
+    src = open(path).read()
     assert before in src, f"mutation anchor for {name} no longer present"
     with tempfile.TemporaryDirectory() as d:
         shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"),
                         ignore=shutil.ignore_patterns("__pycache__"))
         shutil.copytree(os.path.join(ROOT, "tests"), os.path.join(d, "tests"),
                         ignore=shutil.ignore_patterns("__pycache__", "golden"))
-        with open(os.path.join(d, "oracle", "sinkhorn_band.py"), "w") as f:
+        with open(os.path.join(d, "oracle", os.path.basename(path)), "w") as f:
             f.write(src.replace(before, after))
         r = subprocess.run([sys.executable, "-m", "pytest", pins, "-q", "-x",
                             "-p", "no:cacheprovider"], cwd=d, capture_output=True, text=True,
