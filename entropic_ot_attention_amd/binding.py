@@ -19,8 +19,9 @@ SKA_F32, SKA_BF16 = 0, 1
 SKA_ONE_REFERENCE, SKA_DIRECT_FOUR = 0, 1
 SKA_OP_FWD, SKA_OP_VJP, SKA_OP_DUSTBIN_BLOCK_FWD, SKA_OP_DUSTBIN_BLOCK_VJP = 0, 1, 2, 3
 SKA_OP_TAIL_REMAINDER = 4
+SKA_OP_CONTRACTION, SKA_OP_DUSTBIN_BLOCK_CONTRACTION = 5, 6
 SKA_OK = 0
-TIMED_STEP, TIMED_OUT, TIMED_VJP = 0, 1, 2
+TIMED_STEP, TIMED_OUT, TIMED_VJP, TIMED_CERT = 0, 1, 2, 3
 
 SCHEDULES = {"one_reference": SKA_ONE_REFERENCE, "direct_four": SKA_DIRECT_FOUR}
 
@@ -28,7 +29,9 @@ SCHEDULES = {"one_reference": SKA_ONE_REFERENCE, "direct_four": SKA_DIRECT_FOUR}
 EXPORTS = (
     "ska_workspace_bytes", "sinkhorn_attn_fwd", "sinkhorn_attn_vjp",
     "sinkhorn_attn_dustbin_block_fwd", "sinkhorn_attn_dustbin_block_vjp",
-    "sinkhorn_attn_tail_remainder", "ska_status_string", "ska_last_error", "ska_timing_enable", "ska_timing_read",
+    "sinkhorn_attn_tail_remainder", "ska_contraction_layout",
+    "sinkhorn_attn_contraction_certificate", "sinkhorn_attn_dustbin_block_contraction_certificate",
+    "ska_status_string", "ska_last_error", "ska_timing_enable", "ska_timing_read",
 )
 
 
@@ -56,9 +59,17 @@ def _load():
     lib.sinkhorn_attn_vjp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, st, vp, sz, vp]
     lib.sinkhorn_attn_dustbin_block_vjp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, st, vp, sz, vp]
     lib.sinkhorn_attn_tail_remainder.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    i32 = ctypes.c_int32
+    lib.ska_contraction_layout.argtypes = [P, st, i32, ctypes.POINTER(ctypes.c_int64),
+                                           ctypes.POINTER(i32)]
+    lib.sinkhorn_attn_contraction_certificate.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
+    lib.sinkhorn_attn_dustbin_block_contraction_certificate.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
     for name in ("ska_workspace_bytes", "sinkhorn_attn_fwd", "sinkhorn_attn_dustbin_block_fwd",
                  "sinkhorn_attn_vjp", "sinkhorn_attn_dustbin_block_vjp",
-                 "sinkhorn_attn_tail_remainder", "ska_timing_enable", "ska_timing_read"):
+                 "sinkhorn_attn_tail_remainder", "ska_contraction_layout",
+                 "sinkhorn_attn_contraction_certificate",
+                 "sinkhorn_attn_dustbin_block_contraction_certificate",
+                 "ska_timing_enable", "ska_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ska_status_string.argtypes = [ctypes.c_int]
     lib.ska_status_string.restype = ctypes.c_char_p
@@ -163,6 +174,31 @@ def sinkhorn_attn_tail_remainder(problem, Q, K, V, dO, sums, workspace, stream=N
            "sinkhorn_attn_tail_remainder")
 
 
+def ska_contraction_layout(problem, op: int, block: int):
+    """(nb, m) of the contraction certificate's [bh][nb][2 m + 1] outputs."""
+    nb = ctypes.c_int64(0)
+    m = ctypes.c_int32(0)
+    _check(lib.ska_contraction_layout(ctypes.byref(problem), op, block, ctypes.byref(nb),
+                                      ctypes.byref(m)), "ska_contraction_layout")
+    return nb.value, m.value
+
+
+def sinkhorn_attn_contraction_certificate(problem, block, Q, K, delta, kappa=None, delta_max=None,
+                                          stream=None):
+    _check(lib.sinkhorn_attn_contraction_certificate(
+        ctypes.byref(problem), block, _ptr(Q, "Q"), _ptr(K, "K"), _ptr(delta, "delta"),
+        _ptr(kappa, "kappa"), _ptr(delta_max, "delta_max"), _stream(stream)),
+        "sinkhorn_attn_contraction_certificate")
+
+
+def sinkhorn_attn_dustbin_block_contraction_certificate(problem, block, Q, K, delta, kappa=None,
+                                                        delta_max=None, stream=None):
+    _check(lib.sinkhorn_attn_dustbin_block_contraction_certificate(
+        ctypes.byref(problem), block, _ptr(Q, "Q"), _ptr(K, "K"), _ptr(delta, "delta"),
+        _ptr(kappa, "kappa"), _ptr(delta_max, "delta_max"), _stream(stream)),
+        "sinkhorn_attn_dustbin_block_contraction_certificate")
+
+
 def ska_timing_enable(on: bool):
     _check(lib.ska_timing_enable(1 if on else 0), "ska_timing_enable")
 
@@ -263,3 +299,26 @@ def select_tail_depth(Q, K, V, dO, W: int, T: int, epsilon: float = 1.0, tau: fl
         if etas[R] <= tau:
             return R, etas
     return None, etas
+
+
+def contraction_certificate(Q, K, W: int, epsilon: float = 1.0, block: int = 16,
+                            dustbin: bool = False, stream=None):
+    """Projective diameters Delta and Birkhoff-Hopf coefficients kappa of every active block pair,
+    fp32 [bh, nb, 2 m + 1] (-1 where a block pair is not active), and the largest Delta per
+    problem [bh].  Q, K: [bh, tokens, d] (dustbin: the dustbin token as the last row)."""
+    if Q.dim() != 3 or Q.shape != K.shape or Q.dtype != K.dtype:
+        raise ValueError("Q and K must share one shape [bh, tokens, d] and dtype")
+    bh, rows, d = Q.shape
+    L = rows - 1 if dustbin else rows
+    if L < 0:
+        raise ValueError("dustbin inputs need the dustbin row")
+    prob = make_problem(bh, L, d, W, 1, 2, epsilon, Q.dtype)      # T and R do not enter
+    op = SKA_OP_DUSTBIN_BLOCK_CONTRACTION if dustbin else SKA_OP_CONTRACTION
+    nb, m = ska_contraction_layout(prob, op, block)
+    delta = torch.empty(bh, nb, 2 * m + 1, dtype=torch.float32, device=Q.device)
+    kappa = torch.empty_like(delta)
+    delta_max = torch.empty(bh, dtype=torch.float32, device=Q.device)
+    fn = (sinkhorn_attn_dustbin_block_contraction_certificate if dustbin
+          else sinkhorn_attn_contraction_certificate)
+    fn(prob, block, Q, K, delta, kappa, delta_max, stream)
+    return delta, kappa, delta_max

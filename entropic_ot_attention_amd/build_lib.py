@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libsinkhorn_attn.so")
-SOURCES = ["ska_kernels.hip", "ska_fused.hip", "ska_vjp_stream.hip", "ska_wide.hip", "ska_capi.cpp"]
+SOURCES = ["ska_kernels.hip", "ska_fused.hip", "ska_vjp_stream.hip", "ska_wide.hip",
+           "ska_contraction.hip", "ska_capi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -28,8 +29,8 @@ struct Timing {
   bool on = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[ska::kTimedKinds];
   std::vector<std::pair<hipEvent_t, hipEvent_t>> free_pairs;
-  double total_ms[ska::kTimedKinds] = {0, 0, 0};
-  int64_t launches[ska::kTimedKinds] = {0, 0, 0};
+  double total_ms[ska::kTimedKinds] = {};
+  int64_t launches[ska::kTimedKinds] = {};
 };
 thread_local Timing g_timing;
 
@@ -76,8 +77,9 @@ ska_status check_problem(const ska_problem* p, ska_op op, Plan* out) {
     return fail(SKA_ERR_INVALID, "epsilon must be finite and > 0");
   if (p->dtype != SKA_F32 && p->dtype != SKA_BF16) return fail(SKA_ERR_INVALID, "unknown dtype");
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
-  const bool dustbin = (op == SKA_OP_DUSTBIN_BLOCK_FWD || op == SKA_OP_DUSTBIN_BLOCK_VJP);
-  if (op < SKA_OP_FWD || op > SKA_OP_TAIL_REMAINDER) return fail(SKA_ERR_INVALID, "unknown op");
+  const bool dustbin = (op == SKA_OP_DUSTBIN_BLOCK_FWD || op == SKA_OP_DUSTBIN_BLOCK_VJP ||
+                        op == SKA_OP_DUSTBIN_BLOCK_CONTRACTION);
+  if (op < SKA_OP_FWD || op > SKA_OP_DUSTBIN_BLOCK_CONTRACTION) return fail(SKA_ERR_INVALID, "unknown op");
   if (p->R < 0) return fail(SKA_ERR_INVALID, "R must be >= 0");
   if (p->R == 0 && p->T < 1)
     return fail(SKA_ERR_INVALID, "R = 0 needs T >= 1: the output plan's duals come from the base");
@@ -120,6 +122,7 @@ RemLayout rem_layout(const Plan& pl);
 size_t workspace_for(const Plan& pl, ska_op op) {
   if (pl.empty) return 0;
   if (op == SKA_OP_TAIL_REMAINDER) return rem_layout(pl).total;
+  if (op == SKA_OP_CONTRACTION || op == SKA_OP_DUSTBIN_BLOCK_CONTRACTION) return 0;
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   const int64_t vs = pl.g.bh * (int64_t)pl.g.Lpad;
   if (vjp && pl.R != 2) return (size_t)(ska::tail_vecs(pl.R) * vs) * sizeof(float);
@@ -567,6 +570,89 @@ ska_status sinkhorn_attn_tail_remainder(const ska_problem* p, const void* Q, con
   if (e == hipSuccess) e = ska::launch_sq_diff(pl.elt, w + L.dk_f, w + L.dk_r, n, part, sums + 2, stream);
   if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
   return SKA_OK;
+}
+
+namespace {
+
+ska_status contraction_layout(const ska_problem* p, ska_op op, int32_t block, Plan* pl,
+                              int64_t* nb, int32_t* m) {
+  if (op != SKA_OP_CONTRACTION && op != SKA_OP_DUSTBIN_BLOCK_CONTRACTION)
+    return fail(SKA_ERR_INVALID, "not a contraction-certificate op");
+  SKA_TRY(check_problem(p, op, pl));
+  if (block != 16 && block != 32 && block != 64 && block != 128)
+    return fail(SKA_ERR_INVALID, "block must be 16, 32, 64 or 128 tokens");
+  const int64_t n = (pl->g.Lr + block - 1) / block;
+  *nb = n;
+  const int64_t mm = pl->g.h / block;
+  *m = (int32_t)std::max<int64_t>(0, std::min<int64_t>(mm, n - 1));
+  if (n * (2 * (int64_t)*m + 1) >= (int64_t(1) << 31))
+    return fail(SKA_ERR_UNSUPPORTED, "more than 2^31 block pairs per problem");
+  return SKA_OK;
+}
+
+ska_status run_contraction(const ska_problem* p, ska_op op, int32_t block, const void* Q,
+                           const void* K, float* delta, float* kappa, float* delta_max,
+                           hipStream_t st) {
+  Plan pl;
+  int64_t nb = 0;
+  int32_t m = 0;
+  SKA_TRY(contraction_layout(p, op, block, &pl, &nb, &m));
+  if (pl.empty) return SKA_OK;
+  SKA_TRY(check_ptr(Q, "Q"));
+  SKA_TRY(check_ptr(K, "K"));
+  if (!delta || (reinterpret_cast<uintptr_t>(delta) & 3u) != 0)
+    return fail(SKA_ERR_INVALID, "delta is NULL or misaligned");
+  if (kappa && (reinterpret_cast<uintptr_t>(kappa) & 3u) != 0)
+    return fail(SKA_ERR_INVALID, "kappa misaligned");
+  if (delta_max && (reinterpret_cast<uintptr_t>(delta_max) & 3u) != 0)
+    return fail(SKA_ERR_INVALID, "delta_max misaligned");
+  if (delta_max) {
+    hipError_t e = ska::launch_fill(delta_max, pl.g.bh, -1.f, st);
+    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+  }
+  ska::ContractionArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.delta = delta;
+  a.kappa = kappa;
+  a.delta_max = delta_max;
+  a.bh = pl.g.bh;
+  a.Lr = pl.g.Lr;
+  a.h = pl.g.h;
+  a.B = block;
+  a.nb = (int)nb;
+  a.m = m;
+  a.s = pl.g.s;
+  SKA_LAUNCH(ska::kTimedCert, st, ska::launch_contraction(pl.elt, a, st));
+  return SKA_OK;
+}
+
+}  // namespace
+
+ska_status ska_contraction_layout(const ska_problem* p, ska_op op, int32_t block, int64_t* nb,
+                                  int32_t* m) {
+  g_err.clear();
+  if (!nb || !m) return fail(SKA_ERR_INVALID, "nb and m must not be NULL");
+  Plan pl;
+  return contraction_layout(p, op, block, &pl, nb, m);
+}
+
+ska_status sinkhorn_attn_contraction_certificate(const ska_problem* p, int32_t block,
+                                                 const void* Q, const void* K, float* delta,
+                                                 float* kappa, float* delta_max,
+                                                 hipStream_t stream) {
+  g_err.clear();
+  return run_contraction(p, SKA_OP_CONTRACTION, block, Q, K, delta, kappa, delta_max, stream);
+}
+
+ska_status sinkhorn_attn_dustbin_block_contraction_certificate(const ska_problem* p,
+                                                               int32_t block, const void* Q,
+                                                               const void* K, float* delta,
+                                                               float* kappa, float* delta_max,
+                                                               hipStream_t stream) {
+  g_err.clear();
+  return run_contraction(p, SKA_OP_DUSTBIN_BLOCK_CONTRACTION, block, Q, K, delta, kappa,
+                         delta_max, stream);
 }
 
 const char* ska_status_string(ska_status s) {

@@ -150,7 +150,7 @@ inline int wide_window_tiles(int Lr, int h) {
   return (int)(all < band ? all : band);
 }
 
-enum TimedKernel : int { kTimedStep = 0, kTimedOut = 1, kTimedVjp = 2, kTimedKinds = 3 };
+enum TimedKernel : int { kTimedStep = 0, kTimedOut = 1, kTimedVjp = 2, kTimedCert = 3, kTimedKinds = 4 };
 
 // Launchers (return the hipGetLastError() of their launches).  `elt` is 0 for fp32, 1 for bf16.
 hipError_t launch_fill(float* p, int64_t n, float value, hipStream_t st);
@@ -180,4 +180,19 @@ hipError_t launch_sq_diff(int elt, const void* a, const void* b, int64_t n, doub
 // 3 (D: du^(a)), 4 (dQ), 5 (dK).  R = 0 runs A (dV only), dQ and dK.
 hipError_t launch_tail_prep(const float* duals, float* ws, int R, const Geometry& g, hipStream_t st);
 hipError_t launch_tail_pass(int elt, int pass, const WideArgs& a, hipStream_t st);
+
+// Projective contraction certificate: the diameter (and Birkhoff-Hopf coefficient) of every active
+// B x B block pair, [bh][nb][2 m + 1] by (row block, column-block offset + m), -1 where no block
+// pair is active; delta_max[b] (initialised to -1 by the caller) receives the largest diameter.
+struct ContractionArgs {
+  const void* Q;
+  const void* K;
+  float* delta;
+  float* kappa;            // may be null
+  float* delta_max;        // may be null
+  int64_t bh;
+  int Lr, h, B, nb, m;
+  float s;                 // 1 / (sqrt(d) epsilon)
+};
+hipError_t launch_contraction(int elt, const ContractionArgs& a, hipStream_t st);
 }  // namespace ska

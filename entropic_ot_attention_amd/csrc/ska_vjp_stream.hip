@@ -6,7 +6,7 @@
 // P^(a,b) = P^(2,2) exp(u^(a) - u^(2)) exp(v^(b) - v^(2))], with P22 = exp(S + u2 + v2),
 // g_ij = dO_i . V_j and e^{du1} = exp(u1 - u2), e^{dv_b} = exp(v_b - v2), in four passes:
 //
-//   0 (owns queries)  forward output O_i = sum_j P22_ij V_j   [spec output: plan x V]
+//   0 (owns queries)  forward output O_i = sum_j P22_ij V_j   [the reference plan applied to V]
 //   1 (owns keys)     dv2_j = sum_i P22 g
 //   2 (owns queries)  du2_i = sum_j P22 (g - dv2_j);  per-segment column sums sum_i P22 du2_i
 //   3 (owns queries)  dv1_j = -e^{dv1_j} (column sums)  (finished for the window on arrival)

@@ -16,10 +16,10 @@
 // row-normalised plan; wide_finish_kernel adds each column's partials in a fixed order and
 // finishes the column update, exactly where a column's mass underflows.
 //
-// Output and VJP [spec output P^(2,2) V; abstract and technical summaries §2.2: the R = 2
-// score cotangent as the reference plan tile times a modifier field]: wide_pass_kernel runs the
-// output and five VJP passes, each owning the side it reduces over, so no pass needs partial sums
-// across workgroups:
+// Output and VJP [output: the reference plan P^(2,2) applied to V; abstract and technical
+// summaries §2.2: the R = 2 score cotangent as the reference plan tile times a modifier field]:
+// wide_pass_kernel runs the output and five VJP passes, each owning the side it reduces over, so
+// no pass needs partial sums across workgroups:
 //   out (owns queries)  O_i = sum_j P22_ij V_j
 //   A   (owns keys)     dv2_j = sum_i P22 g,  dV_j = sum_i P22_ij dO_i
 //   B   (owns queries)  du2_i = sum_j P22 (g - dv2_j)

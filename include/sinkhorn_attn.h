@@ -73,7 +73,9 @@ typedef enum {
   SKA_OP_VJP = 1,
   SKA_OP_DUSTBIN_BLOCK_FWD = 2,
   SKA_OP_DUSTBIN_BLOCK_VJP = 3,
-  SKA_OP_TAIL_REMAINDER = 4
+  SKA_OP_TAIL_REMAINDER = 4,
+  SKA_OP_CONTRACTION = 5,                /* projective contraction certificate, band support   */
+  SKA_OP_DUSTBIN_BLOCK_CONTRACTION = 6   /* the same on the dustbin_block (dense) support      */
 } ska_op;
 
 typedef struct {
@@ -155,6 +157,37 @@ ska_status sinkhorn_attn_tail_remainder(const ska_problem* p, const void* Q, con
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* Projective contraction certificate of the Sinkhorn map's active blocks (technical summaries
+ * §2.4: Hilbert's projective metric shows that strictly positive active blocks of the Sinkhorn
+ * map are contractions; atlas.scime.ai, Builds on: Birkhoff-Hopf contraction).
+ * The Lr tokens (L, or L + 1 for the dustbin_block entry point) are cut into nb = ceil(Lr / block)
+ * blocks of `block` tokens (16, 32, 64 or 128; the last block ragged).  A block pair (row block
+ * rb, column block cb = rb + o) is active when every pair in it lies on the support (|i - j| <=
+ * W/2; every pair for the dustbin_block support), so its Gibbs kernel exp(S) is strictly
+ * positive.  For each active pair the entry writes its projective diameter
+ *   Delta = max over rows i, i' and columns j, j' of  S_ij + S_i'j' - S_ij' - S_i'j
+ * (the largest log cross ratio of exp(S), S = q.k / (sqrt(d) epsilon) in fp32) and, if kappa is
+ * not NULL, its Birkhoff-Hopf coefficient kappa = tanh(Delta / 4) < 1: a log-domain row or column
+ * half-step restricted to the block shrinks the oscillation of a dual difference by at least
+ * kappa, a full step by kappa^2.  Block pairs that are not active (or lie past either end) get
+ * -1 in both outputs.  Layout of delta and kappa: fp32 [bh][nb][2 m + 1], entry (b, rb, o + m),
+ * with m = min(floor(h / block), nb - 1), h the support half-width (ska_contraction_layout
+ * returns nb and m).  If delta_max is not NULL it receives, per problem b, the largest Delta over
+ * the active pairs, or -1 if there is none.  T and R do not enter (they must still be valid).
+ * Only Q and K are read; no workspace.  An empty problem writes nothing. */
+ska_status ska_contraction_layout(const ska_problem* p, ska_op op, int32_t block, int64_t* nb,
+                                  int32_t* m);
+ska_status sinkhorn_attn_contraction_certificate(const ska_problem* p, int32_t block,
+                                                 const void* Q, const void* K, float* delta,
+                                                 float* kappa, float* delta_max,
+                                                 hipStream_t stream);
+/* The same on the dustbin_block support: Q, K hold L + 1 rows, the dustbin token last. */
+ska_status sinkhorn_attn_dustbin_block_contraction_certificate(const ska_problem* p,
+                                                               int32_t block, const void* Q,
+                                                               const void* K, float* delta,
+                                                               float* kappa, float* delta_max,
+                                                               hipStream_t stream);
+
 /* Static string for a status code. */
 const char* ska_status_string(ska_status s);
 
@@ -162,8 +195,9 @@ const char* ska_status_string(ska_status s);
 const char* ska_last_error(void);
 
 /* Kernel timing for measurement.  While enabled, every launch of the kernel family `kernel`
- * (0: forward Sinkhorn step, 1: forward output, 2: VJP passes) on the calling thread is
- * bracketed by HIP events on its own stream; ska_timing_read() synchronises on those events
+ * (0: forward Sinkhorn step, 1: forward output, 2: VJP passes, 3: contraction certificate) on the
+ * calling thread is bracketed by HIP events on its own stream; ska_timing_read() synchronises on
+ * those events
  * and returns the summed kernel milliseconds and the launch count since ska_timing_enable(1).
  * Enabling creates HIP events (no device memory); disabling destroys them. */
 ska_status ska_timing_enable(int on);

@@ -258,3 +258,31 @@ def test_status_strings():
     assert B.ska_status_string(0) == "ok"
     assert B.ska_status_string(-3) == "workspace too small"
     assert B.ska_status_string(42) == "unknown status"
+
+
+def test_contraction_layout_and_checks():
+    """The certificate's [bh][nb][2 m + 1] layout: nb = ceil(Lr / block), m = min(h // block,
+    nb - 1), the same as the oracle's block_layout; the dustbin entry point counts L + 1 tokens on
+    the dense support; bad blocks and null outputs are rejected before any launch."""
+    import oracle
+    for L, W, blk in ((100, 16, 16), (1000, 256, 16), (1000, 256, 64), (37, 0, 16), (5000, 4000, 128)):
+        nb, m = B.ska_contraction_layout(_prob(L=L, W=W), B.SKA_OP_CONTRACTION, blk)
+        assert (nb, m) == oracle.block_layout(L, min(W // 2, L), blk)
+    nb, m = B.ska_contraction_layout(_prob(L=4096, W=256), B.SKA_OP_DUSTBIN_BLOCK_CONTRACTION, 16)
+    assert (nb, m) == (257, 256) == oracle.block_layout(4097, 4096, 16)
+    for bad in (0, 8, 48, 256):
+        with pytest.raises(B.SinkhornAttnError):
+            B.ska_contraction_layout(_prob(), B.SKA_OP_CONTRACTION, bad)
+    with pytest.raises(B.SinkhornAttnError):
+        B.ska_contraction_layout(_prob(), B.SKA_OP_FWD, 16)
+    st, n = _ws_bytes(_prob(), B.SKA_OP_CONTRACTION)
+    assert st == 0 and n == 0
+    prob = _prob()
+    V = ctypes.c_void_p
+    f = B.lib.sinkhorn_attn_contraction_certificate
+    assert f(ctypes.byref(prob), 16, V(FAKE), V(FAKE), None, None, None, None) == -1
+    assert f(ctypes.byref(prob), 16, V(FAKE), V(FAKE + 4), V(FAKE), None, None, None) == -1
+    assert f(ctypes.byref(prob), 24, V(FAKE), V(FAKE), V(FAKE), None, None, None) == -1
+    assert f(ctypes.byref(prob), 16, V(FAKE), V(FAKE), V(FAKE + 2), None, None, None) == -1
+    empty = _prob(bh=0)
+    assert f(ctypes.byref(empty), 16, None, None, None, None, None, None) == 0
