@@ -82,6 +82,10 @@ def parse():
                     help="time the a posteriori bias certificate eta_R (fp32 inputs) for "
                          "R = 0..--r-max on the workload instead of the forward + VJP step")
     ap.add_argument("--r-max", type=int, default=4)
+    ap.add_argument("--contraction", action="store_true",
+                    help="time the projective contraction certificate of the workload's active "
+                         "blocks instead of the forward + VJP step")
+    ap.add_argument("--block", type=int, default=16)
     ap.add_argument("--tau", type=float, default=1e-5)
     return ap.parse_args()
 
@@ -92,6 +96,116 @@ def tail_pass_flops_per_entry(R: int, d: int) -> int:
     g = dO . V (2 d) in the two vector passes that need them and in the dQ and dK passes, and
     contract one tile (2 d) in the dV, dQ and dK passes: (18 + 4 R) d."""
     return (18 + 4 * R) * d
+
+
+def contraction_main(args):
+    """Projective contraction certificate on the GPU: the diameters and Birkhoff-Hopf coefficients
+    of every active block pair of the workload, timed over --steps calls; the roofline is the
+    certificate kernel's VALU work (B (B - 1) / 2 row pairs x B columns x 2 operations per active
+    block pair: a subtraction, and half of a 3-input maximum and of a 3-input minimum) against the
+    MI355X VALU peak, with its HBM floor (Q and K read once) beside it.
+    The oracle's block_diameters runs beside it on a sample."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from entropic_ot_attention_amd import binding as B
+    from entropic_ot_attention_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    blk = args.block
+    dev = torch.device("cuda:0")
+    x = make_inputs(w, with_cotangent=False)
+    Q, K = x["Q"].to(dev), x["K"].to(dev)
+    rows = w.tokens
+    prob = B.make_problem(w.bh, w.L, w.d, w.W, 1, 2, w.eps, w.torch_dtype)
+    op = B.SKA_OP_DUSTBIN_BLOCK_CONTRACTION if w.dustbin else B.SKA_OP_CONTRACTION
+    nb, m = B.ska_contraction_layout(prob, op, blk)
+    delta = torch.empty(w.bh, nb, 2 * m + 1, dtype=torch.float32, device=dev)
+    kappa = torch.empty_like(delta)
+    dmax = torch.empty(w.bh, dtype=torch.float32, device=dev)
+    fn = (B.sinkhorn_attn_dustbin_block_contraction_certificate if w.dustbin
+          else B.sinkhorn_attn_contraction_certificate)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fn(prob, blk, Q, K, delta, kappa, dmax, stream)
+    torch.cuda.synchronize()
+    B.ska_timing_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        fn(prob, blk, Q, K, delta, kappa, dmax, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    k_ms, k_n = B.ska_timing_read(B.TIMED_CERT)
+    B.ska_timing_enable(False)
+    d = delta.cpu().double().numpy()
+    act = d >= 0
+    # VALU work per active block pair: nr (nr - 1) / 2 row pairs x nc columns x 2 operations
+    sizes = np.minimum(blk, rows - blk * np.arange(nb))
+    o = np.arange(-m, m + 1)
+    nr = sizes[:, None]
+    cb = np.arange(nb)[:, None] + o[None, :]
+    nc = np.where((cb >= 0) & (cb < nb), sizes[np.clip(cb, 0, nb - 1)], 0)
+    ops = float((act * (2.0 * nr * (nr - 1) / 2 * nc)[None]).sum())
+    launch_s = k_ms / max(k_n, 1) / 1e3
+    elt = 2 if w.dtype == "bf16" else 4
+    hbm_bytes = 2 * w.bh * rows * w.d * elt + 2 * delta.numel() * 4
+    achieved = ops / launch_s / 1e12
+    peak = VALU_LANE_OPS_PER_S / 1e12
+    kap = np.tanh(d[act] / 4)
+    out = {
+        "metric": f"projective contraction certificate tokens/s at L={w.L} W={w.W} d={w.d}, "
+                  f"block {blk}; % of VALU roofline",
+        "value": round(w.batch * w.L / (call_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(call_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "L": w.L, "d": w.d,
+                   "W": w.W, "epsilon": w.eps, "block": blk},
+        "certificate": {"active_block_pairs": int(act.sum()),
+                        "delta_max": float(d[act].max()) if act.any() else None,
+                        "delta_median": float(np.median(d[act])) if act.any() else None,
+                        "kappa_max": float(kap.max()) if act.any() else None,
+                        "kappa_median": float(np.median(kap)) if act.any() else None},
+        "roofline": {
+            "bound": "alu",
+            "kernel": f"contraction_kernel<{w.dtype}, {blk}>",
+            "achieved": round(achieved, 3),
+            "peak": round(peak, 3),
+            "unit": "T VALU lane-ops/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "avg_launch_us": round(launch_s * 1e6, 2),
+            "launches_timed": k_n,
+            "algorithmic_work": f"{ops:.4g} lane-ops (2 per row pair and column of each active "
+                                f"block pair)",
+            "hbm_floor_us": round(hbm_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(args.cpu_sample_tokens, rows)
+        n -= n % blk if n > blk else 0
+        Qh, Kh = (x[k][0, :n].double().numpy() for k in ("Q", "K"))
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.block_diameters(Qh, Kh, oracle.BandProblem(W=w.W, T=1, R=2, eps=w.eps), blk,
+                                   w.dustbin)
+            dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(n / (w.bh * dt), 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"head 0 of {w.bh}, tokens 0..{n - 1}, block diameters in fp64 numpy, "
+                      f"{dt:.2f} s; tokens/s = tokens / ({w.bh} heads x time)"}
+    print(json.dumps(out), flush=True)
 
 
 def certificate_main(args):
@@ -254,6 +368,9 @@ def main():
 
     if args.certificate:
         certificate_main(args)
+        return
+    if args.contraction:
+        contraction_main(args)
         return
 
     import torch

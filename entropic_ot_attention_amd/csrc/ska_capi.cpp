@@ -606,10 +606,6 @@ ska_status run_contraction(const ska_problem* p, ska_op op, int32_t block, const
     return fail(SKA_ERR_INVALID, "kappa misaligned");
   if (delta_max && (reinterpret_cast<uintptr_t>(delta_max) & 3u) != 0)
     return fail(SKA_ERR_INVALID, "delta_max misaligned");
-  if (delta_max) {
-    hipError_t e = ska::launch_fill(delta_max, pl.g.bh, -1.f, st);
-    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
-  }
   ska::ContractionArgs a{};
   a.Q = Q;
   a.K = K;

@@ -287,6 +287,15 @@ __device__ __forceinline__ float swap16_sum(float a, float b) {
 __device__ __forceinline__ float lane_group_sum(float x) {
   return swap16_sum(swap32_sum(x, x), swap32_sum(x, x));
 }
+// Maximum over the 64 lanes of a wave, result in every lane: DPP within each 16-lane row, then
+// the two lane swaps across rows.
+__device__ __forceinline__ float wave_max(float x) {
+  x = row16_max(x);
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
 
 __device__ __forceinline__ int floor_div(int a, int b) { return (a >= 0) ? a / b : -((-a + b - 1) / b); }
 

@@ -183,7 +183,7 @@ hipError_t launch_tail_pass(int elt, int pass, const WideArgs& a, hipStream_t st
 
 // Projective contraction certificate: the diameter (and Birkhoff-Hopf coefficient) of every active
 // B x B block pair, [bh][nb][2 m + 1] by (row block, column-block offset + m), -1 where no block
-// pair is active; delta_max[b] (initialised to -1 by the caller) receives the largest diameter.
+// pair is active; delta_max[b], if given, the largest entry of problem b (-1 if none is active).
 struct ContractionArgs {
   const void* Q;
   const void* K;
