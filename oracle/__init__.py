@@ -42,6 +42,11 @@ from .sinkhorn_band import (  # noqa: F401
     sampled_rows,
     BandProblem,
 )
+from .training import (  # noqa: F401
+    TrainConfig,
+    reconstruction_step,
+    reconstruction_loss,
+)
 from .contraction import (  # noqa: F401
     block_layout,
     block_diameters,

@@ -9,6 +9,8 @@
   as well (full backpropagation through time).
 * ``cross_ratio_diameter``: the projective diameter of a positive matrix by enumerating every
   2 x 2 minor's log cross ratio of the exponentiated matrix (Birkhoff's definition).
+* ``dense_reconstruction_grads``: the masked-reconstruction model around the attention layer in
+  dense torch float64, its stopped-base surrogate differentiated by torch autograd.
 """
 
 from __future__ import annotations
@@ -109,3 +111,47 @@ def cross_ratio_diameter(A):
                 for j2 in range(m):
                     best = max(best, math.log((A[i, j] * A[i2, j2]) / (A[i, j2] * A[i2, j])))
     return best
+
+
+def _dense_surrogate_heads(Q, K, V, W, T, R, eps):
+    """Stopped-base tail surrogate for [n, L, d] tensors in the autograd graph: O = P^(R,R) V."""
+    n, L, d = Q.shape
+    idx = torch.arange(L)
+    band = (idx[:, None] - idx[None, :]).abs() <= W // 2
+    S = (Q @ K.transpose(1, 2)) / (math.sqrt(d) * eps)
+    S = S.masked_fill(~band, float("-inf"))
+    with torch.no_grad():
+        u = torch.zeros(n, L, dtype=S.dtype)
+        v = torch.zeros(n, L, dtype=S.dtype)
+        for _ in range(T):
+            u = -torch.logsumexp(S + v[:, None, :], dim=2)
+            v = -torch.logsumexp(S + u[:, :, None], dim=1)
+    u, v = u.detach(), v.detach()
+    for _ in range(R):
+        u = -torch.logsumexp(S + v[:, None, :], dim=2)
+        v = -torch.logsumexp(S + u[:, :, None], dim=1)
+    P = torch.exp(S + u[:, :, None] + v[:, None, :])
+    return P @ V
+
+
+def dense_reconstruction_grads(params, X, mask, heads, W, T, R, eps):
+    """(loss, (dWq, dWk, dWv, dWo)) of the masked-reconstruction model: masked tokens zeroed in
+    the input, Q/K/V projections, per-head stopped-base Sinkhorn attention, output projection,
+    mean squared error over the masked tokens' D features; torch float64 autograd."""
+    Ws = [torch.tensor(np.asarray(w, np.float64), requires_grad=True) for w in params]
+    Xt = torch.tensor(np.asarray(X, np.float64))
+    m = torch.tensor(np.asarray(mask, np.float64))
+    B, L, D = Xt.shape
+    d = D // heads
+    Xin = Xt * (1 - m)[..., None]
+
+    def heads_of(Z):
+        return Z.reshape(B, L, heads, d).permute(0, 2, 1, 3).reshape(B * heads, L, d)
+
+    Q, K, V = (heads_of(Xin @ Ws[k]) for k in range(3))
+    O = _dense_surrogate_heads(Q, K, V, W, T, R, eps)
+    O = O.reshape(B, heads, L, d).permute(0, 2, 1, 3).reshape(B, L, D)
+    Y = O @ Ws[3]
+    loss = (((Y - Xt) * m[..., None]) ** 2).sum() / (m.sum() * D)
+    loss.backward()
+    return float(loss.detach()), tuple(w.grad.numpy() for w in Ws)

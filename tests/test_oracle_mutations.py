@@ -73,9 +73,24 @@ CONTRACTION_MUTATIONS = {
 
 CONTRACTION_SRC = os.path.join(ROOT, "oracle", "contraction.py")
 
+# mistakes in the training step, caught by test_oracle_training.py
+TRAINING_MUTATIONS = {
+    "training_input_not_masked": ("    Xin = X * (1.0 - mask)[..., None]\n    Q, K, V = Xin @ Wq",
+                                  "    Xin = X\n    Q, K, V = Xin @ Wq"),
+    "training_dWo_transposed": ("dWo = O.reshape(-1, D).T @ dY.reshape(-1, D)",
+                                "dWo = (O.reshape(-1, D).T @ dY.reshape(-1, D)).T"),
+    "training_loss_gradient_not_halved": ("dY = 2.0 * diff / n", "dY = diff / n"),
+    "training_heads_merged_wrong": (
+        "    return Xh.transpose(0, 2, 1, 3).reshape(B, L, H * d)",
+        "    return Xh.transpose(0, 2, 3, 1).reshape(B, L, H * d)"),
+}
+
+TRAINING_SRC = os.path.join(ROOT, "oracle", "training.py")
+
 CASES = [(n, "tests/test_oracle.py") for n in sorted(MUTATIONS)] + \
         [(n, "tests/test_oracle_tail.py") for n in sorted(TAIL_MUTATIONS)] + \
-        [(n, "tests/test_oracle_contraction.py") for n in sorted(CONTRACTION_MUTATIONS)]
+        [(n, "tests/test_oracle_contraction.py") for n in sorted(CONTRACTION_MUTATIONS)] + \
+        [(n, "tests/test_oracle_training.py") for n in sorted(TRAINING_MUTATIONS)]
 
 
 @pytest.mark.parametrize("name,pins", CASES, ids=[c[0] for c in CASES])
@@ -83,6 +98,9 @@ def test_pins_catch_planted_mistake(name, pins):
     if name in CONTRACTION_MUTATIONS:
         before, after = CONTRACTION_MUTATIONS[name]
         path = CONTRACTION_SRC
+    elif name in TRAINING_MUTATIONS:
+        before, after = TRAINING_MUTATIONS[name]
+        path = TRAINING_SRC
     else:
         before, after = {**MUTATIONS, **TAIL_MUTATIONS}[name]
         path = SRC
