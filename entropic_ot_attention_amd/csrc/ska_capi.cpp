@@ -4,7 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdint>
 #include <string>
 #include <utility>
@@ -23,20 +25,23 @@ ska_status fail(ska_status s, const std::string& msg) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// optional per-launch timing with HIP events
+// optional per-launch timing with HIP events, process-wide (launches from any thread, e.g. an
+// autograd engine's backward thread, are counted); the lock is taken only while timing is on
 // ---------------------------------------------------------------------------------------------
 struct Timing {
-  bool on = false;
+  std::atomic<bool> on{false};
+  std::mutex mu;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[ska::kTimedKinds];
   std::vector<std::pair<hipEvent_t, hipEvent_t>> free_pairs;
   double total_ms[ska::kTimedKinds] = {};
   int64_t launches[ska::kTimedKinds] = {};
 };
-thread_local Timing g_timing;
+Timing g_timing;
 
 std::pair<hipEvent_t, hipEvent_t> timing_begin(int kind, hipStream_t st) {
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
-  if (!g_timing.on) return ev;
+  if (!g_timing.on.load(std::memory_order_relaxed)) return ev;
+  std::lock_guard<std::mutex> lock(g_timing.mu);
   if (!g_timing.free_pairs.empty()) {
     ev = g_timing.free_pairs.back();
     g_timing.free_pairs.pop_back();
@@ -52,6 +57,7 @@ std::pair<hipEvent_t, hipEvent_t> timing_begin(int kind, hipStream_t st) {
 void timing_end(int kind, std::pair<hipEvent_t, hipEvent_t> ev, hipStream_t st) {
   if (!ev.first) return;
   (void)hipEventRecord(ev.second, st);
+  std::lock_guard<std::mutex> lock(g_timing.mu);
   g_timing.pending[kind].push_back(ev);
 }
 
@@ -666,6 +672,7 @@ const char* ska_last_error(void) { return g_err.c_str(); }
 
 ska_status ska_timing_enable(int on) {
   Timing& t = g_timing;
+  std::lock_guard<std::mutex> lock(t.mu);
   if (on) {
     t.on = true;
     for (int k = 0; k < ska::kTimedKinds; ++k) {
@@ -694,6 +701,7 @@ ska_status ska_timing_read(int kernel, double* total_ms, int64_t* launches) {
   if (kernel < 0 || kernel >= ska::kTimedKinds || !total_ms || !launches)
     return fail(SKA_ERR_INVALID, "bad timing query");
   Timing& t = g_timing;
+  std::lock_guard<std::mutex> lock(t.mu);
   for (auto& ev : t.pending[kernel]) {
     if (hipEventSynchronize(ev.second) != hipSuccess) return fail(SKA_ERR_HIP, "event sync failed");
     float ms = 0.f;

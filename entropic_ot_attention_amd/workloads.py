@@ -72,3 +72,64 @@ def make_inputs(w: Workload, with_cotangent: bool = True):
         x = torch.randn(shape, generator=g, dtype=torch.float32)
         out[n] = x.reshape(w.bh, w.tokens, w.d).to(w.torch_dtype).contiguous()
     return out
+
+
+@dataclass(frozen=True)
+class TrainWorkload:
+    """Masked-reconstruction training step: batch x L tokens of D-wide embeddings (D = 64 heads),
+    a fraction `masked` of the tokens to reconstruct, band W, T base and R tail steps."""
+    name: str
+    batch: int
+    L: int
+    D: int
+    W: int
+    T: int
+    R: int
+    eps: float
+    masked: float
+    lr: float
+    compute: str      # "f32" or "bf16"
+    seed: int
+
+    @property
+    def heads(self) -> int:
+        return self.D // 64
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.compute == "f32" else torch.bfloat16
+
+    def with_(self, **kw) -> "TrainWorkload":
+        return replace(self, **kw)
+
+
+# One device's share of the pages' data-parallel run (64 examples per step over 8 devices) at
+# the width of ESM-2 650M embeddings (1280 = 20 heads of 64) and Pfam-domain lengths.
+TRAIN_B8_L1024 = TrainWorkload("train_b8_L1024_D1280_W256_T15_bf16", 8, 1024, 1280, 256, 15, 2,
+                               1.0, 0.15, 0.05, "bf16", 5)
+
+TRAIN_WORKLOADS = {w.name: w for w in (TRAIN_B8_L1024,)}
+
+
+# Correlation of neighbouring tokens' embeddings in the synthetic training sequences
+TRAIN_RHO = 0.9
+
+
+def make_training_batch(w: TrainWorkload):
+    """Seeded embeddings X [batch, L, D], mask [batch, L] (Bernoulli(masked), at least one masked
+    token per example) and weights (Wq, Wk, Wv, Wo) ~ N(0, 1 / D), fp32 on the CPU, drawn in that
+    order.  The embeddings are a stationary AR(1) sequence along the tokens,
+    X_t = rho X_(t-1) + sqrt(1 - rho^2) e_t with e ~ N(0, 1) and rho = TRAIN_RHO, so that, as in
+    real sequences, a masked token is predictable from its neighbours in the band."""
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    E = torch.randn((w.batch, w.L, w.D), generator=g, dtype=torch.float32)
+    X = torch.empty_like(E)
+    X[:, 0] = E[:, 0]
+    c = (1.0 - TRAIN_RHO ** 2) ** 0.5
+    for t in range(1, w.L):
+        X[:, t] = TRAIN_RHO * X[:, t - 1] + c * E[:, t]
+    mask = (torch.rand((w.batch, w.L), generator=g) < w.masked).to(torch.float32)
+    mask[:, 0] = 1.0
+    weights = tuple(torch.randn((w.D, w.D), generator=g, dtype=torch.float32) / w.D ** 0.5
+                    for _ in range(4))
+    return X, mask, weights

@@ -195,10 +195,10 @@ const char* ska_status_string(ska_status s);
 const char* ska_last_error(void);
 
 /* Kernel timing for measurement.  While enabled, every launch of the kernel family `kernel`
- * (0: forward Sinkhorn step, 1: forward output, 2: VJP passes, 3: contraction certificate) on the
- * calling thread is bracketed by HIP events on its own stream; ska_timing_read() synchronises on
- * those events
- * and returns the summed kernel milliseconds and the launch count since ska_timing_enable(1).
+ * (0: forward Sinkhorn step, 1: forward output, 2: VJP passes, 3: contraction certificate), from
+ * any thread of the process, is bracketed by HIP events on its own stream; ska_timing_read()
+ * synchronises on those events and returns the summed kernel milliseconds and the launch count
+ * since ska_timing_enable(1).
  * Enabling creates HIP events (no device memory); disabling destroys them. */
 ska_status ska_timing_enable(int on);
 ska_status ska_timing_read(int kernel, double* total_ms, int64_t* launches);
