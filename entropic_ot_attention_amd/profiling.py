@@ -8,8 +8,10 @@
 `--kernel-trace --stats --output-format csv` run.  `traffic` turns two `--pmc FETCH_SIZE` and
 `--pmc WRITE_SIZE` runs into HBM bytes per launch of one kernel, each counter scaled by what it
 reads for the calibration kernel in the same run (an elementwise kernel that reads and writes a
-known number of bytes, bench.py --calibration-copy-mib), and records the workload and the SHA-256
-of the kernel's source file so a reader can tell when the record no longer describes the code.
+known number of bytes, bench.py --calibration-copy-mib), and records the workload and a SHA-256
+over everything the kernel's machine code is built from (its source, the device and internal
+headers it includes, the compiler flags), so a reader can tell when the record no longer
+describes the code.
 """
 
 from __future__ import annotations
@@ -22,12 +24,19 @@ import os
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-STEP_KERNEL_SOURCE = os.path.join(PKG, "csrc", "ska_fused.hip")
+STEP_KERNEL_SOURCES = [os.path.join(PKG, "csrc", f)
+                       for f in ("ska_fused.hip", "ska_device.h", "ska_internal.h")]
 
 
-def source_sha(path: str = STEP_KERNEL_SOURCE) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(paths=None) -> str:
+    """SHA-256 over the step kernel's source files and the library's compiler flags."""
+    from .build_lib import HIPCC_FLAGS
+    h = hashlib.sha256()
+    for path in paths or STEP_KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()
 
 
 def stats_markdown(csv_path: str, out_md: str, command: str, top: int = 14) -> None:
