@@ -131,7 +131,18 @@ size_t workspace_for(const Plan& pl, ska_op op) {
   if (op == SKA_OP_CONTRACTION || op == SKA_OP_DUSTBIN_BLOCK_CONTRACTION) return 0;
   const bool vjp = (op == SKA_OP_VJP || op == SKA_OP_DUSTBIN_BLOCK_VJP);
   const int64_t vs = pl.g.bh * (int64_t)pl.g.Lpad;
-  if (vjp && pl.R != 2) return (size_t)(ska::tail_vecs(pl.R) * vs) * sizeof(float);
+  if (vjp && pl.R != 2) {
+    // general depth: the tail vectors; on the streaming engine also two column-partial buffers
+    int64_t part = 0;
+    int nt = 0;
+    const int nw = ska::vjp_stream_waves(pl.elt, pl.g.h, &nt);
+    if (nw > 0 && pl.R <= ska::kStreamMaxR) {
+      int seg_len = 0, nseg = 0;
+      ska::vjp_stream_segments(pl.g.bh, pl.g.Lr, nw, nt, &seg_len, &nseg);
+      part = 2 * pl.g.bh * (int64_t)nseg * (16 * nw * seg_len + 16 * (nt - 1));
+    }
+    return (size_t)(ska::tail_vecs(pl.R) * vs + part) * sizeof(float);
+  }
   if (vjp) {
     // streaming passes (both schedules, bands LDS holds) add dv1 column partials
     int nt = 0;
@@ -426,11 +437,56 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
   float* ws = static_cast<float*>(workspace);
   const bool d4 = (sched == SKA_DIRECT_FOUR);
   if (p->R != 2) {
+    hipError_t e = ska::launch_tail_prep(duals, ws, p->R, g, st);
+    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+    int snt = 0;
+    const int snw = ska::vjp_stream_waves(pl.elt, g.h, &snt);
+    if (snw > 0 && p->R <= ska::kStreamMaxR) {
+      // general tail depth on the streaming engine, R + 3 passes: dv^(R) (1); du^(R) and its
+      // column partials (2); each level a = R-1 .. 1 (5), the partials alternating between two
+      // buffers; dQ (6); dK and dV (7).  R = 0: passes 6 and 7 alone (M = g).
+      ska::VjpArgs a{};
+      a.Q = Q;
+      a.K = K;
+      a.V = V;
+      a.dO = dO;
+      a.ws = ws;
+      a.vec_stride = g.bh * (int64_t)g.Lpad;
+      a.bh = g.bh;
+      a.Lr = g.Lr;
+      a.Lpad = g.Lpad;
+      a.h = g.h;
+      a.nblk = (g.Lr + 16 * snw - 1) / (16 * snw);
+      ska::vjp_stream_segments(g.bh, g.Lr, snw, snt, &a.seg_len, &a.nseg);
+      a.pstride = 16 * snw * a.seg_len + 16 * (snt - 1);
+      a.c2 = g.c2;
+      a.s = g.s;
+      a.R = p->R;
+      const int64_t ps = g.bh * (int64_t)a.nseg * a.pstride;
+      float* parts[2] = {ws + ska::tail_vecs(p->R) * a.vec_stride,
+                         ws + ska::tail_vecs(p->R) * a.vec_stride + ps};
+      a.part = parts[0];
+      a.part_out = parts[1];
+      if (p->R >= 1) {
+        SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 1, a, st));
+        SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 2, a, st));
+      }
+      for (int lev = p->R - 1, k = 0; lev >= 1; --lev, ++k) {
+        a.level = lev;
+        a.part = parts[k % 2];
+        a.part_out = parts[(k + 1) % 2];
+        SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 5, a, st));
+      }
+      a.out0 = dQ;
+      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 6, a, st));
+      a.out0 = dK;
+      a.out1 = dV;
+      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 7, a, st));
+      return SKA_OK;
+    }
     // general tail depth: one-reference-tile adjoint, 2R + 2 passes on the wide decomposition
     // (A: dv^(R) and dV; B: du^(R); C, D for each level a = R-1 .. 1; then dQ and dK); R = 0
     // differentiates the stopped base plan alone: A (dV), then dQ and dK with M = g
-    hipError_t e = ska::launch_tail_prep(duals, ws, p->R, g, st);
-    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
     ska::WideArgs w = wide_args(pl, Q, K, V, dO);
     w.ws = ws;
     w.vec_stride = g.bh * (int64_t)g.Lpad;

@@ -80,16 +80,26 @@ struct VjpArgs {
   float* ws;             // kVjpVecs vectors [bh][Lpad]
   const float* fu;       // pass 0 (forward output): row duals u^(R), log2 units [bh][Lpad]
   const float* fv;       // pass 0: column duals v^(R), log2 units [bh][Lpad]
-  float* part;           // dv1 column partials
+  float* part;           // dv1 column partials (general depth: partials read by a level pass,
+                         // written by pass 2)
+  float* part_out;       // general depth: partials a level pass writes for the next level
   int64_t vec_stride;    // floats between consecutive workspace vectors (bh * Lpad)
   int64_t bh;
   int Lr, Lpad, h, nblk, seg_len, nseg, pstride;
   float c2, s;
+  int R, level;          // general depth: tail depth, and the level a of a level pass
 };
 
 // Streaming VJP geometry for (dtype, h): waves per workgroup (0 if the streaming passes do not
 // cover this band; the chunked passes handle it) and the register-resident tile count.
 int vjp_stream_waves(int elt, int h, int* nt);
+// General tail depth (0 <= R <= kStreamMaxR) on the streaming engine, vectors in the general-depth
+// layout of tail_vecs(R): pass 1 (dv^(R)) and pass 2 (du^(R), column partials) as for R = 2, then
+// for a = R-1 .. 1 a level pass 5 (F_a from the partials, C_a, the next partials), then pass 6
+// (dQ) and pass 7 (dK, dV) with the 2 R-term modifier on the matrix cores.
+constexpr int kStreamMaxR = 4;
+hipError_t launch_vjp_stream_general(int elt, int nt, int nw, int pass, const VjpArgs& a,
+                                     hipStream_t st);
 void vjp_stream_segments(int64_t bh, int Lr, int nw, int nt, int* seg_len, int* nseg);
 
 // Arguments of the wide-band engine (see ska_wide.hip): one workgroup per 16-token row tile

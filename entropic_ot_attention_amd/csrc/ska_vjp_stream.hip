@@ -183,21 +183,45 @@ __device__ __forceinline__ void ring_frag(Frag<float>& f, const float* ring, con
   lds_frag(f, ring, rt + n, g);
 }
 
-template <int PASS, bool D4> struct VjpPass {
-  static constexpr bool owns_keys = (PASS == 1 || PASS == 4);
+template <int PASS, bool D4, int GEN> struct VjpPass {
+  static constexpr bool owns_keys = (PASS == 1 || PASS == 4 || PASS == 7);
+  // owned rows in lane registers and window tokens across lanes (the passes that emit column
+  // partials); the others hold the window in registers and the owned tokens across lanes
+  static constexpr bool rows_in_regs = (PASS == 2 || PASS == 5);
+  static constexpr bool needs_g = (PASS != 0 && PASS != 5);
+  static constexpr bool uses_ring_b = (PASS != 5);
+  static constexpr bool reads_part = (PASS == 3 || PASS == 5);
+  static constexpr bool writes_part = (PASS == 2 || PASS == 5);
+  // general depth, passes 6 and 7: k-steps of the modifier contraction (2 R terms, 4 per step)
+  static constexpr int KS = GEN > 0 ? GEN : 0;
   // window-side vectors kept in LDS rings (direct-four pass 2 also needs v1 for P21)
-  static constexpr int nvec = PASS <= 1 ? 1 : PASS == 2 ? (D4 ? 3 : 2) : PASS == 3 ? 5 : 4;
-  // owned-side values per lane (pass 2: the dual of each of the lane's 4 owned rows)
-  static constexpr int nown = PASS <= 1 ? 1 : PASS == 2 ? 4 : PASS == 3 ? 3 : 5;
+  static constexpr int nvec = PASS <= 1 ? 1 : PASS == 2 ? (D4 ? 3 : 2) : PASS == 3 ? 5
+                            : PASS == 4 ? 4 : PASS == 5 ? 2 : 1 + 4 * KS;
+  // owned-side values per lane (passes 2 and 5: per owned row of the lane's 4)
+  static constexpr int nown = PASS <= 1 ? 1 : PASS == 2 ? 4 : PASS == 3 ? 3 : PASS == 4 ? 5
+                            : PASS == 5 ? 8 : 1 + KS;
 };
 
 // D4: the direct-four schedule, each staircase plan P^(2,2), P^(2,1), P^(1,1), P^(1,0) from its own
 // exponential [technical summaries §2.2: the comparison variant of the adjoint]; passes 0 and 1
 // are the same for both schedules.  Its window- and owned-side vectors are the duals and
 // cotangents themselves (v1, dv1, v0, u1, du1) instead of the orbit factors.
-template <typename T, int NT, int NW, int PASS, bool D4 = false>
+//
+// GEN >= 0: a general tail depth R (a.R) with the vectors of tail_vecs(R) [technical summaries
+// §2.1-§2.2: R differentiable tail steps, every staircase plan in the orbit of P^(R,R)]:
+//   1 (owns keys)     dv^(R)_j = sum_i P g                           -> F_R (EV_R = 1)
+//   2 (owns queries)  du^(R)_i = sum_j P (g - F_R);  column partials sum_i P C_R
+//   5 (owns queries)  level a = R-1 .. 1: F_a = -EV_a^2 (partials of level a), finished for the
+//                     window on arrival; C_a = -EU_a^2 sum_j P F_a;  column partials sum_i P C_a
+//                     for level a - 1
+//   6 (owns queries)  dQ_i = s sum_j P M k_j,   7 (owns keys) dK_j = s sum_i P M q_i,
+//                     dV_j = sum_i P dO_i, with M = g - sum_k alpha_k(i) beta_k(j) over the 2 R
+//                     pairs (alpha, beta) = (EU_a, F_a), (C_a, EV_(a-1)), a = 1 .. R: a rank-2R
+//                     product formed per tile on the matrix cores (fp32, GEN = ceil(2 R / 4)
+//                     k-steps of 4).
+template <typename T, int NT, int NW, int PASS, bool D4 = false, int GEN = -1>
 __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
-  using P = VjpPass<PASS, D4>;
+  using P = VjpPass<PASS, D4, GEN>;
   constexpr int H16 = (NT - 1) / 2;
   constexpr int BR = 16 * NW;                  // owned tokens per block
   constexpr int RING = BR + 32 * H16;          // block window
@@ -207,8 +231,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   __shared__ __attribute__((aligned(16))) T ringA[RING * LS];  // S window operand
   __shared__ __attribute__((aligned(16))) T ringB[RING * LS];  // g window operand
   __shared__ __attribute__((aligned(16))) float wv[NV][RING];  // window vectors
-  __shared__ float pring[PASS == 2 ? RING : 1];
-  __shared__ float cpart[PASS == 2 ? NW * RING : 1];
+  __shared__ float pring[P::writes_part ? RING : 1];
+  __shared__ float cpart[P::writes_part ? NW * RING : 1];
 
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -229,22 +253,55 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   auto vec = [&](int which) -> float* { return a.ws + which * a.vec_stride + vo; };
   const bool exact_h = (h == 16 * H16);
   const float* part_h = a.part + head * (int64_t)a.nseg * a.pstride;
+  // workspace vector indices: the R = 2 layout, or the general-depth layout of tail_vecs(R)
+  // (u, v, EU_1..R, EV_0..R, F_1..R, C_1..R)
+  const int R = a.R, lev = a.level;
+  constexpr bool G = GEN >= 0;
+  const int ix_u = G ? 0 : (int)kU2, ix_v = G ? 1 : (int)kV2;
+  const int ix_dv = G ? 2 + 3 * R : (int)kDV2;          // F_R = dv^(R)
+  const int ix_du = G ? 2 + 4 * R : (int)kDU2;          // C_R = du^(R)
+  auto ix_eu = [&](int q) { return 1 + q; };
+  auto ix_ev = [&](int b) { return 2 + R + b; };
+  auto ix_f = [&](int q) { return 2 + 2 * R + q; };
+  auto ix_c = [&](int q) { return 2 + 3 * R + q; };
+  // modifier pairs k = 0 .. 2R - 1: alpha (row side) and beta (column side); 0 past 2R
+  auto alpha_at = [&](int k, int t) -> float {
+    if (k >= 2 * R) return 0.f;
+    return vec(k < R ? ix_eu(k + 1) : ix_c(k - R + 1))[t];
+  };
+  auto beta_at = [&](int k, int t) -> float {
+    if (k >= 2 * R) return 0.f;
+    return vec(k < R ? ix_f(k + 1) : ix_ev(k - R))[t];
+  };
 
   // ---- window-side vectors of token j: raw loads and a 0/1 weight applied when stored ----
   struct VecIn {
     float v[NV];
     float w;               // token inside the sequence
-    float p0, p1, w0, w1;  // pass 3: dv1 column partials of the pass-2 segments and weights
+    float p0, p1, w0, w1;  // passes 3, 5: column partials of the previous pass's segments, weights
+    float e;               // pass 5: EV_a of the token
   };
   auto vec_raw = [&](int jc, VecIn& r) {
     if constexpr (PASS == 0) {
       r.v[0] = a.fv[vo + jc];
     } else if constexpr (PASS == 1) {
-      r.v[0] = vec(kU2)[jc];
+      r.v[0] = vec(ix_u)[jc];
     } else if constexpr (PASS == 2) {
-      r.v[0] = vec(kV2)[jc];
-      r.v[1] = vec(kDV2)[jc];
+      r.v[0] = vec(ix_v)[jc];
+      r.v[1] = vec(ix_dv)[jc];
       if constexpr (D4) r.v[2 % NV] = vec(kV1)[jc];
+    } else if constexpr (PASS == 5) {
+      r.v[0] = vec(ix_v)[jc];
+      r.v[1 % NV] = 0.f;             // F_a: from the partials when stored
+      r.e = vec(ix_ev(lev))[jc];
+    } else if constexpr (PASS == 6) {
+      r.v[0] = vec(ix_v)[jc];
+#pragma unroll
+      for (int k = 0; k < 4 * P::KS; ++k) r.v[1 + k] = beta_at(k, jc);
+    } else if constexpr (PASS == 7) {
+      r.v[0] = vec(ix_u)[jc];
+#pragma unroll
+      for (int k = 0; k < 4 * P::KS; ++k) r.v[1 + k] = alpha_at(k, jc);
     } else if constexpr (PASS == 3) {
       r.v[0] = vec(kV2)[jc];
       r.v[1] = vec(kDV2)[jc];
@@ -265,7 +322,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     vec_raw(jc, r);
     r.w = (j >= 0 && j < Lr) ? 1.f : 0.f;
     r.p0 = r.p1 = r.w0 = r.w1 = 0.f;
-    if constexpr (PASS == 3) {
+    if constexpr (P::reads_part) {
       const int S = BR * a.seg_len;
       const int k0 = max(0, floor_div(jc - halo, S)), k1 = min(a.nseg - 1, floor_div(jc + halo, S));
       float pp[2];
@@ -291,7 +348,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     vec_raw(in ? j : Lr - 1, r);
     r.w = in ? 1.f : 0.f;
     r.p0 = r.p1 = r.w0 = r.w1 = 0.f;
-    if constexpr (PASS == 3) {
+    if constexpr (P::reads_part) {
       const int c0 = j - c_lo, c1 = c0 - BR * a.seg_len;
       const bool two = in & (c1 >= 0) & (seg + 1 < a.nseg);
       const int c0i = in ? c0 : 0;      // offset 0 of a segment row is always written
@@ -318,22 +375,42 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       const float dv1 = -(in.p0 * in.w0 + in.p1 * in.w1) * in.w;
       wv[3][slot] = dv1;
       if (in.w != 0.f && j >= own_lo && j < own_hi) vec(kDV1)[j] = dv1;
+    } else if constexpr (PASS == 5) {
+      // dv^(a) = -EV_a (partials), F_a = dv^(a) EV_a
+      const float E = in.e * in.w;
+      const float F = -E * E * (in.p0 * in.w0 + in.p1 * in.w1);
+      wv[1][slot] = F;
+      if (in.w != 0.f && j >= own_lo && j < own_hi) vec(ix_f(lev))[j] = F;
     }
   };
 
   // ---- owned-side values of the block rows o0 .. o0 + 15 (raw loads), and their prepared
   // form: own[0] (pass 2: own[0..3]) becomes the owned dual / c2 for the accumulator ----
   auto own_loads = [&](int o0, float (&o)[NO]) {
-    if constexpr (PASS == 2) {
-      const f32x4 u = load4(vec(kU2) + min(o0 + 4 * g, a.Lpad - 4));
+    if constexpr (P::rows_in_regs) {
+      const int oc4 = min(o0 + 4 * g, a.Lpad - 4);
+      const f32x4 u = load4(vec(ix_u) + oc4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] = u[r];
+      if constexpr (PASS == 5) {
+        const f32x4 e = load4(vec(ix_eu(lev)) + oc4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[4 + r] = e[r];
+      }
     } else {
       const int oc = min(o0 + n, Lr - 1);
       if constexpr (PASS == 0) {
         o[0] = a.fu[vo + oc];
       } else if constexpr (PASS == 1) {
-        o[0] = vec(kV2)[oc];
+        o[0] = vec(ix_v)[oc];
+      } else if constexpr (PASS == 6) {
+        o[0] = vec(ix_u)[oc];
+#pragma unroll
+        for (int st = 0; st < P::KS; ++st) o[1 + st] = alpha_at(4 * st + g, oc);
+      } else if constexpr (PASS == 7) {
+        o[0] = vec(ix_v)[oc];
+#pragma unroll
+        for (int st = 0; st < P::KS; ++st) o[1 + st] = beta_at(4 * st + g, oc);
       } else if constexpr (PASS == 3) {
         o[0] = vec(kU2)[oc];
         o[1] = vec(kDU2)[oc];
@@ -349,7 +426,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   };
   auto own_prep = [&](float (&o)[NO]) {
     if constexpr (D4) return;      // direct: plain duals, added to the exponents explicitly
-    if constexpr (PASS == 2) {
+    if constexpr (P::rows_in_regs) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] *= inv_c2;
     } else {
@@ -361,13 +438,13 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   {
     RowStage<T, RING, NTHR> ra, rb;
     ra.load(winA, c_lo, Lr);
-    rb.load(winB, c_lo, Lr);
+    if constexpr (P::uses_ring_b) rb.load(winB, c_lo, Lr);
     ra.template store<RING>(ringA, c_lo);
-    rb.template store<RING>(ringB, c_lo);
+    if constexpr (P::uses_ring_b) rb.template store<RING>(ringB, c_lo);
   }
   for (int c = threadIdx.x; c < RING; c += NTHR)
     vec_store(c_lo + c, (c_lo + c + 4 * RING) % RING, vec_loads_any(c_lo + c));
-  if constexpr (PASS == 2) {
+  if constexpr (P::writes_part) {
     for (int c = threadIdx.x; c < RING; c += NTHR) pring[c] = 0.f;
     for (int c = threadIdx.x; c < NW * RING; c += NTHR) cpart[c] = 0.f;
   }
@@ -376,7 +453,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   {
     const int o = BR * blk0 + 16 * wave + n;
     load_frag(fA, ownA + (int64_t)o * kD, o < Lr, g);
-    if (PASS != 0) load_frag(fB, ownB + (int64_t)o * kD, o < Lr, g);
+    if (P::needs_g) load_frag(fB, ownB + (int64_t)o * kD, o < Lr, g);
     own_loads(BR * blk0 + 16 * wave, own);
     own_prep(own);
   }
@@ -404,16 +481,16 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     if (more) {
       if (cb + RING + BR <= Lr) {
         na.load_inside(winA, cb + RING);
-        nb.load_inside(winB, cb + RING);
+        if constexpr (P::uses_ring_b) nb.load_inside(winB, cb + RING);
       } else {
         na.load(winA, cb + RING, Lr);
-        nb.load(winB, cb + RING, Lr);
+        if constexpr (P::uses_ring_b) nb.load(winB, cb + RING, Lr);
       }
       if ((int)threadIdx.x < BR) nv = vec_loads_next(cb + RING + (int)threadIdx.x);
       const int on = b0 + BR + 16 * wave + n;
       const bool next_in = (b0 + 2 * BR <= Lr) || (on < Lr);
       load_frag(fA_next, ownA + (int64_t)on * kD, next_in, g);
-      if (PASS != 0) load_frag(fB_next, ownB + (int64_t)on * kD, next_in, g);
+      if (P::needs_g) load_frag(fB_next, ownB + (int64_t)on * kD, next_in, g);
       own_loads(b0 + BR + 16 * wave, own_next);
     }
 
@@ -462,25 +539,33 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       constexpr int kDepth = SKA_VJP_DEPTH;
       Frag<T> fw[2], fwg[2];
       f32x4 sc[2], gv[2];
-      // window vectors of the tile, read with its fragments (pass 2: two per lane)
-      constexpr int NWV = (PASS == 2) ? 1 : NV;
+      // window vectors of the tile, read with its fragments (passes 2 and 5: two per lane;
+      // passes 6 and 7: the window dual, then the lane's modifier operands, one per k-step)
+      constexpr bool MODK = (PASS == 6 || PASS == 7);
+      constexpr int NWV = P::rows_in_regs ? 1 : MODK ? 2 : NV;
       f32x4 wb[2][NWV];
+      f32x4 md[2];      // passes 6 and 7: modifier tile sum_k alpha_k beta_k, same layout as sc
       const f32x4 ci = D4 ? f32x4{0.f, 0.f, 0.f, 0.f}
-                   : (PASS == 2) ? f32x4{own[0], own[1 % NO], own[2 % NO], own[3 % NO]}
-                                 : f32x4{own[0], own[0], own[0], own[0]};
+                   : P::rows_in_regs ? f32x4{own[0], own[1 % NO], own[2 % NO], own[3 % NO]}
+                                     : f32x4{own[0], own[0], own[0], own[0]};
       // (fragments of tile t + 2 are read before the vector work on tile t, its window vectors
       // after it: wb[t & 1] still holds tile t's until then)
       auto load_frags = [&](int t) {
         const int rt = tile_slot(t);
         ring_frag(fw[t & 1], ringA, laneA, rt, g, n);
-        if constexpr (PASS != 0) ring_frag(fwg[t & 1], ringB, laneB, rt, g, n);
+        if constexpr (P::needs_g) ring_frag(fwg[t & 1], ringB, laneB, rt, g, n);
       };
       auto load_vecs = [&](int t) {
         const int rt = tile_slot(t);
-        if constexpr (PASS == 2) {
+        if constexpr (P::rows_in_regs) {
           wb[t & 1][0][0] = wv[0][rt + n];
           wb[t & 1][0][1] = wv[1][rt + n];
           if constexpr (D4) wb[t & 1][0][2] = wv[2 % NV][rt + n];
+        } else if constexpr (MODK) {
+          wb[t & 1][0] = wvec4(0, rt);
+          // A operand of k-step st: lane (g, n) gives the tile's window token n, pair 4 st + g
+#pragma unroll
+          for (int st = 0; st < P::KS; ++st) wb[t & 1][1 % NWV][st] = wv[(1 + 4 * st + g) % NV][rt + n];
         } else {
 #pragma unroll
           for (int k = 0; k < NWV; ++k) wb[t & 1][k] = wvec4(k, rt);
@@ -492,16 +577,24 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       auto pair_fetch = [&](int t) {
         const int r0 = tile_slot(t), r1 = (t + 1 < NT) ? tile_slot(t + 1) : r0;
         if constexpr (PASS == 0) opB.fetch(ringB, trl, r0, r1);
-        if constexpr (PASS == 3 || PASS == 4) opA.fetch(ringA, trl, r0, r1);
-        if constexpr (PASS == 4) opB.fetch(ringB, trl, r0, r1);
+        if constexpr (PASS == 3 || PASS == 4 || PASS == 6 || PASS == 7) opA.fetch(ringA, trl, r0, r1);
+        if constexpr (PASS == 4 || PASS == 7) opB.fetch(ringB, trl, r0, r1);
       };
       auto mma = [&](int t) {
-        if constexpr (PASS == 2) {
+        if constexpr (P::rows_in_regs) {
           sc[t & 1] = dot_tile(fA, fw[t & 1], ci);
-          gv[t & 1] = dot_tile(fB, fwg[t & 1]);
+          if constexpr (P::needs_g) gv[t & 1] = dot_tile(fB, fwg[t & 1]);
         } else {
           sc[t & 1] = dot_tile(fw[t & 1], fA, ci);
           if constexpr (PASS != 0) gv[t & 1] = dot_tile(fwg[t & 1], fB);
+          if constexpr (MODK) {
+            // md[r] = sum_k (window token 4 g + r side)_k (owned token n side)_k
+            f32x4 m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < P::KS; ++st)
+              m = __builtin_amdgcn_mfma_f32_16x16x4f32(wb[t & 1][1 % NWV][st], own[(1 + st) % NO], m, 0, 0, 0);
+            md[t & 1] = m;
+          }
         }
       };
       auto pipeline = [&](auto&& valu) {
@@ -583,7 +676,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
           }
         });
         const float dv2 = lane_group_sum(acc);
-        if (g == 0 && o0 + n < Lr) vec(kDV2)[o0 + n] = dv2;
+        if (g == 0 && o0 + n < Lr) vec(ix_dv)[o0 + n] = dv2;
       } else if constexpr (PASS == 2) {
         // ---- du2_i = sum_j P22 (g - dv2_j); column sums of P22 du2 (owned rows in registers) ----
         f32x4 x[NT];
@@ -621,7 +714,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         if (n < 4) {
           const int i = o0 + 4 * g + n;
           const float di = (n == 0) ? du2[0] : (n == 1) ? du2[1] : (n == 2) ? du2[2] : du2[3];
-          if (i < Lr) vec(kDU2)[i] = di;
+          if (i < Lr) vec(ix_du)[i] = di;
         }
         float cp[NT + 3];
 #pragma unroll
@@ -698,7 +791,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
             for (int r = 0; r < 4; ++r) r4[b][r] = X[b][r] - Ci * Y[b][r];
           store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, r4, a.s, g);
         }
-      } else {
+      } else if constexpr (PASS == 4) {
         // ---- dK, dV (owned key j across lanes, window queries in registers) ----
         const float Dj = own[1 % NO], Ej = own[2 % NO], Fj = own[3 % NO], Gj = own[4 % NO];
         f32x4 X[4], Y[4];
@@ -745,35 +838,139 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
           store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, X, a.s, g);
           store_row(static_cast<T*>(a.out1) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
         }
+      } else if constexpr (PASS == 5) {
+        // ---- level a: C_a = -EU_a^2 sum_j P F_a; column sums of P C_a (owned rows in
+        // registers) ----
+        f32x4 x[NT];
+        float racc[4] = {0.f, 0.f, 0.f, 0.f};
+        pipeline([&](int t, const f32x4& s, const f32x4&) {
+          if (dead(t)) {
+            x[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            return;
+          }
+          const float v2j = wb[t & 1][0][0], fj = wb[t & 1][0][1];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(fmaf(s[r], c2, v2j));
+            const float p = keep_o(t, r) ? e : 0.f;
+            x[t][r] = p;
+            racc[r] = fmaf(p, fj, racc[r]);
+          }
+        });
+        float ca[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ca[r] = -own[4 + r] * own[4 + r] * row16_sum(racc[r]);
+        if (n < 4) {
+          const int i = o0 + 4 * g + n;
+          const float ci_ = (n == 0) ? ca[0] : (n == 1) ? ca[1] : (n == 2) ? ca[2] : ca[3];
+          if (i < Lr) vec(ix_c(lev))[i] = ci_;
+        }
+        if (lev > 1) {
+          float cp[NT + 3];
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            cp[t] = x[t][0] * ca[0] + x[t][1] * ca[1] + x[t][2] * ca[2] + x[t][3] * ca[3];
+#pragma unroll
+          for (int t = NT; t < NT + 3; ++t) cp[t] = 0.f;
+          const int gsel = (g == 1) ? 2 : (g == 2) ? 1 : g;
+#pragma unroll
+          for (int q = 0; q < NT; q += 4) {
+            const float s4 = swap16_sum(swap32_sum(cp[q], cp[q + 1]), swap32_sum(cp[q + 2], cp[q + 3]));
+            const int t = q + gsel;
+            if (t < NT) cpart[wave * RING + 16 * wave + 16 * t + n] = s4;
+          }
+        }
+      } else if constexpr (PASS == 6) {
+        // ---- dQ with the general modifier (owned query i across lanes, window keys in
+        // registers) ----
+        f32x4 X[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) X[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float z[2][4];
+        pipeline([&](int t, const f32x4& s, const f32x4& gg) {
+          const int tt = t & 1;
+          if (tt == 0) pair_fetch(t);
+          const f32x4 vw = wb[t & 1][0], mm = md[t & 1];
+          const bool live = !dead(t);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(fmaf(s[r], c2, vw[r]));
+            const float p = (keep_w(t, r) && live) ? e : 0.f;
+            z[tt][r] = p * (gg[r] - mm[r]);
+          }
+          if (tt == 1 || t == NT - 1) {
+            if (tt == 0) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) z[1][r] = 0.f;
+            }
+            opA.contract(X, ringA, trl, z, g, n);
+          }
+        });
+        if (o0 + n < Lr) store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, X, a.s, g);
+      } else {
+        // ---- dK, dV with the general modifier (owned key j across lanes, window queries in
+        // registers) ----
+        f32x4 X[4], Y[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float z1[2][4], z2[2][4];
+        pipeline([&](int t, const f32x4& s, const f32x4& gg) {
+          const int tt = t & 1;
+          if (tt == 0) pair_fetch(t);
+          const f32x4 uw = wb[t & 1][0], mm = md[t & 1];
+          const bool live = !dead(t);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(fmaf(s[r], c2, uw[r]));
+            const float p = (keep_w(t, r) && live) ? e : 0.f;
+            z1[tt][r] = p * (gg[r] - mm[r]);
+            z2[tt][r] = p;
+          }
+          if (tt == 1 || t == NT - 1) {
+            if (tt == 0) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) z1[1][r] = z2[1][r] = 0.f;
+            }
+            opA.contract(X, ringA, trl, z1, g, n);
+            opB.contract(Y, ringB, trl, z2, g, n);
+          }
+        });
+        if (o0 + n < Lr) {
+          store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, X, a.s, g);
+          store_row(static_cast<T*>(a.out1) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
+        }
       }
     };
     if (interior) body(std::true_type{});
     else body(std::false_type{});
 
     __syncthreads();   // every wave is done with this block's window
-    if constexpr (PASS == 2) {
-      // block column sums (fixed wave order) into the segment accumulator; columns [cb, cb + BR)
-      // leave the window with this block and are written out
-      float* out = a.part + (head * (int64_t)a.nseg + seg) * a.pstride + (cb - c_lo);
-      for (int c = threadIdx.x; c < RING; c += NTHR) {
-        float sacc = 0.f;
+    if constexpr (P::writes_part) {
+      if (PASS == 2 || lev > 1) {
+        // block column sums (fixed wave order) into the segment accumulator; columns [cb, cb + BR)
+        // leave the window with this block and are written out
+        float* out = (PASS == 5 ? a.part_out : a.part) + (head * (int64_t)a.nseg + seg) * a.pstride +
+                     (cb - c_lo);
+        for (int c = threadIdx.x; c < RING; c += NTHR) {
+          float sacc = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) sacc += cpart[w * RING + c];
-        const int slot = slot_of(c);
-        if (!more) {
-          out[c] = pring[slot] + sacc;
-        } else if (c < BR) {
-          out[c] = pring[slot] + sacc;
-          pring[slot] = 0.f;
-        } else {
-          pring[slot] += sacc;
+          for (int w = 0; w < NW; ++w) sacc += cpart[w * RING + c];
+          const int slot = slot_of(c);
+          if (!more) {
+            out[c] = pring[slot] + sacc;
+          } else if (c < BR) {
+            out[c] = pring[slot] + sacc;
+            pring[slot] = 0.f;
+          } else {
+            pring[slot] += sacc;
+          }
         }
       }
     }
     if (more) {
       if ((int)threadIdx.x < BR) vec_store(cb + RING + (int)threadIdx.x, slot_of(threadIdx.x), nv);
       na.template store_slots<RING>(ringA, s_cb);
-      nb.template store_slots<RING>(ringB, s_cb);
+      if constexpr (P::uses_ring_b) nb.template store_slots<RING>(ringB, s_cb);
       fA = fA_next;
       fB = fB_next;
       own_prep(own_next);
@@ -813,6 +1010,27 @@ void vjp_stream_segments(int64_t bh, int Lr, int nw, int nt, int* seg_len, int* 
 }
 
 template <typename T, int NT, int NW>
+static void launch_nt_general(int pass, const VjpArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.bh * (int64_t)a.nseg)), block(NW * 64);
+  const int ks = (2 * a.R + 3) / 4;          // modifier k-steps of passes 6 and 7
+  switch (pass) {
+    case 1: vjp_stream_kernel<T, NT, NW, 1, false, 0><<<grid, block, 0, st>>>(a); break;
+    case 2: vjp_stream_kernel<T, NT, NW, 2, false, 0><<<grid, block, 0, st>>>(a); break;
+    case 5: vjp_stream_kernel<T, NT, NW, 5, false, 0><<<grid, block, 0, st>>>(a); break;
+    case 6:
+      if (ks == 0) vjp_stream_kernel<T, NT, NW, 6, false, 0><<<grid, block, 0, st>>>(a);
+      else if (ks == 1) vjp_stream_kernel<T, NT, NW, 6, false, 1><<<grid, block, 0, st>>>(a);
+      else vjp_stream_kernel<T, NT, NW, 6, false, 2><<<grid, block, 0, st>>>(a);
+      break;
+    default:
+      if (ks == 0) vjp_stream_kernel<T, NT, NW, 7, false, 0><<<grid, block, 0, st>>>(a);
+      else if (ks == 1) vjp_stream_kernel<T, NT, NW, 7, false, 1><<<grid, block, 0, st>>>(a);
+      else vjp_stream_kernel<T, NT, NW, 7, false, 2><<<grid, block, 0, st>>>(a);
+      break;
+  }
+}
+
+template <typename T, int NT, int NW>
 static void launch_nt(int pass, bool d4, const VjpArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.bh * (int64_t)a.nseg)), block(NW * 64);
   switch (pass) {
@@ -831,6 +1049,23 @@ static void launch_nt(int pass, bool d4, const VjpArgs& a, hipStream_t st) {
       else vjp_stream_kernel<T, NT, NW, 4><<<grid, block, 0, st>>>(a);
       break;
   }
+}
+
+hipError_t launch_vjp_stream_general(int elt, int nt, int nw, int pass, const VjpArgs& a,
+                                     hipStream_t st) {
+  if (a.R < 0 || a.R > kStreamMaxR || (pass != 1 && pass != 2 && pass != 5 && pass != 6 && pass != 7))
+    return hipErrorInvalidValue;
+  if ((pass == 1 || pass == 2) && a.R < 1) return hipErrorInvalidValue;
+  if (pass == 5 && (a.level < 1 || a.level >= a.R)) return hipErrorInvalidValue;
+  if (elt == 1) {
+    if (nt == 5) launch_nt_general<bf16, 5, SKA_BF16_NW>(pass, a, st);
+    else if (nt == 9) launch_nt_general<bf16, 9, SKA_BF16_NW>(pass, a, st);
+    else launch_nt_general<bf16, 17, SKA_BF16_NW>(pass, a, st);
+  } else {
+    if (nt == 5) launch_nt_general<float, 5, 4>(pass, a, st);
+    else launch_nt_general<float, 9, 4>(pass, a, st);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, bool d4, const VjpArgs& a,

@@ -197,14 +197,31 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert g(ctypes.byref(prob), *(args[:5] + [None] + args[6:]), 0, V(FAKE), needv, None) == -1
 
 
+def _stream_partials(bh, L, nw, nt):
+    """Floats of one column-partial buffer of the streaming passes: nseg segments of seg_len
+    blocks of 16 nw tokens per problem, each segment row 16 nw seg_len + 16 (nt - 1) long, with
+    about one workgroup per compute unit (256) and a segment spanning at least twice the halo."""
+    br = 16 * nw
+    nblk = -(-L // br)
+    seg_len = max(-(-(bh * nblk) // 256), -(-(16 * (nt - 1)) // br), 1)
+    seg_len = min(seg_len, nblk)
+    nseg = -(-nblk // seg_len)
+    return bh * nseg * (16 * nw * seg_len + 16 * (nt - 1))
+
+
 @pytest.mark.parametrize("R", [0, 1, 3, 4])
 def test_general_tail_depth_workspace(R):
     """VJP of a tail depth other than 2: 3 + 4 R vectors [bh][Lpad] (u^(R), v^(R), R row and
-    R + 1 column orbit factors, R + R scaled cotangents), whatever the band and dtype; the
-    dustbin entry point sizes its L + 1 rows the same way."""
-    for kw in (dict(L=1000, bh=3, W=16), dict(L=1000, bh=3, W=600, dtype=B.SKA_BF16)):
-        st, n = _ws_bytes(_prob(R=R, **kw), B.SKA_OP_VJP)
-        assert st == 0 and n == (3 + 4 * R) * 3 * 1024 * 4
+    R + 1 column orbit factors, R + R scaled cotangents); bands the streaming passes cover
+    (fp32 h <= 64, bf16 h <= 128) add two column-partial buffers for the level passes; the
+    dustbin entry point (dense support, wide passes) sizes its L + 1 rows with the vectors
+    alone."""
+    st, n = _ws_bytes(_prob(R=R, L=1000, bh=3, W=16), B.SKA_OP_VJP)            # fp32, h = 8
+    assert st == 0 and n == ((3 + 4 * R) * 3 * 1024 + 2 * _stream_partials(3, 1000, 4, 5)) * 4
+    st, n = _ws_bytes(_prob(R=R, L=1000, bh=3, W=256, dtype=B.SKA_BF16), B.SKA_OP_VJP)  # h = 128
+    assert st == 0 and n == ((3 + 4 * R) * 3 * 1024 + 2 * _stream_partials(3, 1000, 8, 17)) * 4
+    st, n = _ws_bytes(_prob(R=R, L=1000, bh=3, W=600, dtype=B.SKA_BF16), B.SKA_OP_VJP)  # wide
+    assert st == 0 and n == (3 + 4 * R) * 3 * 1024 * 4
     st, n = _ws_bytes(_prob(R=R, L=4096, bh=4), B.SKA_OP_DUSTBIN_BLOCK_VJP)
     assert st == 0 and n == (3 + 4 * R) * 4 * 4160 * 4
 
