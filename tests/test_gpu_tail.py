@@ -29,6 +29,13 @@ CASES = [
     ("R0_L600_W256_bf16", 2, 600, 256, 4, 1.0, BF16, 0),
     ("R0_L900_W600_wide", 1, 900, 600, 3, 0.8, F32, 0),
     ("R0_L20_W0_T1", 1, 20, 0, 1, 1.0, F32, 0),
+    # streaming general passes: shorter than one block, one block plus one token, the diagonal
+    # band in bf16, and many segments (level partials across segment boundaries)
+    ("R4_L1_W64_bf16", 2, 1, 64, 3, 1.0, BF16, 4),
+    ("R3_L129_W32_bf16", 2, 129, 32, 4, 1.0, BF16, 3),
+    ("R4_L97_W0_bf16", 1, 97, 0, 2, 1.0, BF16, 4),
+    ("R3_L6000_W96_f32_segments", 3, 6000, 96, 5, 0.9, F32, 3),
+    ("R1_L4500_W256_bf16_segments", 2, 4500, 256, 6, 1.0, BF16, 1),
 ]
 
 
