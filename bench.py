@@ -95,11 +95,13 @@ def parse():
 
 
 def tail_pass_flops_per_entry(R: int, d: int) -> int:
-    """Matrix-core flops per band entry of the general-depth adjoint at tail depth R >= 1: the
-    passes recompute the score tile (2 d) in each of their 2 R + 2 passes, the value scores
-    g = dO . V (2 d) in the two vector passes that need them and in the dQ and dK passes, and
-    contract one tile (2 d) in the dV, dQ and dK passes: (18 + 4 R) d."""
-    return (18 + 4 * R) * d
+    """Matrix-core flops per band entry of the one-reference adjoint at tail depth R >= 1, with
+    one score recompute per sweep over the band: dv^(R) (score and value scores g = dO . V, 4 d),
+    du^(R) (4 d), one sweep per level a = R-1 .. 1 that both reduces its row sums and emits the
+    next level's column partials (score, 2 d each), dQ (score, g and the contraction, 6 d), dK and
+    dV (score, g and two contractions, 8 d): (20 + 2 R) d.  The streaming passes run exactly this;
+    the wide engine's passes, with two sweeps per level, do more."""
+    return (20 + 2 * R) * d
 
 
 def contraction_main(args):
@@ -380,8 +382,7 @@ def certificate_main(args):
     tflops = flops / vjp_s / 1e12
     roofline = {
         "bound": "mfma",
-        "kernel": f"tail_pass_kernel, full backpropagation = adjoint at depth T + 2 = {Rf} "
-                  f"({2 * Rf + 2} passes)",
+        "kernel": f"VJP passes of full backpropagation = the adjoint at depth T + 2 = {Rf}",
         "achieved": round(tflops, 2),
         "peak": MFMA_F32_PEAK_TFLOPS,
         "unit": "TFLOP/s",
@@ -390,7 +391,7 @@ def certificate_main(args):
         "avg_launch_us": round(kvjp_ms / max(kvjp_n, 1) * 1e3, 2),
         "launches_timed": kvjp_n,
         "algorithmic_flops": flops,
-        "algorithmic_work": f"(18 + 4 x {Rf}) x {w.d} flops x {nnz} band entries per VJP",
+        "algorithmic_work": f"(20 + 2 x {Rf}) x {w.d} flops x {nnz} band entries per VJP",
     }
     out = {
         "metric": f"bias certificate eta_R tokens/s at L={L} W={w.W} d={w.d} T={w.T}, R=2; "

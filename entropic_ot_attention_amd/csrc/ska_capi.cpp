@@ -136,7 +136,7 @@ size_t workspace_for(const Plan& pl, ska_op op) {
     int64_t part = 0;
     int nt = 0;
     const int nw = ska::vjp_stream_waves(pl.elt, pl.g.h, &nt);
-    if (nw > 0 && pl.R <= ska::kStreamMaxR) {
+    if (nw > 0) {
       int seg_len = 0, nseg = 0;
       ska::vjp_stream_segments(pl.g.bh, pl.g.Lr, nw, nt, &seg_len, &nseg);
       part = 2 * pl.g.bh * (int64_t)nseg * (16 * nw * seg_len + 16 * (nt - 1));
@@ -441,10 +441,13 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
     if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
     int snt = 0;
     const int snw = ska::vjp_stream_waves(pl.elt, g.h, &snt);
-    if (snw > 0 && p->R <= ska::kStreamMaxR) {
+    if (snw > 0) {
       // general tail depth on the streaming engine, R + 3 passes: dv^(R) (1); du^(R) and its
       // column partials (2); each level a = R-1 .. 1 (5), the partials alternating between two
-      // buffers; dQ (6); dK and dV (7).  R = 0: passes 6 and 7 alone (M = g).
+      // buffers; dQ (6); dK and dV (7).  R = 0: passes 6 and 7 alone (M = g).  Beyond R = 4 (the
+      // deep adjoint of full backpropagation) the wide engine's pass A (dv^(R), dV) replaces pass
+      // 1, and its dQ and dK passes, which accumulate the 2 R modifier terms level by level,
+      // replace passes 6 and 7.
       ska::VjpArgs a{};
       a.Q = Q;
       a.K = K;
@@ -467,8 +470,19 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
                          ws + ska::tail_vecs(p->R) * a.vec_stride + ps};
       a.part = parts[0];
       a.part_out = parts[1];
+      const bool deep = p->R > ska::kStreamMaxR;
+      ska::WideArgs w = wide_args(pl, Q, K, V, dO);
+      w.ws = ws;
+      w.vec_stride = g.bh * (int64_t)g.Lpad;
+      w.R = p->R;
       if (p->R >= 1) {
-        SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 1, a, st));
+        if (deep) {
+          // the wide pass A gives dv^(R) and dV (the streaming dK/dV pass is not run)
+          w.out0 = dV;
+          SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 0, w, st));
+        } else {
+          SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 1, a, st));
+        }
         SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 2, a, st));
       }
       for (int lev = p->R - 1, k = 0; lev >= 1; --lev, ++k) {
@@ -477,11 +491,18 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
         a.part_out = parts[(k + 1) % 2];
         SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 5, a, st));
       }
-      a.out0 = dQ;
-      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 6, a, st));
-      a.out0 = dK;
-      a.out1 = dV;
-      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 7, a, st));
+      if (!deep) {
+        a.out0 = dQ;
+        SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 6, a, st));
+        a.out0 = dK;
+        a.out1 = dV;
+        SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 7, a, st));
+        return SKA_OK;
+      }
+      w.out0 = dQ;
+      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 4, w, st));
+      w.out0 = dK;
+      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 5, w, st));
       return SKA_OK;
     }
     // general tail depth: one-reference-tile adjoint, 2R + 2 passes on the wide decomposition

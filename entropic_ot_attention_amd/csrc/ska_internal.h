@@ -93,10 +93,11 @@ struct VjpArgs {
 // Streaming VJP geometry for (dtype, h): waves per workgroup (0 if the streaming passes do not
 // cover this band; the chunked passes handle it) and the register-resident tile count.
 int vjp_stream_waves(int elt, int h, int* nt);
-// General tail depth (0 <= R <= kStreamMaxR) on the streaming engine, vectors in the general-depth
-// layout of tail_vecs(R): pass 1 (dv^(R)) and pass 2 (du^(R), column partials) as for R = 2, then
-// for a = R-1 .. 1 a level pass 5 (F_a from the partials, C_a, the next partials), then pass 6
-// (dQ) and pass 7 (dK, dV) with the 2 R-term modifier on the matrix cores.
+// General tail depth on the streaming engine, vectors in the general-depth layout of
+// tail_vecs(R): pass 1 (dv^(R)) and pass 2 (du^(R), column partials) as for R = 2, then for
+// a = R-1 .. 1 a level pass 5 (F_a from the partials, C_a, the next partials) (any R up to
+// kTailMaxR), then pass 6 (dQ) and pass 7 (dK, dV) with the 2 R-term modifier on the matrix cores
+// (R <= kStreamMaxR).
 constexpr int kStreamMaxR = 4;
 hipError_t launch_vjp_stream_general(int elt, int nt, int nw, int pass, const VjpArgs& a,
                                      hipStream_t st);

@@ -1053,8 +1053,9 @@ static void launch_nt(int pass, bool d4, const VjpArgs& a, hipStream_t st) {
 
 hipError_t launch_vjp_stream_general(int elt, int nt, int nw, int pass, const VjpArgs& a,
                                      hipStream_t st) {
-  if (a.R < 0 || a.R > kStreamMaxR || (pass != 1 && pass != 2 && pass != 5 && pass != 6 && pass != 7))
+  if (a.R < 0 || a.R > kTailMaxR || (pass != 1 && pass != 2 && pass != 5 && pass != 6 && pass != 7))
     return hipErrorInvalidValue;
+  if ((pass == 6 || pass == 7) && a.R > kStreamMaxR) return hipErrorInvalidValue;
   if ((pass == 1 || pass == 2) && a.R < 1) return hipErrorInvalidValue;
   if (pass == 5 && (a.level < 1 || a.level >= a.R)) return hipErrorInvalidValue;
   if (elt == 1) {
