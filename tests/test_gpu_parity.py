@@ -137,13 +137,35 @@ def test_forward_general_tail_depth(R):
     compare(got, ref, torch.float32, f"forward R={R}")
 
 
-def test_repeat_runs_are_bitwise_identical():
-    w, x = _inputs(2, 700, 128, 6, 1.0, BF16, seed=5)
-    say("[gpu] determinism bf16 L=700")
-    a = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 128, 6)
-    b = gpu_run(x["Q"], x["K"], x["V"], x["dO"], 128, 6)
+@pytest.mark.parametrize("R,W,dtype", [(2, 128, BF16), (3, 128, BF16), (0, 96, BF16),
+                                       (4, 600, F32), (1, 64, F32)])
+def test_repeat_runs_are_bitwise_identical(R, W, dtype):
+    """Every reduction runs in a fixed order (no atomics on the forward or VJP paths), so two runs
+    give the same bits: the R = 2 passes, the general-depth streaming passes (R = 0, 1, 3) and the
+    wide passes (W = 600)."""
+    w, x = _inputs(2, 700, W, 6, 1.0, dtype, seed=5)
+    say(f"[gpu] determinism L=700 W={W} R={R} {dtype}")
+    a = gpu_run(x["Q"], x["K"], x["V"], x["dO"], W, 6, R)
+    b = gpu_run(x["Q"], x["K"], x["V"], x["dO"], W, 6, R)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_certificates_are_bitwise_repeatable():
+    """The bias certificate's fp64 norm sums and the contraction certificate's diameters and
+    per-problem maxima repeat bit for bit."""
+    from entropic_ot_attention_amd import binding as B
+    w, x = _inputs(2, 500, 64, 5, 1.0, F32, seed=6)
+    dev = torch.device("cuda:0")
+    Q, K, V, dO = (x[k].to(dev) for k in ("Q", "K", "V", "dO"))
+    say("[gpu] determinism of the certificates")
+    r1 = B.tail_remainder(Q, K, V, dO, 64, 5, 2, 1.0)
+    r2 = B.tail_remainder(Q, K, V, dO, 64, 5, 2, 1.0)
+    assert r1 == r2
+    c1 = B.contraction_certificate(Q, K, 64, 1.0, 16)
+    c2 = B.contraction_certificate(Q, K, 64, 1.0, 16)
+    for u, v in zip(c1, c2):
+        assert torch.equal(u, v)
 
 
 def _full_oracle(w, x, heads, schedule="one_reference"):
