@@ -213,7 +213,9 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
         // down, the previous segment's row while j - c_lo < 2 halo.  Partials are summed in
         // ascending segment order, as column_loads does.
         const int j = enter0 + lane;
-        const float vp = a.v_prev[vo + min(j, Lr - 1)];
+        // walking down, the first blocks of a problem take keys j < 0 into the window: their
+        // (unused) dual is read at a clamped index, inside the problem's vector
+        const float vp = a.v_prev[vo + min(max(j, 0), Lr - 1)];
         if (part_prev_h) {
           const int S = 64 * a.seg_len, c0 = j - c_lo;
           const float* own_row = part_prev_h + (int64_t)seg * a.pstride;
