@@ -25,15 +25,17 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# VALU roofline of MI355X from unit counts and clock: 256 CUs x 4 SIMDs, each issuing a wave64
-# fp32 VALU instruction every 2 cycles (32 lanes per cycle, the rate behind the 157.3 TFLOP/s
-# fp32 vector peak with FMA counted as 2 flops), at 2.4 GHz: 78.6e12 lane-operations per second.
-# v_exp_f32 is quarter rate, so one exponential takes 4 issue slots.
-VALU_LANE_OPS_PER_S = 256 * 4 * 32 * 2.4e9
-EXP_SLOTS = 4
+# VALU roofline of MI355X from unit counts and clock: 256 CUs x 4 SIMDs x 16 fp32 lanes per cycle
+# x 2.4 GHz = 39.3e12 lane-operations per second for unpacked fp32 instructions (a wave64
+# instruction occupies its SIMD for 4 cycles).  The 157.3 TFLOP/s fp32 vector peak counts packed
+# fp32 instructions (two values per lane) and an FMA as 2 flops; every kernel here is built without
+# packed fp32, so 39.3e12 is its ceiling.  v_exp_f32 issues at half that rate (18.3e12 per second
+# measured on MI355X), so one exponential takes 2 issue slots.
+VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
+EXP_SLOTS = 2
 # Minimal VALU work of one fused balanced Sinkhorn step per band entry: form the exponent with the
-# row shift already in the matrix-core accumulator (1 fma), exponentiate (1 exp = 4 slots),
-# accumulate the row sum (1 add) and the column sum of the normalised plan (1 fma): 7 issue slots.
+# row shift already in the matrix-core accumulator (1 fma), exponentiate (1 exp = 2 slots),
+# accumulate the row sum (1 add) and the column sum of the normalised plan (1 fma): 5 issue slots.
 SLOTS_PER_ENTRY_STEP = 3 + EXP_SLOTS
 HBM_PEAK_GBS = 8000.0
 # O(L) fp32 vectors one step reads and writes per token and head: previous column duals, previous
@@ -556,7 +558,7 @@ def main():
     avg_launch_s = (kstep_ms / max(kstep_n, 1)) / 1e3
     # Rooflines of the dominant kernel (one full Sinkhorn step per launch).  HBM binds: the
     # step must stream the query and key rows once plus O(L) fp32 vectors, which takes longer at
-    # 8 TB/s than the step's minimal VALU work (7 issue slots per band entry) or matrix-core work
+    # 8 TB/s than the step's minimal VALU work (5 issue slots per band entry) or matrix-core work
     # (2 d flops per band entry) at their peaks.
     elt = 2 if w.dtype == "bf16" else 4
     alg_bytes = w.bh * rows * (2 * w.d * elt + STEP_VECTOR_BYTES_PER_TOKEN)
