@@ -177,7 +177,14 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   }
   __syncthreads();
 
+  // Graded wave priority.  Each SIMD runs waves of three workgroups, and a workgroup passes its
+  // block barriers only when all four of its waves arrive.  A wave starts each block at priority
+  // 0 and raises it as it gets through its strip (1 and 2 at about 5/17 and 11/17 of the tiles, 3
+  // once the strip is done), so the SIMD favours the waves closest to their barrier: whole
+  // workgroups spend less time waiting there (about 8% off each launch at h = 128).
+  constexpr int kPrio1 = (5 * NT) / 17, kPrio2 = (11 * NT) / 17;
   for (int it = 0; it < blk1 - blk0; ++it) {
+    __builtin_amdgcn_s_setprio(0);
     const int blk = REV ? blk1 - 1 - it : blk0 + it;
     const int b0 = 64 * blk;
     const int cb = b0 - 16 * H16;             // block window [cb, cb + RING)
@@ -277,6 +284,8 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
         for (int t = 0; t < NT; ++t) {
           const int rt = tile_row(t);
           if (t + KA < NT) kfrag(fk[(t + KA) % (KA + 1)], tile_row(t + KA));
+          if (t == kPrio1 && t > 0) __builtin_amdgcn_s_setprio(1);
+          if (t == kPrio2) __builtin_amdgcn_s_setprio(2);
           const float vjt = vlane[rt];
           x[t] = dot_tile(fq, fk[t % (KA + 1)], shc);
 #pragma unroll
@@ -359,6 +368,7 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
       f32x4 x[NT];
       float ll[4] = {0.f, 0.f, 0.f, 0.f};
       strip(x, ll);
+      __builtin_amdgcn_s_setprio(3);
       float mx[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (!SHIFT) {
 #pragma unroll
