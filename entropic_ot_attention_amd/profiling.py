@@ -3,6 +3,7 @@
     python -m entropic_ot_attention_amd.profiling stats <kernel_stats.csv> <out.md> "<command>"
     python -m entropic_ot_attention_amd.profiling traffic <fetch.csv> <write.csv> <out.json> \
         <kernel substring> <calibration kernel substring> <calibration bytes> "<command>" <workload>
+    python -m entropic_ot_attention_amd.profiling counters <out.md> "<commands>" <counters.csv> ...
 
 `stats` writes a short markdown table (calls, average and total duration per kernel) from a
 `--kernel-trace --stats --output-format csv` run.  `traffic` turns two `--pmc FETCH_SIZE` and
@@ -61,6 +62,60 @@ def stats_markdown(csv_path: str, out_md: str, command: str, top: int = 14) -> N
         f.write("\n".join(lines) + "\n")
 
 
+# MI355X: 8 XCDs, 256 CUs, 4 SIMDs per CU (GRBM_GUI_ACTIVE is summed over the XCDs; the SQ
+# counters over every SIMD).
+N_XCD, N_SIMD = 8, 256 * 4
+
+
+def counters_markdown(csv_paths, out_md: str, command: str, regex_note: str = "") -> None:
+    """Per-kernel averages of SQ counters over the dispatches of one or more `--pmc` runs, with
+    the unit utilisations derived from them:
+      kernel cycles = GRBM_GUI_ACTIVE / 8 XCDs;
+      VALU busy = 4 SQ_ACTIVE_INST_VALU / (1024 SIMDs x cycles)   (quad-cycle units);
+      LDS busy  = 4 SQ_ACTIVE_INST_LDS / (1024 SIMDs x cycles);
+      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))   # name -> counter -> [v]
+    for path in csv_paths:
+        disp = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        for r in csv.DictReader(open(path)):
+            disp[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        for d, cs in disp.items():
+            for c, v in cs.items():
+                per[names[d]][c].append(v)
+    lines = ["# rocprofv3 SQ counters", "", "Commands (one counter pass each):", "", "```",
+             command, "```", ""]
+    if regex_note:
+        lines += [regex_note, ""]
+    for name in sorted(per, key=lambda k: -sum(per[k].get("GRBM_GUI_ACTIVE", [0]))):
+        m = {c: sum(v) / len(v) for c, v in per[name].items()}
+        cyc = m.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        w = m.get("SQ_WAVES", 0.0)
+        lines += [f"## `{name[:96]}`", "",
+                  f"dispatches averaged: {len(per[name].get('GRBM_GUI_ACTIVE', []))}; "
+                  f"kernel cycles {cyc:.0f} ({cyc / 2.4e3:.1f} us at 2.4 GHz)", "",
+                  "| quantity | value |", "|---|---:|"]
+        if w:
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+                      "SQ_INSTS_SALU"):
+                if c in m:
+                    lines.append(f"| {c} per wave | {m[c] / w:.0f} |")
+            lines.append(f"| waves | {w:.0f} |")
+        if cyc:
+            for label, c, k in (("VALU busy", "SQ_ACTIVE_INST_VALU", 4.0),
+                                ("LDS busy", "SQ_ACTIVE_INST_LDS", 4.0),
+                                ("MFMA busy", "SQ_VALU_MFMA_BUSY_CYCLES", 1.0)):
+                if c in m:
+                    lines.append(f"| {label} | {k * m[c] / (N_SIMD * cyc):.3f} |")
+        for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"):
+            if c in m and cyc:
+                lines.append(f"| {c} / (256 CUs x cycles) | {m[c] / (256 * cyc):.3f} |")
+        lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def _per_dispatch(csv_path: str, counter: str):
     """{dispatch id: (kernel name, summed counter value)} for one counter."""
     out = collections.defaultdict(lambda: ["", 0.0])
@@ -97,6 +152,8 @@ def traffic_record(fetch_csv: str, write_csv: str, kernel: str, calib_kernel: st
 def main(argv):
     if argv[1] == "stats":
         stats_markdown(argv[2], argv[3], argv[4])
+    elif argv[1] == "counters":
+        counters_markdown(argv[4:], argv[2], argv[3])
     elif argv[1] == "traffic":
         rec = traffic_record(argv[2], argv[3], argv[5], argv[6], int(argv[7]), argv[8], argv[9])
         with open(argv[4], "w") as f:
