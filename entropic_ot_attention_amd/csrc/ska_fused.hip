@@ -346,15 +346,16 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     // Lane group g of a reduced quad (tiles q, q+1, q+2, q+3) holds tile q + {0, 2, 1, 3}[g].
     const int gsel = (g == 1) ? 2 : (g == 2) ? 1 : g;
     // cp[t]: this lane's key of tile t summed over its 4 rows of the new plan
-    auto emit_columns = [&](float (&cp)[NT + 3]) {
+    auto emit_columns = [&](float (&cp)[NT]) {
 #pragma unroll
-      for (int t = NT; t < NT + 3; ++t) cp[t] = 0.f;
-#pragma unroll
-      for (int q = 0; q < NT; q += 4) {
+      for (int q = 0; q + 4 <= NT; q += 4) {
         const float s4 = swap16_sum(swap32_sum(cp[q], cp[q + 1]), swap32_sum(cp[q + 2], cp[q + 3]));
-        const int t = q + gsel;
-        if (t < NT) cpart[wave * RING + 16 * wave + 16 * t + n] = s4;
+        cpart[wave * RING + 16 * wave + 16 * (q + gsel) + n] = s4;
       }
+      // the tile left over after the quads: one sum over the lane groups, stored by group 0
+      static_assert(NT % 4 == 1, "every tile class leaves one tile after the quads");
+      const float s1 = lane_group_sum(cp[NT - 1]);
+      if (g == 0) cpart[wave * RING + 16 * wave + 16 * (NT - 1) + n] = s1;
     };
 
     // Row log-sum-exp.  With SHIFT the previous row duals are already in x, and then 2^x is an
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     // is needed.  Without SHIFT (the first step, from u = 0) the exact row maximum is subtracted.
     // u = -log2 sum_j 2^(c2 S_ij + v_j) either way.
     float u[4];
-    float cp[NT + 3];
+    float cp[NT];
     {
       f32x4 x[NT];
       float ll[4] = {0.f, 0.f, 0.f, 0.f};
@@ -395,8 +396,10 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         ll[r] = row16_sum(ll[r]);
-        const bool empty = (ll[r] == 0.f);          // no terms: rows past the sequence
-        u[r] = empty ? 0.f : fmaf(shc[r], c2, -(mx[r] + fast_log2(ll[r])));
+        // no terms: rows past the sequence (never on interior blocks)
+        const bool empty = !interior && (ll[r] == 0.f);
+        const float lg = SHIFT ? fast_log2(ll[r]) : mx[r] + fast_log2(ll[r]);
+        u[r] = empty ? 0.f : fmaf(shc[r], c2, -lg);
         rinv[r] = empty ? 0.f : __builtin_amdgcn_rcpf(ll[r]);
       }
 #pragma unroll
