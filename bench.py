@@ -8,7 +8,8 @@ L / (t_fwd + t_vjp) for all heads together.
 
 Prints ONE JSON line.  Besides the throughput it reports, for the dominant kernel (the fused
 balanced Sinkhorn step, T + R launches per step), its average launch time measured with HIP
-events on its own stream during the timed steps, the achieved fraction of its binding roofline
+events on its own stream during the last timed step (per-launch events add GPU idle time, so
+they are kept out of the other timed steps), the achieved fraction of its binding roofline
 (HBM: algorithmic bytes per launch over launch time) with the VALU and matrix-core fractions
 beside it, and, when a current rocprofv3 record exists, its measured HBM bytes per launch; and
 the fp64 CPU oracle timed on a bounded sample of the same workload.
@@ -96,6 +97,42 @@ def parse():
     return ap.parse_args()
 
 
+def warm_up(run, warmup: int, instrumented: int = 1) -> None:
+    """`warmup` untimed calls; the library's per-launch timing is on during the last
+    `instrumented` of them, so the HIP events that the timed region's instrumented calls use
+    exist before that region starts."""
+    import torch
+    from entropic_ot_attention_amd import binding as B
+    for i in range(warmup):
+        if i == max(0, warmup - instrumented):
+            B.ska_timing_enable(True)
+        run()
+    torch.cuda.synchronize()
+    B.ska_timing_enable(False)
+
+
+def timed_region(run, steps: int, stream, instrumented: int = 1):
+    """Time `steps` calls run(i) between two HIP events on `stream`, synchronised on both sides.
+    The library's per-launch HIP events (for the roofline's launch average) are on only during
+    the last `instrumented` calls: each event pair leaves the GPU idle for a few microseconds
+    between launches, which would otherwise be charged to every timed step.
+    Returns (ms per call, host wall seconds, number of instrumented calls)."""
+    import torch
+    from entropic_ot_attention_amd import binding as B
+    n_inst = max(1, min(instrumented, steps))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        if i == steps - n_inst:
+            B.ska_timing_enable(True)
+        run(i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / steps, time.perf_counter() - t0, n_inst
+
+
 def tail_pass_flops_per_entry(R: int, d: int) -> int:
     """Matrix-core flops per band entry of the one-reference adjoint at tail depth R >= 1, with
     one score recompute per sweep over the band: dv^(R) (score and value scores g = dO . V, 4 d),
@@ -135,17 +172,9 @@ def contraction_main(args):
     fn = (B.sinkhorn_attn_dustbin_block_contraction_certificate if w.dustbin
           else B.sinkhorn_attn_contraction_certificate)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        fn(prob, blk, Q, K, delta, kappa, dmax, stream)
-    torch.cuda.synchronize()
-    B.ska_timing_enable(True)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(stream)
-    for _ in range(args.steps):
-        fn(prob, blk, Q, K, delta, kappa, dmax, stream)
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    call_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    warm_up(lambda: fn(prob, blk, Q, K, delta, kappa, dmax, stream), args.warmup, instrumented=3)
+    call_ms, _, _ = timed_region(lambda i: fn(prob, blk, Q, K, delta, kappa, dmax, stream),
+                                 args.steps, stream, instrumented=3)
     k_ms, k_n = B.ska_timing_read(B.TIMED_CERT)
     B.ska_timing_enable(False)
     d = delta.cpu().double().numpy()
@@ -236,25 +265,16 @@ def train_main(args):
     Xd, md = X.to(dev), mask.to(dev)
     model = ReconstructionModel([x.to(dev) for x in weights], w.heads, w.W, w.T, w.R, w.eps,
                                 w.torch_dtype)
-    for _ in range(args.warmup):
-        sgd_step(model, Xd, md, w.lr)
-    torch.cuda.synchronize()
-    B.ska_timing_enable(True)
+    warm_up(lambda: sgd_step(model, Xd, md, w.lr), args.warmup)
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     losses = []
-    ev[0].record(stream)
-    for _ in range(args.steps):
-        loss, _ = sgd_step(model, Xd, md, w.lr)
-        losses.append(loss)
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    step_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    step_ms, _, n_inst = timed_region(lambda i: losses.append(sgd_step(model, Xd, md, w.lr)[0]),
+                                      args.steps, stream)
     kstep_ms, kstep_n = B.ska_timing_read(B.TIMED_STEP)
     kout_ms, _ = B.ska_timing_read(B.TIMED_OUT)
     kvjp_ms, _ = B.ska_timing_read(B.TIMED_VJP)
     B.ska_timing_enable(False)
-    attn_ms = (kstep_ms + kout_ms + kvjp_ms) / args.steps
+    attn_ms = (kstep_ms + kout_ms + kvjp_ms) / n_inst     # per instrumented step
     bh, rows = w.batch * w.heads, w.L
     avg_launch_s = (kstep_ms / max(kstep_n, 1)) / 1e3
     elt = 2 if w.compute == "bf16" else 4
@@ -279,9 +299,9 @@ def train_main(args):
                    "W": w.W, "T": w.T, "R": w.R, "epsilon": w.eps, "masked": w.masked,
                    "lr": w.lr, "optimizer": "sgd"},
         "breakdown": {"attention_kernels_ms": round(attn_ms, 4),
-                      "step_kernels_ms": round(kstep_ms / args.steps, 4),
-                      "out_kernel_ms": round(kout_ms / args.steps, 4),
-                      "vjp_kernels_ms": round(kvjp_ms / args.steps, 4),
+                      "step_kernels_ms": round(kstep_ms / n_inst, 4),
+                      "out_kernel_ms": round(kout_ms / n_inst, 4),
+                      "vjp_kernels_ms": round(kvjp_ms / n_inst, 4),
                       "rest_ms": round(step_ms - attn_ms, 4),
                       "projection_gemm_tflops_if_rest": round(gemm_flops / max(step_ms - attn_ms, 1e-9) / 1e9, 1),
                       "loss_first": float(losses[0]), "loss_last": float(losses[-1])},
@@ -531,25 +551,20 @@ def main():
         torch.cuda.synchronize()
         del src, dst, evict
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(lambda: step(), args.warmup)
 
-    B.ska_timing_enable(True)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    vjp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+    step_ms, wall, n_inst = timed_region(lambda i: step(), args.steps, stream)
     kstep_ms, kstep_n = B.ska_timing_read(B.TIMED_STEP)
     kout_ms, kout_n = B.ska_timing_read(B.TIMED_OUT)
     kvjp_ms, kvjp_n = B.ska_timing_read(B.TIMED_VJP)
     B.ska_timing_enable(False)
+    # forward / VJP split, after the timed region: the same steps with an event between the halves
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    vjp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
 
     tokens_per_step = w.batch * L
     value = tokens_per_step / (step_ms / 1e3)
@@ -605,9 +620,10 @@ def main():
                    "W": w.W, "T": w.T, "R": w.R, "epsilon": w.eps, "schedule": args.schedule},
         "breakdown": {"fwd_ms": round(fwd_ms, 4), "vjp_ms": round(vjp_ms, 4),
                       "wall_s": round(wall, 3),
-                      "step_kernels_ms": round(kstep_ms / args.steps, 4),
-                      "out_kernel_ms": round(kout_ms / args.steps, 4),
-                      "vjp_kernels_ms": round(kvjp_ms / args.steps, 4)},
+                      "step_kernels_ms": round(kstep_ms / n_inst, 4),
+                      "out_kernel_ms": round(kout_ms / n_inst, 4),
+                      "vjp_kernels_ms": round(kvjp_ms / n_inst, 4),
+                      "instrumented_steps": n_inst},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -703,6 +703,11 @@ ska_status run_contraction(const ska_problem* p, ska_op op, int32_t block, const
   a.m = m;
   a.s = pl.g.s;
   SKA_LAUNCH(ska::kTimedCert, st, ska::launch_contraction(pl.elt, a, st));
+  if (delta_max) {
+    const hipError_t e = ska::launch_contraction_max(a, st);
+    if (e != hipSuccess)
+      return fail(SKA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  }
   return SKA_OK;
 }
 
@@ -766,11 +771,8 @@ ska_status ska_timing_enable(int on) {
     }
     t.pending[k].clear();
   }
-  for (auto& ev : t.free_pairs) {
-    (void)hipEventDestroy(ev.first);
-    (void)hipEventDestroy(ev.second);
-  }
-  t.free_pairs.clear();
+  // the event pairs stay in the pool for the next enable: creating events between timed
+  // launches would stall the host
   return SKA_OK;
 }
 

@@ -200,13 +200,20 @@ static hipError_t launch_contraction_t(const ContractionArgs& a, hipStream_t st)
   return hipGetLastError();
 }
 
-hipError_t launch_contraction(int elt, const ContractionArgs& a, hipStream_t st) {
+static bool contraction_shape_ok(const ContractionArgs& a) {
   const int64_t pairs = (int64_t)a.nb * (2 * a.m + 1);
-  if (a.bh < 1 || a.bh > 65535 || a.nb < 1 || a.m < 0 || pairs >= (int64_t(1) << 31))
-    return hipErrorInvalidValue;
-  hipError_t e = elt == 1 ? launch_contraction_t<bf16>(a, st) : launch_contraction_t<float>(a, st);
-  if (e != hipSuccess || !a.delta_max) return e;
-  e = launch_fill(a.delta_max, a.bh, -1.f, st);
+  return a.bh >= 1 && a.bh <= 65535 && a.nb >= 1 && a.m >= 0 && pairs < (int64_t(1) << 31);
+}
+
+hipError_t launch_contraction(int elt, const ContractionArgs& a, hipStream_t st) {
+  if (!contraction_shape_ok(a)) return hipErrorInvalidValue;
+  return elt == 1 ? launch_contraction_t<bf16>(a, st) : launch_contraction_t<float>(a, st);
+}
+
+hipError_t launch_contraction_max(const ContractionArgs& a, hipStream_t st) {
+  if (!contraction_shape_ok(a) || !a.delta_max) return hipErrorInvalidValue;
+  const int64_t pairs = (int64_t)a.nb * (2 * a.m + 1);
+  const hipError_t e = launch_fill(a.delta_max, a.bh, -1.f, st);
   if (e != hipSuccess) return e;
   block_max_kernel<<<dim3((unsigned)((pairs + kMaxChunk - 1) / kMaxChunk), (unsigned)a.bh), dim3(256), 0,
                      st>>>(a.delta, a.delta_max, pairs);

@@ -205,5 +205,8 @@ struct ContractionArgs {
   int Lr, h, B, nb, m;
   float s;                 // 1 / (sqrt(d) epsilon)
 };
+// diameters and coefficients of every block pair (the timed kernel), then, separately, the
+// per-problem maximum into delta_max
 hipError_t launch_contraction(int elt, const ContractionArgs& a, hipStream_t st);
+hipError_t launch_contraction_max(const ContractionArgs& a, hipStream_t st);
 }  // namespace ska

@@ -195,11 +195,15 @@ const char* ska_status_string(ska_status s);
 const char* ska_last_error(void);
 
 /* Kernel timing for measurement.  While enabled, every launch of the kernel family `kernel`
- * (0: forward Sinkhorn step, 1: forward output, 2: VJP passes, 3: contraction certificate), from
+ * (0: forward Sinkhorn step, 1: forward output, 2: VJP passes, 3: the contraction certificate's
+ * diameter kernel, without the per-problem maximum), from
  * any thread of the process, is bracketed by HIP events on its own stream; ska_timing_read()
  * synchronises on those events and returns the summed kernel milliseconds and the launch count
  * since ska_timing_enable(1).
- * Enabling creates HIP events (no device memory); disabling destroys them. */
+ * Launches create HIP event pairs as they need them (no device memory); disabling returns them
+ * to a pool that the next enable reuses, so a region timed after an earlier enable creates none.
+ * The pool lives until the process ends.  Each event pair leaves the GPU idle for a few
+ * microseconds between launches: enable timing only around the launches to be measured. */
 ska_status ska_timing_enable(int on);
 ska_status ska_timing_read(int kernel, double* total_ms, int64_t* launches);
 
