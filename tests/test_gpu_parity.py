@@ -38,6 +38,10 @@ SMALL = [
     ("L900_W128_bf16", 2, 900, 128, 6, 1.0, BF16),
     ("L1500_W256_eps05_bf16", 1, 1500, 256, 4, 0.5, BF16),
     ("L600_W128_T4", 2, 600, 128, 4, 1.0, F32),
+    # the widest register-resident class (25 tiles, h up to 192): interior blocks (h = 192,
+    # bf16) and a half-width below the class's halo (h = 160, fp32)
+    ("L1400_W384_bf16", 1, 1400, 384, 4, 1.0, BF16),
+    ("L900_W320_T3", 1, 900, 320, 3, 1.0, F32),
     # wide engine: register-strip fused step (windows up to 8 x 33 tiles) and window-split passes
     ("L900_W600_bf16_wide", 2, 900, 600, 5, 1.0, BF16),
     ("L700_W2000_dense", 1, 700, 2000, 4, 1.0, F32),
