@@ -78,7 +78,9 @@ def parse():
     ap.add_argument("--tail-depth", type=int, default=0,
                     help="run the named workload with this tail depth R (1..4) instead of its own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None,
+                    help="tokens of head 0 in the oracle's CPU sample (default: about 10-30 s of "
+                         "single-core work per mode)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="one device copy of this many MiB before warmup (counter calibration)")
     ap.add_argument("--certificate", action="store_true",
@@ -230,7 +232,7 @@ def contraction_main(args):
     }
     if not args.no_cpu_baseline:
         import oracle
-        n = min(args.cpu_sample_tokens, rows)
+        n = min(args.cpu_sample_tokens or 262144, rows)
         n -= n % blk if n > blk else 0
         Qh, Kh = (x[k][0, :n].double().numpy() for k in ("Q", "K"))
         with threadpool_limits(limits=1):
@@ -322,15 +324,17 @@ def train_main(args):
         import oracle
         cfg = oracle.TrainConfig(heads=w.heads, W=w.W, T=w.T, R=w.R, eps=w.eps, lr=w.lr)
         params = tuple(x.double().numpy() for x in weights)
+        nex = min(6, w.batch)
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
-            oracle.reconstruction_step(params, X[:1].double().numpy(), mask[:1].double().numpy(), cfg)
+            oracle.reconstruction_step(params, X[:nex].double().numpy(), mask[:nex].double().numpy(),
+                                       cfg)
             dt = time.perf_counter() - t0
         out["cpu_baseline"] = {
-            "value": round(1 / dt, 4), "unit": "examples/s", "cores": 1, "kind": "oracle",
-            "sample": f"example 0 of {w.batch} (all {w.heads} heads, L = {w.L}), one fp64 step "
-                      f"(projections, attention forward and one-reference VJP, loss, SGD) in "
-                      f"numpy, {dt:.2f} s"}
+            "value": round(nex / dt, 4), "unit": "examples/s", "cores": 1, "kind": "oracle",
+            "sample": f"examples 0..{nex - 1} of {w.batch} (all {w.heads} heads, L = {w.L}), one "
+                      f"fp64 step (projections, attention forward and one-reference VJP, loss, "
+                      f"SGD) in numpy, {dt:.2f} s"}
     print(json.dumps(out), flush=True)
 
 
@@ -439,7 +443,7 @@ def certificate_main(args):
     }
     if not args.no_cpu_baseline:
         import oracle
-        n = min(args.cpu_sample_tokens, rows)
+        n = min(args.cpu_sample_tokens or 32768, rows)
         Qh, Kh, Vh, dOh = (x[k][0, :n].double().numpy() for k in ("Q", "K", "V", "dO"))
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
@@ -478,9 +482,12 @@ def cpu_baseline(w, sample_tokens: int):
         dt = time.perf_counter() - t0
     # one token of the workload spans all heads: scale the single-head sample accordingly
     value = n / (w.bh * dt)
+    import resource
     return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"head 0 of {w.bh}, tokens 0..{n - 1} of {w.tokens}, fwd + one-reference "
-                      f"VJP in fp64 numpy, {dt:.2f} s; tokens/s = tokens / ({w.bh} heads x time)"}
+                      f"VJP in fp64 numpy, {dt:.2f} s; tokens/s = tokens / ({w.bh} heads x time)",
+            "host_cores_available": len(os.sched_getaffinity(0)),
+            "peak_rss_mb": round(resource.getrusage(resource.RUSAGE_SELF).ru_maxrss / 1024.0, 1)}
 
 
 def main():
@@ -627,7 +634,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens or 131072)
     print(json.dumps(out), flush=True)
 
 
