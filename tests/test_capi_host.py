@@ -164,6 +164,12 @@ def test_workspace_sizes():
     (dict(dtype=7), B.SKA_OP_FWD, -1),
     (dict(bh=-1), B.SKA_OP_FWD, -1),
     (dict(bh=70000), B.SKA_OP_FWD, -2),
+    (dict(L=-1), B.SKA_OP_FWD, -1),
+    (dict(L=(1 << 30) + 1), B.SKA_OP_FWD, -2),
+    (dict(L=1 << 30), B.SKA_OP_DUSTBIN_BLOCK_FWD, -2),     # L + 1 tokens with the dustbin
+    (dict(T=250, R=7), B.SKA_OP_TAIL_REMAINDER, -2),        # adjoint depth T + R > 256
+    (dict(epsilon=float("inf")), B.SKA_OP_FWD, -1),
+    (dict(W=-1), B.SKA_OP_VJP, -1),
 ])
 def test_invalid_problems_are_rejected(kw, op, status):
     st, _ = _ws_bytes(_prob(**kw), op)
