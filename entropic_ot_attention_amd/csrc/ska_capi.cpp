@@ -755,6 +755,15 @@ const char* ska_last_error(void) { return g_err.c_str(); }
 ska_status ska_timing_enable(int on) {
   Timing& t = g_timing;
   std::lock_guard<std::mutex> lock(t.mu);
+  // launches still pending from an earlier enable are dropped from the counts (their events go
+  // back to the pool)
+  for (int k = 0; k < ska::kTimedKinds; ++k) {
+    for (auto& ev : t.pending[k]) {
+      (void)hipEventSynchronize(ev.second);
+      t.free_pairs.push_back(ev);
+    }
+    t.pending[k].clear();
+  }
   if (on) {
     t.on = true;
     for (int k = 0; k < ska::kTimedKinds; ++k) {
@@ -764,13 +773,6 @@ ska_status ska_timing_enable(int on) {
     return SKA_OK;
   }
   t.on = false;
-  for (int k = 0; k < ska::kTimedKinds; ++k) {
-    for (auto& ev : t.pending[k]) {
-      (void)hipEventSynchronize(ev.second);
-      t.free_pairs.push_back(ev);
-    }
-    t.pending[k].clear();
-  }
   // the event pairs stay in the pool for the next enable: creating events between timed
   // launches would stall the host
   return SKA_OK;
