@@ -493,8 +493,8 @@ def cpu_baseline(w, sample_tokens: int):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(every problem is independent; sharding over batch*heads is a design note only). "
+        print("bench.py measures one GPU: the library has no multi-GPU path (every (batch, "
+              "head) problem is independent, and sharding over them is a design note only). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
