@@ -28,10 +28,14 @@ ska_status fail(ska_status s, const std::string& msg) {
 // optional per-launch timing with HIP events, process-wide (launches from any thread, e.g. an
 // autograd engine's backward thread, are counted); the lock is taken only while timing is on
 // ---------------------------------------------------------------------------------------------
+struct TimedBracket {
+  std::pair<hipEvent_t, hipEvent_t> ev;
+  int64_t launches;   // launches of the family between the two events
+};
 struct Timing {
   std::atomic<bool> on{false};
   std::mutex mu;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[ska::kTimedKinds];
+  std::vector<TimedBracket> pending[ska::kTimedKinds];
   std::vector<std::pair<hipEvent_t, hipEvent_t>> free_pairs;
   double total_ms[ska::kTimedKinds] = {};
   int64_t launches[ska::kTimedKinds] = {};
@@ -54,11 +58,14 @@ std::pair<hipEvent_t, hipEvent_t> timing_begin(int kind, hipStream_t st) {
   return ev;
 }
 
-void timing_end(int kind, std::pair<hipEvent_t, hipEvent_t> ev, hipStream_t st) {
+// `launches`: how many launches of the family the bracket covers (consecutive launches on one
+// stream may share a bracket; the short gaps between them are then included)
+void timing_end(int kind, std::pair<hipEvent_t, hipEvent_t> ev, hipStream_t st,
+                int64_t launches = 1) {
   if (!ev.first) return;
   (void)hipEventRecord(ev.second, st);
   std::lock_guard<std::mutex> lock(g_timing.mu);
-  g_timing.pending[kind].push_back(ev);
+  g_timing.pending[kind].push_back(TimedBracket{ev, launches});
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -291,6 +298,8 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
     a.save_v_stride = dstride;
     a.save_u_stride = dstride;
     const int K_steps = p->T + p->R;
+    // the T + R step launches run back to back: one timing bracket covers them all
+    const auto run_ev = timing_begin(ska::kTimedStep, st);
     for (int k = 1; k <= K_steps; ++k) {
       a.v_prev = vbuf[(k - 1) % 2];
       a.part_prev = (k > 1) ? part[(k - 1) % 2] : nullptr;
@@ -302,8 +311,13 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
       a.save_u = save_at(ska::dual_slot_u(k, p->T, p->R));
       // alternate the walk direction: each step starts where the previous one ended, on data
       // still in the last-level cache
-      SKA_LAUNCH(ska::kTimedStep, st, ska::launch_fused_step(pl.elt, nt, a, (k % 2) == 0, st));
+      const hipError_t le = ska::launch_fused_step(pl.elt, nt, a, (k % 2) == 0, st);
+      if (le != hipSuccess) {
+        timing_end(ska::kTimedStep, run_ev, st, k - 1);
+        return fail(SKA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(le));
+      }
     }
+    timing_end(ska::kTimedStep, run_ev, st, K_steps);
     a.v_prev = vbuf[K_steps % 2];
     a.part_prev = part[K_steps % 2];
     a.u_prev = ubuf[K_steps % 2];
@@ -550,11 +564,18 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
     a.pstride = 16 * nw * a.seg_len + 16 * (nt - 1);
     a.c2 = g.c2;
     a.s = g.s;
+    // the four passes run back to back: one timing bracket covers them all
+    const auto run_ev = timing_begin(ska::kTimedVjp, st);
     for (int pass = 1; pass <= 4; ++pass) {
       a.out0 = (pass == 3) ? dQ : dK;
       a.out1 = dV;
-      SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_pass(pl.elt, nt, nw, pass, d4, a, st));
+      const hipError_t le = ska::launch_vjp_stream_pass(pl.elt, nt, nw, pass, d4, a, st);
+      if (le != hipSuccess) {
+        timing_end(ska::kTimedVjp, run_ev, st, pass - 1);
+        return fail(SKA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(le));
+      }
     }
+    timing_end(ska::kTimedVjp, run_ev, st, 4);
     return SKA_OK;
   }
   // wide passes A..E (bands wider than the streaming passes hold): each owns the side it reduces
@@ -758,9 +779,9 @@ ska_status ska_timing_enable(int on) {
   // launches still pending from an earlier enable are dropped from the counts (their events go
   // back to the pool)
   for (int k = 0; k < ska::kTimedKinds; ++k) {
-    for (auto& ev : t.pending[k]) {
-      (void)hipEventSynchronize(ev.second);
-      t.free_pairs.push_back(ev);
+    for (auto& br : t.pending[k]) {
+      (void)hipEventSynchronize(br.ev.second);
+      t.free_pairs.push_back(br.ev);
     }
     t.pending[k].clear();
   }
@@ -783,14 +804,14 @@ ska_status ska_timing_read(int kernel, double* total_ms, int64_t* launches) {
     return fail(SKA_ERR_INVALID, "bad timing query");
   Timing& t = g_timing;
   std::lock_guard<std::mutex> lock(t.mu);
-  for (auto& ev : t.pending[kernel]) {
-    if (hipEventSynchronize(ev.second) != hipSuccess) return fail(SKA_ERR_HIP, "event sync failed");
+  for (auto& br : t.pending[kernel]) {
+    if (hipEventSynchronize(br.ev.second) != hipSuccess) return fail(SKA_ERR_HIP, "event sync failed");
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, ev.first, ev.second) != hipSuccess)
+    if (hipEventElapsedTime(&ms, br.ev.first, br.ev.second) != hipSuccess)
       return fail(SKA_ERR_HIP, "event elapsed time failed");
     t.total_ms[kernel] += ms;
-    t.launches[kernel] += 1;
-    t.free_pairs.push_back(ev);
+    t.launches[kernel] += br.launches;
+    t.free_pairs.push_back(br.ev);
   }
   t.pending[kernel].clear();
   *total_ms = t.total_ms[kernel];

@@ -194,12 +194,14 @@ const char* ska_status_string(ska_status s);
 /* Detail of the last error returned on the calling thread ("" if none). */
 const char* ska_last_error(void);
 
-/* Kernel timing for measurement.  While enabled, every launch of the kernel family `kernel`
+/* Kernel timing for measurement.  While enabled, the launches of the kernel family `kernel`
  * (0: forward Sinkhorn step, 1: forward output, 2: VJP passes, 3: the contraction certificate's
- * diameter kernel, without the per-problem maximum), from
- * any thread of the process, is bracketed by HIP events on its own stream; ska_timing_read()
- * synchronises on those events and returns the summed kernel milliseconds and the launch count
- * since ska_timing_enable(1).
+ * diameter kernel, without the per-problem maximum), from any thread of the process, are
+ * bracketed by HIP events on their own stream: the T + R fused step launches of a forward, and
+ * the four streaming passes of an R = 2 VJP, each under one bracket (the short gaps between
+ * those back-to-back launches included); every other launch under its own.  ska_timing_read()
+ * synchronises on those events and returns the summed milliseconds and the number of launches
+ * covered since ska_timing_enable(1).
  * Launches create HIP event pairs as they need them (no device memory); disabling returns them
  * to a pool that the next enable reuses, so a region timed after an earlier enable creates none.
  * The pool lives until the process ends.  Each event pair leaves the GPU idle for a few
