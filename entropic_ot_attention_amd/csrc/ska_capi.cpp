@@ -280,8 +280,10 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
     float* vbuf[2] = {wsf, wsf + vs};
     float* ubuf[2] = {wsf + 2 * vs, wsf + 3 * vs};
     float* part[2] = {wsf + 4 * vs, wsf + 4 * vs + ps};
-    hipError_t e = ska::launch_fill(wsf, 4 * vs, 0.f, st);
-    if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+    // no initialisation: the first step reads no duals (it starts from v = 0 and needs no row
+    // shift), every step writes its row duals for all Lpad rows (0 past the sequence), and column
+    // duals are read only inside the sequence
+    hipError_t e = hipSuccess;
     ska::StepArgs a{};
     a.Q = Q;
     a.K = K;

@@ -139,9 +139,10 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     store_owned_v(j, v);
     return v;
   };
+  // the first step (no column partials yet) starts from v = 0 and reads no column duals
   auto loads_for = [&](int j) -> ColIn {
     if (part_prev_h) return column_loads(j, a.v_prev + vo, part_prev_h, a);
-    return ColIn{0.f, 0.f, a.v_prev[vo + min(max(j, 0), Lr - 1)], 0.f, 0.f};
+    return ColIn{0.f, 0.f, 0.f, 0.f, 0.f};
   };
   // previous row duals of rows o, .., o + 3 (log2 units); the dual buffers are padded to Lpad,
   // a multiple of 64, and hold 0 past Lr
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
         const int j = enter0 + lane;
         // walking down, the first blocks of a problem take keys j < 0 into the window: their
         // (unused) dual is read at a clamped index, inside the problem's vector
-        const float vp = a.v_prev[vo + min(max(j, 0), Lr - 1)];
+        const float vp = part_prev_h ? a.v_prev[vo + min(max(j, 0), Lr - 1)] : 0.f;
         if (part_prev_h) {
           const int S = 64 * a.seg_len, c0 = j - c_lo;
           const float* own_row = part_prev_h + (int64_t)seg * a.pstride;
@@ -412,7 +413,9 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     // Global stores of the block are issued after its end-of-block wait for the prefetched
     // registers: loads and stores share one counter, so a store issued earlier would be waited
     // for there as well.
-    const int st_i = (n < 4) ? o0 + 4 * g + n : Lr;      // row dual (lanes n < 4 of each group)
+    // row dual (lanes n < 4 of each group), for every row of the block: rows past the sequence
+    // (empty, u = 0) keep the padding of the row-dual buffer at 0 for the next step's shifts
+    const int st_i = (n < 4) ? o0 + 4 * g + n : a.Lpad;
     const float st_u = (n == 0) ? u[0] : (n == 1) ? u[1] : (n == 2) ? u[2] : u[3];
     int st_pj = -1, st_vj = Lr;                           // column partial / finished column dual
     float st_pv = 0.f, st_vv = 0.f;
@@ -452,9 +455,9 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
       shc = shift_acc(ush_next);
       __syncthreads();
     }
-    if (st_i < Lr) {
+    if (st_i < a.Lpad) {
       a.u_out[vo + st_i] = st_u;
-      if (a.save_u) a.save_u[head * a.save_u_stride + st_i] = st_u * kLn2;
+      if (a.save_u && st_i < Lr) a.save_u[head * a.save_u_stride + st_i] = st_u * kLn2;
     }
     if (st_pj >= 0) part_out_h[st_pj] = st_pv;
     store_owned_v(st_vj, st_vv);

@@ -243,3 +243,34 @@ def test_long_L262144_sampled_rows():
     rows = {0: [0, w.L - 1], 1: [int(rng.integers(0, w.L))], 2: [w.L // 2 + 7],
             3: [int(rng.integers(0, w.L)), w.L - 100]}
     _sampled(w, x, got, rows, w.name)
+
+
+@pytest.mark.parametrize("L,W,T,R,dtype", [(1000, 256, 4, 2, BF16), (333, 50, 3, 0, F32),
+                                           (777, 128, 2, 1, BF16)])
+def test_workspace_contents_do_not_matter(L, W, T, R, dtype):
+    """The forward and VJP read no workspace location they have not written in the same call:
+    a workspace filled with NaN bit patterns gives the same results, bit for bit, as a zeroed
+    one (ragged L, several segments, R = 0, 1, 2)."""
+    from entropic_ot_attention_amd import binding as B
+    say(f"[gpu] workspace contents L={L} W={W} T={T} R={R} {dtype}")
+    w, x = _inputs(2, L, W, T, 1.0, dtype, seed=31)
+    dev = torch.device("cuda:0")
+    Q, K, V, dO = (x[k].to(dev) for k in ("Q", "K", "V", "dO"))
+    prob = B.make_problem(2, L, 64, W, T, R, 1.0, w.torch_dtype)
+    outs = []
+    for fill in (0, 255):
+        ws_f = B.workspace_for(prob, B.SKA_OP_FWD, dev)
+        ws_v = B.workspace_for(prob, B.SKA_OP_VJP, dev)
+        ws_f.fill_(fill)
+        ws_v.fill_(fill)
+        O = torch.empty_like(Q)
+        duals = torch.empty(2, B.n_duals(R), L, dtype=torch.float32, device=dev)
+        B.sinkhorn_attn_fwd(prob, Q, K, V, O, duals, ws_f)
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+        B.sinkhorn_attn_vjp(prob, Q, K, V, duals, dO, dQ, dK, dV, B.SCHEDULES["one_reference"],
+                            ws_v)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (O, duals, dQ, dK, dV)])
+    for a, b in zip(*outs):
+        assert torch.isfinite(a.float()).all()
+        assert torch.equal(a, b)
