@@ -1,0 +1,86 @@
+"""Host checks of the profile-record helpers (entropic_ot_attention_amd/profiling.py) on small
+synthetic rocprofv3 CSV files: the traffic record scales each counter by its calibration copy,
+the counter summary derives the busy fractions it documents, and the source hash follows the
+step kernel's sources."""
+
+import csv
+import json
+import os
+
+import pytest
+
+from entropic_ot_attention_amd import profiling as P
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+          "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+          "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+          "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def _write(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for d, name, counter, value in rows:
+            r = {k: 0 for k in FIELDS}
+            r.update(Dispatch_Id=d, Kernel_Name=name, Counter_Name=counter, Counter_Value=value)
+            w.writerow(r)
+
+
+def test_traffic_record_scales_by_the_calibration_copy(tmp_path):
+    calib = 1 << 20                    # the copy moves 1 MiB each way
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    # the fetch counter reads half the true bytes, the write counter all of them; counters are
+    # summed over the rows of one dispatch (one row per XCD here)
+    _write(f, [(1, "neg_kernel", "FETCH_SIZE", 256.0), (1, "neg_kernel", "FETCH_SIZE", 256.0),
+               (2, "sinkhorn_step_kernel<17>", "FETCH_SIZE", 100.0),
+               (3, "sinkhorn_step_kernel<17>", "FETCH_SIZE", 300.0)])
+    _write(w, [(1, "neg_kernel", "WRITE_SIZE", 1024.0),
+               (2, "sinkhorn_step_kernel<17>", "WRITE_SIZE", 10.0),
+               (3, "sinkhorn_step_kernel<17>", "WRITE_SIZE", 30.0)])
+    rec = P.traffic_record(str(f), str(w), "sinkhorn_step_kernel", "neg_kernel", calib, "cmd", "wl")
+    assert rec["fetch_scale"] == pytest.approx(2.0)
+    assert rec["write_scale"] == pytest.approx(1.0)
+    assert rec["fetch_bytes_per_launch"] == pytest.approx(200.0 * 1024 * 2.0)
+    assert rec["write_bytes_per_launch"] == pytest.approx(20.0 * 1024)
+    assert rec["bytes_per_launch"] == pytest.approx(rec["fetch_bytes_per_launch"] +
+                                                   rec["write_bytes_per_launch"])
+    assert rec["fetch_launches"] == 2 and rec["source_sha256"] == P.source_sha()
+    json.dumps(rec)
+
+
+def test_traffic_record_needs_both_kernels(tmp_path):
+    f = tmp_path / "f.csv"
+    _write(f, [(1, "neg_kernel", "FETCH_SIZE", 1.0)])
+    with pytest.raises(RuntimeError):
+        P.traffic_record(str(f), str(f), "sinkhorn_step_kernel", "neg_kernel", 1, "cmd", "wl")
+
+
+def test_counter_summary_fractions(tmp_path):
+    cyc = 240000.0                      # kernel cycles per XCD
+    simd = 1024
+    rows = [(1, "k", "GRBM_GUI_ACTIVE", cyc * 8), (1, "k", "SQ_WAVES", 1000.0),
+            (1, "k", "SQ_INSTS_VALU", 5e6),
+            (1, "k", "SQ_ACTIVE_INST_VALU", 0.5 * simd * cyc / 4),       # quad-cycle units
+            (1, "k", "SQ_VALU_MFMA_BUSY_CYCLES", 0.25 * simd * cyc)]
+    c = tmp_path / "c.csv"
+    _write(c, rows)
+    out = tmp_path / "c.md"
+    P.counters_markdown([str(c)], str(out), "rocprofv3 --pmc ...")
+    text = out.read_text()
+    assert "| VALU busy | 0.500 |" in text
+    assert "| MFMA busy | 0.250 |" in text
+    assert "| SQ_INSTS_VALU per wave | 5000 |" in text
+    assert "kernel cycles 240000 (100.0 us at 2.4 GHz)" in text
+
+
+def test_source_hash_follows_the_step_kernel_sources(tmp_path):
+    paths = []
+    for name in ("a.hip", "b.h"):
+        p = tmp_path / name
+        p.write_text(name)
+        paths.append(str(p))
+    h0 = P.source_sha(paths)
+    (tmp_path / "a.hip").write_text("a.hip changed")
+    assert P.source_sha(paths) != h0
+    assert all(os.path.exists(p) for p in P.STEP_KERNEL_SOURCES)
