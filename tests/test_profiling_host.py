@@ -84,3 +84,25 @@ def test_source_hash_follows_the_step_kernel_sources(tmp_path):
     (tmp_path / "a.hip").write_text("a.hip changed")
     assert P.source_sha(paths) != h0
     assert all(os.path.exists(p) for p in P.STEP_KERNEL_SOURCES)
+
+
+def test_bench_band_entries_and_roofline_constants():
+    """bench.py's per-launch work counts: the band size by brute force, and the VALU ceiling of
+    unpacked fp32 (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz) with 5 issue slots per band entry."""
+    import bench
+    for L in (0, 1, 2, 7, 64, 100):
+        for h in (0, 1, 3, 50, 200):
+            brute = sum(1 for i in range(L) for j in range(L) if abs(i - j) <= h)
+            assert bench.band_entries(L, h) == brute
+    assert bench.VALU_LANE_OPS_PER_S == pytest.approx(39.3216e12)
+    assert bench.SLOTS_PER_ENTRY_STEP == 5
+    assert bench.tail_pass_flops_per_entry(2, 64) == 24 * 64
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "one GPU" in r.stderr
