@@ -1,16 +1,21 @@
-"""Compile libsinkhorn_attn.so for gfx950 with hipcc (in-tree, into entropic_ot_attention_amd/_lib)."""
+"""Compile libsinkhorn_attn.so for gfx950 with hipcc (in-tree, into entropic_ot_attention_amd/_lib).
+
+Each source is compiled to its own object in parallel (no relocatable device code: every kernel
+is launched from the translation unit that defines it), then the objects are linked."""
 
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libsinkhorn_attn.so")
+OBJ_DIR = os.path.join(LIB_DIR, "obj")
 SOURCES = ["ska_kernels.hip", "ska_fused.hip", "ska_vjp_stream.hip", "ska_wide.hip",
            "ska_contraction.hip", "ska_capi.cpp"]
 
@@ -19,13 +24,13 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # keep hipcc from forming packed fp32 instructions (v_pk_fma_f32 and friends)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # matrix-core results in ordinary VGPRs (no copies out of the accumulation registers)
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
+NOISE = "'-packed-fp32-ops' is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -33,20 +38,40 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    err = "\n".join(l for l in r.stderr.splitlines() if NOISE not in l)
+    return r.returncode, err
+
+
+def compile_cmd(src: str, obj: str) -> list:
+    return [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
+            os.path.join(CSRC, src), "-o", obj]
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    if jobs is None:
+        jobs = min(len(SOURCES), max(1, len(os.sched_getaffinity(0))), 16)
+    objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [compile_cmd(s, o) for s, o in zip(SOURCES, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    for src, (rc, err) in zip(SOURCES, results):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({rc}):\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    tmp = LIB_PATH + ".tmp"
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    rc, err = _run(link)
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{err}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
