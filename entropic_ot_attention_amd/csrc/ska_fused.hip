@@ -465,11 +465,17 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
 }
 
 // Finish the last column update of the forward for every token; also writes the saved dual.
+// The padding [Lr, Lpad) of the finished column duals is written as 0, so an output pass that
+// loads whole vector groups of them reads defined values there.
 template <typename T>
 __global__ __launch_bounds__(256) void finish_columns_kernel(StepArgs a) {
   const int64_t head = blockIdx.y;
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= a.Lr) return;
+  if (j >= a.Lpad) return;
+  if (j >= a.Lr) {
+    a.v_next[head * (int64_t)a.Lpad + j] = 0.f;
+    return;
+  }
   const T* Qh = static_cast<const T*>(a.Q) + head * (int64_t)a.Lr * kD;
   const T* Kh = static_cast<const T*>(a.K) + head * (int64_t)a.Lr * kD;
   const int64_t vo = head * (int64_t)a.Lpad;
@@ -531,7 +537,7 @@ hipError_t launch_fused_step(int elt, int nt, const StepArgs& a, bool rev, hipSt
 }
 
 hipError_t launch_finish_columns(int elt, const StepArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)((a.Lr + 255) / 256), (unsigned)a.bh);
+  dim3 grid((unsigned)((a.Lpad + 255) / 256), (unsigned)a.bh);
   if (elt == 1) finish_columns_kernel<bf16><<<grid, dim3(256), 0, st>>>(a);
   else finish_columns_kernel<float><<<grid, dim3(256), 0, st>>>(a);
   return hipGetLastError();

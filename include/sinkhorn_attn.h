@@ -147,7 +147,10 @@ ska_status sinkhorn_attn_dustbin_block_vjp(const ska_problem* p, const void* Q, 
  *   sums[2] = ||dK_full - dK_R||^2,  sums[3] = ||dK_full||^2
  * (dV has no remainder: V enters only the output).  eta_R = sqrt((sums[0] + sums[2]) /
  * (sums[1] + sums[3])).  `sums` is a device pointer to 4 doubles; the sums are taken in double in
- * a fixed order.  Requires T + R <= 256 (and T >= 1 when R = 0); workspace from
+ * a fixed order.  Forming eta_R from the four sums, and selecting the smallest certified R by
+ * calling this entry point for R = 0, 1, 2, .. until eta_R <= tau, are left to the caller: two
+ * scalar operations on the host after the sums are copied back, which the Python binding does
+ * (tail_remainder, select_tail_depth).  Requires T + R <= 256 (and T >= 1 when R = 0); workspace from
  * ska_workspace_bytes(p, SKA_OP_TAIL_REMAINDER): O(bh L (T + R)) floats of duals and cotangent
  * vectors plus seven [bh][L][d] tensors.  Gradients are formed in the input dtype, so with bf16
  * inputs remainders below the bf16 rounding of the gradients (about 4e-3 relative) are not

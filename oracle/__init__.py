@@ -40,6 +40,7 @@ from .sinkhorn_band import (  # noqa: F401
     dustbin_block_vjp,
     dependency_radius,
     sampled_rows,
+    row_range,
     BandProblem,
 )
 from .training import (  # noqa: F401

@@ -650,3 +650,28 @@ def sampled_rows(Q, K, V, dO, prob: BandProblem, rows, schedule: str = "one_refe
         for k, X in (("O", O), ("dQ", dQ), ("dK", dK), ("dV", dV)):
             out[k][n] = X[int(r) - a]
     return out
+
+
+def row_range(Q, K, V, dO, prob: BandProblem, start: int, stop: int,
+              schedules=("one_reference",)):
+    """Exact O, saved duals and, per adjoint schedule, dQ, dK, dV (fp64) of the rows
+    [start, stop) of one long head, computed on the tokens within dependency_radius of that
+    range (the sequence ends are real boundaries and are kept).  The forward runs once and each
+    schedule's VJP reads its duals.  Returns {"O": [n, d], "duals": [n_d, n],
+    schedule: {"dQ", "dK", "dV": [n, d]}} with n = stop - start."""
+    L = Q.shape[0]
+    if not 0 <= start <= stop <= L:
+        raise ValueError("row range outside the sequence")
+    H = dependency_radius(prob)
+    a, b = max(0, start - H), min(L, stop + H)
+    sl, keep = slice(a, b), slice(start - a, stop - a)
+    O, duals = forward(Q[sl], K[sl], V[sl], prob)
+    out = {"O": O[keep], "duals": duals[:, keep]}
+    for schedule in schedules:
+        if prob.R == 2:
+            fn = vjp_one_reference if schedule == "one_reference" else vjp_direct_four
+        else:
+            fn = vjp_tail_one_reference if schedule == "one_reference" else vjp_tail
+        dQ, dK, dV = fn(Q[sl], K[sl], V[sl], dO[sl], duals, prob)
+        out[schedule] = {"dQ": dQ[keep], "dK": dK[keep], "dV": dV[keep]}
+    return out

@@ -4,10 +4,14 @@ fp64 oracle on the same seeded inputs, and compare at the tolerance of the input
 
 from __future__ import annotations
 
+import os
 import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 import oracle
 
@@ -35,6 +39,29 @@ def gpu_run(Q, K, V, dO, W, T, R=2, eps=1.0, schedule="one_reference", dustbin=F
         out.update(dQ=dQ, dK=dK, dV=dV)
     torch.cuda.synchronize()
     return {k: v.float().cpu().double().numpy() for k, v in out.items()}
+
+
+def gpu_run_schedules(Q, K, V, dO, W, T, R=2, eps=1.0,
+                      schedules=("one_reference", "direct_four"), dustbin=False):
+    """One forward and one VJP per schedule through the C ABI; returns {"O", "duals",
+    schedule: {"dQ", "dK", "dV"}} as fp64 numpy arrays [bh, ...]."""
+    from entropic_ot_attention_amd import binding as B
+    dev = torch.device("cuda:0")
+    Qd, Kd, Vd, dOd = (x.to(dev) for x in (Q, K, V, dO))
+    O, duals = B.forward(Qd, Kd, Vd, W, T, R, eps, dustbin=dustbin)
+    host = lambda t: t.float().cpu().double().numpy()
+    out = {"O": host(O), "duals": host(duals)}
+    for s in schedules:
+        dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=s, dustbin=dustbin)
+        torch.cuda.synchronize()
+        out[s] = {"dQ": host(dQ), "dK": host(dK), "dV": host(dV)}
+    torch.cuda.synchronize()
+    return out
+
+
+def for_schedule(res: dict, schedule: str) -> dict:
+    """The flat {"O", "duals", "dQ", "dK", "dV"} view of one schedule's results."""
+    return {"O": res["O"], "duals": res["duals"], **res[schedule]}
 
 
 def oracle_head(Q, K, V, dO, W, T, R=2, eps=1.0, schedule="one_reference", dustbin=False):
@@ -87,3 +114,52 @@ def compare(got: dict, ref: dict, dtype: torch.dtype, label: str, heads=None):
             assert rel <= TOL_BF16_RELL2, f"{label}: {name} rel-l2 {rel:.3e} > {TOL_BF16_RELL2}"
     say(f"{label}: " + ", ".join(f"{k} maxabs={v[0]:.2e} rell2={v[1]:.2e}" for k, v in report.items()))
     return report
+
+
+def oracle_workers() -> int:
+    """Threads for the oracle: the host cores this process may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def parallel(fn, items, label: str):
+    """fn over items on oracle_workers() threads, each numpy call single-threaded (numpy
+    releases the interpreter lock inside its array loops); results in item order."""
+    t0 = time.time()
+    done = [0]
+
+    def run(item):
+        r = fn(item)
+        done[0] += 1
+        say(f"  {label}: {done[0]}/{len(items)} oracle tasks done ({time.time() - t0:.1f} s)")
+        return r
+
+    with threadpool_limits(1), ThreadPoolExecutor(min(oracle_workers(), len(items))) as ex:
+        return list(ex.map(run, items))
+
+
+def oracle_ranges(x: dict, tasks, prob, schedules, label: str):
+    """oracle.row_range for each task (head, start, stop) on the seeded inputs x, in parallel."""
+    heads = sorted({t[0] for t in tasks})
+    arrs = {b: tuple(as64(x[k][b]) for k in ("Q", "K", "V", "dO")) for b in heads}
+    return parallel(lambda t: oracle.row_range(*arrs[t[0]], prob, t[1], t[2], schedules),
+                    list(tasks), label)
+
+
+def oracle_every_row(x: dict, heads, prob, schedules, label: str, chunk: int = 65536):
+    """Every row of the given heads from the oracle, each head cut into contiguous ranges of at
+    most `chunk` rows evaluated on their own windows (exact: oracle.row_range).  Returns
+    {"O": [nh, L, d], "duals": [nh, n_d, L], schedule: {"dQ", "dK", "dV": [nh, L, d]}}."""
+    L = x["Q"].shape[1]
+    tasks = [(b, a, min(L, a + chunk)) for b in heads for a in range(0, L, chunk)]
+    parts = oracle_ranges(x, tasks, prob, schedules, label)
+    out = {"O": [], "duals": []}
+    for s in schedules:
+        out[s] = {"dQ": [], "dK": [], "dV": []}
+    for b in heads:
+        mine = [p for t, p in zip(tasks, parts) if t[0] == b]
+        out["O"].append(np.concatenate([p["O"] for p in mine]))
+        out["duals"].append(np.concatenate([p["duals"] for p in mine], axis=1))
+        for s in schedules:
+            for k in ("dQ", "dK", "dV"):
+                out[s][k].append(np.concatenate([p[s][k] for p in mine]))
+    return out

@@ -2,9 +2,10 @@
 
 Small cases compare every element and span several tiles, ragged tails, W = 0, a band
 wider than the sequence, T = 0, L = 1 and a non-unit epsilon.  The named workloads run at
-their full sizes in the launch configuration bench.py times; where the oracle cannot finish
-a full long sequence in seconds, rows are sampled (each computed exactly on the window of
-tokens that can influence it, see oracle.sampled_rows)."""
+their full sizes in the launch configuration the benchmark times and are compared on every
+element, with both adjoint schedules: the long sequences are cut into contiguous row ranges
+that the oracle evaluates exactly on windows of the tokens that can influence them
+(oracle.row_range), in parallel threads."""
 
 import numpy as np
 import pytest
@@ -12,7 +13,9 @@ import torch
 
 from entropic_ot_attention_amd.workloads import (BATCH_L2048, DUSTBIN_L4096, HEADS8_L32K,
                                                  LONG_L262K, TINY_L512, Workload, make_inputs)
-from tests.gpu_common import as64, compare, gpu_run, oracle_head, say
+import oracle
+from tests.gpu_common import (as64, compare, for_schedule, gpu_run, gpu_run_schedules,
+                              oracle_every_row, oracle_head, parallel, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -172,85 +175,95 @@ def test_certificates_are_bitwise_repeatable():
         assert torch.equal(u, v)
 
 
-def _full_oracle(w, x, heads, schedule="one_reference"):
-    ref = {k: [] for k in ("O", "duals", "dQ", "dK", "dV")}
-    for b in heads:
-        r = oracle_head(*(as64(x[k][b]) for k in ("Q", "K", "V", "dO")), w.W, w.T, w.R, w.eps,
-                        schedule, dustbin=w.dustbin)
-        for k in ref:
-            ref[k].append(r[k])
+BOTH = ("one_reference", "direct_four")
+
+
+def _full_oracle(w, x, heads, schedules=BOTH):
+    """The oracle on whole heads (one forward, each schedule's VJP), heads in parallel."""
+    args = {b: tuple(as64(x[k][b]) for k in ("Q", "K", "V", "dO")) for b in heads}
+
+    def one(b):
+        r = {s: oracle_head(*args[b], w.W, w.T, w.R, w.eps, s, dustbin=w.dustbin)
+             for s in schedules}
+        return r
+
+    per_head = parallel(one, list(heads), w.name)
+    ref = {}
+    for s in schedules:
+        ref[s] = {k: [r[s][k] for r in per_head] for k in ("O", "duals", "dQ", "dK", "dV")}
     return ref
 
 
 def test_tiny_L512_full():
+    """Every element of the tiny workload, both adjoint schedules."""
     w = TINY_L512
     x = make_inputs(w)
     say(f"[gpu] {w.name}")
-    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps)
-    compare(got, _full_oracle(w, x, range(w.bh)), w.torch_dtype, w.name)
+    got = gpu_run_schedules(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps)
+    ref = _full_oracle(w, x, range(w.bh))
+    for s in BOTH:
+        compare(for_schedule(got, s), ref[s], w.torch_dtype, f"{w.name}/{s}")
 
 
 def test_batch4x8_L2048_full():
+    """Every element of all 32 problems of the batch workload, both adjoint schedules."""
     w = BATCH_L2048
     x = make_inputs(w)
     say(f"[gpu] {w.name}")
-    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps)
-    compare(got, _full_oracle(w, x, range(w.bh)), w.torch_dtype, w.name)
+    got = gpu_run_schedules(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps)
+    ref = _full_oracle(w, x, range(w.bh))
+    for s in BOTH:
+        compare(for_schedule(got, s), ref[s], w.torch_dtype, f"{w.name}/{s}")
 
 
-@pytest.mark.parametrize("heads", [(0,), (3,)])
-def test_dustbin_block_L4096_full_heads(heads):
+@pytest.mark.timeout(600)
+def test_dustbin_block_L4096_all_heads():
+    """Every element of all four dustbin_block problems (4097 tokens, dense support), both
+    adjoint schedules through sinkhorn_attn_dustbin_block_vjp."""
     w = DUSTBIN_L4096
     x = make_inputs(w)
-    say(f"[gpu] {w.name} heads {heads}")
-    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps, dustbin=True)
-    compare(got, _full_oracle(w, x, heads), w.torch_dtype, f"{w.name} heads {heads}",
-            heads=list(heads))
+    say(f"[gpu] {w.name} all heads, both schedules")
+    got = gpu_run_schedules(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps, dustbin=True)
+    ref = _full_oracle(w, x, range(w.bh))
+    for s in BOTH:
+        compare(for_schedule(got, s), ref[s], w.torch_dtype, f"{w.name}/{s}")
 
 
-def _sampled(w, x, got, rows_by_head, label, schedule="one_reference"):
-    import oracle
-    p = oracle.BandProblem(W=w.W, T=w.T, R=w.R, eps=w.eps)
-    ref = {k: [] for k in ("O", "dQ", "dK", "dV")}
-    sub = {k: [] for k in ref}
-    for b, rows in rows_by_head.items():
-        r = oracle.sampled_rows(*(as64(x[k][b]) for k in ("Q", "K", "V", "dO")), p, rows, schedule)
-        for k in ref:
-            ref[k].append(r[k])
-            sub[k].append(got[k][b][rows])
-    compare({k: np.concatenate(v) for k, v in sub.items()},
-            {k: np.concatenate(v) for k, v in ref.items()},
-            w.torch_dtype, label)
-
-
-@pytest.mark.parametrize("schedule", ["one_reference", "direct_four"])
-def test_heads8_L32768_sampled_rows(schedule):
-    w = HEADS8_L32K
+def _every_row(w, chunk):
     x = make_inputs(w)
-    say(f"[gpu] {w.name} schedule={schedule}")
-    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps, schedule)
-    rng = np.random.default_rng(2)
-    rows = {0: [0, w.L - 1], 5: [int(rng.integers(0, w.L))], 7: [w.L // 2]}
-    _sampled(w, x, got, rows, f"{w.name}/{schedule}", schedule)
+    say(f"[gpu] {w.name}: forward + both VJPs")
+    got = gpu_run_schedules(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps)
+    prob = oracle.BandProblem(W=w.W, T=w.T, R=w.R, eps=w.eps)
+    ref = oracle_every_row(x, range(w.bh), prob, BOTH, w.name, chunk=chunk)
+    for s in BOTH:
+        compare(for_schedule(got, s), {"O": ref["O"], "duals": ref["duals"], **ref[s]},
+                w.torch_dtype, f"{w.name}/{s} (every row)")
 
 
-def test_long_L262144_sampled_rows():
-    w = LONG_L262K
-    x = make_inputs(w)
-    say(f"[gpu] {w.name}")
-    got = gpu_run(x["Q"], x["K"], x["V"], x["dO"], w.W, w.T, w.R, w.eps)
-    rng = np.random.default_rng(3)
-    rows = {0: [0, w.L - 1], 1: [int(rng.integers(0, w.L))], 2: [w.L // 2 + 7],
-            3: [int(rng.integers(0, w.L)), w.L - 100]}
-    _sampled(w, x, got, rows, w.name)
+@pytest.mark.timeout(600)
+def test_heads8_L32768_every_row():
+    """Every element of all 8 heads at L = 32768 (T = 20): O, the saved duals and both
+    schedules' dQ, dK, dV against the oracle, each head evaluated whole."""
+    _every_row(HEADS8_L32K, chunk=32768)
+
+
+@pytest.mark.timeout(900)
+def test_long_L262144_every_row():
+    """Every element of all 4 heads at L = 262144 (1,048,576 rows, the launch geometry the
+    benchmark times): O, the saved duals and both schedules' dQ, dK, dV against the oracle.
+    Each head is cut into ranges of 65536 rows, each evaluated exactly on its own window
+    (oracle.row_range), so every segment seam of every kernel is covered, and both ends."""
+    _every_row(LONG_L262K, chunk=65536)
 
 
 @pytest.mark.parametrize("L,W,T,R,dtype", [(1000, 256, 4, 2, BF16), (333, 50, 3, 0, F32),
-                                           (777, 128, 2, 1, BF16)])
+                                           (777, 128, 2, 1, BF16), (1000, 200, 3, 2, F32),
+                                           (1000, 352, 3, 2, BF16), (700, 600, 3, 2, F32)])
 def test_workspace_contents_do_not_matter(L, W, T, R, dtype):
     """The forward and VJP read no workspace location they have not written in the same call:
     a workspace filled with NaN bit patterns gives the same results, bit for bit, as a zeroed
-    one (ragged L, several segments, R = 0, 1, 2)."""
+    one (ragged L, several segments, R = 0, 1, 2; the fused step feeding the wide output pass,
+    fp32 W = 200 and bf16 W = 352; the wide step, W = 600)."""
     from entropic_ot_attention_amd import binding as B
     say(f"[gpu] workspace contents L={L} W={W} T={T} R={R} {dtype}")
     w, x = _inputs(2, L, W, T, 1.0, dtype, seed=31)

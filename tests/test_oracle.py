@@ -278,3 +278,31 @@ def test_sampled_rows_equal_full_evaluation():
     assert oracle.dependency_radius(prob) < 700
     for name, X in (("O", O), ("dQ", dQ), ("dK", dK), ("dV", dV)):
         np.testing.assert_allclose(got[name], X[rows], atol=1e-13)
+
+
+def test_row_ranges_tile_the_full_evaluation():
+    """Contiguous row ranges, each evaluated on its own window, put together give the full
+    evaluation of every output, every saved dual and both schedules' gradients; the ranges
+    meet away from the sequence ends, so each window is cut on both sides."""
+    L, W = 2000, 8
+    Q, K, V, dO = _qkv(L, seed=32)
+    prob = sb.BandProblem(W=W, T=3, R=2)
+    O, duals = oracle.forward(Q, K, V, prob)
+    ref = {s: fn(Q, K, V, dO, duals, prob) for s, fn in
+           (("one_reference", oracle.vjp_one_reference), ("direct_four", oracle.vjp_direct_four))}
+    cuts = [0, 450, 1200, 1201, 2000]
+    assert oracle.dependency_radius(prob) < 450
+    parts = [oracle.row_range(Q, K, V, dO, prob, a, b, ("one_reference", "direct_four"))
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    np.testing.assert_allclose(np.concatenate([p["O"] for p in parts]), O, atol=1e-13)
+    np.testing.assert_allclose(np.concatenate([p["duals"] for p in parts], axis=1), duals,
+                               atol=1e-12)
+    for s, (dQ, dK, dV) in ref.items():
+        for name, X in (("dQ", dQ), ("dK", dK), ("dV", dV)):
+            np.testing.assert_allclose(np.concatenate([p[s][name] for p in parts]), X, atol=1e-13)
+    # the output reaches (2 (T + R) + 1) h tokens: a window cut one hop closer than that
+    # moves the output row visibly
+    short = prob.h * 2 * (prob.T + prob.R)
+    assert short < oracle.dependency_radius(prob)
+    O_cut, _ = oracle.forward(Q[:1000 + short + 1], K[:1000 + short + 1], V[:1000 + short + 1], prob)
+    assert np.abs(O_cut[1000] - O[1000]).max() > 1e-10
