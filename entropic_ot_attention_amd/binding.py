@@ -27,7 +27,7 @@ SCHEDULES = {"one_reference": SKA_ONE_REFERENCE, "direct_four": SKA_DIRECT_FOUR}
 
 # every entry point the header declares
 EXPORTS = (
-    "ska_workspace_bytes", "sinkhorn_attn_fwd", "sinkhorn_attn_vjp",
+    "ska_workspace_bytes", "sinkhorn_attn_fwd", "sinkhorn_attn_fwd_noalloc", "sinkhorn_attn_vjp",
     "sinkhorn_attn_dustbin_block_fwd", "sinkhorn_attn_dustbin_block_vjp",
     "sinkhorn_attn_tail_remainder", "ska_contraction_layout",
     "sinkhorn_attn_contraction_certificate", "sinkhorn_attn_dustbin_block_contraction_certificate",
@@ -56,6 +56,7 @@ def _load():
     lib.ska_workspace_bytes.argtypes = [P, st, ctypes.POINTER(sz)]
     lib.sinkhorn_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sinkhorn_attn_dustbin_block_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sinkhorn_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sinkhorn_attn_vjp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, st, vp, sz, vp]
     lib.sinkhorn_attn_dustbin_block_vjp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, st, vp, sz, vp]
     lib.sinkhorn_attn_tail_remainder.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -64,7 +65,8 @@ def _load():
                                            ctypes.POINTER(i32)]
     lib.sinkhorn_attn_contraction_certificate.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
     lib.sinkhorn_attn_dustbin_block_contraction_certificate.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
-    for name in ("ska_workspace_bytes", "sinkhorn_attn_fwd", "sinkhorn_attn_dustbin_block_fwd",
+    for name in ("ska_workspace_bytes", "sinkhorn_attn_fwd", "sinkhorn_attn_fwd_noalloc",
+                 "sinkhorn_attn_dustbin_block_fwd",
                  "sinkhorn_attn_vjp", "sinkhorn_attn_dustbin_block_vjp",
                  "sinkhorn_attn_tail_remainder", "ska_contraction_layout",
                  "sinkhorn_attn_contraction_certificate",
@@ -138,6 +140,13 @@ def sinkhorn_attn_fwd(problem, Q, K, V, O, duals, workspace, stream=None):
     _check(lib.sinkhorn_attn_fwd(ctypes.byref(problem), _ptr(Q, "Q"), _ptr(K, "K"), _ptr(V, "V"),
                                  _ptr(O, "O"), _ptr(duals, "duals"), ws, nb, _stream(stream)),
            "sinkhorn_attn_fwd")
+
+
+def sinkhorn_attn_fwd_noalloc(problem, Q, K, V, O, duals, stream=None):
+    _check(lib.sinkhorn_attn_fwd_noalloc(ctypes.byref(problem), _ptr(Q, "Q"), _ptr(K, "K"),
+                                         _ptr(V, "V"), _ptr(O, "O"), _ptr(duals, "duals"),
+                                         _stream(stream)),
+           "sinkhorn_attn_fwd_noalloc")
 
 
 def sinkhorn_attn_dustbin_block_fwd(problem, Q, K, V, O, duals, workspace, stream=None):

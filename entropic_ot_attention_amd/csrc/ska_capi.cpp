@@ -594,6 +594,8 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
 
 }  // namespace
 
+ska_status ska::set_error(ska_status s, const std::string& msg) { return fail(s, msg); }
+
 extern "C" {
 
 ska_status ska_workspace_bytes(const ska_problem* p, ska_op op, size_t* bytes) {

@@ -4,7 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "sinkhorn_attn.h"
+
 namespace ska {
+
+// Records `msg` as the calling thread's ska_last_error() detail and returns `s`.
+ska_status set_error(ska_status s, const std::string& msg);
 
 constexpr int kD = 64;          // head dimension the kernels are built for
 constexpr int kWaves = 4;       // waves per workgroup; each wave owns 16 tokens

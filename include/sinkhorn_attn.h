@@ -116,6 +116,21 @@ ska_status sinkhorn_attn_vjp(const ska_problem* p, const void* Q, const void* K,
                              ska_schedule schedule, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Forward pass that allocates nothing, for callers that cannot allocate device memory around the
+ * call (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as sinkhorn_attn_fwd, with no workspace argument: the
+ * workspace is a static device array of the library, SKA_NOALLOC_SCRATCH_BYTES bytes (32 MiB) per
+ * GPU, which every GPU the library runs on holds from module load until the process ends.  A
+ * problem whose forward workspace (ska_workspace_bytes with SKA_OP_FWD) is larger is rejected
+ * with SKA_ERR_UNSUPPORTED before anything is enqueued; 4 problems of 262,144 tokens at W = 256
+ * (about 26.7 MB) fit.  The entry point calls no hipMalloc, hipFree or other allocating routine;
+ * on its first call on a device (the current device, which must be the stream's) it looks up
+ * that device's copy of the array once.  All calls on one GPU share its array: calls that may
+ * overlap on one GPU (other streams, other host threads) race and must be ordered by the caller. */
+#define SKA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ska_status sinkhorn_attn_fwd_noalloc(const ska_problem* p, const void* Q, const void* K,
+                                     const void* V, void* O, float* duals, hipStream_t stream);
+
 /* dustbin_block forward: tensors hold L real tokens followed by the learned dustbin token at
  * row L ([bh][L+1][d]); duals are [bh][n_d][L+1].  Tile padding beyond row L acts as the
  * inactive fill tokens (no support, zero target).  The support is every pair of the L+1 active
