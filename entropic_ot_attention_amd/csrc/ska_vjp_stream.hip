@@ -192,11 +192,16 @@ template <int PASS, bool D4, int GEN> struct VjpPass {
   static constexpr bool uses_ring_b = (PASS != 5);
   static constexpr bool reads_part = (PASS == 3 || PASS == 5);
   static constexpr bool writes_part = (PASS == 2 || PASS == 5);
-  // general depth, passes 6 and 7: k-steps of the modifier contraction (2 R terms, 4 per step)
-  static constexpr int KS = GEN > 0 ? GEN : 0;
-  // window-side vectors kept in LDS rings (direct-four pass 2 also needs v1 for P21)
+  // the modifier field on the matrix cores (one fp32 16x16x4 product per k-step of 4 terms):
+  // general depth passes 6 and 7, and the one-reference passes 3 (D + A E + B F) and
+  // 4 (D + A E + B F + C G)
+  static constexpr bool modk = (PASS == 6 || PASS == 7) || ((PASS == 3 || PASS == 4) && !D4 && GEN < 0);
+  // k-steps of the modifier contraction (general depth: 2 R terms, 4 per step)
+  static constexpr int KS = GEN > 0 ? GEN : (modk && GEN < 0) ? 1 : 0;
+  // window-side vectors kept in LDS rings (direct-four pass 2 also needs v1 for P21; the
+  // one-reference pass 4 adds a vector of ones, the modifier's constant term on its window side)
   static constexpr int nvec = PASS <= 1 ? 1 : PASS == 2 ? (D4 ? 3 : 2) : PASS == 3 ? 5
-                            : PASS == 4 ? 4 : PASS == 5 ? 2 : 1 + 4 * KS;
+                            : PASS == 4 ? (modk ? 5 : 4) : PASS == 5 ? 2 : 1 + 4 * KS;
   // owned-side values per lane (passes 2 and 5: per owned row of the lane's 4)
   static constexpr int nown = PASS <= 1 ? 1 : PASS == 2 ? 4 : PASS == 3 ? 3 : PASS == 4 ? 5
                             : PASS == 5 ? 8 : 1 + KS;
@@ -313,6 +318,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       r.v[1] = vec(kDU2)[jc];
       r.v[2] = vec(D4 ? kU1 : kEB)[jc];
       r.v[3] = vec(D4 ? kDU1 : kCC)[jc];
+      if constexpr (NV > 4) r.v[4 % NV] = 1.f;
     }
   };
   // any token j (window of the first block): clamped loads, partials found by segment division
@@ -432,6 +438,16 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     } else {
       o[0] *= inv_c2;
     }
+    if constexpr (P::modk && GEN < 0) {
+      // owned-side operand of the modifier product for lane group g (k-slot g):
+      // pass 3: (1, A_i, B_i, 0) against the window's (D_j, E_j, F_j, G_j);
+      // pass 4: (E_j, F_j, G_j, D_j) against the window's (A_i, B_i, C_i, 1)
+      if constexpr (PASS == 3) {
+        o[1 % NO] = (g == 0) ? 1.f : (g == 1) ? o[1 % NO] : (g == 2) ? o[2 % NO] : 0.f;
+      } else {
+        o[1 % NO] = (g == 0) ? o[2 % NO] : (g == 1) ? o[3 % NO] : (g == 2) ? o[4 % NO] : o[1 % NO];
+      }
+    }
   };
 
   // ---- prologue: the first block's window, vectors and owned operands ----
@@ -503,7 +519,11 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     };
     const bool interior = exact_h & (cb >= 0) & (cb + RING <= Lr) & (b0 + BR <= Lr);
     // window vector k of the lane's 4 window tokens 4 g + r of the tile at slot rt
-    auto wvec4 = [&](int k, int rt) -> f32x4 { return *reinterpret_cast<const f32x4*>(&wv[k][rt + 4 * g]); };
+    // (indexed as 16-byte groups, so that the read is one ds_read_b128 at a constant offset per
+    // vector: tile slots are multiples of 16)
+    auto wvec4 = [&](int k, int rt) -> f32x4 {
+      return reinterpret_cast<const f32x4*>(&wv[k][0])[(rt >> 2) + g];
+    };
 
     // Score tile t with the owned dual in the accumulator: the exponent of P22 is
     // c2 * sc + (window dual).  Masks: I (interior) needs them only on tiles 0 and NT - 1, along
@@ -541,8 +561,10 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       f32x4 sc[2], gv[2];
       // window vectors of the tile, read with its fragments (passes 2 and 5: two per lane;
       // passes 6 and 7: the window dual, then the lane's modifier operands, one per k-step)
-      constexpr bool MODK = (PASS == 6 || PASS == 7);
-      constexpr int NWV = P::rows_in_regs ? 1 : MODK ? 2 : NV;
+      constexpr bool MODK = P::modk;
+      // MODK: the window dual, the lane's modifier operands, and (pass 3) F and G for du1 and
+      // the second dQ contraction
+      constexpr int NWV = P::rows_in_regs ? 1 : MODK ? (PASS == 3 ? 4 : 2) : NV;
       f32x4 wb[2][NWV];
       f32x4 md[2];      // passes 6 and 7: modifier tile sum_k alpha_k beta_k, same layout as sc
       const f32x4 ci = D4 ? f32x4{0.f, 0.f, 0.f, 0.f}
@@ -566,6 +588,10 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
           // A operand of k-step st: lane (g, n) gives the tile's window token n, pair 4 st + g
 #pragma unroll
           for (int st = 0; st < P::KS; ++st) wb[t & 1][1 % NWV][st] = wv[(1 + 4 * st + g) % NV][rt + n];
+          if constexpr (PASS == 3) {
+            wb[t & 1][2 % NWV] = wvec4(3, rt);     // F
+            wb[t & 1][3 % NWV] = wvec4(4, rt);     // G
+          }
         } else {
 #pragma unroll
           for (int k = 0; k < NWV; ++k) wb[t & 1][k] = wvec4(k, rt);
@@ -741,19 +767,22 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
           const int tt = t & 1;
           if (tt == 0) pair_fetch(t);
-          const f32x4 vw = wb[t & 1][0], Dw = wb[t & 1][1 % NWV], Ew = wb[t & 1][2 % NWV],
-                      Fw = wb[t & 1][3 % NWV], Gw = wb[t & 1][4 % NWV];
           const bool live = !dead(t);
           if constexpr (!D4) {
+            // md = D_j + A_i E_j + B_i F_j from the matrix cores
+            const f32x4 vw = wb[t & 1][0], Fw = wb[t & 1][2 % NWV], Gw = wb[t & 1][3 % NWV],
+                        mm = md[t & 1];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float e = fast_exp2(fmaf(s[r], c2, vw[r]));
               const float p = (keep_w(t, r) && live) ? e : 0.f;
               acc = fmaf(p, Fw[r], acc);
-              z1[tt][r] = p * (gg[r] - fmaf(Bi, Fw[r], fmaf(Ai, Ew[r], Dw[r])));
+              z1[tt][r] = p * (gg[r] - mm[r]);
               z2[tt][r] = p * Gw[r];
             }
           } else {
+            const f32x4 vw = wb[t & 1][0], Dw = wb[t & 1][1 % NWV], Ew = wb[t & 1][2 % NWV],
+                        Fw = wb[t & 1][3 % NWV], Gw = wb[t & 1][4 % NWV];
             // direct: Ai = du2, Bi = u1 of the owned query; window E = v1, F = dv1, G = v0
             const float u2i = own[0];
 #pragma unroll
@@ -801,18 +830,20 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
           const int tt = t & 1;
           if (tt == 0) pair_fetch(t);
-          const f32x4 uw = wb[t & 1][0], Aw = wb[t & 1][1 % NWV], Bw = wb[t & 1][2 % NWV],
-                      Cw = wb[t & 1][3 % NWV];
+          const f32x4 uw = wb[t & 1][0];
           const bool live = !dead(t);
           if constexpr (!D4) {
+            // md = D_j + A_i E_j + B_i F_j + C_i G_j from the matrix cores
+            const f32x4 mm = md[t & 1];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float e = fast_exp2(fmaf(s[r], c2, uw[r]));
               const float p = (keep_w(t, r) && live) ? e : 0.f;
-              z1[tt][r] = p * (gg[r] - fmaf(Cw[r], Gj, fmaf(Bw[r], Fj, fmaf(Aw[r], Ej, Dj))));
+              z1[tt][r] = p * (gg[r] - mm[r]);
               z2[tt][r] = p;
             }
           } else {
+            const f32x4 Aw = wb[t & 1][1 % NWV], Bw = wb[t & 1][2 % NWV], Cw = wb[t & 1][3 % NWV];
             // direct: owned D = dv2, E = v1, F = dv1, G = v0; window A = du2, B = u1, C = du1
             const float v2j = own[0];
 #pragma unroll
