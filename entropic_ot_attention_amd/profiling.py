@@ -4,6 +4,8 @@
     python -m entropic_ot_attention_amd.profiling traffic <fetch.csv> <write.csv> <out.json> \
         <kernel substring> <calibration kernel substring> <calibration bytes> "<command>" <workload>
     python -m entropic_ot_attention_amd.profiling counters <out.md> "<commands>" <counters.csv> ...
+    python -m entropic_ot_attention_amd.profiling step-counters <out.json> <kernel substring> \
+        <workload> <record .md> <counters.csv> ...
 
 `stats` writes a short markdown table (calls, average and total duration per kernel) from a
 `--kernel-trace --stats --output-format csv` run.  `traffic` turns two `--pmc FETCH_SIZE` and
@@ -116,6 +118,37 @@ def counters_markdown(csv_paths, out_md: str, command: str, regex_note: str = ""
         f.write("\n".join(lines) + "\n")
 
 
+def kernel_busy(csv_paths, kernel: str) -> dict:
+    """Busy fractions (as in counters_markdown) averaged over every dispatch of the kernels whose
+    name contains `kernel`, across the counter passes."""
+    sums = collections.defaultdict(float)
+    counts = collections.defaultdict(int)
+    for path in csv_paths:
+        disp = collections.defaultdict(lambda: collections.defaultdict(float))
+        for r in csv.DictReader(open(path)):
+            if kernel in r["Kernel_Name"]:
+                disp[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        for cs in disp.values():
+            for c, v in cs.items():
+                sums[c] += v
+                counts[c] += 1
+    m = {c: sums[c] / counts[c] for c in sums}
+    cyc = m.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+    if not cyc:
+        raise RuntimeError(f"no GRBM_GUI_ACTIVE for '{kernel}'")
+    out = {"cycles": cyc}
+    for label, c, k in (("valu_busy", "SQ_ACTIVE_INST_VALU", 4.0),
+                        ("lds_busy", "SQ_ACTIVE_INST_LDS", 4.0),
+                        ("mfma_busy", "SQ_VALU_MFMA_BUSY_CYCLES", 1.0)):
+        out[label] = round(k * m[c] / (N_SIMD * cyc), 4) if c in m else None
+    w = m.get("SQ_WAVES", 0.0)
+    out["waves"] = round(w) if w else None
+    out["valu_insts_per_wave"] = round(m["SQ_INSTS_VALU"] / w) if w and "SQ_INSTS_VALU" in m else None
+    out["trans_insts_per_wave"] = (round(m["SQ_INSTS_VALU_TRANS_F32"] / w)
+                                   if w and "SQ_INSTS_VALU_TRANS_F32" in m else None)
+    return out
+
+
 def _per_dispatch(csv_path: str, counter: str):
     """{dispatch id: (kernel name, summed counter value)} for one counter."""
     out = collections.defaultdict(lambda: ["", 0.0])
@@ -154,6 +187,11 @@ def main(argv):
         stats_markdown(argv[2], argv[3], argv[4])
     elif argv[1] == "counters":
         counters_markdown(argv[4:], argv[2], argv[3])
+    elif argv[1] == "step-counters":
+        rec = kernel_busy(argv[6:], argv[3])
+        rec.update(kernel=argv[3], workload=argv[4], record=argv[5], source_sha256=source_sha())
+        with open(argv[2], "w") as f:
+            json.dump(rec, f, indent=1)
     elif argv[1] == "traffic":
         rec = traffic_record(argv[2], argv[3], argv[5], argv[6], int(argv[7]), argv[8], argv[9])
         with open(argv[4], "w") as f:

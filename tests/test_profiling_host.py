@@ -106,3 +106,21 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_kernel_busy_record(tmp_path):
+    """The step-kernel counter record averages every dispatch of the named kernel over the
+    passes and derives the busy fractions as the markdown summary does."""
+    cyc = 240000.0
+    p1, p2 = tmp_path / "p1.csv", tmp_path / "p2.csv"
+    k = "sinkhorn_step_kernel<17>"
+    _write(p1, [(1, k, "GRBM_GUI_ACTIVE", 8 * cyc), (1, k, "SQ_WAVES", 100.0),
+                (1, k, "SQ_INSTS_VALU", 1000.0), (2, "other", "GRBM_GUI_ACTIVE", 1.0)])
+    _write(p2, [(5, k, "GRBM_GUI_ACTIVE", 8 * cyc),
+                (5, k, "SQ_ACTIVE_INST_VALU", 0.25 * 1024 * cyc / 4),
+                (5, k, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1024 * cyc)])
+    rec = P.kernel_busy([str(p1), str(p2)], "sinkhorn_step_kernel")
+    assert rec["cycles"] == pytest.approx(cyc)
+    assert rec["valu_busy"] == pytest.approx(0.25)
+    assert rec["mfma_busy"] == pytest.approx(0.5)
+    assert rec["lds_busy"] is None and rec["waves"] == 100 and rec["valu_insts_per_wave"] == 10
