@@ -73,15 +73,16 @@ def _oracle_certificate(x, W, T, R, eps):
 
 
 # The certified remainder eta_R = ||grad_full - grad_R|| / ||grad_full|| is formed from two fp32
-# gradients; their rounding (a few units of 2^-24 relative to the gradient's norm) moves eta by
-# an absolute amount of that size, whatever eta is.  Comparisons allow 1e-3 relative plus that
-# absolute floor.
+# gradients.  Full backpropagation runs 2 (T + R) reduction sweeps, each adding about one unit of
+# fp32 rounding (2^-24) relative to the gradient's norm, so the difference of the two gradients
+# carries an absolute error of about 2 (T + R) 2^-24 in eta units whatever eta is (measured:
+# up to 7e-7 at T + R = 18, where eta_3 ~ 1e-7 is below it).  Comparisons allow 1e-3 relative
+# plus that floor.
 ETA_REL = 1e-3
-ETA_FLOOR = 1e-7
 
 
-def _eta_close(g, o):
-    return abs(g - o) <= ETA_REL * o + ETA_FLOOR
+def _eta_close(g, o, T, R):
+    return abs(g - o) <= ETA_REL * o + 2 * (T + R) * 2.0 ** -24
 
 
 @pytest.mark.parametrize("R", [0, 1, 2, 4])
@@ -96,7 +97,7 @@ def test_certificate_matches_oracle(R):
     say(f"eta gpu {g['eta']:.9e} oracle {o['eta']:.9e} diff {abs(g['eta'] - o['eta']):.2e}")
     for k in ("full_dQ2", "full_dK2"):
         assert abs(g[k] - o[k]) <= 1e-5 * o[k], (k, g[k], o[k])
-    assert _eta_close(g["eta"], o["eta"]), (g["eta"], o["eta"])
+    assert _eta_close(g["eta"], o["eta"], T, R), (g["eta"], o["eta"])
 
 
 @pytest.mark.parametrize("qk_scale,expect_R", [(0.5, 2), (0.56, 3)])
@@ -117,8 +118,9 @@ def test_certificate_resolves_tau_from_either_side(qk_scale, expect_R):
     say(f"gpu R={R} etas={etas}  oracle R={Ro} etas={etas_o}")
     assert Ro == expect_R and 0.5e-5 <= etas_o[2] <= 2e-5
     assert R == Ro and sorted(etas) == sorted(etas_o)
+    say(f"eta_2 gpu - oracle = {etas[2] - etas_o[2]:.2e} (tau - eta_2 = {1e-5 - etas_o[2]:.2e})")
     for k in etas:
-        assert _eta_close(etas[k], etas_o[k]), (k, etas[k], etas_o[k])
+        assert _eta_close(etas[k], etas_o[k], T, k), (k, etas[k], etas_o[k])
 
 
 def test_certificate_selects_r2_on_a_contracting_problem():
@@ -137,7 +139,7 @@ def test_certificate_selects_r2_on_a_contracting_problem():
     say(f"gpu R={R} etas={etas}  oracle R={Ro} etas={etas_o}")
     assert R == Ro == 2 and sorted(etas) == sorted(etas_o) == [0, 1, 2]
     for k in etas:
-        assert _eta_close(etas[k], etas_o[k]), (k, etas[k], etas_o[k])
+        assert _eta_close(etas[k], etas_o[k], T, k), (k, etas[k], etas_o[k])
 
 
 def test_tiny_workload_certificate():
@@ -149,4 +151,4 @@ def test_tiny_workload_certificate():
     g = _certificate(x, w.W, w.T, 2, w.eps)
     o = _oracle_certificate(x, w.W, w.T, 2, w.eps)
     say(f"tiny eta gpu {g['eta']:.6e} oracle {o['eta']:.6e}")
-    assert _eta_close(g["eta"], o["eta"]), (g["eta"], o["eta"])
+    assert _eta_close(g["eta"], o["eta"], w.T, 2), (g["eta"], o["eta"])
