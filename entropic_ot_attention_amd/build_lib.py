@@ -17,7 +17,8 @@ LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libsinkhorn_attn.so")
 OBJ_DIR = os.path.join(LIB_DIR, "obj")
 SOURCES = ["ska_kernels.hip", "ska_fused.hip", "ska_vjp_stream.hip", "ska_wide.hip",
-           "ska_contraction.hip", "ska_noalloc.hip", "ska_capi.cpp"]
+           "ska_contraction.hip", "ska_noalloc.hip", "ska_geometry.cpp",
+           "ska_capi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

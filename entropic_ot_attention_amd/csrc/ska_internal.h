@@ -16,6 +16,8 @@ ska_status set_error(ska_status s, const std::string& msg);
 constexpr int kD = 64;          // head dimension the kernels are built for
 constexpr int kWaves = 4;       // waves per workgroup; each wave owns 16 tokens
 constexpr int kOwnPerBlock = 64;
+constexpr int kBf16StreamWaves = 8;   // waves per workgroup of the bf16 streaming passes
+constexpr int kWideWaves = 8;         // waves per workgroup of the wide-band engine
 
 // Vectors kept per head in the workspace are padded to a multiple of this many tokens.
 inline int64_t pad_tokens(int64_t Lr) { return (Lr + 63) / 64 * 64; }

@@ -1,8 +1,8 @@
 // Streaming passes of the forward output and of the exact R = 2 tail VJP, one-reference-tile
 // schedule (gfx950).
 //
-// The adjoint [abstract: the R = 2 score cotangent is the reference plan tile times a modifier
-// field of vector cotangents and dual differences; technical summaries §2.2: orbit equation
+// The adjoint [abstract: dS = P22 * M, M formed from the tail's vector cotangents and the
+// exp(u^(a) - u^(2)), exp(v^(b) - v^(2)) factors; technical summaries §2.2: orbit equation
 // P^(a,b) = P^(2,2) exp(u^(a) - u^(2)) exp(v^(b) - v^(2))], with P22 = exp(S + u2 + v2),
 // g_ij = dO_i . V_j and e^{du1} = exp(u1 - u2), e^{dv_b} = exp(v_b - v2), in four passes:
 //
@@ -1012,34 +1012,6 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   }
 }
 
-#ifndef SKA_BF16_NW
-#define SKA_BF16_NW 8
-#endif
-// Waves per workgroup of the streaming passes: bf16 uses 8 waves (128-token blocks, two waves per
-// SIMD with room for the pipelined strips' registers) with two window rings of 128 + 32 H16 rows,
-// fp32 4 waves; both up to the halo LDS holds (one workgroup per CU).
-int vjp_stream_waves(int elt, int h, int* nt) {
-  const int h16 = (h + 15) / 16;
-  const int H16 = (h16 <= 2) ? 2 : (h16 <= 4) ? 4 : (h16 <= 8) ? 8 : 0;
-  if (H16 == 0) return 0;
-  if (elt == 0 && H16 > 4) return 0;
-  *nt = 1 + 2 * H16;
-  return (elt == 1) ? SKA_BF16_NW : 4;
-}
-
-void vjp_stream_segments(int64_t bh, int Lr, int nw, int nt, int* seg_len, int* nseg) {
-  const int br = 16 * nw;
-  const int64_t nblk = (Lr + br - 1) / br;
-  const int64_t target = 256;   // one workgroup per CU
-  int64_t sl = (bh * nblk + target - 1) / target;
-  const int64_t min_sl = (16 * (nt - 1) + br - 1) / br;   // 2 * halo <= seg span
-  if (sl < min_sl) sl = min_sl;
-  if (sl < 1) sl = 1;
-  if (sl > nblk) sl = nblk;
-  *seg_len = (int)sl;
-  *nseg = (int)((nblk + sl - 1) / sl);
-}
-
 template <typename T, int NT, int NW>
 static void launch_nt_general(int pass, const VjpArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.bh * (int64_t)a.nseg)), block(NW * 64);
@@ -1090,9 +1062,9 @@ hipError_t launch_vjp_stream_general(int elt, int nt, int nw, int pass, const Vj
   if ((pass == 1 || pass == 2) && a.R < 1) return hipErrorInvalidValue;
   if (pass == 5 && (a.level < 1 || a.level >= a.R)) return hipErrorInvalidValue;
   if (elt == 1) {
-    if (nt == 5) launch_nt_general<bf16, 5, SKA_BF16_NW>(pass, a, st);
-    else if (nt == 9) launch_nt_general<bf16, 9, SKA_BF16_NW>(pass, a, st);
-    else launch_nt_general<bf16, 17, SKA_BF16_NW>(pass, a, st);
+    if (nt == 5) launch_nt_general<bf16, 5, kBf16StreamWaves>(pass, a, st);
+    else if (nt == 9) launch_nt_general<bf16, 9, kBf16StreamWaves>(pass, a, st);
+    else launch_nt_general<bf16, 17, kBf16StreamWaves>(pass, a, st);
   } else {
     if (nt == 5) launch_nt_general<float, 5, 4>(pass, a, st);
     else launch_nt_general<float, 9, 4>(pass, a, st);
@@ -1103,9 +1075,9 @@ hipError_t launch_vjp_stream_general(int elt, int nt, int nw, int pass, const Vj
 hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, bool d4, const VjpArgs& a,
                                   hipStream_t st) {
   if (elt == 1) {
-    if (nt == 5) launch_nt<bf16, 5, SKA_BF16_NW>(pass, d4, a, st);
-    else if (nt == 9) launch_nt<bf16, 9, SKA_BF16_NW>(pass, d4, a, st);
-    else launch_nt<bf16, 17, SKA_BF16_NW>(pass, d4, a, st);
+    if (nt == 5) launch_nt<bf16, 5, kBf16StreamWaves>(pass, d4, a, st);
+    else if (nt == 9) launch_nt<bf16, 9, kBf16StreamWaves>(pass, d4, a, st);
+    else launch_nt<bf16, 17, kBf16StreamWaves>(pass, d4, a, st);
   } else {
     if (nt == 5) launch_nt<float, 5, 4>(pass, d4, a, st);
     else launch_nt<float, 9, 4>(pass, d4, a, st);

@@ -17,7 +17,7 @@
 // finishes the column update, exactly where a column's mass underflows.
 //
 // Output and VJP [output: the reference plan P^(2,2) applied to V; abstract and technical
-// summaries §2.2: the R = 2 score cotangent as the reference plan tile times a modifier field]:
+// summaries §2.2: dS = P22 * M, M from the vector cotangents and the dual-difference factors]:
 // wide_pass_kernel runs the output and five VJP passes, each owning the side it reduces over, so
 // no pass needs partial sums across workgroups:
 //   out (owns queries)  O_i = sum_j P22_ij V_j
@@ -48,7 +48,6 @@
 
 namespace ska {
 
-constexpr int kWideWaves = 8;
 constexpr int kWideThreads = 64 * kWideWaves;
 
 // Window of row tile rt: tiles t0 .. t0 + nt - 1; wave w takes tiles wt0 .. wt0 + wnt - 1.
@@ -898,13 +897,6 @@ __global__ __launch_bounds__(kWideThreads) void tail_pass_kernel(WideArgs a) {
 // =============================================================================================
 // launchers
 // =============================================================================================
-int wide_step_tiles(int Lr, int h) {
-  const int per_wave = (wide_window_tiles(Lr, h) + kWideWaves - 1) / kWideWaves;
-  for (int kt : {4, 8, 12, 16, 24, 33})
-    if (per_wave <= kt) return kt;
-  return 0;
-}
-
 static dim3 wide_grid(const WideArgs& a) {
   const int64_t nwork = a.bh * (int64_t)a.nrt;
   return dim3((unsigned)(8 * ((nwork + 7) / 8)), 1, 1);

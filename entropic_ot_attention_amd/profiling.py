@@ -28,7 +28,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 STEP_KERNEL_SOURCES = [os.path.join(PKG, "csrc", f)
-                       for f in ("ska_fused.hip", "ska_device.h", "ska_internal.h")]
+                       for f in ("ska_fused.hip", "ska_device.h", "ska_internal.h",
+                                 "ska_geometry.cpp")]
 
 
 def source_sha(paths=None) -> str:

@@ -309,3 +309,19 @@ def test_contraction_layout_and_checks():
     assert f(ctypes.byref(prob), 16, V(FAKE), V(FAKE), V(FAKE + 2), None, None, None) == -1
     empty = _prob(bh=0)
     assert f(ctypes.byref(empty), 16, None, None, None, None, None, None) == 0
+
+
+def test_noalloc_forward_checks_arguments_and_size_on_the_host():
+    """sinkhorn_attn_fwd_noalloc rejects a malformed problem, and one whose forward workspace is
+    larger than its static array (32 MiB), before it touches a device; 4 problems of 262144
+    tokens at W = 256 fit, 8 do not."""
+    vp = ctypes.c_void_p(FAKE)
+    big = _prob(bh=8, L=262144, W=256, T=15, dtype=B.SKA_BF16)
+    st, n = _ws_bytes(big, B.SKA_OP_FWD)
+    assert st == 0 and n > (32 << 20)
+    assert B.lib.sinkhorn_attn_fwd_noalloc(ctypes.byref(big), vp, vp, vp, vp, vp, None) == -2
+    assert "static scratch" in B.ska_last_error()
+    st, n = _ws_bytes(_prob(bh=4, L=262144, W=256, T=15, dtype=B.SKA_BF16), B.SKA_OP_FWD)
+    assert st == 0 and n <= (32 << 20)
+    assert B.lib.sinkhorn_attn_fwd_noalloc(ctypes.byref(_prob(W=15)), vp, vp, vp, vp, vp, None) == -1
+    assert B.lib.sinkhorn_attn_fwd_noalloc(None, vp, vp, vp, vp, vp, None) == -1
