@@ -108,9 +108,9 @@ ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K,
  * 2 R + 2 passes of the one-reference adjoint, the modifier field then holding 2 R terms; R = 0
  * runs dV, dQ and dK of the base plan with both duals fixed (score cotangent P * g)
  * (technical summaries §2.1: R differentiable tail steps; §4.1: tail gradients from R = 0 up).
- * (abstract: one-reference-tile schedule, score cotangent = reference tile times a modifier
- * field of vector cotangents and dual differences; atlas.scime.ai Key results: complete
- * arbitrary-cotangent Q/K/V VJP.) */
+ * (abstract: one-reference-tile schedule, dS = P^(R,R) * M with M formed from the vector
+ * cotangents and the exp(u^(a) - u^(R)), exp(v^(b) - v^(R)) factors; atlas.scime.ai Key
+ * results: complete arbitrary-cotangent Q/K/V VJP.) */
 ska_status sinkhorn_attn_vjp(const ska_problem* p, const void* Q, const void* K, const void* V,
                              const float* duals, const void* dO, void* dQ, void* dK, void* dV,
                              ska_schedule schedule, void* workspace, size_t workspace_bytes,

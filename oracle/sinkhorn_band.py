@@ -356,9 +356,9 @@ def vjp_one_reference(Q, K, V, dO, duals, prob: BandProblem, active=None, want_p
     Modifier field and score cotangent:
       M_ij = g_ij - dv2_j - du2_i e^{dv1_j} - e^{du1_i} dv1_j e^{dv1_j} - du1_i e^{du1_i} e^{dv0_j}
       (with e^{du_a} = exp(u^(a) - u^(2)), e^{dv_b} = exp(v^(b) - v^(2))),  dS = P22 * M.
-    [abstract: the R = 2 score cotangent is one reference plan tile times an explicit
-    modifier field built from vector cotangents and dual differences; technical
-    summaries §2.2: orbit equation P^(a,b) = P^(2,2) * exp(u^(a)-u^(2)) * exp(v^(b)-v^(2))]"""
+    [abstract (dS = P22 * M, with M formed from the tail's vector cotangents and the
+    exp(u^(a) - u^(2)), exp(v^(b) - v^(2)) factors); technical summaries §2.2: orbit
+    equation P^(a,b) = P^(2,2) * exp(u^(a)-u^(2)) * exp(v^(b)-v^(2))]"""
     if prob.R != 2:
         raise ValueError("the one-reference schedule here is the R = 2 case")
     h = prob.h
@@ -472,8 +472,8 @@ def vjp_tail_one_reference(Q, K, V, dO, duals, prob: BandProblem, active=None,
       M_ij = g_ij - sum_a eu_a(i) ev_a(j) dv^(a)_j - sum_a eu_a(i) du^(a)_i ev_{a-1}(j),
       dS = P * M.
     R = 2 is vjp_one_reference; R = 0 has no levels, so M = g.
-    [abstract: one reference plan tile times a modifier field of vector cotangents and dual
-    differences; technical summaries §2.2: orbit equation P^(a,b) = P^(R,R) exp(du) exp(dv)]"""
+    [abstract (dS = P^(R,R) * M, M of rank 2 R from the vector cotangents and the dual
+    differences); technical summaries §2.2: orbit equation P^(a,b) = P^(R,R) exp(du) exp(dv)]"""
     R = prob.R
     h = prob.h
     d = np.asarray(Q).shape[1]
