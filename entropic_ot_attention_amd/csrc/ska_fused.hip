@@ -277,20 +277,29 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
             lds_frag(f, kring, rt + n, g);
           }
         };
-        // key fragments KA tiles ahead of the matrix cores (an LDS read takes longer than the
-        // work on one tile)
+        // key fragments and column duals KA tiles ahead of the matrix cores (an LDS read takes
+        // longer than the work on one tile; reads complete in order, so a dual read just before
+        // its use would also wait for the fragments issued ahead of it)
         constexpr int KA = 2;
         Frag<T> fk[KA + 1];
+        float vj[KA + 1];
 #pragma unroll
-        for (int t = 0; t < KA && t < NT; ++t) kfrag(fk[t], tile_row(t));
+        for (int t = 0; t < KA && t < NT; ++t) {
+          kfrag(fk[t], tile_row(t));
+          vj[t] = vlane[tile_row(t)];
+        }
+        // the matrix-core products run one tile ahead of the vector work on them
+        x[0] = dot_tile(fq, fk[0], shc);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const int rt = tile_row(t);
-          if (t + KA < NT) kfrag(fk[(t + KA) % (KA + 1)], tile_row(t + KA));
+          if (t + 1 < NT) x[t + 1] = dot_tile(fq, fk[(t + 1) % (KA + 1)], shc);
+          if (t + KA < NT) {
+            kfrag(fk[(t + KA) % (KA + 1)], tile_row(t + KA));
+            vj[(t + KA) % (KA + 1)] = vlane[tile_row(t + KA)];
+          }
           if (t == kPrio1 && t > 0) __builtin_amdgcn_s_setprio(1);
           if (t == kPrio2) __builtin_amdgcn_s_setprio(2);
-          const float vjt = vlane[rt];
-          x[t] = dot_tile(fq, fk[t % (KA + 1)], shc);
+          const float vjt = vj[t % (KA + 1)];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float xv = fmaf(x[t][r], c2, vjt);
@@ -483,29 +492,6 @@ __global__ __launch_bounds__(256) void finish_columns_kernel(StepArgs a) {
                                    a.u_prev + vo, Qh, Kh, a);
   a.v_next[vo + j] = v;
   if (a.save_v) a.save_v[head * a.save_v_stride + j] = v * kLn2;
-}
-
-int fused_tiles_for(int h) {
-  const int h16 = (h + 15) / 16;     // halo tiles; classes use an even count
-  if (h16 <= 2) return 5;
-  if (h16 <= 4) return 9;
-  if (h16 <= 8) return 17;
-  if (h16 <= 12) return 25;
-  return 0;
-}
-
-// Segments: enough workgroups to fill the GPU about once (256 CUs x 3 resident workgroups),
-// and at least H16 / 2 blocks each so a column's partials come from at most two segments.
-void fused_segments(int64_t bh, int Lr, int nt, int* seg_len, int* nseg) {
-  const int64_t nblk = (Lr + 63) / 64;
-  const int64_t target = 768;
-  int64_t sl = (bh * nblk + target - 1) / target;
-  const int64_t min_sl = ((nt - 1) / 2 + 1) / 2;
-  if (sl < min_sl) sl = min_sl;
-  if (sl < 1) sl = 1;
-  if (sl > nblk) sl = nblk;
-  *seg_len = (int)sl;
-  *nseg = (int)((nblk + sl - 1) / sl);
 }
 
 template <typename T, int NT>
