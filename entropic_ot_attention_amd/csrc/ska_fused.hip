@@ -152,6 +152,8 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
   };
 
   const bool exact_h = (h == 16 * H16);
+  // per-lane offsets of the lane's query row (from a block's first row) and row-shift group
+  const int q_lane = (16 * wave + n) * kD, u_lane = 16 * wave + 4 * g;
   // per-wave column sums live at columns [16 wave, 16 wave + 16 NT) of a RING-wide row; the
   // other columns stay zero so the block sum below needs no coverage tests
   for (int c = threadIdx.x; c < kWaves * RING; c += 256) cpart[c] = 0.f;
@@ -212,9 +214,17 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
     if (more) {
       if (enter0 >= 0 && enter0 + 64 <= Lr) nr.load_inside(Kh, enter0);
       else nr.load(Kh, enter0, Lr);
-      const int on = b0n + 16 * wave + n;
-      load_frag(fq_next, Qh + (int64_t)on * kD, (b0n + 64 <= Lr) || (on < Lr), g);
-      ush_next = shift_rows(b0n + 16 * wave + 4 * g);
+      if (b0n >= 0 && b0n + 64 <= Lr) {
+        // every row of the next block lies inside the sequence: a block base plus the lane's
+        // fixed offset, with no validity test
+        load_frag_raw(fq_next, Qh + (int64_t)b0n * kD + q_lane, g);
+        if constexpr (SHIFT) ush_next = load4(u_prev_h + b0n + u_lane);
+        else ush_next = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        const int on = b0n + 16 * wave + n;
+        load_frag(fq_next, Qh + (int64_t)on * kD, on < Lr, g);
+        ush_next = shift_rows(b0n + u_lane);
+      }
       if (wave == dw) {
         // Keys j = enter0 + lane enter with the next block.  Inside a segment their column
         // partials sit at fixed offsets (no divisions): the segment's own row at j - c_lo, and,
@@ -406,13 +416,24 @@ __global__ __launch_bounds__(256) void sinkhorn_step_kernel(StepArgs a) {
       }
       float rinv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ll[r] = row16_sum(ll[r]);
-        // no terms: rows past the sequence (never on interior blocks)
-        const bool empty = !interior && (ll[r] == 0.f);
-        const float lg = SHIFT ? fast_log2(ll[r]) : mx[r] + fast_log2(ll[r]);
-        u[r] = empty ? 0.f : fmaf(shc[r], c2, -lg);
-        rinv[r] = empty ? 0.f : __builtin_amdgcn_rcpf(ll[r]);
+      for (int r = 0; r < 4; ++r) ll[r] = row16_sum(ll[r]);
+      if (interior) {
+        // every row has band entries
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float lg = SHIFT ? fast_log2(ll[r]) : mx[r] + fast_log2(ll[r]);
+          u[r] = fmaf(shc[r], c2, -lg);
+          rinv[r] = __builtin_amdgcn_rcpf(ll[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // no terms: rows past the sequence
+          const bool empty = (ll[r] == 0.f);
+          const float lg = SHIFT ? fast_log2(ll[r]) : mx[r] + fast_log2(ll[r]);
+          u[r] = empty ? 0.f : fmaf(shc[r], c2, -lg);
+          rinv[r] = empty ? 0.f : __builtin_amdgcn_rcpf(ll[r]);
+        }
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t)
