@@ -192,6 +192,12 @@ template <int PASS, bool D4, int GEN> struct VjpPass {
   static constexpr bool uses_ring_b = (PASS != 5);
   static constexpr bool reads_part = (PASS == 3 || PASS == 5);
   static constexpr bool writes_part = (PASS == 2 || PASS == 5);
+  // contracts the reference plan (or the score cotangent) with a window tensor, tile pair by
+  // tile pair
+  // (the direct-four passes 3 and 4 run at phase 0 only: two phases of their wider tile work
+  // exceed the register file)
+  static constexpr bool contracts = (PASS == 0 || ((PASS == 3 || PASS == 4) && !D4) || PASS == 6 ||
+                                     PASS == 7);
   // the modifier field on the matrix cores (one fp32 16x16x4 product per k-step of 4 terms):
   // general depth passes 6 and 7, and the one-reference passes 3 (D + A E + B F) and
   // 4 (D + A E + B F + C G)
@@ -241,6 +247,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
 
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // pairing phase of the wave: waves w and w + 4 of an 8-wave workgroup share a SIMD
+  const bool phase = NW == 8 && ((wave >> 2) & 1) != 0;
   const int64_t head = blockIdx.x / a.nseg;
   const int seg = blockIdx.x % a.nseg;
   const int blk0 = seg * a.seg_len, blk1 = min(blk0 + a.seg_len, a.nblk);
@@ -480,6 +488,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   const T* laneB = ringB + n * LS + 16 * g;
   const TrLane trl(g, n);
 
+  // the block walk, with the pairing phase of this wave fixed for the whole walk
+  auto walk = [&](auto phase_c) {
   for (int blk = blk0; blk < blk1; ++blk) {
     const int b0 = BR * blk;
     const int cb = b0 - halo;                  // block window [cb, cb + RING)
@@ -528,8 +538,16 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     // Score tile t with the owned dual in the accumulator: the exponent of P22 is
     // c2 * sc + (window dual).  Masks: I (interior) needs them only on tiles 0 and NT - 1, along
     // fixed lane patterns; otherwise per entry, and tiles off the band or the sequence are dead.
-    auto body = [&](auto interior_c) {
+    auto body = [&](auto interior_c, auto phase_c) {
       constexpr bool I = decltype(interior_c)::value;
+      // Pairing phase of the contractions over window-tile pairs: phase 0 pairs tiles (0, 1),
+      // (2, 3), ..., phase 1 (0), (1, 2), (3, 4), ...  The two waves that share a SIMD take
+      // opposite phases, so one issues its burst of contraction products while the other works
+      // on its vector operations.
+      constexpr int PH = decltype(phase_c)::value;
+      auto zslot = [](int t) { return (t + PH) & 1; };
+      auto pair_starts = [&](int t) { return zslot(t) == 0 || t == 0; };
+      auto pair_ends = [&](int t) { return zslot(t) == 1 || t == NT - 1; };
       auto dead = [&](int t) -> bool {
         if constexpr (I) return false;
         const int j0 = cw + 16 * t;
@@ -598,10 +616,11 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         }
       };
       // transposed contraction operands of the pair starting at tile t (fetched at its first
-      // tile, used after its second)
+      // tile, used after its second).  A single-tile pair (the first tile at phase 1, the last
+      // one where the count is odd) reads its own rows twice against a zero half.
       PairOps<T> opA, opB;
       auto pair_fetch = [&](int t) {
-        const int r0 = tile_slot(t), r1 = (t + 1 < NT) ? tile_slot(t + 1) : r0;
+        const int r0 = tile_slot(t), r1 = (zslot(t) == 0 && t + 1 < NT) ? tile_slot(t + 1) : r0;
         if constexpr (PASS == 0) opB.fetch(ringB, trl, r0, r1);
         if constexpr (PASS == 3 || PASS == 4 || PASS == 6 || PASS == 7) opA.fetch(ringA, trl, r0, r1);
         if constexpr (PASS == 4 || PASS == 7) opB.fetch(ringB, trl, r0, r1);
@@ -672,18 +691,18 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         for (int b = 0; b < 4; ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4&) {
-          const int tt = t & 1;
-          if (tt == 0) pair_fetch(t);
+          const int tt = zslot(t);
+          if (pair_starts(t)) pair_fetch(t);
           const f32x4 vw = wb[t & 1][0];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = fast_exp2(fmaf(s[r], c2, vw[r]));
             z[tt][r] = (keep_w(t, r) && !dead(t)) ? p : 0.f;
           }
-          if (tt == 1 || t == NT - 1) {
-            if (tt == 0) {
+          if (pair_ends(t)) {
+            if (pair_starts(t)) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) z[1][r] = 0.f;
+              for (int r = 0; r < 4; ++r) z[1 - tt][r] = 0.f;
             }
             opB.contract(Y, ringB, trl, z, g, n);
           }
@@ -765,8 +784,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z1[2][4], z2[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
-          const int tt = t & 1;
-          if (tt == 0) pair_fetch(t);
+          const int tt = zslot(t);
+          if (pair_starts(t)) pair_fetch(t);
           const bool live = !dead(t);
           if constexpr (!D4) {
             // md = D_j + A_i E_j + B_i F_j from the matrix cores
@@ -796,10 +815,10 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
               z2[tt][r] = keep ? p10 : 0.f;
             }
           }
-          if (tt == 1 || t == NT - 1) {
-            if (tt == 0) {
+          if (pair_ends(t)) {
+            if (pair_starts(t)) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) z1[1][r] = z2[1][r] = 0.f;
+              for (int r = 0; r < 4; ++r) z1[1 - tt][r] = z2[1 - tt][r] = 0.f;
             }
             opA.contract2(X, Y, ringA, trl, z1, z2, g, n);
           }
@@ -828,8 +847,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z1[2][4], z2[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
-          const int tt = t & 1;
-          if (tt == 0) pair_fetch(t);
+          const int tt = zslot(t);
+          if (pair_starts(t)) pair_fetch(t);
           const f32x4 uw = wb[t & 1][0];
           const bool live = !dead(t);
           if constexpr (!D4) {
@@ -856,10 +875,10 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
               z2[tt][r] = keep ? p22 : 0.f;
             }
           }
-          if (tt == 1 || t == NT - 1) {
-            if (tt == 0) {
+          if (pair_ends(t)) {
+            if (pair_starts(t)) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) z1[1][r] = z2[1][r] = 0.f;
+              for (int r = 0; r < 4; ++r) z1[1 - tt][r] = z2[1 - tt][r] = 0.f;
             }
             opA.contract(X, ringA, trl, z1, g, n);
             opB.contract(Y, ringB, trl, z2, g, n);
@@ -919,8 +938,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         for (int b = 0; b < 4; ++b) X[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
-          const int tt = t & 1;
-          if (tt == 0) pair_fetch(t);
+          const int tt = zslot(t);
+          if (pair_starts(t)) pair_fetch(t);
           const f32x4 vw = wb[t & 1][0], mm = md[t & 1];
           const bool live = !dead(t);
 #pragma unroll
@@ -929,10 +948,10 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
             const float p = (keep_w(t, r) && live) ? e : 0.f;
             z[tt][r] = p * (gg[r] - mm[r]);
           }
-          if (tt == 1 || t == NT - 1) {
-            if (tt == 0) {
+          if (pair_ends(t)) {
+            if (pair_starts(t)) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) z[1][r] = 0.f;
+              for (int r = 0; r < 4; ++r) z[1 - tt][r] = 0.f;
             }
             opA.contract(X, ringA, trl, z, g, n);
           }
@@ -946,8 +965,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z1[2][4], z2[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
-          const int tt = t & 1;
-          if (tt == 0) pair_fetch(t);
+          const int tt = zslot(t);
+          if (pair_starts(t)) pair_fetch(t);
           const f32x4 uw = wb[t & 1][0], mm = md[t & 1];
           const bool live = !dead(t);
 #pragma unroll
@@ -957,10 +976,10 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
             z1[tt][r] = p * (gg[r] - mm[r]);
             z2[tt][r] = p;
           }
-          if (tt == 1 || t == NT - 1) {
-            if (tt == 0) {
+          if (pair_ends(t)) {
+            if (pair_starts(t)) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) z1[1][r] = z2[1][r] = 0.f;
+              for (int r = 0; r < 4; ++r) z1[1 - tt][r] = z2[1 - tt][r] = 0.f;
             }
             opA.contract(X, ringA, trl, z1, g, n);
             opB.contract(Y, ringB, trl, z2, g, n);
@@ -972,8 +991,11 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         }
       }
     };
-    if (interior) body(std::true_type{});
-    else body(std::false_type{});
+    if (interior) {
+      body(std::true_type{}, phase_c);
+    } else {
+      body(std::false_type{}, std::integral_constant<int, 0>{});
+    }
 
     __syncthreads();   // every wave is done with this block's window
     if constexpr (P::writes_part) {
@@ -1010,6 +1032,9 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       __syncthreads();
     }
   }
+  };
+  if (P::contracts && phase) walk(std::integral_constant<int, 1>{});
+  else walk(std::integral_constant<int, 0>{});
 }
 
 template <typename T, int NT, int NW>
