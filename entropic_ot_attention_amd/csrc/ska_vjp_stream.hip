@@ -52,6 +52,21 @@ __device__ __forceinline__ s16x4 tr_read(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p));
 }
 
+// Four fp32 values as bf16 (high, low) parts, (h0, h1, h2, h3, l0, l1, l2, l3) with
+// h = bf16(x) and l = bf16(x - h), both rounded to nearest: x = h + l + e, |e| <= 2^-18 |x|, so a
+// product x y formed as hx hy + lx hy + hx ly on the bf16 matrix cores (fp32 accumulation) is
+// within about 2^-16 of x y relative.
+__device__ __forceinline__ bf16x8 split_bf16x4(const float (&x)[4]) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16 h = (bf16)x[e];
+    r[e] = h;
+    r[4 + e] = (bf16)(x[e] - (float)h);
+  }
+  return r;
+}
+
 // z[tt][r] -> bf16 B operand (rows 4 g + r of tile tt of the pair)
 __device__ __forceinline__ bf16x8 pack_z(const float (&z)[2][4]) {
   bf16x8 zb;
@@ -244,6 +259,10 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   __shared__ __attribute__((aligned(16))) float wv[NV][RING];  // window vectors
   __shared__ float pring[P::writes_part ? RING : 1];
   __shared__ float cpart[P::writes_part ? NW * RING : 1];
+  // bf16 one-reference passes 3 and 4: the modifier's window-side factors of each window token,
+  // split into high and low bf16 parts, (h0, h1, h2, h3, l0, l1, l2, l3)
+  constexpr bool SPLITMOD = P::modk && GEN < 0 && std::is_same<T, bf16>::value;
+  __shared__ __attribute__((aligned(16))) bf16x8 wmod[SPLITMOD ? RING : 1];
 
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -376,6 +395,23 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   auto vec_store = [&](int j, int slot, const VecIn& in) {
 #pragma unroll
     for (int k = 0; k < NV; ++k) wv[k][slot] = in.v[k] * in.w;
+    if constexpr (SPLITMOD) {
+      // pass 3: (D, E, F, 0); pass 4: (A, B, C, 1)
+      float m[4];
+      if constexpr (PASS == 3) {
+        const float E = in.v[2] * in.w;
+        m[0] = in.v[1] * in.w;
+        m[1] = E;
+        m[2] = -E * E * (in.p0 * in.w0 + in.p1 * in.w1);
+        m[3] = 0.f;
+      } else {
+        m[0] = in.v[1] * in.w;
+        m[1] = in.v[2] * in.w;
+        m[2] = in.v[3] * in.w;
+        m[3] = in.w;
+      }
+      wmod[slot] = split_bf16x4(m);
+    }
     if constexpr (PASS == 3 && !D4) {
       const float E = in.v[2] * in.w;
       const float dv1 = -E * (in.p0 * in.w0 + in.p1 * in.w1);
@@ -446,7 +482,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     } else {
       o[0] *= inv_c2;
     }
-    if constexpr (P::modk && GEN < 0) {
+    if constexpr (P::modk && GEN < 0 && !SPLITMOD) {
       // owned-side operand of the modifier product for lane group g (k-slot g):
       // pass 3: (1, A_i, B_i, 0) against the window's (D_j, E_j, F_j, G_j);
       // pass 4: (E_j, F_j, G_j, D_j) against the window's (A_i, B_i, C_i, 1)
@@ -457,6 +493,35 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       }
     }
   };
+
+  // bf16 one-reference passes 3 and 4: the owned side of the modifier product, negated (the
+  // product is added to the g tile) and split: lane group 0 gives (h0..h3, h0..h3) against the
+  // window's (h0..h3, l0..l3), lane group 1 (l0..l3, 0..0), lane groups 2 and 3 zeros, so the
+  // product sums hw ho + lw ho + hw lo over the four factors.
+  // pass 3: (1, A_i, B_i, 0); pass 4: (E_j, F_j, G_j, D_j)
+  auto mod_operand = [&](const float (&o)[NO]) -> bf16x8 {
+    float m[4];
+    if constexpr (PASS == 3) {
+      m[0] = -1.f;
+      m[1] = -o[1 % NO];
+      m[2] = -o[2 % NO];
+      m[3] = 0.f;
+    } else {
+      m[0] = -o[2 % NO];
+      m[1] = -o[3 % NO];
+      m[2] = -o[4 % NO];
+      m[3] = -o[1 % NO];
+    }
+    const bf16x8 hl = split_bf16x4(m);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (g == 0) ? hl[e] : (g == 1) ? hl[4 + e] : (bf16)0.f;
+      r[4 + e] = (g == 0) ? hl[e] : (bf16)0.f;
+    }
+    return r;
+  };
+  bf16x8 ownmod;
 
   // ---- prologue: the first block's window, vectors and owned operands ----
   {
@@ -480,6 +545,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     if (P::needs_g) load_frag(fB, ownB + (int64_t)o * kD, o < Lr, g);
     own_loads(BR * blk0 + 16 * wave, own);
     own_prep(own);
+    if constexpr (SPLITMOD) ownmod = mod_operand(own);
   }
   __syncthreads();
 
@@ -585,6 +651,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       constexpr int NWV = P::rows_in_regs ? 1 : MODK ? (PASS == 3 ? 4 : 2) : NV;
       f32x4 wb[2][NWV];
       f32x4 md[2];      // passes 6 and 7: modifier tile sum_k alpha_k beta_k, same layout as sc
+      bf16x8 wm[2];     // bf16 passes 3 and 4: the window side of the split modifier product
       const f32x4 ci = D4 ? f32x4{0.f, 0.f, 0.f, 0.f}
                    : P::rows_in_regs ? f32x4{own[0], own[1 % NO], own[2 % NO], own[3 % NO]}
                                      : f32x4{own[0], own[0], own[0], own[0]};
@@ -603,9 +670,13 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
           if constexpr (D4) wb[t & 1][0][2] = wv[2 % NV][rt + n];
         } else if constexpr (MODK) {
           wb[t & 1][0] = wvec4(0, rt);
-          // A operand of k-step st: lane (g, n) gives the tile's window token n, pair 4 st + g
+          if constexpr (SPLITMOD) {
+            wm[t & 1] = wmod[rt + n];            // A operand: window token n, every lane group
+          } else {
+            // A operand of k-step st: lane (g, n) gives the tile's window token n, pair 4 st + g
 #pragma unroll
-          for (int st = 0; st < P::KS; ++st) wb[t & 1][1 % NWV][st] = wv[(1 + 4 * st + g) % NV][rt + n];
+            for (int st = 0; st < P::KS; ++st) wb[t & 1][1 % NWV][st] = wv[(1 + 4 * st + g) % NV][rt + n];
+          }
           if constexpr (PASS == 3) {
             wb[t & 1][2 % NWV] = wvec4(3, rt);     // F
             wb[t & 1][3 % NWV] = wvec4(4, rt);     // G
@@ -631,8 +702,15 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
           if constexpr (P::needs_g) gv[t & 1] = dot_tile(fB, fwg[t & 1]);
         } else {
           sc[t & 1] = dot_tile(fw[t & 1], fA, ci);
-          if constexpr (PASS != 0) gv[t & 1] = dot_tile(fwg[t & 1], fB);
-          if constexpr (MODK) {
+          if constexpr (SPLITMOD) {
+            // g - (modifier) in one accumulator
+            gv[t & 1] = dot_tile(fwg[t & 1], fB,
+                                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(wm[t & 1], ownmod,
+                                                                         f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0));
+          } else if constexpr (PASS != 0) {
+            gv[t & 1] = dot_tile(fwg[t & 1], fB);
+          }
+          if constexpr (MODK && !SPLITMOD) {
             // md[r] = sum_k (window token 4 g + r side)_k (owned token n side)_k
             f32x4 m = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -796,7 +874,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
               const float e = fast_exp2(fmaf(s[r], c2, vw[r]));
               const float p = (keep_w(t, r) && live) ? e : 0.f;
               acc = fmaf(p, Fw[r], acc);
-              z1[tt][r] = p * (gg[r] - mm[r]);
+              z1[tt][r] = SPLITMOD ? p * gg[r] : p * (gg[r] - mm[r]);
               z2[tt][r] = p * Gw[r];
             }
           } else {
@@ -858,7 +936,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
             for (int r = 0; r < 4; ++r) {
               const float e = fast_exp2(fmaf(s[r], c2, uw[r]));
               const float p = (keep_w(t, r) && live) ? e : 0.f;
-              z1[tt][r] = p * (gg[r] - mm[r]);
+              z1[tt][r] = SPLITMOD ? p * gg[r] : p * (gg[r] - mm[r]);
               z2[tt][r] = p;
             }
           } else {
@@ -1029,6 +1107,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       own_prep(own_next);
 #pragma unroll
       for (int k = 0; k < NO; ++k) own[k] = own_next[k];
+      if constexpr (SPLITMOD) ownmod = mod_operand(own);
       __syncthreads();
     }
   }
