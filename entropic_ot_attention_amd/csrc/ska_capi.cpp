@@ -131,6 +131,8 @@ struct RemLayout {
   size_t o, dq_r, dk_r, dv_r, dq_f, dk_f, dv_f, duals_r, duals_f, part, inner, inner_bytes, total;
 };
 RemLayout rem_layout(const Plan& pl);
+int64_t wide_part_floats(const Plan& pl);
+int64_t wide_plane_floats(const Plan& pl);
 
 size_t workspace_for(const Plan& pl, ska_op op) {
   if (pl.empty) return 0;
@@ -164,17 +166,27 @@ size_t workspace_for(const Plan& pl, ska_op op) {
   }
   const int nt = ska::fused_tiles_for(pl.g.h);
   if (nt == 0) {
-    // wide path: row and column duals plus one partial row per 16-token row tile; split path
-    // (windows wider than the wide step holds in registers): the two duals
-    const int64_t part = ska::wide_step_tiles(pl.g.Lr, pl.g.h) > 0
-                             ? pl.g.bh * ((pl.g.Lr + 15) / 16) * (16 * (int64_t)ska::wide_window_tiles(pl.g.Lr, pl.g.h))
-                             : 0;
-    return (size_t)(ska::kFwdVecs * vs + part) * sizeof(float);
+    // wide path: row and column duals plus one partial row per 16-token row tile (fp32: then Q
+    // and K as bf16 planes); split path (windows wider than the wide step holds in registers):
+    // the two duals
+    return (size_t)(ska::kFwdVecs * vs + wide_part_floats(pl) + wide_plane_floats(pl)) * sizeof(float);
   }
   int seg_len = 0, nseg = 0;
   ska::fused_segments(pl.g.bh, pl.g.Lr, nt, &seg_len, &nseg);
   const int64_t ps = pl.g.bh * (int64_t)nseg * ska::fused_pstride(nt, seg_len);
   return (size_t)(4 * vs + 2 * ps) * sizeof(float);
+}
+
+// Wide forward path: floats of the column partials (one partial row per 16-token row tile),
+// rounded up to 256 bytes, and of the fp32 step's bf16 planes of Q and K that follow them.
+int64_t wide_part_floats(const Plan& pl) {
+  if (ska::fused_tiles_for(pl.g.h) != 0 || ska::wide_step_tiles(pl.g.Lr, pl.g.h) <= 0) return 0;
+  const int64_t n = pl.g.bh * ((pl.g.Lr + 15) / 16) * (16 * (int64_t)ska::wide_window_tiles(pl.g.Lr, pl.g.h));
+  return (n + 63) / 64 * 64;
+}
+int64_t wide_plane_floats(const Plan& pl) {
+  if (pl.elt == SKA_BF16 || wide_part_floats(pl) == 0) return 0;
+  return 2 * pl.g.bh * (int64_t)pl.g.Lr * (ska::kPlaneRowElems / 2);
 }
 
 // Tail-remainder workspace: O, the two gradient sets (tail at depth R, full at depth T + R),
@@ -372,6 +384,16 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
     a.save_stride = dstride;
     hipError_t e = ska::launch_fill(u, 2 * vs, 0.f, st);
     if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+    if (pl.elt != SKA_BF16) {
+      // the fp32 step's matrix-core operands: Q and K as bf16 planes, after the partial rows
+      float* planes = a.part + wide_part_floats(pl);
+      const int64_t rows = g.bh * (int64_t)g.Lr;
+      a.Qs = planes;
+      a.Ks = planes + rows * (ska::kPlaneRowElems / 2);
+      e = ska::launch_split3(static_cast<const float*>(Q), const_cast<void*>(a.Qs), rows, st);
+      if (e == hipSuccess) e = ska::launch_split3(static_cast<const float*>(K), const_cast<void*>(a.Ks), rows, st);
+      if (e != hipSuccess) return fail(SKA_ERR_HIP, hipGetErrorString(e));
+    }
     const int K_steps = p->T + p->R;
     for (int k = 1; k <= K_steps; ++k) {
       // step k: u_k from v_{k-1}; saves u_k and v_{k-1} where the layout keeps them

@@ -122,6 +122,8 @@ struct WideArgs {
   const void* K;
   const void* V;
   const void* dO;
+  const void* Qs;          // fp32 step: Q and K as three bf16 planes per row, [bh][Lr][192]
+  const void* Ks;
   void* out0;              // output pass: O; pass A: dV; pass D: dQ; pass E: dK
   const float* v_in;       // step / finish: column duals before the step (log2) [bh][Lpad]
   float* u_out;            // step: row duals of the step (log2); finish: read by the exact fallback
@@ -187,6 +189,11 @@ hipError_t launch_vjp_stream_pass(int elt, int nt, int nw, int pass, bool d4, co
 // steps shift the row log-sum-exp by the previous row duals (read from u_out before it is rewritten)
 hipError_t launch_wide_step(int elt, int kt, bool first, const WideArgs& a, hipStream_t st);
 hipError_t launch_wide_finish(int elt, const WideArgs& a, hipStream_t st);
+// x [rows][64] fp32 -> out [rows][192] bf16: the planes (h, m, l) of x = h + m + l (the fp32
+// wide step's matrix-core operands)
+hipError_t launch_split3(const float* x, void* out, int64_t rows, hipStream_t st);
+// bf16 elements of one tensor's planes per row
+constexpr int kPlaneRowElems = 3 * 64;
 // pass: 0 output, 1..5 the VJP passes A..E
 hipError_t launch_wide_pass(int elt, int pass, bool d4, const WideArgs& a, hipStream_t st);
 hipError_t launch_vjp_prep(const float* duals, float* ws, const Geometry& g, hipStream_t st);

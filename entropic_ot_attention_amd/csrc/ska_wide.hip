@@ -108,6 +108,75 @@ struct WaveStage {
   }
 };
 
+// fp32 inputs on the bf16 matrix cores.  Each value becomes three bf16 parts, x = h + m + l with
+// h = bf16(x), m = bf16(x - h), l = bf16(x - h - m), all rounded to nearest (the two differences
+// are exact in fp32), so |x - h - m - l| <= 2^-24 |x|; a row of 64 values is stored as the three
+// planes (h, m, l), 192 bf16.  A dot product q . k is then the six bf16 products
+// hq hk + hq mk + mq hk + hq lk + lq hk + mq mk with fp32 accumulation; the three dropped ones are
+// below 2^-24 |q| |k| per term, so the score keeps fp32 accuracy at twelve bf16 16x16x32 products
+// per tile instead of sixteen fp32 16x16x4 ones (a SIMD spends about 204 cycles on the former and
+// 512 on the latter).
+constexpr int kPlaneRow = 3 * kD;
+__global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ x, bf16* __restrict__ out,
+                                                     int64_t rows) {
+  typedef __bf16 bf16x4v __attribute__((__vector_size__(8)));
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // 4 values of one row
+  if (i >= rows * (kD / 4)) return;
+  const int64_t row = i / (kD / 4);
+  const int c = (int)(i % (kD / 4)) * 4;
+  const f32x4 v = *reinterpret_cast<const f32x4*>(x + row * kD + c);
+  bf16x4v hv, mv, lv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16 h = (bf16)v[e];
+    const float r1 = v[e] - (float)h;
+    const bf16 m = (bf16)r1;
+    hv[e] = h;
+    mv[e] = m;
+    lv[e] = (bf16)(r1 - (float)m);
+  }
+  bf16* o = out + row * kPlaneRow + c;
+  *reinterpret_cast<bf16x4v*>(o) = hv;
+  *reinterpret_cast<bf16x4v*>(o + kD) = mv;
+  *reinterpret_cast<bf16x4v*>(o + 2 * kD) = lv;
+}
+
+// q . k of a 16 x 16 tile from the three planes of each side (A: q, B: k), smallest terms first
+__device__ __forceinline__ f32x4 dot_tile3(const Frag<bf16> (&q)[3], const Frag<bf16> (&k)[3], f32x4 acc) {
+  acc = dot_tile(q[2], k[0], acc);
+  acc = dot_tile(q[0], k[2], acc);
+  acc = dot_tile(q[1], k[1], acc);
+  acc = dot_tile(q[1], k[0], acc);
+  acc = dot_tile(q[0], k[1], acc);
+  return dot_tile(q[0], k[0], acc);
+}
+
+// 16 window rows of three-plane bf16 [L][192] held per lane between their global load and their
+// LDS store (rows of kPlaneStage bf16; rows outside the sequence become zeros when stored)
+constexpr int kPlaneStage = kPlaneRow + 8;
+struct PlaneStage {
+  static constexpr int kCPR = kPlaneRow * 2 / 16;          // 16-byte chunks per row: 24
+  static constexpr int kPer = 16 * kCPR / 64;              // per lane: 6
+  uint4 x[kPer];
+  __device__ __forceinline__ void load(const bf16* base, int r0, int Lr, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * 64 + lane, row = c / kCPR, col = (c % kCPR) * 8;
+      const int t = min(r0 + row, Lr - 1);
+      x[i] = *reinterpret_cast<const uint4*>(base + (int64_t)t * kPlaneRow + col);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* lds, int r0, int Lr, int lane) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * 64 + lane, row = c / kCPR, col = (c % kCPR) * 8;
+      const bool ok = r0 + row < Lr;
+      *reinterpret_cast<uint4*>(lds + row * kPlaneStage + col) =
+          uint4{ok ? x[i].x : 0u, ok ? x[i].y : 0u, ok ? x[i].z : 0u, ok ? x[i].w : 0u};
+    }
+  }
+};
+
 // =============================================================================================
 // Fused step: row update of the row tile against its window, plus the tile's column partials.
 // =============================================================================================
@@ -135,24 +204,48 @@ __global__ __launch_bounds__(kWideThreads) void wide_step_kernel(WideArgs a) {
   // per-lane fragment loads.  Loads are never conditional (rows clamped into the sequence, chunks
   // past the wave's run re-read its rows) and validity is applied to the results, so a load is
   // waited on only where its data is used and the next chunk stays in flight.
-  __shared__ __attribute__((aligned(16))) T kstage[kWideWaves][32 * Lds<T>::stride];
-  T* sK = kstage[wave];
+  // fp32 (S3): Q and K arrive as three bf16 planes each (split3_kernel), the window one tile per
+  // chunk; bf16: the tensors themselves, two tiles per chunk.
+  constexpr bool S3 = std::is_same<T, float>::value;
+  constexpr int CT = S3 ? 1 : 2;           // tiles per staged chunk
+  __shared__ __attribute__((aligned(16))) T kstage[S3 ? 1 : kWideWaves][S3 ? 4 : 32 * Lds<T>::stride];
+  __shared__ __attribute__((aligned(16))) bf16 pstage[S3 ? kWideWaves : 1][S3 ? 16 * kPlaneStage : 8];
+  T* sK = kstage[S3 ? 0 : wave];
+  bf16* sP = pstage[S3 ? wave : 0];
+  const bf16* Qp = static_cast<const bf16*>(a.Qs) + head * (int64_t)Lr * kPlaneRow;
+  const bf16* Kp = static_cast<const bf16*>(a.Ks) + head * (int64_t)Lr * kPlaneRow;
   Frag<T> fq;
-  load_frag_raw(fq, Qh + (int64_t)min(o0 + n, Lr - 1) * kD, g);
-  constexpr int NC = (KT + 1) / 2;         // chunks of two tiles
+  Frag<bf16> fq3[3];
+  if constexpr (S3) {
+    const bf16* qrow = Qp + (int64_t)min(o0 + n, Lr - 1) * kPlaneRow;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) load_frag_raw(fq3[p], qrow + p * kD, g);
+  } else {
+    load_frag_raw(fq, Qh + (int64_t)min(o0 + n, Lr - 1) * kD, g);
+  }
+  constexpr int NC = (KT + CT - 1) / CT;
   WaveStage<T> ns;
+  PlaneStage ps;
   float vj[3][2];                          // v of key n of each tile of a chunk, chunk c in slot c % 3
-  auto chunk_row0 = [&](int c) { return 16 * (wt.wt0 + min(2 * c, max(wt.wnt - 1, 0))); };
+  auto chunk_row0 = [&](int c) { return 16 * (wt.wt0 + min(CT * c, max(wt.wnt - 1, 0))); };
   auto load_vj = [&](int c) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) vj[c % 3][tt] = vin[min(chunk_row0(c) + 16 * tt + n, Lr - 1)];
+    for (int tt = 0; tt < CT; ++tt) vj[c % 3][tt] = vin[min(chunk_row0(c) + 16 * tt + n, Lr - 1)];
+  };
+  auto stage_load = [&](int c) {
+    if constexpr (S3) ps.load(Kp, chunk_row0(c), Lr, lane);
+    else ns.load(Kh, chunk_row0(c), Lr, lane);
+  };
+  auto stage_store = [&](int c) {
+    if constexpr (S3) ps.store(sP, chunk_row0(c), Lr, lane);
+    else ns.store(sK, chunk_row0(c), Lr, lane);
   };
   load_vj(0);
-  ns.load(Kh, chunk_row0(0), Lr, lane);
-  ns.store(sK, chunk_row0(0), Lr, lane);
+  stage_load(0);
+  stage_store(0);
   if (NC > 1) {
     load_vj(1);
-    ns.load(Kh, chunk_row0(1), Lr, lane);
+    stage_load(1);
   }
   __builtin_amdgcn_wave_barrier();
 
@@ -191,30 +284,40 @@ __global__ __launch_bounds__(kWideThreads) void wide_step_kernel(WideArgs a) {
   // tile t + 1 is issued ahead of the vector work on tile t and the two interleave within the
   // wave, instead of the two waves of a SIMD alternating between whole MFMA and VALU phases.
   auto mma = [&](int t) -> f32x4 {
-    Frag<T> fk;
-    lds_frag(fk, sK, 16 * (t & 1) + n, g);
-    return dot_tile(fq, fk, ci);
+    if constexpr (S3) {
+      Frag<bf16> fk3[3];
+      const bf16* krow = sP + n * kPlaneStage;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) load_frag_raw(fk3[p], krow + p * kD, g);
+      return dot_tile3(fq3, fk3, ci);
+    } else {
+      Frag<T> fk;
+      lds_frag(fk, sK, 16 * (t & 1) + n, g);
+      return dot_tile(fq, fk, ci);
+    }
   };
   f32x4 sc[2];
   sc[0] = mma(0);
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     if (t + 1 < KT) {
-      if (t & 1) {
-        // tile t + 1 opens chunk c + 1: into the buffer, and chunk c + 2 into registers
-        const int c1 = (t + 1) >> 1;
+      if ((t + 1) % CT == 0) {
+        // tile t + 1 opens chunk c + 1: into the buffer (whose reads by the earlier products were
+        // issued before, and LDS accesses of a wave complete in order), and chunk c + 2 into
+        // registers
+        const int c1 = (t + 1) / CT;
         __builtin_amdgcn_wave_barrier();
-        ns.store(sK, chunk_row0(c1), Lr, lane);
+        stage_store(c1);
         __builtin_amdgcn_wave_barrier();
         if (c1 + 1 < NC) {
           load_vj(c1 + 1);
-          ns.load(Kh, chunk_row0(c1 + 1), Lr, lane);
+          stage_load(c1 + 1);
         }
       }
       sc[(t + 1) & 1] = mma(t + 1);
     }
     const f32x4 s = sc[t & 1];
-    const float vjt = vj[(t >> 1) % 3][t & 1];
+    const float vjt = vj[(t / CT) % 3][t % CT];
     const int j = 16 * (wt.wt0 + t) + n;
     const bool jv = (j < Lr) & (t < wt.wnt);
 #pragma unroll
@@ -924,6 +1027,13 @@ hipError_t launch_wide_step(int elt, int kt, bool first, const WideArgs& a, hipS
     if (first) wide_step_t<float, false>(kt, a, st);
     else wide_step_t<float, true>(kt, a, st);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_split3(const float* x, void* out, int64_t rows, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t n = rows * (kD / 4);
+  split3_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, static_cast<bf16*>(out), rows);
   return hipGetLastError();
 }
 

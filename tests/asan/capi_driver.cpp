@@ -32,6 +32,7 @@ hipError_t launch_vjp_stream_pass(int, int, int, int, bool, const VjpArgs&, hipS
 hipError_t launch_vjp_stream_general(int, int, int, int, const VjpArgs&, hipStream_t) { return stub(); }
 hipError_t launch_wide_step(int, int, bool, const WideArgs&, hipStream_t) { return stub(); }
 hipError_t launch_wide_finish(int, const WideArgs&, hipStream_t) { return stub(); }
+hipError_t launch_split3(const float*, void*, int64_t, hipStream_t) { return stub(); }
 hipError_t launch_wide_pass(int, int, bool, const WideArgs&, hipStream_t) { return stub(); }
 hipError_t launch_vjp_prep(const float*, float*, const Geometry&, hipStream_t) { return stub(); }
 hipError_t launch_sq_diff(int, const void*, const void*, int64_t, double*, double*, hipStream_t) { return stub(); }

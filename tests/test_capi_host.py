@@ -89,15 +89,18 @@ def _fused_fwd_bytes(bh, L, W):
     return (4 * bh * Lpad + 2 * bh * nseg * pst) * 4
 
 
-def _wide_fwd_bytes(bh, Lr, h):
+def _wide_fwd_bytes(bh, Lr, h, fp32=True):
     """Forward workspace of bands wider than the register-resident step: 2 dual vectors
     [bh][Lpad] plus, while a row tile's window (at most min(ceil(Lr / 16), (2 h + 15) // 16 + 2)
     tiles) fits 8 waves x 33 register tiles, one partial row of 16 x window floats per 16-token
-    row tile; wider windows (split half-steps) need only the duals."""
+    row tile, rounded up to 64 floats, and for fp32 Q and K as three bf16 planes (192 bf16 = 96
+    floats per row each); wider windows (split half-steps) need only the duals."""
     Lpad = -(-Lr // 64) * 64
     ntw = min(-(-Lr // 16), (2 * h + 15) // 16 + 2)
     part = bh * -(-Lr // 16) * 16 * ntw if -(-ntw // 8) <= 33 else 0
-    return (2 * bh * Lpad + part) * 4
+    part = -(-part // 64) * 64
+    planes = 2 * bh * Lr * 96 if part and fp32 else 0
+    return (2 * bh * Lpad + part + planes) * 4
 
 
 def _vjp_bytes(bh, L, W, bf16=False):
@@ -136,9 +139,11 @@ def test_workspace_sizes():
     # wider bands: the wide step's per-row-tile column partials, or only the duals once the
     # window outgrows the registers
     st, n = _ws_bytes(_prob(L=2000, bh=2, W=1000), B.SKA_OP_FWD)
-    assert st == 0 and n == _wide_fwd_bytes(2, 2000, 500) == (2 * 2 * 2048 + 2 * 125 * 16 * 65) * 4
+    assert st == 0 and n == _wide_fwd_bytes(2, 2000, 500) == (2 * 2 * 2048 + 260032 + 2 * 2 * 2000 * 96) * 4
+    st, n = _ws_bytes(_prob(L=2000, bh=2, W=1000, dtype=B.SKA_BF16), B.SKA_OP_FWD)
+    assert st == 0 and n == _wide_fwd_bytes(2, 2000, 500, fp32=False) == (2 * 2 * 2048 + 260032) * 4
     st, n = _ws_bytes(_prob(L=4096, bh=4), B.SKA_OP_DUSTBIN_BLOCK_FWD)   # 4097 rows, dense
-    assert st == 0 and n == _wide_fwd_bytes(4, 4097, 4096) == (2 * 4 * 4160 + 4 * 257 * 16 * 257) * 4
+    assert st == 0 and n == _wide_fwd_bytes(4, 4097, 4096) == (2 * 4 * 4160 + 4 * 257 * 16 * 257 + 2 * 4 * 4097 * 96) * 4
     st, n = _ws_bytes(_prob(L=10000, bh=2, W=20000), B.SKA_OP_FWD)      # 625-tile windows
     assert st == 0 and n == _wide_fwd_bytes(2, 10000, 10000) == 2 * 2 * 10048 * 4
     st, n = _ws_bytes(_prob(L=0), B.SKA_OP_VJP)
