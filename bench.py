@@ -28,18 +28,26 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# VALU roofline of MI355X from unit counts and clock: 256 CUs x 4 SIMDs x 16 fp32 lanes per cycle
-# x 2.4 GHz = 39.3e12 lane-operations per second for unpacked fp32 instructions (a wave64
-# instruction occupies its SIMD for 4 cycles).  The 157.3 TFLOP/s fp32 vector peak counts packed
-# fp32 instructions (two values per lane) and an FMA as 2 flops; every kernel here is built without
-# packed fp32, so 39.3e12 is its ceiling.  v_exp_f32 issues at half that rate (18.3e12 per second
-# measured on MI355X), so one exponential takes 2 issue slots.
-VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
-EXP_SLOTS = 2
+# VALU roofline of MI355X from unit counts and clock: the fp32 vector peak of 157.3 TFLOP/s is
+# 256 CUs x 4 SIMDs x 32 fma lanes per cycle x 2 flops x 2.4 GHz, i.e. a wave64 fp32 instruction
+# every 2 cycles per SIMD: 78.6e12 lane-operations per second.  Unpacked instructions reach it
+# (measured with the shader clock: 2.5 cycles per wave64 fma with two or more waves per SIMD, 5
+# with one).  v_exp_f32 issues at a quarter of that rate (8.5-10 cycles measured), so one
+# exponential takes 4 issue slots.
+VALU_LANE_OPS_PER_S = 256 * 4 * 32 * 2.4e9
+EXP_SLOTS = 4
 # Minimal VALU work of one fused balanced Sinkhorn step per band entry: form the exponent with the
-# row shift already in the matrix-core accumulator (1 fma), exponentiate (1 exp = 2 slots),
-# accumulate the row sum (1 add) and the column sum of the normalised plan (1 fma): 5 issue slots.
+# row shift already in the matrix-core accumulator (1 fma), exponentiate (1 exp = 4 slots),
+# accumulate the row sum (1 add) and the column sum of the normalised plan (1 fma): 7 issue slots.
 SLOTS_PER_ENTRY_STEP = 3 + EXP_SLOTS
+# Issue time on a SIMD: matrix-core products and vector instructions of one SIMD do not overlap
+# (measured: a wave of bf16 products beside a wave of fmas takes the sum of their times), so the
+# step's SIMD floor adds its products' cycles (two bf16 16x16x32 products of 16 cycles per 16 x 16
+# tile) and its VALU cycles (2 per issue slot of a wave64 instruction).
+N_SIMD = 256 * 4
+CLOCK_HZ = 2.4e9
+BF16_MFMA_CYCLES = 16
+VALU_SLOT_CYCLES = 2
 HBM_PEAK_GBS = 8000.0
 # O(L) fp32 vectors one step reads and writes per token and head: previous column duals, previous
 # row duals, column partials in; row duals, column duals, column partials out
@@ -704,26 +712,35 @@ def main():
     step_fam = fam["step"]
     valu_peak = VALU_LANE_OPS_PER_S / 1e12
     if w.dtype == "bf16":
-        # The step's floors: Q and K read once (the per-pass byte count of the method's cost
-        # model) at 8 TB/s, against its minimal VALU work (5 issue slots per band entry) at the
-        # unpacked VALU peak; the VALU floor is the higher one, so the step is ALU-bound, and the
-        # SQ counters name the VALU as its busiest unit.
+        # The step's floors per launch: Q and K read once (the per-pass byte count of the method's
+        # cost model) at 8 TB/s, its minimal VALU work (7 issue slots per band entry) at the fp32
+        # vector peak, and its matrix-core flops at the bf16 peak.  The HBM floor is the highest,
+        # so the line reports "hbm".  Beside it: the VALU and MFMA fractions, the SIMD issue floor
+        # (products and vector instructions add on a SIMD), and the SQ counters' busy fractions,
+        # which name the VALU as the busiest unit in practice.
+        simd_cycles = nnz * (2 * BF16_MFMA_CYCLES / 256 + SLOTS_PER_ENTRY_STEP * VALU_SLOT_CYCLES / 64)
+        simd_floor_s = simd_cycles / (N_SIMD * CLOCK_HZ)
         roofline = {
-            "bound": "alu",
+            "bound": "hbm",
             "kernel": "sinkhorn_step_kernel (fused balanced Sinkhorn step)",
-            "achieved": step_fam["valu_T_per_s"],
-            "peak": round(valu_peak, 3),
-            "unit": "T VALU lane-slots/s",
-            "frac": step_fam["valu_frac"],
+            "achieved": step_fam["hbm_GB_per_s"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": step_fam["hbm_frac"],
             "traffic": traffic,
             "avg_launch_us": round(avg_launch_s * 1e6, 2),
             "launches_timed": kstep_n,
-            "algorithmic_work": f"{SLOTS_PER_ENTRY_STEP} VALU issue slots (fma, exp = 2, add, "
-                                f"fma) x {nnz} band entries per launch",
-            "hbm": {"achieved": step_fam["hbm_GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": step_fam["hbm_frac"], "algorithmic_bytes": step_fam["bytes"],
-                    "work": f"{w.bh * rows} token rows x 2 x {w.d} x {elt} B (Q and K read once) "
-                            f"per launch"},
+            "algorithmic_work": f"{w.bh * rows} token rows x 2 x {w.d} x {elt} B (Q and K read "
+                                f"once) = {step_fam['bytes']} B per launch",
+            "valu": {"achieved": step_fam["valu_T_per_s"], "peak": round(valu_peak, 3),
+                     "unit": "T VALU lane-slots/s", "frac": step_fam["valu_frac"],
+                     "work": f"{SLOTS_PER_ENTRY_STEP} issue slots (fma, exp = {EXP_SLOTS}, add, "
+                             f"fma) x {nnz} band entries per launch"},
+            "simd_issue": {"floor_us": round(simd_floor_s * 1e6, 2),
+                           "frac": round(simd_floor_s / avg_launch_s, 4),
+                           "work": f"per band entry {2 * BF16_MFMA_CYCLES}/256 product cycles + "
+                                   f"{SLOTS_PER_ENTRY_STEP} x {VALU_SLOT_CYCLES}/64 VALU cycles, "
+                                   f"over {N_SIMD} SIMDs at {CLOCK_HZ / 1e9:g} GHz"},
             "hbm_with_vectors": {
                 "achieved": round(step_fam["bytes_with_vectors"] / avg_launch_s / 1e9, 1),
                 "frac": round(step_fam["bytes_with_vectors"] / avg_launch_s / 1e9 / HBM_PEAK_GBS, 4),

@@ -87,16 +87,20 @@ def test_source_hash_follows_the_step_kernel_sources(tmp_path):
 
 
 def test_bench_band_entries_and_roofline_constants():
-    """bench.py's per-launch work counts: the band size by brute force, and the VALU ceiling of
-    unpacked fp32 (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz) with 5 issue slots per band entry."""
+    """bench.py's per-launch work counts: the band size by brute force, the VALU ceiling (the fp32
+    vector peak, 256 CUs x 4 SIMDs x 32 fma lanes x 2.4 GHz) with 7 issue slots per band entry, and
+    the SIMD issue floor of the long workload's step launch (about 37.7 us)."""
     import bench
     for L in (0, 1, 2, 7, 64, 100):
         for h in (0, 1, 3, 50, 200):
             brute = sum(1 for i in range(L) for j in range(L) if abs(i - j) <= h)
             assert bench.band_entries(L, h) == brute
-    assert bench.VALU_LANE_OPS_PER_S == pytest.approx(39.3216e12)
-    assert bench.SLOTS_PER_ENTRY_STEP == 5
+    assert bench.VALU_LANE_OPS_PER_S == pytest.approx(78.6432e12)     # 157.3 TFLOP/s / 2
+    assert bench.SLOTS_PER_ENTRY_STEP == 7
     assert bench.tail_pass_flops_per_entry(2, 64) == 24 * 64
+    nnz = bench.band_entries(262144, 128) * 4
+    cyc = nnz * (2 * bench.BF16_MFMA_CYCLES / 256 + bench.SLOTS_PER_ENTRY_STEP * bench.VALU_SLOT_CYCLES / 64)
+    assert cyc / (bench.N_SIMD * bench.CLOCK_HZ) == pytest.approx(37.69e-6, rel=1e-3)
 
 
 def test_bench_refuses_more_than_one_gpu():
