@@ -16,6 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libsinkhorn_attn.so")
 OBJ_DIR = os.path.join(LIB_DIR, "obj")
+PROBE_PATH = os.path.join(LIB_DIR, "issue_probe")
 SOURCES = ["ska_kernels.hip", "ska_fused.hip", "ska_vjp_stream.hip", "ska_wide.hip",
            "ska_contraction.hip", "ska_noalloc.hip", "ska_geometry.cpp",
            "ska_capi.cpp"]
@@ -74,6 +75,13 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     if rc != 0:
         raise RuntimeError(f"link failed ({rc}):\n{err}")
     os.replace(tmp, LIB_PATH)
+    # the issue-cost probe behind the VALU and issue rooflines (a standalone program)
+    probe = [hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, "issue_probe.hip"), "-o", PROBE_PATH]
+    if verbose:
+        print(" ".join(probe), flush=True)
+    rc, err = _run(probe)
+    if rc != 0:
+        raise RuntimeError(f"hipcc failed on issue_probe.hip ({rc}):\n{err}")
     return LIB_PATH
 
 
