@@ -49,6 +49,8 @@ SMALL = [
     ("L900_W600_bf16_wide", 2, 900, 600, 5, 1.0, BF16),
     ("L700_W2000_dense", 1, 700, 2000, 4, 1.0, F32),
     ("L1300_W700_eps05_wide", 1, 1300, 700, 3, 0.5, F32),
+    # fp32 wide step on three-plane operands with a last row tile of one row (L = 16 k + 1)
+    ("L1009_W700_wide_single_row_tile", 1, 1009, 700, 3, 1.0, F32),
 ]
 
 
