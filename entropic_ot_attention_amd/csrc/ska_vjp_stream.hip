@@ -213,9 +213,10 @@ template <int PASS, bool D4, int GEN> struct VjpPass {
   // exceed the register file)
   static constexpr bool contracts = (PASS == 0 || ((PASS == 3 || PASS == 4) && !D4) || PASS == 6 ||
                                      PASS == 7);
-  // the modifier field on the matrix cores (one fp32 16x16x4 product per k-step of 4 terms):
-  // general depth passes 6 and 7, and the one-reference passes 3 (D + A E + B F) and
-  // 4 (D + A E + B F + C G)
+  // the modifier field on the matrix cores: general depth passes 6 and 7, and the one-reference
+  // passes 3 (D + A E + B F) and 4 (D + A E + B F + C G); one fp32 16x16x4 product per k-step of
+  // 4 terms, except for bf16 inputs at R = 2, where it is one split-bf16 16x16x32 product added to
+  // the g tile (SPLITMOD in the kernel)
   static constexpr bool modk = (PASS == 6 || PASS == 7) || ((PASS == 3 || PASS == 4) && !D4 && GEN < 0);
   // k-steps of the modifier contraction (general depth: 2 R terms, 4 per step)
   static constexpr int KS = GEN > 0 ? GEN : (modk && GEN < 0) ? 1 : 0;
