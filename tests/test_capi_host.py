@@ -330,3 +330,34 @@ def test_noalloc_forward_checks_arguments_and_size_on_the_host():
     assert st == 0 and n <= (32 << 20)
     assert B.lib.sinkhorn_attn_fwd_noalloc(ctypes.byref(_prob(W=15)), vp, vp, vp, vp, vp, None) == -1
     assert B.lib.sinkhorn_attn_fwd_noalloc(None, vp, vp, vp, vp, vp, None) == -1
+
+
+def test_last_error_is_per_thread():
+    """Two host threads, each failing with its own argument error at the same time, read back the
+    detail of their own last error (the ABI keeps ska_last_error() per thread)."""
+    import threading
+    barrier = threading.Barrier(2, timeout=30)
+    bad = []
+
+    def worker(kw, expect):
+        try:
+            for _ in range(100):
+                n = ctypes.c_size_t(0)
+                st = B.lib.ska_workspace_bytes(ctypes.byref(_prob(**kw)), B.SKA_OP_FWD,
+                                               ctypes.byref(n))
+                barrier.wait()      # both threads have recorded an error before either reads
+                got = B.ska_last_error()
+                barrier.wait()
+                if st >= 0 or expect not in got:
+                    bad.append((kw, st, got))
+        except threading.BrokenBarrierError:
+            bad.append("barrier timed out")
+
+    threads = [threading.Thread(target=worker, args=(dict(d=32), "head dimension")),
+               threading.Thread(target=worker, args=(dict(L=-1), "L must be"))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(60)
+    assert not any(t.is_alive() for t in threads)
+    assert not bad, bad[:3]

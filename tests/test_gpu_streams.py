@@ -82,3 +82,37 @@ def test_two_problems_in_flight_on_two_streams():
     sb.synchronize()
     _same(ref_a, got_a, a_case[0] + " beside " + b_case[0])
     _same(ref_b, got_b, b_case[0] + " beside " + a_case[0])
+
+
+def test_two_host_threads_on_two_streams():
+    """Two host threads call the library at once, each on its own stream (the binding releases
+    the interpreter lock during the calls): the results match the single-thread ones."""
+    import threading
+    say("[gpu] streams: two host threads")
+    cases = [CASES[0], CASES[1]]
+    tensors = [_inputs(c, 41 + i) for i, c in enumerate(cases)]
+    refs = [_run(c, t) for c, t in zip(cases, tensors)]
+    torch.cuda.synchronize()
+    got = [None, None]
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.default_stream())
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    got[i] = _run(cases[i], tensors[i])
+            s.synchronize()
+        except Exception as e:      # reported below, in the test's own thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+    for c, r, g in zip(cases, refs, got):
+        _same(r, g, c[0] + " (two host threads)")
