@@ -114,7 +114,7 @@ struct WaveStage {
 // planes (h, m, l), 192 bf16.  A dot product q . k is then the six bf16 products
 // hq hk + hq mk + mq hk + hq lk + lq hk + mq mk with fp32 accumulation; the three dropped ones are
 // below 2^-24 |q| |k| per term, so the score keeps fp32 accuracy at twelve bf16 16x16x32 products
-// per tile instead of sixteen fp32 16x16x4 ones (a SIMD spends about 204 cycles on the former and
+// per tile instead of sixteen fp32 16x16x4 ones (a SIMD spends about 193 cycles on the former and
 // 512 on the latter).
 constexpr int kPlaneRow = 3 * kD;
 __global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ x, bf16* __restrict__ out,
