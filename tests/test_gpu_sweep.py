@@ -1,8 +1,9 @@
-"""A seeded sweep of small random configurations through the C ABI against the fp64 oracle: token
-counts from 1 to 2000 (ragged against every tile and block size), even band widths from 0 to
-600 (streaming, register-resident and wide engines), T from 0 to 6, tail depths R = 0..4,
-epsilon 0.5..2, bf16 and fp32, both adjoint schedules at R = 2, and the dustbin augmentation.
-Every element is compared at the tolerances of the other parity tests.
+"""A seeded sweep of random configurations through the C ABI against the fp64 oracle: token counts
+from 1 to 2000 (ragged against every tile and block size), even band widths from 0 to 600
+(streaming, register-resident and wide engines), T from 0 to 6, tail depths R = 0..4, epsilon
+0.5..2, bf16 and fp32, both adjoint schedules at R = 2, and the dustbin augmentation; then a few
+mid-size problems (3000-12000 tokens, up to three heads: many segments and seams) and calls of
+16-160 short problems.  Every element is compared at the tolerances of the other parity tests.
 
 At W = 0 each row's plan holds a single entry: the plan is the identity whatever the scores, so
 the exact dQ and dK are zero.  A relative bar is meaningless against an exact zero; those are
@@ -16,7 +17,7 @@ import numpy as np
 import pytest
 
 from entropic_ot_attention_amd.workloads import Workload, make_inputs
-from tests.gpu_common import compare, for_schedule, gpu_run_schedules, oracle_head, say
+from tests.gpu_common import compare, for_schedule, gpu_run_schedules, oracle_head, parallel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +44,28 @@ def _configs(seed=3, n=48):
     return out
 
 
-CONFIGS = _configs()
+def _mid_configs(seed=5, n=3):
+    """Mid-size problems: many segments per head at varied segment lengths and seams."""
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        L = rng.randint(3000, 12000)
+        W = 2 * rng.randint(16, 200)
+        dt = rng.choice(["bf16", "f32"])
+        out.append((rng.choice([1, 2, 3]), L, W, rng.randint(1, 3), rng.choice([0, 2, 2, 3]),
+                    rng.choice([0.5, 1.0, 2.0]), dt, False, rng.randint(0, 10**6)))
+    return out
+
+
+def _many_head_configs(seed=13, n=3):
+    """Many short problems in one call (one segment each)."""
+    rng = random.Random(seed)
+    return [(rng.choice([16, 64, 160]), rng.randint(1, 300), 2 * rng.randint(0, 150),
+             rng.randint(1, 4), rng.choice([0, 2, 3]), rng.choice([0.5, 1.0, 2.0]),
+             rng.choice(["bf16", "f32"]), False, rng.randint(0, 10**6)) for _ in range(n)]
+
+
+CONFIGS = _configs() + _mid_configs() + _many_head_configs()
 
 
 def _id(c):
@@ -63,7 +85,7 @@ def test_random_configuration_matches_the_oracle(cfg):
                             dustbin=dustbin)
     heads = [tuple(x[k][b].double().numpy() for k in ("Q", "K", "V", "dO")) for b in range(bh)]
     for s in schedules:
-        refs = [oracle_head(*h, W, T, R, eps, s, dustbin=dustbin) for h in heads]
+        refs = parallel(lambda h: oracle_head(*h, W, T, R, eps, s, dustbin=dustbin), heads, label)
         ref = {k: [r[k] for r in refs] for k in refs[0]}
         g = for_schedule(got, s)
         for k in ("dQ", "dK", "dV"):
