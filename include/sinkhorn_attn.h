@@ -54,7 +54,8 @@ typedef enum { SKA_F32 = 0, SKA_BF16 = 1 } ska_dtype;
 /* Adjoint schedule of the VJP.
  * SKA_ONE_REFERENCE: only the reference plan P^(R,R) is exponentiated; the other staircase
  *   plans enter through the orbit factors exp(u^(a)-u^(R)), exp(v^(b)-v^(R)) (abstract;
- *   technical summaries §2.2, orbit equation).  Any R from 1 to 256.
+ *   technical summaries §2.2, orbit equation).  Any R from 0 to 256 (R = 0: the stopped base's
+ *   own last plan, with u^(0) and v^(0) both held fixed).
  * SKA_DIRECT_FOUR: R = 2 only; every staircase plan P^(2,2), P^(2,1), P^(1,1), P^(1,0) is
  *   exponentiated on its own (the direct four-plan adjoint, atlas.scime.ai Key results); kept
  *   for comparison.  Other R return SKA_ERR_UNSUPPORTED. */
@@ -84,7 +85,7 @@ typedef struct {
   int64_t d;       /* head dimension; 64 is built                                               */
   int64_t W;       /* band width, even, >= 0; support |i - j| <= W / 2                          */
   int32_t T;       /* stopped base steps, >= 0                                                  */
-  int32_t R;       /* tail steps: forward >= 1, VJP 1..256 (direct-four schedule: 2)            */
+  int32_t R;       /* tail steps >= 0 (R = 0 needs T >= 1); VJP <= 256; direct-four: 2          */
   float epsilon;   /* entropic temperature, finite and > 0                                      */
   int32_t dtype;   /* ska_dtype of Q, K, V, O, dO, dQ, dK, dV (duals are always fp32)           */
 } ska_problem;
