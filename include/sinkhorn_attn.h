@@ -27,10 +27,13 @@
  * n_d = 2 rows u^(0), v^(0).  The last two rows are always the output plan's duals.
  *
  * Ownership and memory: every pointer is a device pointer owned by the caller, including the
- * workspace (size from ska_workspace_bytes).  The library allocates and frees nothing, keeps no
- * state between calls and never synchronises: work is enqueued on `stream` and completes
- * asynchronously.  Tensor pointers must be 16-byte aligned; outputs must not alias inputs or
- * the workspace.  Calls on different streams must use different workspaces.
+ * workspace (size from ska_workspace_bytes).  The library allocates and frees nothing and never
+ * synchronises: work is enqueued on `stream` and completes asynchronously.  Between calls it
+ * keeps only the allocation-free forward's static scratch and the timing functions' event pool.
+ * The compute entry points enqueue kernels only (no memset or copy nodes, no waits; timing, when
+ * enabled, adds events), so they can be captured into a HIP graph.  Tensor pointers must be
+ * 16-byte aligned; outputs must not alias inputs or the workspace.  Calls on different streams
+ * must use different workspaces.
  *
  * Errors: argument errors are detected on the host before anything is enqueued and return
  * SKA_ERR_INVALID / SKA_ERR_UNSUPPORTED / SKA_ERR_WORKSPACE; a failed kernel launch returns
