@@ -4,6 +4,7 @@
     python -m entropic_ot_attention_amd.profiling traffic <fetch.csv> <write.csv> <out.json> \
         <kernel substring> <calibration kernel substring> <calibration bytes> "<command>" <workload>
     python -m entropic_ot_attention_amd.profiling counters <out.md> "<commands>" <counters.csv> ...
+    python -m entropic_ot_attention_amd.profiling mem-counters <out.md> "<commands>" <counters.csv> ...
     python -m entropic_ot_attention_amd.profiling step-counters <out.json> <kernel substring> \
         <workload> <record .md> <counters.csv> ...
 
@@ -70,14 +71,9 @@ def stats_markdown(csv_path: str, out_md: str, command: str, top: int = 14) -> N
 N_XCD, N_SIMD = 8, 256 * 4
 
 
-def counters_markdown(csv_paths, out_md: str, command: str, regex_note: str = "") -> None:
-    """Per-kernel averages of SQ counters over the dispatches of one or more `--pmc` runs, with
-    the unit utilisations derived from them:
-      kernel cycles = GRBM_GUI_ACTIVE / 8 XCDs;
-      VALU busy = 4 SQ_ACTIVE_INST_VALU / (1024 SIMDs x cycles)   (quad-cycle units);
-      LDS busy  = 4 SQ_ACTIVE_INST_LDS / (1024 SIMDs x cycles);
-      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles)."""
-    per = collections.defaultdict(lambda: collections.defaultdict(list))   # name -> counter -> [v]
+def _per_kernel(csv_paths):
+    """kernel name -> counter -> [value per dispatch], over one or more `--pmc` runs."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
     for path in csv_paths:
         disp = collections.defaultdict(lambda: collections.defaultdict(float))
         names = {}
@@ -87,6 +83,17 @@ def counters_markdown(csv_paths, out_md: str, command: str, regex_note: str = ""
         for d, cs in disp.items():
             for c, v in cs.items():
                 per[names[d]][c].append(v)
+    return per
+
+
+def counters_markdown(csv_paths, out_md: str, command: str, regex_note: str = "") -> None:
+    """Per-kernel averages of SQ counters over the dispatches of one or more `--pmc` runs, with
+    the unit utilisations derived from them:
+      kernel cycles = GRBM_GUI_ACTIVE / 8 XCDs;
+      VALU busy = 4 SQ_ACTIVE_INST_VALU / (1024 SIMDs x cycles)   (quad-cycle units);
+      LDS busy  = 4 SQ_ACTIVE_INST_LDS / (1024 SIMDs x cycles);
+      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles)."""
+    per = _per_kernel(csv_paths)
     lines = ["# rocprofv3 SQ counters", "", "Commands (one counter pass each):", "", "```",
              command, "```", ""]
     if regex_note:
@@ -114,6 +121,62 @@ def counters_markdown(csv_paths, out_md: str, command: str, regex_note: str = ""
         for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"):
             if c in m and cyc:
                 lines.append(f"| {c} / (256 CUs x cycles) | {m[c] / (256 * cyc):.3f} |")
+        lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+# MI355X L2: 16 channels per XCD, each taking one 128-byte request per cycle.
+N_L2_CHANNELS, L2_LINE = 16 * N_XCD, 128
+
+
+def memory_counters_markdown(csv_paths, out_md: str, command: str) -> None:
+    """Per-kernel averages of the cache counters over the dispatches of `--pmc` runs:
+      kernel cycles    = GRBM_GUI_ACTIVE / 8 XCDs;
+      L2 requests      = TCC_REQ_sum per launch, and per kernel cycle against the 128 channels;
+      L2 hit rate      = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum);
+      L1 hit rate      = 1 - TCP_TCC_READ_REQ_sum / TCP_TOTAL_CACHE_ACCESSES_sum;
+      address unit     = TA_BUSY_avr and TA_BUSY_max over the CUs, per kernel cycle;
+      L1 pending stall = TCP_PENDING_STALL_CYCLES_sum / (256 CUs x cycles).
+    TCC_BUSY counts a channel busy while it waits on the fabric too, so it is no measure of the
+    L2's own load; it is listed as read."""
+    per = _per_kernel(csv_paths)
+    lines = ["# rocprofv3 cache counters", "", "Commands (one counter pass each):", "", "```",
+             command, "```", "",
+             "L2 requests are 128-byte lines; the L2 has 16 channels per XCD, 128 in all, each "
+             "taking one request per cycle.", ""]
+    for name in sorted(per, key=lambda k: -sum(per[k].get("GRBM_GUI_ACTIVE", [0]))):
+        m = {c: sum(v) / len(v) for c, v in per[name].items()}
+        cyc = m.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        n = min(len(v) for v in per[name].values())
+        lines += [f"## `{name[:96]}`", "",
+                  f"dispatches averaged per pass: {n}; kernel cycles {cyc:.0f}", "",
+                  "| quantity | value |", "|---|---:|"]
+        req = m.get("TCC_REQ_sum")
+        if req is not None:
+            lines.append(f"| L2 requests per launch | {req:.4g} ({req * L2_LINE / 1e9:.3f} GB) |")
+            if cyc:
+                lines.append(f"| L2 requests per cycle | {req / cyc:.1f} "
+                             f"({req / cyc / N_L2_CHANNELS:.3f} of the channels' rate) |")
+        if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m:
+            tot = m["TCC_HIT_sum"] + m["TCC_MISS_sum"]
+            if tot:
+                lines.append(f"| L2 hit rate | {m['TCC_HIT_sum'] / tot:.3f} |")
+        if "TCP_TOTAL_CACHE_ACCESSES_sum" in m and "TCP_TCC_READ_REQ_sum" in m:
+            acc = m["TCP_TOTAL_CACHE_ACCESSES_sum"]
+            lines.append(f"| L1 accesses per launch | {acc:.4g} |")
+            if acc:
+                lines.append(f"| L1 hit rate (reads sent on to L2) | "
+                             f"{1 - m['TCP_TCC_READ_REQ_sum'] / acc:.3f} |")
+        if cyc:
+            for label, c, k in (("address unit busy (mean CU)", "TA_BUSY_avr", 1.0),
+                                ("address unit busy (busiest CU)", "TA_BUSY_max", 1.0),
+                                ("L1 pending-request stall per CU", "TCP_PENDING_STALL_CYCLES_sum",
+                                 1.0 / 256)):
+                if c in m:
+                    lines.append(f"| {label} | {k * m[c] / cyc:.3f} |")
+        if m.get("TCC_CYCLE_sum") and "TCC_BUSY_sum" in m:
+            lines.append(f"| TCC_BUSY / TCC_CYCLE | {m['TCC_BUSY_sum'] / m['TCC_CYCLE_sum']:.3f} |")
         lines.append("")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -188,6 +251,8 @@ def main(argv):
         stats_markdown(argv[2], argv[3], argv[4])
     elif argv[1] == "counters":
         counters_markdown(argv[4:], argv[2], argv[3])
+    elif argv[1] == "mem-counters":
+        memory_counters_markdown(argv[4:], argv[2], argv[3])
     elif argv[1] == "step-counters":
         rec = kernel_busy(argv[6:], argv[3])
         rec.update(kernel=argv[3], workload=argv[4], record=argv[5], source_sha256=source_sha())

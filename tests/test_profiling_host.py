@@ -74,6 +74,32 @@ def test_counter_summary_fractions(tmp_path):
     assert "kernel cycles 240000 (100.0 us at 2.4 GHz)" in text
 
 
+def test_memory_counter_summary(tmp_path):
+    cyc = 100000.0                      # kernel cycles per XCD
+    # two passes over two dispatches each; counters summed over the rows of one dispatch
+    p1 = [(d, "k", c, v) for d in (1, 2) for c, v in
+          (("GRBM_GUI_ACTIVE", cyc * 8), ("TCC_REQ_sum", 0.25 * 128 * cyc),
+           ("TCC_HIT_sum", 0.9 * 0.25 * 128 * cyc), ("TCC_MISS_sum", 0.1 * 0.25 * 128 * cyc))]
+    p2 = [(d, "k", c, v) for d in (1, 2) for c, v in
+          (("GRBM_GUI_ACTIVE", cyc * 8), ("TCP_TOTAL_CACHE_ACCESSES_sum", 4e6),
+           ("TCP_TCC_READ_REQ_sum", 1e6), ("TA_BUSY_avr", 0.4 * cyc), ("TA_BUSY_max", 0.6 * cyc),
+           ("TCP_PENDING_STALL_CYCLES_sum", 0.2 * 256 * cyc))]
+    a, b = tmp_path / "a.csv", tmp_path / "b.csv"
+    _write(a, p1)
+    _write(b, p2)
+    out = tmp_path / "m.md"
+    P.memory_counters_markdown([str(a), str(b)], str(out), "rocprofv3 --pmc ...")
+    text = out.read_text()
+    assert "dispatches averaged per pass: 2; kernel cycles 100000" in text
+    assert "| L2 requests per cycle | 32.0 (0.250 of the channels' rate) |" in text
+    assert "| L2 requests per launch | 3.2e+06 (0.410 GB) |" in text
+    assert "| L2 hit rate | 0.900 |" in text
+    assert "| L1 hit rate (reads sent on to L2) | 0.750 |" in text
+    assert "| address unit busy (mean CU) | 0.400 |" in text
+    assert "| address unit busy (busiest CU) | 0.600 |" in text
+    assert "| L1 pending-request stall per CU | 0.200 |" in text
+
+
 def test_source_hash_follows_the_step_kernel_sources(tmp_path):
     paths = []
     for name in ("a.hip", "b.h"):
