@@ -480,9 +480,10 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
     int snt = 0;
     const int snw = ska::vjp_stream_waves(pl.elt, g.h, &snt);
     if (snw > 0) {
-      // general tail depth on the streaming engine, R + 3 passes: dv^(R) (1); du^(R) and its
-      // column partials (2); each level a = R-1 .. 1 (5), the partials alternating between two
-      // buffers; dQ (6); dK and dV (7).  R = 0: passes 6 and 7 alone (M = g).  Beyond R = 4 (the
+      // general tail depth on the streaming engine, R + 3 passes: dV and dv^(R) = V . dV (1);
+      // du^(R) and its column partials (2); each level a = R-1 .. 1 (5), the partials alternating
+      // between two buffers; dQ (6); dK (7).  R = 0: passes 6 and 7 alone (M = g), pass 7 also
+      // giving dV.  Beyond R = 4 (the
       // deep adjoint of full backpropagation) the wide engine's pass A (dv^(R), dV) replaces pass
       // 1, and its dQ and dK passes, which accumulate the 2 R modifier terms level by level,
       // replace passes 6 and 7.
@@ -519,6 +520,7 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
           w.out0 = dV;
           SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 0, w, st));
         } else {
+          a.out1 = dV;
           SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 1, a, st));
         }
         SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_vjp_stream_general(pl.elt, snt, snw, 2, a, st));
@@ -569,8 +571,8 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
   int nt = 0;
   const int nw = ska::vjp_stream_waves(pl.elt, g.h, &nt);
   if (nw > 0) {
-    // streaming passes: dv2 (owns keys), du2 + dv1 column sums (owns queries), du1 + dQ (owns
-    // queries), dK + dV (owns keys)
+    // streaming passes: dV and dv2 = V . dV (owns keys), du2 + dv1 column sums (owns queries),
+    // du1 + dQ (owns queries), dK (owns keys)
     ska::VjpArgs a{};
     a.Q = Q;
     a.K = K;

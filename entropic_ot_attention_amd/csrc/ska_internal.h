@@ -84,8 +84,8 @@ struct VjpArgs {
   const void* K;
   const void* V;
   const void* dO;
-  void* out0;            // pass 0: O; pass 3: dQ; pass 4: dK
-  void* out1;            // pass 4: dV
+  void* out0;            // pass 0: O; passes 3 and 6: dQ; passes 4 and 7: dK
+  void* out1;            // pass 1 (and general pass 7 at R = 0): dV
   float* ws;             // kVjpVecs vectors [bh][Lpad]
   const float* fu;       // pass 0 (forward output): row duals u^(R), log2 units [bh][Lpad]
   const float* fv;       // pass 0: column duals v^(R), log2 units [bh][Lpad]

@@ -7,14 +7,13 @@
 // g_ij = dO_i . V_j and e^{du1} = exp(u1 - u2), e^{dv_b} = exp(v_b - v2), in four passes:
 //
 //   0 (owns queries)  forward output O_i = sum_j P22_ij V_j   [the reference plan applied to V]
-//   1 (owns keys)     dv2_j = sum_i P22 g
+//   1 (owns keys)     dV_j = sum_i P22_ij dO_i,  dv2_j = sum_i P22 g = V_j . dV_j
 //   2 (owns queries)  du2_i = sum_j P22 (g - dv2_j);  per-segment column sums sum_i P22 du2_i
 //   3 (owns queries)  dv1_j = -e^{dv1_j} (column sums)  (finished for the window on arrival)
 //                     du1_i = -e^{du1_i} sum_j P22 e^{dv1_j} dv1_j
 //                     dQ_i  = s sum_j dS_ij k_j,  dS = Z1 - C_i Z2 with
 //                             Z1 = P22 (g - D_j - A_i E_j - B_i F_j), Z2 = P22 G_j
 //   4 (owns keys)     dK_j = s sum_i dS_ij q_i,  dS = P22 (g - D_j - A_i E_j - B_i F_j - C_i G_j)
-//                     dV_j = sum_i P22_ij dO_i
 // (A = du2, B = e^{du1}, C = du1 e^{du1}, D = dv2, E = e^{dv1}, F = dv1 e^{dv1}, G = e^{dv0}).
 //
 // Work decomposition as in the fused forward step: a workgroup of NW waves walks a segment of
@@ -77,6 +76,27 @@ __device__ __forceinline__ bf16x8 pack_z(const float (&z)[2][4]) {
   }
   return zb;
 }
+
+// Part of row `row` of a [., 64] tensor in the layout store_row writes (lane holds columns
+// 16 b + 4 g + r, r = 0..3), kept as loaded until at() converts it.
+template <typename T> struct RowPart;
+template <> struct RowPart<bf16> {
+  typedef __bf16 bf16x4 __attribute__((__vector_size__(8)));
+  bf16x4 v[4];
+  __device__ __forceinline__ void load(const bf16* row, int g) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[b] = *reinterpret_cast<const bf16x4*>(row + 16 * b + 4 * g);
+  }
+  __device__ __forceinline__ float at(int b, int r) const { return (float)v[b][r]; }
+};
+template <> struct RowPart<float> {
+  f32x4 v[4];
+  __device__ __forceinline__ void load(const float* row, int g) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[b] = *reinterpret_cast<const f32x4*>(row + 16 * b + 4 * g);
+  }
+  __device__ __forceinline__ float at(int b, int r) const { return v[b][r]; }
+};
 
 // Contractions over the 32 window rows of a tile pair (ring slots rt0, rt1):
 //   acc[b][r] (lane (g, n)) += sum_rows Op[row][16 b + 4 g + r] * Z[row][n]
@@ -203,7 +223,10 @@ template <int PASS, bool D4, int GEN> struct VjpPass {
   // owned rows in lane registers and window tokens across lanes (the passes that emit column
   // partials); the others hold the window in registers and the owned tokens across lanes
   static constexpr bool rows_in_regs = (PASS == 2 || PASS == 5);
-  static constexpr bool needs_g = (PASS != 0 && PASS != 5);
+  // pass 1 contracts the plan with the window's dO (dV) and takes dv = V . dV, so it needs no g
+  static constexpr bool needs_g = (PASS != 0 && PASS != 1 && PASS != 5);
+  // writes dV: pass 1, and pass 7 at R = 0 (GEN 0 there), where no pass 1 runs
+  static constexpr bool writes_dv = (PASS == 1) || (PASS == 7 && GEN == 0);
   static constexpr bool uses_ring_b = (PASS != 5);
   static constexpr bool reads_part = (PASS == 3 || PASS == 5);
   static constexpr bool writes_part = (PASS == 2 || PASS == 5);
@@ -211,8 +234,8 @@ template <int PASS, bool D4, int GEN> struct VjpPass {
   // tile pair
   // (the direct-four passes 3 and 4 run at phase 0 only: two phases of their wider tile work
   // exceed the register file)
-  static constexpr bool contracts = (PASS == 0 || ((PASS == 3 || PASS == 4) && !D4) || PASS == 6 ||
-                                     PASS == 7);
+  static constexpr bool contracts = (PASS == 0 || PASS == 1 || ((PASS == 3 || PASS == 4) && !D4) ||
+                                     PASS == 6 || PASS == 7);
   // the modifier field on the matrix cores: general depth passes 6 and 7, and the one-reference
   // passes 3 (D + A E + B F) and 4 (D + A E + B F + C G); one fp32 16x16x4 product per k-step of
   // 4 terms, except for bf16 inputs at R = 2, where it is one split-bf16 16x16x32 product added to
@@ -236,13 +259,13 @@ template <int PASS, bool D4, int GEN> struct VjpPass {
 //
 // GEN >= 0: a general tail depth R (a.R) with the vectors of tail_vecs(R) [technical summaries
 // §2.1-§2.2: R differentiable tail steps, every staircase plan in the orbit of P^(R,R)]:
-//   1 (owns keys)     dv^(R)_j = sum_i P g                           -> F_R (EV_R = 1)
+//   1 (owns keys)     dV_j = sum_i P dO_i,  dv^(R)_j = sum_i P g = V_j . dV_j   -> F_R (EV_R = 1)
 //   2 (owns queries)  du^(R)_i = sum_j P (g - F_R);  column partials sum_i P C_R
 //   5 (owns queries)  level a = R-1 .. 1: F_a = -EV_a^2 (partials of level a), finished for the
 //                     window on arrival; C_a = -EU_a^2 sum_j P F_a;  column partials sum_i P C_a
 //                     for level a - 1
-//   6 (owns queries)  dQ_i = s sum_j P M k_j,   7 (owns keys) dK_j = s sum_i P M q_i,
-//                     dV_j = sum_i P dO_i, with M = g - sum_k alpha_k(i) beta_k(j) over the 2 R
+//   6 (owns queries)  dQ_i = s sum_j P M k_j,   7 (owns keys) dK_j = s sum_i P M q_i (and
+//                     dV_j = sum_i P dO_i at R = 0), with M = g - sum_k alpha_k(i) beta_k(j) over the 2 R
 //                     pairs (alpha, beta) = (EU_a, F_a), (C_a, EV_(a-1)), a = 1 .. R: a rank-2R
 //                     product formed per tile on the matrix cores (fp32, GEN = ceil(2 R / 4)
 //                     k-steps of 4).
@@ -540,10 +563,12 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   }
   Frag<T> fA, fB;   // owned operands of the score and value-score products
   float own[NO];
+  RowPart<T> vj;    // pass 1: V of the owned key, for dv2 = V . dV
   {
     const int o = BR * blk0 + 16 * wave + n;
     load_frag(fA, ownA + (int64_t)o * kD, o < Lr, g);
     if (P::needs_g) load_frag(fB, ownB + (int64_t)o * kD, o < Lr, g);
+    if constexpr (PASS == 1) vj.load(ownB + (int64_t)min(o, Lr - 1) * kD, g);
     own_loads(BR * blk0 + 16 * wave, own);
     own_prep(own);
     if constexpr (SPLITMOD) ownmod = mod_operand(own);
@@ -570,6 +595,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     RowStage<T, BR, NTHR> na, nb;
     VecIn nv;
     Frag<T> fA_next, fB_next;
+    RowPart<T> vj_next;
     float own_next[NO];
     if (more) {
       if (cb + RING + BR <= Lr) {
@@ -584,6 +610,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       const bool next_in = (b0 + 2 * BR <= Lr) || (on < Lr);
       load_frag(fA_next, ownA + (int64_t)on * kD, next_in, g);
       if (P::needs_g) load_frag(fB_next, ownB + (int64_t)on * kD, next_in, g);
+      if constexpr (PASS == 1) vj_next.load(ownB + (int64_t)min(on, Lr - 1) * kD, g);
       own_loads(b0 + BR + 16 * wave, own_next);
     }
 
@@ -693,9 +720,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       PairOps<T> opA, opB;
       auto pair_fetch = [&](int t) {
         const int r0 = tile_slot(t), r1 = (zslot(t) == 0 && t + 1 < NT) ? tile_slot(t + 1) : r0;
-        if constexpr (PASS == 0) opB.fetch(ringB, trl, r0, r1);
+        if constexpr (PASS == 0 || P::writes_dv) opB.fetch(ringB, trl, r0, r1);
         if constexpr (PASS == 3 || PASS == 4 || PASS == 6 || PASS == 7) opA.fetch(ringA, trl, r0, r1);
-        if constexpr (PASS == 4 || PASS == 7) opB.fetch(ringB, trl, r0, r1);
       };
       auto mma = [&](int t) {
         if constexpr (P::rows_in_regs) {
@@ -788,19 +814,39 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         });
         if (o0 + n < Lr) store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
       } else if constexpr (PASS == 1) {
-        // ---- dv2_j = sum_i P22 g (owned key j across lanes, window queries in registers) ----
-        float acc = 0.f;
-        pipeline([&](int t, const f32x4& s, const f32x4& gg) {
-          if (dead(t)) return;
+        // ---- dV_j = sum_i P22_ij dO_i and dv2_j = sum_i P22 g = V_j . dV_j (owned key j across
+        // lanes, window queries in registers) ----
+        f32x4 Y[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float z[2][4];
+        pipeline([&](int t, const f32x4& s, const f32x4&) {
+          const int tt = zslot(t);
+          if (pair_starts(t)) pair_fetch(t);
           const f32x4 uw = wb[t & 1][0];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = fast_exp2(fmaf(s[r], c2, uw[r]));
-            acc = keep_w(t, r) ? fmaf(p, gg[r], acc) : acc;
+            z[tt][r] = (keep_w(t, r) && !dead(t)) ? p : 0.f;
+          }
+          if (pair_ends(t)) {
+            if (pair_starts(t)) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) z[1 - tt][r] = 0.f;
+            }
+            opB.contract(Y, ringB, trl, z, g, n);
           }
         });
+        float acc = 0.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc = fmaf(vj.at(b, r), Y[b][r], acc);
         const float dv2 = lane_group_sum(acc);
-        if (g == 0 && o0 + n < Lr) vec(ix_dv)[o0 + n] = dv2;
+        if (o0 + n < Lr) {
+          if (g == 0) vec(ix_dv)[o0 + n] = dv2;
+          store_row(static_cast<T*>(a.out1) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
+        }
       } else if constexpr (PASS == 2) {
         // ---- du2_i = sum_j P22 (g - dv2_j); column sums of P22 du2 (owned rows in registers) ----
         f32x4 x[NT];
@@ -919,12 +965,12 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
           store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, r4, a.s, g);
         }
       } else if constexpr (PASS == 4) {
-        // ---- dK, dV (owned key j across lanes, window queries in registers) ----
+        // ---- dK (owned key j across lanes, window queries in registers) ----
         const float Dj = own[1 % NO], Ej = own[2 % NO], Fj = own[3 % NO], Gj = own[4 % NO];
-        f32x4 X[4], Y[4];
+        f32x4 X[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float z1[2][4], z2[2][4];
+        for (int b = 0; b < 4; ++b) X[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float z1[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
           const int tt = zslot(t);
           if (pair_starts(t)) pair_fetch(t);
@@ -938,7 +984,6 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
               const float e = fast_exp2(fmaf(s[r], c2, uw[r]));
               const float p = (keep_w(t, r) && live) ? e : 0.f;
               z1[tt][r] = SPLITMOD ? p * gg[r] : p * (gg[r] - mm[r]);
-              z2[tt][r] = p;
             }
           } else {
             const f32x4 Aw = wb[t & 1][1 % NWV], Bw = wb[t & 1][2 % NWV], Cw = wb[t & 1][3 % NWV];
@@ -951,22 +996,17 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
               const float p11 = fast_exp2(xs + Bw[r] + Ej), p10 = fast_exp2(xs + Bw[r] + Gj);
               const bool keep = keep_w(t, r) && live;
               z1[tt][r] = keep ? p22 * (gg[r] - Dj) - p21 * Aw[r] - p11 * Fj - p10 * Cw[r] : 0.f;
-              z2[tt][r] = keep ? p22 : 0.f;
             }
           }
           if (pair_ends(t)) {
             if (pair_starts(t)) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) z1[1 - tt][r] = z2[1 - tt][r] = 0.f;
+              for (int r = 0; r < 4; ++r) z1[1 - tt][r] = 0.f;
             }
             opA.contract(X, ringA, trl, z1, g, n);
-            opB.contract(Y, ringB, trl, z2, g, n);
           }
         });
-        if (o0 + n < Lr) {
-          store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, X, a.s, g);
-          store_row(static_cast<T*>(a.out1) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
-        }
+        if (o0 + n < Lr) store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, X, a.s, g);
       } else if constexpr (PASS == 5) {
         // ---- level a: C_a = -EU_a^2 sum_j P F_a; column sums of P C_a (owned rows in
         // registers) ----
@@ -1037,11 +1077,14 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
         });
         if (o0 + n < Lr) store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, X, a.s, g);
       } else {
-        // ---- dK, dV with the general modifier (owned key j across lanes, window queries in
-        // registers) ----
-        f32x4 X[4], Y[4];
+        // ---- dK with the general modifier, and dV at R = 0 (owned key j across lanes, window
+        // queries in registers) ----
+        constexpr bool DV = P::writes_dv;
+        f32x4 X[4], Y[DV ? 4 : 1];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) X[b] = Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 4; ++b) X[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < (DV ? 4 : 1); ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float z1[2][4], z2[2][4];
         pipeline([&](int t, const f32x4& s, const f32x4& gg) {
           const int tt = zslot(t);
@@ -1061,12 +1104,12 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
               for (int r = 0; r < 4; ++r) z1[1 - tt][r] = z2[1 - tt][r] = 0.f;
             }
             opA.contract(X, ringA, trl, z1, g, n);
-            opB.contract(Y, ringB, trl, z2, g, n);
+            if constexpr (DV) opB.contract(Y, ringB, trl, z2, g, n);
           }
         });
         if (o0 + n < Lr) {
           store_row(static_cast<T*>(a.out0) + tb + (int64_t)(o0 + n) * kD, X, a.s, g);
-          store_row(static_cast<T*>(a.out1) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
+          if constexpr (DV) store_row(static_cast<T*>(a.out1) + tb + (int64_t)(o0 + n) * kD, Y, 1.f, g);
         }
       }
     };
@@ -1105,6 +1148,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       if constexpr (P::uses_ring_b) nb.template store_slots<RING>(ringB, s_cb);
       fA = fA_next;
       fB = fB_next;
+      if constexpr (PASS == 1) vj = vj_next;
       own_prep(own_next);
 #pragma unroll
       for (int k = 0; k < NO; ++k) own[k] = own_next[k];
