@@ -448,7 +448,7 @@ ska_status run_fwd(const ska_problem* p, ska_op op, const void* Q, const void* K
 }
 
 ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K, const void* V,
-                   const float* duals, const void* dO, void* dQ, void* dK, void* dV,
+                   const float* duals, const void* dO, const void* O, void* dQ, void* dK, void* dV,
                    ska_schedule sched, void* workspace, size_t workspace_bytes, hipStream_t st) {
   Plan pl;
   SKA_TRY(check_problem(p, op, &pl));
@@ -461,6 +461,7 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
   SKA_TRY(check_ptr(K, "K"));
   SKA_TRY(check_ptr(V, "V"));
   SKA_TRY(check_ptr(dO, "dO"));
+  if (O) SKA_TRY(check_ptr(O, "O"));
   SKA_TRY(check_ptr(dQ, "dQ"));
   SKA_TRY(check_ptr(dK, "dK"));
   SKA_TRY(check_ptr(dV, "dV"));
@@ -578,6 +579,7 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
     a.K = K;
     a.V = V;
     a.dO = dO;
+    a.O = O;          // optional: du2 from delta = dO . O in the second pass
     a.ws = ws;
     a.vec_stride = g.bh * (int64_t)g.Lpad;
     a.part = ws + ska::kVjpVecs * a.vec_stride;
@@ -638,11 +640,11 @@ ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K,
 }
 
 ska_status sinkhorn_attn_vjp(const ska_problem* p, const void* Q, const void* K, const void* V,
-                             const float* duals, const void* dO, void* dQ, void* dK, void* dV,
-                             ska_schedule schedule, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+                             const float* duals, const void* dO, const void* O, void* dQ, void* dK,
+                             void* dV, ska_schedule schedule, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   g_err.clear();
-  return run_vjp(p, SKA_OP_VJP, Q, K, V, duals, dO, dQ, dK, dV, schedule, workspace,
+  return run_vjp(p, SKA_OP_VJP, Q, K, V, duals, dO, O, dQ, dK, dV, schedule, workspace,
                  workspace_bytes, stream);
 }
 
@@ -660,7 +662,7 @@ ska_status sinkhorn_attn_dustbin_block_vjp(const ska_problem* p, const void* Q, 
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream) {
   g_err.clear();
-  return run_vjp(p, SKA_OP_DUSTBIN_BLOCK_VJP, Q, K, V, duals, dO, dQ, dK, dV, schedule,
+  return run_vjp(p, SKA_OP_DUSTBIN_BLOCK_VJP, Q, K, V, duals, dO, nullptr, dQ, dK, dV, schedule,
                  workspace, workspace_bytes, stream);
 }
 
@@ -691,10 +693,10 @@ ska_status sinkhorn_attn_tail_remainder(const ska_problem* p, const void* Q, con
   float* dr = reinterpret_cast<float*>(w + L.duals_r);
   float* df = reinterpret_cast<float*>(w + L.duals_f);
   SKA_TRY(run_fwd(&pr, SKA_OP_FWD, Q, K, V, w + L.o, dr, inner, L.inner_bytes, stream));
-  SKA_TRY(run_vjp(&pr, SKA_OP_VJP, Q, K, V, dr, dO, w + L.dq_r, w + L.dk_r, w + L.dv_r,
+  SKA_TRY(run_vjp(&pr, SKA_OP_VJP, Q, K, V, dr, dO, w + L.o, w + L.dq_r, w + L.dk_r, w + L.dv_r,
                   SKA_ONE_REFERENCE, inner, L.inner_bytes, stream));
   SKA_TRY(run_fwd(&pf, SKA_OP_FWD, Q, K, V, w + L.o, df, inner, L.inner_bytes, stream));
-  SKA_TRY(run_vjp(&pf, SKA_OP_VJP, Q, K, V, df, dO, w + L.dq_f, w + L.dk_f, w + L.dv_f,
+  SKA_TRY(run_vjp(&pf, SKA_OP_VJP, Q, K, V, df, dO, nullptr, w + L.dq_f, w + L.dk_f, w + L.dv_f,
                   SKA_ONE_REFERENCE, inner, L.inner_bytes, stream));
   const int64_t n = pl.g.bh * (int64_t)pl.g.Lr * ska::kD;
   double* part = reinterpret_cast<double*>(w + L.part);

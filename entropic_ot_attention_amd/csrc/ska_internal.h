@@ -84,6 +84,7 @@ struct VjpArgs {
   const void* K;
   const void* V;
   const void* dO;
+  const void* O;         // R = 2 pass 2: the forward's output for delta = dO . O, or null
   void* out0;            // pass 0: O; passes 3 and 6: dQ; passes 4 and 7: dK
   void* out1;            // pass 1 (and general pass 7 at R = 0): dV
   float* ws;             // kVjpVecs vectors [bh][Lpad]

@@ -98,6 +98,25 @@ template <> struct RowPart<float> {
   __device__ __forceinline__ float at(int b, int r) const { return v[b][r]; }
 };
 
+// Partial dot product of two rows held as fragments in the same layout (this lane's d-slice).
+__device__ __forceinline__ float frag_dot(const Frag<bf16>& x, const Frag<bf16>& y) {
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc = fmaf((float)x.a[e], (float)y.a[e], acc);
+    acc = fmaf((float)x.b[e], (float)y.b[e], acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float frag_dot(const Frag<float>& x, const Frag<float>& y) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(x.v[i][e], y.v[i][e], acc);
+  return acc;
+}
+
 // Contractions over the 32 window rows of a tile pair (ring slots rt0, rt1):
 //   acc[b][r] (lane (g, n)) += sum_rows Op[row][16 b + 4 g + r] * Z[row][n]
 // with Op read transposed from the ring and z[tt][r] = Z[rt_tt + 4 g + r][n].
@@ -218,16 +237,20 @@ __device__ __forceinline__ void ring_frag(Frag<float>& f, const float* ring, con
   lds_frag(f, ring, rt + n, g);
 }
 
-template <int PASS, bool D4, int GEN> struct VjpPass {
+template <int PASS, bool D4, int GEN, bool DELTA> struct VjpPass {
   static constexpr bool owns_keys = (PASS == 1 || PASS == 4 || PASS == 7);
+  // pass 2 given the forward's output O: sum_j P22_ij g_ij = dO_i . O_i (delta_i), so the pass
+  // forms du2_i = delta_i - sum_j P22_ij dv2_j from the owned dO and O rows, without g or the
+  // window's V
+  static constexpr bool delta = DELTA && PASS == 2;
   // owned rows in lane registers and window tokens across lanes (the passes that emit column
   // partials); the others hold the window in registers and the owned tokens across lanes
   static constexpr bool rows_in_regs = (PASS == 2 || PASS == 5);
   // pass 1 contracts the plan with the window's dO (dV) and takes dv = V . dV, so it needs no g
-  static constexpr bool needs_g = (PASS != 0 && PASS != 1 && PASS != 5);
+  static constexpr bool needs_g = (PASS != 0 && PASS != 1 && PASS != 5 && !delta);
   // writes dV: pass 1, and pass 7 at R = 0 (GEN 0 there), where no pass 1 runs
   static constexpr bool writes_dv = (PASS == 1) || (PASS == 7 && GEN == 0);
-  static constexpr bool uses_ring_b = (PASS != 5);
+  static constexpr bool uses_ring_b = (PASS != 5 && !delta);
   static constexpr bool reads_part = (PASS == 3 || PASS == 5);
   static constexpr bool writes_part = (PASS == 2 || PASS == 5);
   // contracts the reference plan (or the score cotangent) with a window tensor, tile pair by
@@ -269,9 +292,9 @@ template <int PASS, bool D4, int GEN> struct VjpPass {
 //                     pairs (alpha, beta) = (EU_a, F_a), (C_a, EV_(a-1)), a = 1 .. R: a rank-2R
 //                     product formed per tile on the matrix cores (fp32, GEN = ceil(2 R / 4)
 //                     k-steps of 4).
-template <typename T, int NT, int NW, int PASS, bool D4 = false, int GEN = -1>
+template <typename T, int NT, int NW, int PASS, bool D4 = false, int GEN = -1, bool DELTA = false>
 __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
-  using P = VjpPass<PASS, D4, GEN>;
+  using P = VjpPass<PASS, D4, GEN, DELTA>;
   constexpr int H16 = (NT - 1) / 2;
   constexpr int BR = 16 * NW;                  // owned tokens per block
   constexpr int RING = BR + 32 * H16;          // block window
@@ -305,6 +328,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   const T* winB = static_cast<const T*>(P::owns_keys ? a.dO : a.V) + tb;
   const T* ownA = static_cast<const T*>(P::owns_keys ? a.K : a.Q) + tb;
   const T* ownB = static_cast<const T*>(P::owns_keys ? a.V : a.dO) + tb;
+  const T* ownO = static_cast<const T*>(a.O) + tb;   // delta: the forward's output
   const int64_t vo = head * (int64_t)a.Lpad;
   auto vec = [&](int which) -> float* { return a.ws + which * a.vec_stride + vo; };
   const bool exact_h = (h == 16 * H16);
@@ -564,10 +588,12 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   Frag<T> fA, fB;   // owned operands of the score and value-score products
   float own[NO];
   RowPart<T> vj;    // pass 1: V of the owned key, for dv2 = V . dV
+  Frag<T> fO;       // delta: O of the owned query (fB holds its dO)
   {
     const int o = BR * blk0 + 16 * wave + n;
     load_frag(fA, ownA + (int64_t)o * kD, o < Lr, g);
-    if (P::needs_g) load_frag(fB, ownB + (int64_t)o * kD, o < Lr, g);
+    if (P::needs_g || P::delta) load_frag(fB, ownB + (int64_t)o * kD, o < Lr, g);
+    if constexpr (P::delta) load_frag(fO, ownO + (int64_t)o * kD, o < Lr, g);
     if constexpr (PASS == 1) vj.load(ownB + (int64_t)min(o, Lr - 1) * kD, g);
     own_loads(BR * blk0 + 16 * wave, own);
     own_prep(own);
@@ -594,7 +620,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
     // prefetch the next block: its BR new window rows, vectors, owned operands and values
     RowStage<T, BR, NTHR> na, nb;
     VecIn nv;
-    Frag<T> fA_next, fB_next;
+    Frag<T> fA_next, fB_next, fO_next;
     RowPart<T> vj_next;
     float own_next[NO];
     if (more) {
@@ -609,7 +635,8 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       const int on = b0 + BR + 16 * wave + n;
       const bool next_in = (b0 + 2 * BR <= Lr) || (on < Lr);
       load_frag(fA_next, ownA + (int64_t)on * kD, next_in, g);
-      if (P::needs_g) load_frag(fB_next, ownB + (int64_t)on * kD, next_in, g);
+      if (P::needs_g || P::delta) load_frag(fB_next, ownB + (int64_t)on * kD, next_in, g);
+      if constexpr (P::delta) load_frag(fO_next, ownO + (int64_t)on * kD, next_in, g);
       if constexpr (PASS == 1) vj_next.load(ownB + (int64_t)min(on, Lr - 1) * kD, g);
       own_loads(b0 + BR + 16 * wave, own_next);
     }
@@ -863,7 +890,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
               const float e = fast_exp2(fmaf(s[r], c2, v2j));
               const float p = keep_o(t, r) ? e : 0.f;
               x[t][r] = p;
-              racc[r] = fmaf(p, gg[r] - dj, racc[r]);
+              racc[r] = P::delta ? fmaf(p, -dj, racc[r]) : fmaf(p, gg[r] - dj, racc[r]);
             }
           } else {
             // direct: du2 from P22, the column sums from P21 = exp(S + u2 + v1)
@@ -874,13 +901,21 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
               const bool keep = keep_o(t, r);
               const float p22 = fast_exp2(xs + v2j), p21 = fast_exp2(xs + v1j);
               x[t][r] = keep ? p21 : 0.f;
-              racc[r] = keep ? fmaf(p22, gg[r] - dj, racc[r]) : racc[r];
+              racc[r] = keep ? (P::delta ? fmaf(p22, -dj, racc[r]) : fmaf(p22, gg[r] - dj, racc[r]))
+                             : racc[r];
             }
           }
         });
         float du2[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) du2[r] = row16_sum(racc[r]);
+        if constexpr (P::delta) {
+          // delta of owned row n (fragments: row n, d-slice of lane group g), summed over the
+          // lane groups, then moved to the rows_in_regs layout (rows 4 g + r)
+          const float dn = lane_group_sum(frag_dot(fB, fO));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) du2[r] += __shfl(dn, 4 * g + r);
+        }
         if (n < 4) {
           const int i = o0 + 4 * g + n;
           const float di = (n == 0) ? du2[0] : (n == 1) ? du2[1] : (n == 2) ? du2[2] : du2[3];
@@ -1148,6 +1183,7 @@ __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
       if constexpr (P::uses_ring_b) nb.template store_slots<RING>(ringB, s_cb);
       fA = fA_next;
       fB = fB_next;
+      if constexpr (P::delta) fO = fO_next;
       if constexpr (PASS == 1) vj = vj_next;
       own_prep(own_next);
 #pragma unroll
@@ -1189,8 +1225,13 @@ static void launch_nt(int pass, bool d4, const VjpArgs& a, hipStream_t st) {
     case 0: vjp_stream_kernel<T, NT, NW, 0><<<grid, block, 0, st>>>(a); break;
     case 1: vjp_stream_kernel<T, NT, NW, 1><<<grid, block, 0, st>>>(a); break;
     case 2:
-      if (d4) vjp_stream_kernel<T, NT, NW, 2, true><<<grid, block, 0, st>>>(a);
-      else vjp_stream_kernel<T, NT, NW, 2><<<grid, block, 0, st>>>(a);
+      if (a.O != nullptr) {
+        if (d4) vjp_stream_kernel<T, NT, NW, 2, true, -1, true><<<grid, block, 0, st>>>(a);
+        else vjp_stream_kernel<T, NT, NW, 2, false, -1, true><<<grid, block, 0, st>>>(a);
+      } else {
+        if (d4) vjp_stream_kernel<T, NT, NW, 2, true><<<grid, block, 0, st>>>(a);
+        else vjp_stream_kernel<T, NT, NW, 2><<<grid, block, 0, st>>>(a);
+      }
       break;
     case 3:
       if (d4) vjp_stream_kernel<T, NT, NW, 3, true><<<grid, block, 0, st>>>(a);

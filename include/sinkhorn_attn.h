@@ -107,8 +107,12 @@ ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K,
                              hipStream_t stream);
 
 /* Exact tail VJP (0 <= R <= 256): given the forward's duals and an arbitrary cotangent dO, writes
- * dQ, dK, dV [bh][L][d].  Scores are recomputed per band tile; extra memory is O(L) vectors
- * (3 + 4 R of them for R != 2).  R = 2 runs the two-level passes (both schedules); other R run
+ * dQ, dK, dV [bh][L][d].  O is optional (NULL, or the [bh][L][d] output sinkhorn_attn_fwd wrote
+ * for the same problem, Q, K, V and duals; it is only read): where the R = 2 band passes run, the
+ * row cotangent sum_j P_ij (dO_i . V_j) is then taken as dO_i . O_i, so the du2 pass reads neither
+ * V's window nor forms dO . V^T; other paths ignore it, and the results agree either way within
+ * rounding.  An O that is not that output gives wrong gradients.  Scores are recomputed per band
+ * tile; extra memory is O(L) vectors (3 + 4 R of them for R != 2).  R = 2 runs the two-level passes (both schedules); other R run
  * 2 R + 2 passes of the one-reference adjoint, the modifier field then holding 2 R terms; R = 0
  * runs dV, dQ and dK of the base plan with both duals fixed (score cotangent P * g)
  * (technical summaries §2.1: R differentiable tail steps; §4.1: tail gradients from R = 0 up).
@@ -116,9 +120,9 @@ ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K,
  * cotangents and the exp(u^(a) - u^(R)), exp(v^(b) - v^(R)) factors; atlas.scime.ai Key
  * results: complete arbitrary-cotangent Q/K/V VJP.) */
 ska_status sinkhorn_attn_vjp(const ska_problem* p, const void* Q, const void* K, const void* V,
-                             const float* duals, const void* dO, void* dQ, void* dK, void* dV,
-                             ska_schedule schedule, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream);
+                             const float* duals, const void* dO, const void* O, void* dQ, void* dK,
+                             void* dV, ska_schedule schedule, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /* Forward pass that allocates nothing, for callers that cannot allocate device memory around the
  * call (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).

@@ -92,7 +92,7 @@ int main() {
             for (int sch = 0; sch < 2; ++sch) {
               s = dust ? sinkhorn_attn_dustbin_block_vjp(&p, Q, K, V, duals, dO, dQ, dK, dV,
                                                          (ska_schedule)sch, ws, n, st)
-                       : sinkhorn_attn_vjp(&p, Q, K, V, duals, dO, dQ, dK, dV, (ska_schedule)sch, ws,
+                       : sinkhorn_attn_vjp(&p, Q, K, V, duals, dO, O, dQ, dK, dV, (ska_schedule)sch, ws,
                                            n, st);
               const ska_status want = (sch == 1 && R != 2) ? SKA_ERR_UNSUPPORTED : SKA_OK;
               EXPECT(s == want, "vjp L=%lld W=%lld R=%d sch=%d: %d", (long long)L, (long long)W, R, sch, s);
@@ -100,8 +100,8 @@ int main() {
                 // one byte short of the VJP's workspace
                 s = dust ? sinkhorn_attn_dustbin_block_vjp(&p, Q, K, V, duals, dO, dQ, dK, dV,
                                                            (ska_schedule)sch, ws, nv - 1, st)
-                         : sinkhorn_attn_vjp(&p, Q, K, V, duals, dO, dQ, dK, dV, (ska_schedule)sch,
-                                             ws, nv - 1, st);
+                         : sinkhorn_attn_vjp(&p, Q, K, V, duals, dO, nullptr, dQ, dK, dV,
+                                             (ska_schedule)sch, ws, nv - 1, st);
                 EXPECT(s == (want == SKA_OK ? SKA_ERR_WORKSPACE : want), "short vjp ws: %d", s);
               }
             }
@@ -155,7 +155,7 @@ int main() {
     EXPECT(std::strlen(ska_last_error()) > 0, "error detail");
   }
   ska_problem deep{2, 100, 64, 16, 3, 257, 1.0f, SKA_F32};
-  EXPECT(sinkhorn_attn_vjp(&deep, Q, K, V, duals, dO, dQ, dK, dV, SKA_ONE_REFERENCE, ws, 1 << 30, st) ==
+  EXPECT(sinkhorn_attn_vjp(&deep, Q, K, V, duals, dO, nullptr, dQ, dK, dV, SKA_ONE_REFERENCE, ws, 1 << 30, st) ==
              SKA_ERR_UNSUPPORTED, "R above 256");
   EXPECT(ska_workspace_bytes(nullptr, SKA_OP_FWD, &need) == SKA_ERR_INVALID, "null problem");
   EXPECT(ska_workspace_bytes(&good, SKA_OP_FWD, nullptr) == SKA_ERR_INVALID, "null out");
@@ -166,8 +166,10 @@ int main() {
   EXPECT(sinkhorn_attn_fwd(&good, Q, K, V, O, nullptr, ws, need, st) == SKA_ERR_INVALID, "null duals");
   EXPECT(sinkhorn_attn_fwd(&good, Q, K, V, O, duals, nullptr, need, st) == SKA_ERR_WORKSPACE, "null ws");
   EXPECT(sinkhorn_attn_fwd(&good, Q, K, V, O, duals, ws, need - 1, st) == SKA_ERR_WORKSPACE, "short ws");
-  EXPECT(sinkhorn_attn_vjp(&good, Q, K, V, duals, dO, dQ, dK, dV, (ska_schedule)5, ws, 1 << 30, st) ==
+  EXPECT(sinkhorn_attn_vjp(&good, Q, K, V, duals, dO, nullptr, dQ, dK, dV, (ska_schedule)5, ws, 1 << 30, st) ==
              SKA_ERR_INVALID, "bad schedule");
+  EXPECT(sinkhorn_attn_vjp(&good, Q, K, V, duals, dO, static_cast<char*>(O) + 4, dQ, dK, dV, SKA_ONE_REFERENCE,
+                           ws, 1 << 30, st) == SKA_ERR_INVALID, "misaligned O");
   EXPECT(sinkhorn_attn_tail_remainder(&good, Q, K, V, dO, reinterpret_cast<double*>(static_cast<char*>(fake(11)) + 4),
                                       ws, 1 << 30, st) == SKA_ERR_INVALID, "misaligned sums");
   int64_t nb = 0;

@@ -35,16 +35,22 @@ def gpu_run(Q, K, V, dO, W, T, R=2, eps=1.0, schedule="one_reference", dustbin=F
     O, duals = B.forward(Qd, Kd, Vd, W, T, R, eps, dustbin=dustbin)
     out = dict(O=O, duals=duals)
     if R <= 4:
-        dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=schedule, dustbin=dustbin)
+        # the VJP given the forward's output (as the autograd wrapper calls it), and without it
+        dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=schedule, dustbin=dustbin,
+                           O=None if dustbin else O)
         out.update(dQ=dQ, dK=dK, dV=dV)
+        if not dustbin:
+            dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=schedule)
+            out.update(dQ_noO=dQ, dK_noO=dK, dV_noO=dV)
     torch.cuda.synchronize()
     return {k: v.float().cpu().double().numpy() for k, v in out.items()}
 
 
 def gpu_run_schedules(Q, K, V, dO, W, T, R=2, eps=1.0,
                       schedules=("one_reference", "direct_four"), dustbin=False):
-    """One forward and one VJP per schedule through the C ABI; returns {"O", "duals",
-    schedule: {"dQ", "dK", "dV"}} as fp64 numpy arrays [bh, ...]."""
+    """One forward and, per schedule, the VJP through the C ABI given the forward's output O and
+    (band support) without it; returns {"O", "duals", schedule: {"dQ", "dK", "dV", and
+    "dQ_noO", "dK_noO", "dV_noO"}} as fp64 numpy arrays [bh, ...]."""
     from entropic_ot_attention_amd import binding as B
     dev = torch.device("cuda:0")
     Qd, Kd, Vd, dOd = (x.to(dev) for x in (Q, K, V, dO))
@@ -52,9 +58,14 @@ def gpu_run_schedules(Q, K, V, dO, W, T, R=2, eps=1.0,
     host = lambda t: t.float().cpu().double().numpy()
     out = {"O": host(O), "duals": host(duals)}
     for s in schedules:
-        dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=s, dustbin=dustbin)
+        dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=s, dustbin=dustbin,
+                           O=None if dustbin else O)
         torch.cuda.synchronize()
         out[s] = {"dQ": host(dQ), "dK": host(dK), "dV": host(dV)}
+        if not dustbin:
+            dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=s)
+            torch.cuda.synchronize()
+            out[s].update(dQ_noO=host(dQ), dK_noO=host(dK), dV_noO=host(dV))
     torch.cuda.synchronize()
     return out
 
@@ -93,13 +104,15 @@ def as64(x: torch.Tensor) -> np.ndarray:
 
 
 def compare(got: dict, ref: dict, dtype: torch.dtype, label: str, heads=None):
-    """got: arrays [bh, ...]; ref: dict of lists per head (or arrays with leading head axis)."""
+    """got: arrays [bh, ...]; ref: dict of lists per head (or arrays with leading head axis).
+    Gradients the VJP gave without the forward's output (keys "<name>_noO") are held to the
+    same bar against the same reference."""
     report = {}
-    for name in ("O", "dQ", "dK", "dV", "duals"):
-        if name not in ref:
-            continue
+    names = [n for n in ("O", "dQ", "dK", "dV", "duals") if n in ref]
+    names += [n + "_noO" for n in ("dQ", "dK", "dV") if n in ref and n + "_noO" in got]
+    for name in names:
         g = got[name] if heads is None else got[name][heads]
-        r = np.asarray(ref[name])
+        r = np.asarray(ref[name.replace("_noO", "")])
         assert g.shape == r.shape, (name, g.shape, r.shape)
         assert np.all(np.isfinite(g)), f"{label}: non-finite values in {name}"
         err = float(np.abs(g - r).max())

@@ -198,14 +198,18 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert f(ctypes.byref(prob), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), V(FAKE), need - 4, None) == -3
     g = B.lib.sinkhorn_attn_vjp
     _, needv = _ws_bytes(prob, B.SKA_OP_VJP)
-    args = [V(FAKE)] * 8
+    args = [V(FAKE)] * 9
     assert g(ctypes.byref(prob), *args, 5, V(FAKE), needv, None) == -1      # unknown schedule
     prob3 = _prob(R=3)
     _, need3 = _ws_bytes(prob3, B.SKA_OP_VJP)
     assert g(ctypes.byref(prob3), *args, 1, V(FAKE), need3, None) == -2     # direct-four needs R = 2
     assert "R == 2" in B.ska_last_error()
     assert g(ctypes.byref(prob), *args, 0, V(FAKE), needv - 1, None) == -3
-    assert g(ctypes.byref(prob), *(args[:5] + [None] + args[6:]), 0, V(FAKE), needv, None) == -1
+    assert g(ctypes.byref(prob), *(args[:6] + [None] + args[7:]), 0, V(FAKE), needv, None) == -1
+    # O (optional) may be NULL, but not misaligned
+    assert g(ctypes.byref(prob), *(args[:5] + [V(FAKE + 4)] + args[6:]), 0, V(FAKE), needv,
+             None) == -1
+    assert "O is not 16-byte aligned" in B.ska_last_error()
 
 
 def _stream_partials(bh, L, nw, nt):
@@ -276,7 +280,7 @@ def test_empty_problems_enqueue_nothing():
         assert B.lib.sinkhorn_attn_fwd(ctypes.byref(prob), None, None, None, None, None, None, 0,
                                        None) == 0
         assert B.lib.sinkhorn_attn_vjp(ctypes.byref(prob), None, None, None, None, None, None,
-                                       None, None, 0, None, 0, None) == 0
+                                       None, None, None, 0, None, 0, None) == 0
     prob = _prob(bh=0)
     assert B.lib.sinkhorn_attn_dustbin_block_fwd(ctypes.byref(prob), None, None, None, None, None,
                                                  None, 0, None) == 0

@@ -79,7 +79,7 @@ def test_captured_forward_and_vjp_replay_match_the_eager_calls(case):
 
     def step():
         B.sinkhorn_attn_fwd(prob, Q, K, V, O, d, ws_f)
-        B.sinkhorn_attn_vjp(prob, Q, K, V, d, dO, dQ, dK, dV, sch, ws_v)
+        B.sinkhorn_attn_vjp(prob, Q, K, V, d, dO, dQ, dK, dV, sch, ws_v, O=O)
 
     step()
     torch.cuda.synchronize()

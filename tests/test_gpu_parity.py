@@ -265,7 +265,8 @@ def test_workspace_contents_do_not_matter(L, W, T, R, dtype):
     """The forward and VJP read no workspace location they have not written in the same call:
     a workspace filled with NaN bit patterns gives the same results, bit for bit, as a zeroed
     one (ragged L, several segments, R = 0, 1, 2; the fused step feeding the wide output pass,
-    fp32 W = 200 and bf16 W = 352; the wide step, W = 600)."""
+    fp32 W = 200 and bf16 W = 352; the wide step, W = 600), for the VJP with and without the
+    forward's output."""
     from entropic_ot_attention_amd import binding as B
     say(f"[gpu] workspace contents L={L} W={W} T={T} R={R} {dtype}")
     w, x = _inputs(2, L, W, T, 1.0, dtype, seed=31)
@@ -281,11 +282,15 @@ def test_workspace_contents_do_not_matter(L, W, T, R, dtype):
         O = torch.empty_like(Q)
         duals = torch.empty(2, B.n_duals(R), L, dtype=torch.float32, device=dev)
         B.sinkhorn_attn_fwd(prob, Q, K, V, O, duals, ws_f)
-        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
-        B.sinkhorn_attn_vjp(prob, Q, K, V, duals, dO, dQ, dK, dV, B.SCHEDULES["one_reference"],
-                            ws_v)
+        res = [O, duals]
+        for given_o in (None, O):
+            dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+            ws_v.fill_(fill)
+            B.sinkhorn_attn_vjp(prob, Q, K, V, duals, dO, dQ, dK, dV, B.SCHEDULES["one_reference"],
+                                ws_v, O=given_o)
+            res += [dQ, dK, dV]
         torch.cuda.synchronize()
-        outs.append([t.clone() for t in (O, duals, dQ, dK, dV)])
+        outs.append([t.clone() for t in res])
     for a, b in zip(*outs):
         assert torch.isfinite(a.float()).all()
         assert torch.equal(a, b)
