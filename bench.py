@@ -656,11 +656,8 @@ def main():
         fwd(prob, Q, K, V, O, duals, ws_f)
         if ev is not None:
             ev[1].record(stream)
-        if w.dustbin:
-            vjp(prob, Q, K, V, duals, dO, dQ, dK, dV, sched, ws)
-        else:
-            # the VJP given the forward's output, as the autograd wrapper calls it
-            vjp(prob, Q, K, V, duals, dO, dQ, dK, dV, sched, ws, O=O)
+        # the VJP given the forward's output, as the autograd wrapper calls it
+        vjp(prob, Q, K, V, duals, dO, dQ, dK, dV, sched, ws, O=O)
         if ev is not None:
             ev[2].record(stream)
 

@@ -58,7 +58,8 @@ def _load():
     lib.sinkhorn_attn_dustbin_block_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sinkhorn_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sinkhorn_attn_vjp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, st, vp, sz, vp]
-    lib.sinkhorn_attn_dustbin_block_vjp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, st, vp, sz, vp]
+    lib.sinkhorn_attn_dustbin_block_vjp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, st, vp, sz,
+                                                    vp]
     lib.sinkhorn_attn_tail_remainder.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     i32 = ctypes.c_int32
     lib.ska_contraction_layout.argtypes = [P, st, i32, ctypes.POINTER(ctypes.c_int64),
@@ -168,12 +169,13 @@ def sinkhorn_attn_vjp(problem, Q, K, V, duals, dO, dQ, dK, dV, schedule, workspa
 
 
 def sinkhorn_attn_dustbin_block_vjp(problem, Q, K, V, duals, dO, dQ, dK, dV, schedule, workspace,
-                                    stream=None):
+                                    stream=None, O=None):
+    """O (optional): the forward's output for the same inputs and duals."""
     ws, nb = _ws(workspace)
     _check(lib.sinkhorn_attn_dustbin_block_vjp(ctypes.byref(problem), _ptr(Q, "Q"), _ptr(K, "K"),
                                                _ptr(V, "V"), _ptr(duals, "duals"), _ptr(dO, "dO"),
-                                               _ptr(dQ, "dQ"), _ptr(dK, "dK"), _ptr(dV, "dV"),
-                                               schedule, ws, nb, _stream(stream)),
+                                               _ptr(O, "O"), _ptr(dQ, "dQ"), _ptr(dK, "dK"),
+                                               _ptr(dV, "dV"), schedule, ws, nb, _stream(stream)),
            "sinkhorn_attn_dustbin_block_vjp")
 
 
@@ -265,15 +267,13 @@ def forward(Q, K, V, W: int, T: int, R: int = 2, epsilon: float = 1.0, dustbin: 
 def vjp(Q, K, V, duals, dO, W: int, T: int, R: int = 2, epsilon: float = 1.0,
         schedule: str = "one_reference", dustbin: bool = False,
         workspace: torch.Tensor | None = None, stream=None, O: torch.Tensor | None = None):
-    """dQ, dK, dV for cotangent dO given the forward's duals (and optionally its output O,
-    which the band path uses to skip work; the dustbin_block path takes none)."""
+    """dQ, dK, dV for cotangent dO given the forward's duals (and optionally its output O, from
+    which the R = 2 passes take the row cotangent sums)."""
     bh, rows, d, L = _shape_check(Q, K, V, dustbin)
     if dO.shape != Q.shape or dO.dtype != Q.dtype:
         raise ValueError("dO must match Q in shape and dtype")
     if O is not None and (O.shape != Q.shape or O.dtype != Q.dtype):
         raise ValueError("O must match Q in shape and dtype")
-    if O is not None and dustbin:
-        raise ValueError("the dustbin_block VJP takes no O")
     if duals.shape != (bh, n_duals(R), rows) or duals.dtype != torch.float32:
         raise ValueError("duals must be fp32 [bh, n_duals(R), tokens]")
     prob = make_problem(bh, L, d, W, T, R, epsilon, Q.dtype)
@@ -281,12 +281,8 @@ def vjp(Q, K, V, duals, dO, W: int, T: int, R: int = 2, epsilon: float = 1.0,
     if workspace is None:
         workspace = workspace_for(prob, op, Q.device)
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
-    if dustbin:
-        sinkhorn_attn_dustbin_block_vjp(prob, Q, K, V, duals, dO, dQ, dK, dV, SCHEDULES[schedule],
-                                        workspace, stream)
-    else:
-        sinkhorn_attn_vjp(prob, Q, K, V, duals, dO, dQ, dK, dV, SCHEDULES[schedule], workspace,
-                          stream, O=O)
+    fn = sinkhorn_attn_dustbin_block_vjp if dustbin else sinkhorn_attn_vjp
+    fn(prob, Q, K, V, duals, dO, dQ, dK, dV, SCHEDULES[schedule], workspace, stream, O=O)
     return dQ, dK, dV
 
 

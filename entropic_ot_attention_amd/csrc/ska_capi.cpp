@@ -608,6 +608,7 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
   }
   // wide passes A..E (bands wider than the streaming passes hold): each owns the side it reduces
   ska::WideArgs w = wide_args(pl, Q, K, V, dO);
+  w.O = O;          // optional: du2 from delta = dO . O in pass B
   w.ws = ws;
   w.vec_stride = g.bh * (int64_t)g.Lpad;
   void* outs[6] = {nullptr, dV, nullptr, nullptr, dQ, dK};
@@ -658,11 +659,11 @@ ska_status sinkhorn_attn_dustbin_block_fwd(const ska_problem* p, const void* Q, 
 
 ska_status sinkhorn_attn_dustbin_block_vjp(const ska_problem* p, const void* Q, const void* K,
                                            const void* V, const float* duals, const void* dO,
-                                           void* dQ, void* dK, void* dV, ska_schedule schedule,
-                                           void* workspace, size_t workspace_bytes,
-                                           hipStream_t stream) {
+                                           const void* O, void* dQ, void* dK, void* dV,
+                                           ska_schedule schedule, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
   g_err.clear();
-  return run_vjp(p, SKA_OP_DUSTBIN_BLOCK_VJP, Q, K, V, duals, dO, nullptr, dQ, dK, dV, schedule,
+  return run_vjp(p, SKA_OP_DUSTBIN_BLOCK_VJP, Q, K, V, duals, dO, O, dQ, dK, dV, schedule,
                  workspace, workspace_bytes, stream);
 }
 

@@ -85,6 +85,25 @@ __device__ __forceinline__ void load_frag_il(Frag<float>& f, const float* row, i
   for (int i = 0; i < 4; ++i) f.v[i] = *reinterpret_cast<const f32x4*>(row + 16 * i + 4 * g);
 }
 
+// Partial dot product of two rows held as fragments in the same layout (this lane's d-slice).
+__device__ __forceinline__ float frag_dot(const Frag<bf16>& x, const Frag<bf16>& y) {
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc = fmaf((float)x.a[e], (float)y.a[e], acc);
+    acc = fmaf((float)x.b[e], (float)y.b[e], acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float frag_dot(const Frag<float>& x, const Frag<float>& y) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(x.v[i][e], y.v[i][e], acc);
+  return acc;
+}
+
 // init + w.o over d = 64 for a 16 x 16 tile (init enters the matrix-core accumulator)
 __device__ __forceinline__ f32x4 dot_tile(const Frag<bf16>& w, const Frag<bf16>& o,
                                           f32x4 init = f32x4{0.f, 0.f, 0.f, 0.f}) {

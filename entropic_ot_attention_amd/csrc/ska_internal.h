@@ -123,6 +123,7 @@ struct WideArgs {
   const void* K;
   const void* V;
   const void* dO;
+  const void* O;           // R = 2 pass B: the forward's output for delta = dO . O, or null
   const void* Qs;          // fp32 step: Q and K as three bf16 planes per row, [bh][Lr][192]
   const void* Ks;
   void* out0;              // output pass: O; pass A: dV; pass D: dQ; pass E: dK

@@ -98,25 +98,6 @@ template <> struct RowPart<float> {
   __device__ __forceinline__ float at(int b, int r) const { return v[b][r]; }
 };
 
-// Partial dot product of two rows held as fragments in the same layout (this lane's d-slice).
-__device__ __forceinline__ float frag_dot(const Frag<bf16>& x, const Frag<bf16>& y) {
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    acc = fmaf((float)x.a[e], (float)y.a[e], acc);
-    acc = fmaf((float)x.b[e], (float)y.b[e], acc);
-  }
-  return acc;
-}
-__device__ __forceinline__ float frag_dot(const Frag<float>& x, const Frag<float>& y) {
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = fmaf(x.v[i][e], y.v[i][e], acc);
-  return acc;
-}
-
 // Contractions over the 32 window rows of a tile pair (ring slots rt0, rt1):
 //   acc[b][r] (lane (g, n)) += sum_rows Op[row][16 b + 4 g + r] * Z[row][n]
 // with Op read transposed from the ring and z[tt][r] = Z[rt_tt + 4 g + r][n].

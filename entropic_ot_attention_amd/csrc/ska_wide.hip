@@ -449,19 +449,22 @@ __global__ __launch_bounds__(256) void wide_finish_kernel(WideArgs a) {
 // =============================================================================================
 enum WidePass : int { kWOut = 0, kWA, kWB, kWC, kWD, kWE };
 
-template <int P> struct WideTraits {
+// A forms dV = P22^T dO and takes dv2_j = sum_i P22 g = V_j . dV_j, without g; B given the
+// forward's output (DELTA) takes sum_j P22_ij g_ij = dO_i . O_i, without g or V's window.
+template <int P, bool DELTA = false> struct WideTraits {
+  static constexpr bool delta = DELTA && P == kWB;
   static constexpr bool owns_keys = (P == kWA || P == kWC || P == kWE);
-  static constexpr bool needs_g = (P == kWA || P == kWB || P == kWD || P == kWE);
-  static constexpr int nstage = (P == kWC) ? 1 : 2;   // window tensors staged per wave
+  static constexpr bool needs_g = ((P == kWB) && !delta) || P == kWD || P == kWE;
+  static constexpr int nstage = (P == kWC || delta) ? 1 : 2;   // window tensors staged per wave
   // staged tensor the contraction reads: 0 = the score operand, 1 = the second tensor, -1 none
   static constexpr int csrc = (P == kWOut || P == kWA) ? 1 : (P == kWD || P == kWE) ? 0 : -1;
   static constexpr int nacc = (P == kWD) ? 2 : (csrc >= 0) ? 1 : 0;   // 16 x 64 accumulators
-  static constexpr bool has_red = (P != kWOut && P != kWE);
+  static constexpr bool has_red = (P != kWOut && P != kWA && P != kWE);
 };
 
-template <typename T, int P>
+template <typename T, int P, bool DELTA>
 struct WideSmem {
-  using TR = WideTraits<P>;
+  using TR = WideTraits<P, DELTA>;
   static constexpr int kStageElems = 32 * Lds<T>::stride;   // one staged tensor of one wave
   static constexpr int kStageBytes = kWideWaves * TR::nstage * kStageElems * (int)sizeof(T);
   static constexpr int kRedFloats = (TR::nacc * 16 + 1) * 64;   // one wave's partials
@@ -469,10 +472,10 @@ struct WideSmem {
   static constexpr int kBytes = kStageBytes > kRedBytes ? kStageBytes : kRedBytes;
 };
 
-template <typename T, int P, bool D4>
+template <typename T, int P, bool D4, bool DELTA = false>
 __global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
-  using TR = WideTraits<P>;
-  using SM = WideSmem<T, P>;
+  using TR = WideTraits<P, DELTA>;
+  using SM = WideSmem<T, P, DELTA>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::kBytes];
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -499,10 +502,11 @@ __global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
   T* sB = sA + SM::kStageElems;
 
   // (loads are never conditional: rows clamped into the sequence, results masked where used)
-  Frag<T> fo, fog;
+  Frag<T> fo, fog, foo;
   const int oc = min(o, Lr - 1);
   load_frag_raw(fo, own_s + (int64_t)oc * kD, g);
-  if (TR::needs_g) load_frag_raw(fog, own_g + (int64_t)oc * kD, g);
+  if (TR::needs_g || TR::delta) load_frag_raw(fog, own_g + (int64_t)oc * kD, g);
+  if constexpr (TR::delta) load_frag_raw(foo, static_cast<const T*>(a.O) + tb + (int64_t)oc * kD, g);
 
   // owned-token vectors (o < Lpad always; padding entries are zero)
   float own_u2 = 0.f, own_v2 = 0.f, ox0 = 0.f, ox1 = 0.f, ox2 = 0.f, ox3 = 0.f;
@@ -607,7 +611,6 @@ __global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
           const float xq = fmaf(sc[r], c2, wu2[r]);                 // log2(e) S + u2_i
           const float p22 = fast_exp2(xq + own_v2);
           if constexpr (P == kWA) {
-            red = keep ? fmaf(p22, gv[r], red) : red;
             z1[tt][r] = keep ? p22 : 0.f;
           } else if constexpr (P == kWC) {
             const float pw = D4 ? fast_exp2(xq + ox0) : p22;        // P21 (direct) or P22
@@ -634,7 +637,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
           const float xs = sc[r] * c2;
           const float p22 = fast_exp2(xs + own_u2 + wv2[r]);
           if constexpr (P == kWB) {
-            red = keep ? fmaf(p22, gv[r] - wd[r], red) : red;
+            red = keep ? fmaf(p22, TR::delta ? -wd[r] : gv[r] - wd[r], red) : red;
           } else {  // D
             if constexpr (D4) {
               const float p21 = fast_exp2(xs + own_u2 + we[r]);
@@ -694,6 +697,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
     if constexpr (TR::has_red) red += theirs[TR::nacc * 16 * 64 + lane];
   }
 
+  if constexpr (TR::delta) red += group_sum(frag_dot(fog, foo));   // + dO_o . O_o
   const bool valid = o < Lr;
   if (!valid) return;
   float* ws = a.ws;
@@ -702,7 +706,14 @@ __global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
   if constexpr (P == kWOut) {
     store_row(out_row, acc, 1.f, g);
   } else if constexpr (P == kWA) {
-    if (g == 0) ws[kDV2 * a.vec_stride + ob] = red;
+    // dv2 = V . dV over the lane's columns 16 b + 4 g + r, summed over the lane groups
+    float vd = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vd = fmaf((float)Vp[(int64_t)o * kD + 16 * b + 4 * g + r], acc[b][r], vd);
+    vd = group_sum(vd);
+    if (g == 0) ws[kDV2 * a.vec_stride + ob] = vd;
     store_row(out_row, acc, 1.f, g);
   } else if constexpr (P == kWB) {
     if (g == 0) ws[kDU2 * a.vec_stride + ob] = red;
@@ -1050,7 +1061,10 @@ static void wide_pass_t(int pass, const WideArgs& a, hipStream_t st) {
   switch (pass) {
     case kWOut: wide_pass_kernel<T, kWOut, false><<<grid, block, 0, st>>>(a); break;
     case kWA: wide_pass_kernel<T, kWA, false><<<grid, block, 0, st>>>(a); break;
-    case kWB: wide_pass_kernel<T, kWB, false><<<grid, block, 0, st>>>(a); break;
+    case kWB:
+      if (a.O != nullptr) wide_pass_kernel<T, kWB, false, true><<<grid, block, 0, st>>>(a);
+      else wide_pass_kernel<T, kWB, false><<<grid, block, 0, st>>>(a);
+      break;
     case kWC: wide_pass_kernel<T, kWC, D4><<<grid, block, 0, st>>>(a); break;
     case kWD: wide_pass_kernel<T, kWD, D4><<<grid, block, 0, st>>>(a); break;
     default: wide_pass_kernel<T, kWE, D4><<<grid, block, 0, st>>>(a); break;

@@ -108,9 +108,9 @@ ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K,
 
 /* Exact tail VJP (0 <= R <= 256): given the forward's duals and an arbitrary cotangent dO, writes
  * dQ, dK, dV [bh][L][d].  O is optional (NULL, or the [bh][L][d] output sinkhorn_attn_fwd wrote
- * for the same problem, Q, K, V and duals; it is only read): where the R = 2 band passes run, the
- * row cotangent sum_j P_ij (dO_i . V_j) is then taken as dO_i . O_i, so the du2 pass reads neither
- * V's window nor forms dO . V^T; other paths ignore it, and the results agree either way within
+ * for the same problem, Q, K, V and duals; it is only read): at R = 2 the row cotangent
+ * sum_j P_ij (dO_i . V_j) is then taken as dO_i . O_i, so the du2 pass reads neither V's window
+ * nor forms dO . V^T; other tail depths ignore it, and the results agree either way within
  * rounding.  An O that is not that output gives wrong gradients.  Scores are recomputed per band
  * tile; extra memory is O(L) vectors (3 + 4 R of them for R != 2).  R = 2 runs the two-level passes (both schedules); other R run
  * 2 R + 2 passes of the one-reference adjoint, the modifier field then holding 2 R terms; R = 0
@@ -151,12 +151,14 @@ ska_status sinkhorn_attn_dustbin_block_fwd(const ska_problem* p, const void* Q, 
                                            const void* V, void* O, float* duals, void* workspace,
                                            size_t workspace_bytes, hipStream_t stream);
 
-/* dustbin_block VJP: gradients for all L+1 rows, the dustbin token included. */
+/* dustbin_block VJP: gradients for all L+1 rows, the dustbin token included.  O is optional as
+ * for sinkhorn_attn_vjp: NULL, or the [bh][L+1][d] output sinkhorn_attn_dustbin_block_fwd wrote
+ * for the same problem, inputs and duals. */
 ska_status sinkhorn_attn_dustbin_block_vjp(const ska_problem* p, const void* Q, const void* K,
                                            const void* V, const float* duals, const void* dO,
-                                           void* dQ, void* dK, void* dV, ska_schedule schedule,
-                                           void* workspace, size_t workspace_bytes,
-                                           hipStream_t stream);
+                                           const void* O, void* dQ, void* dK, void* dV,
+                                           ska_schedule schedule, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
 
 /* A posteriori bias certificate of the stopped base (technical summaries §2.4: a measurement of
  * the gradient remainder eta_R that the stop-gradient on the base drops, certified against a

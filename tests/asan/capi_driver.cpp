@@ -90,7 +90,7 @@ int main() {
                                 : sinkhorn_attn_fwd(&p, Q, K, V, O, duals, ws, n, st);
             EXPECT(s == SKA_OK, "fwd L=%lld W=%lld R=%d dt=%d dust=%d: %d", (long long)L, (long long)W, R, dt, dust, s);
             for (int sch = 0; sch < 2; ++sch) {
-              s = dust ? sinkhorn_attn_dustbin_block_vjp(&p, Q, K, V, duals, dO, dQ, dK, dV,
+              s = dust ? sinkhorn_attn_dustbin_block_vjp(&p, Q, K, V, duals, dO, O, dQ, dK, dV,
                                                          (ska_schedule)sch, ws, n, st)
                        : sinkhorn_attn_vjp(&p, Q, K, V, duals, dO, O, dQ, dK, dV, (ska_schedule)sch, ws,
                                            n, st);
@@ -98,7 +98,7 @@ int main() {
               EXPECT(s == want, "vjp L=%lld W=%lld R=%d sch=%d: %d", (long long)L, (long long)W, R, sch, s);
               if (nv > 0) {
                 // one byte short of the VJP's workspace
-                s = dust ? sinkhorn_attn_dustbin_block_vjp(&p, Q, K, V, duals, dO, dQ, dK, dV,
+                s = dust ? sinkhorn_attn_dustbin_block_vjp(&p, Q, K, V, duals, dO, nullptr, dQ, dK, dV,
                                                            (ska_schedule)sch, ws, nv - 1, st)
                          : sinkhorn_attn_vjp(&p, Q, K, V, duals, dO, nullptr, dQ, dK, dV,
                                              (ska_schedule)sch, ws, nv - 1, st);

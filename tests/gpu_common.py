@@ -37,11 +37,10 @@ def gpu_run(Q, K, V, dO, W, T, R=2, eps=1.0, schedule="one_reference", dustbin=F
     if R <= 4:
         # the VJP given the forward's output (as the autograd wrapper calls it), and without it
         dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=schedule, dustbin=dustbin,
-                           O=None if dustbin else O)
+                           O=O)
         out.update(dQ=dQ, dK=dK, dV=dV)
-        if not dustbin:
-            dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=schedule)
-            out.update(dQ_noO=dQ, dK_noO=dK, dV_noO=dV)
+        dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=schedule, dustbin=dustbin)
+        out.update(dQ_noO=dQ, dK_noO=dK, dV_noO=dV)
     torch.cuda.synchronize()
     return {k: v.float().cpu().double().numpy() for k, v in out.items()}
 
@@ -49,7 +48,7 @@ def gpu_run(Q, K, V, dO, W, T, R=2, eps=1.0, schedule="one_reference", dustbin=F
 def gpu_run_schedules(Q, K, V, dO, W, T, R=2, eps=1.0,
                       schedules=("one_reference", "direct_four"), dustbin=False):
     """One forward and, per schedule, the VJP through the C ABI given the forward's output O and
-    (band support) without it; returns {"O", "duals", schedule: {"dQ", "dK", "dV", and
+    without it; returns {"O", "duals", schedule: {"dQ", "dK", "dV", and
     "dQ_noO", "dK_noO", "dV_noO"}} as fp64 numpy arrays [bh, ...]."""
     from entropic_ot_attention_amd import binding as B
     dev = torch.device("cuda:0")
@@ -58,14 +57,12 @@ def gpu_run_schedules(Q, K, V, dO, W, T, R=2, eps=1.0,
     host = lambda t: t.float().cpu().double().numpy()
     out = {"O": host(O), "duals": host(duals)}
     for s in schedules:
-        dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=s, dustbin=dustbin,
-                           O=None if dustbin else O)
+        dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=s, dustbin=dustbin, O=O)
         torch.cuda.synchronize()
         out[s] = {"dQ": host(dQ), "dK": host(dK), "dV": host(dV)}
-        if not dustbin:
-            dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=s)
-            torch.cuda.synchronize()
-            out[s].update(dQ_noO=host(dQ), dK_noO=host(dK), dV_noO=host(dV))
+        dQ, dK, dV = B.vjp(Qd, Kd, Vd, duals, dOd, W, T, R, eps, schedule=s, dustbin=dustbin)
+        torch.cuda.synchronize()
+        out[s].update(dQ_noO=host(dQ), dK_noO=host(dK), dV_noO=host(dV))
     torch.cuda.synchronize()
     return out
 
