@@ -493,6 +493,7 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
       a.K = K;
       a.V = V;
       a.dO = dO;
+      a.O = O;        // optional: du^(R) from delta = dO . O in pass 2
       a.ws = ws;
       a.vec_stride = g.bh * (int64_t)g.Lpad;
       a.bh = g.bh;

@@ -264,7 +264,8 @@ template <int PASS, bool D4, int GEN, bool DELTA> struct VjpPass {
 // GEN >= 0: a general tail depth R (a.R) with the vectors of tail_vecs(R) [technical summaries
 // §2.1-§2.2: R differentiable tail steps, every staircase plan in the orbit of P^(R,R)]:
 //   1 (owns keys)     dV_j = sum_i P dO_i,  dv^(R)_j = sum_i P g = V_j . dV_j   -> F_R (EV_R = 1)
-//   2 (owns queries)  du^(R)_i = sum_j P (g - F_R);  column partials sum_i P C_R
+//   2 (owns queries)  du^(R)_i = sum_j P (g - F_R) (given O: delta_i - sum_j P F_R);
+//                     column partials sum_i P C_R
 //   5 (owns queries)  level a = R-1 .. 1: F_a = -EV_a^2 (partials of level a), finished for the
 //                     window on arrival; C_a = -EU_a^2 sum_j P F_a;  column partials sum_i P C_a
 //                     for level a - 1
@@ -1184,7 +1185,10 @@ static void launch_nt_general(int pass, const VjpArgs& a, hipStream_t st) {
   const int ks = (2 * a.R + 3) / 4;          // modifier k-steps of passes 6 and 7
   switch (pass) {
     case 1: vjp_stream_kernel<T, NT, NW, 1, false, 0><<<grid, block, 0, st>>>(a); break;
-    case 2: vjp_stream_kernel<T, NT, NW, 2, false, 0><<<grid, block, 0, st>>>(a); break;
+    case 2:
+      if (a.O != nullptr) vjp_stream_kernel<T, NT, NW, 2, false, 0, true><<<grid, block, 0, st>>>(a);
+      else vjp_stream_kernel<T, NT, NW, 2, false, 0><<<grid, block, 0, st>>>(a);
+      break;
     case 5: vjp_stream_kernel<T, NT, NW, 5, false, 0><<<grid, block, 0, st>>>(a); break;
     case 6:
       if (ks == 0) vjp_stream_kernel<T, NT, NW, 6, false, 0><<<grid, block, 0, st>>>(a);

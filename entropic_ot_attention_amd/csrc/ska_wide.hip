@@ -473,7 +473,8 @@ struct WideSmem {
 };
 
 template <typename T, int P, bool D4, bool DELTA = false>
-__global__ __launch_bounds__(kWideThreads) void wide_pass_kernel(WideArgs a) {
+__global__ __launch_bounds__(kWideThreads, (WideTraits<P, DELTA>::delta ? 4 : 1))
+void wide_pass_kernel(WideArgs a) {
   using TR = WideTraits<P, DELTA>;
   using SM = WideSmem<T, P, DELTA>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::kBytes];

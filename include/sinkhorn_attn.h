@@ -108,10 +108,11 @@ ska_status sinkhorn_attn_fwd(const ska_problem* p, const void* Q, const void* K,
 
 /* Exact tail VJP (0 <= R <= 256): given the forward's duals and an arbitrary cotangent dO, writes
  * dQ, dK, dV [bh][L][d].  O is optional (NULL, or the [bh][L][d] output sinkhorn_attn_fwd wrote
- * for the same problem, Q, K, V and duals; it is only read): at R = 2 the row cotangent
- * sum_j P_ij (dO_i . V_j) is then taken as dO_i . O_i, so the du2 pass reads neither V's window
- * nor forms dO . V^T; other tail depths ignore it, and the results agree either way within
- * rounding.  An O that is not that output gives wrong gradients.  Scores are recomputed per band
+ * for the same problem, Q, K, V and duals; it is only read): the row cotangent
+ * sum_j P_ij (dO_i . V_j) of the last tail level is then taken as dO_i . O_i, so that pass reads
+ * neither V's window nor forms dO . V^T (every R >= 1 on bands the streaming passes hold, R = 2
+ * on wider bands and the dustbin_block support; elsewhere O is not read), and the results agree
+ * either way within rounding.  An O that is not that output gives wrong gradients.  Scores are recomputed per band
  * tile; extra memory is O(L) vectors (3 + 4 R of them for R != 2).  R = 2 runs the two-level passes (both schedules); other R run
  * 2 R + 2 passes of the one-reference adjoint, the modifier field then holding 2 R terms; R = 0
  * runs dV, dQ and dK of the base plan with both duals fixed (score cotangent P * g)

@@ -6,22 +6,17 @@ mid-size problems (3000-12000 tokens, up to three heads: many segments and seams
 16-160 short problems.  Every element is compared at the tolerances of the other parity tests.
 
 At W = 0 each row's plan holds a single entry: the plan is the identity whatever the scores, so
-the exact dQ and dK are zero.  A relative bar is meaningless against an exact zero; those are
-held to an absolute bound instead.  The bf16 passes form the modifier as a split-bf16 product,
-within about 2^-16 of its terms (|g| ~ 10), so dS keeps a residual near 1e-4 there; 1e-3 bounds
-it with room.  (fp32 keeps the exact fp32 product: about 1e-12.)"""
+the exact dQ and dK are zero; compare holds bf16 gradients against an exact zero to an absolute
+bound (ZERO_GRAD_MAXABS)."""
 
 import random
 
-import numpy as np
 import pytest
 
 from entropic_ot_attention_amd.workloads import Workload, make_inputs
 from tests.gpu_common import compare, for_schedule, gpu_run_schedules, oracle_head, parallel, say
 
 pytestmark = pytest.mark.gpu
-
-ZERO_GRAD_MAXABS = 1e-3
 
 
 def _configs(seed=3, n=48):
@@ -87,10 +82,4 @@ def test_random_configuration_matches_the_oracle(cfg):
     for s in schedules:
         refs = parallel(lambda h: oracle_head(*h, W, T, R, eps, s, dustbin=dustbin), heads, label)
         ref = {k: [r[k] for r in refs] for k in refs[0]}
-        g = for_schedule(got, s)
-        for k in ("dQ", "dK", "dV"):
-            if k in ref and float(np.abs(np.asarray(ref[k])).max()) == 0.0:
-                m = float(np.abs(g[k]).max())
-                assert m <= ZERO_GRAD_MAXABS, f"{label} {s}: {k} max-abs {m:.2e} against an exact zero"
-                ref.pop(k)
-        compare(g, ref, w.torch_dtype, f"{label} {s}")
+        compare(for_schedule(got, s), ref, w.torch_dtype, f"{label} {s}")
