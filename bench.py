@@ -97,14 +97,21 @@ def step_counters(workload: str):
         return None
 
 
+# matrix-core flops per band entry of the R = 2 VJP given the forward's output, in units of d:
+# pass 1 score + dV contraction (4), pass 2 score (2), pass 3 score + g + two dQ contractions (8),
+# pass 4 score + g + dK contraction (6)
+VJP_R2_FLOPS_PER_ENTRY_D = 20
+
+
 def family_rooflines(w, rows, nnz, elt, schedule, step_launch_ms, out_launch_ms, vjp_ms, step_ms):
     """Algorithmic work and achieved fractions of each kernel family of one forward + VJP, from
     their HIP-event times: one Sinkhorn step launch, the output pass, the R = 2 VJP passes
-    (the four streaming passes: dv2; du2 with the dv1 column partials; du1 and dQ; dK and dV) and
-    the whole step.  Bytes are each family's compulsory tensor traffic (every pass streams the
-    tensors it reads once and writes its outputs once); flops are matrix-core flops per band
-    entry with the scores (and value scores g) recomputed in every pass; exponentials per band
-    entry: 1 per step and output pass, 1 per VJP pass (one-reference) or 1 + 2 + 4 + 4
+    (the four streaming passes, given the forward's output: dV and dv2 = V . dV; du2 from dO . O
+    with the dv1 column partials; du1 and dQ; dK) and the whole step.  Bytes are each family's
+    compulsory tensor traffic (every pass streams the tensors it reads once and writes its outputs
+    once); flops are matrix-core flops per band entry with the scores (and value scores g)
+    recomputed in every pass that needs them: 4 d, 2 d, 8 d and 6 d, 20 d in all; exponentials
+    per band entry: 1 per step and output pass, 1 per VJP pass (one-reference) or 1 + 2 + 4 + 4
     (direct-four)."""
     d, bh = w.d, w.bh
     tens = bh * rows * d * elt                       # bytes of one [bh, tokens, d] tensor
@@ -133,12 +140,12 @@ def family_rooflines(w, rows, nnz, elt, schedule, step_launch_ms, out_launch_ms,
     res = {"step": step, "output": out}
     if w.R == 2:
         vexp = (1 + 2 + 4 + 4) if schedule == "direct_four" else 4
-        vjp = fr(vjp_ms, 19 * tens, 24 * d * nnz, vexp * nnz,
-                 {"per": "one VJP: 4 passes reading 4 tensors each, writing dQ, dK, dV"})
+        vjp = fr(vjp_ms, 19 * tens, VJP_R2_FLOPS_PER_ENTRY_D * d * nnz, vexp * nnz,
+                 {"per": "one VJP given O: 4 passes reading 4 tensors each, writing dQ, dK, dV"})
         res["vjp"] = vjp
         whole_exps = (n_steps + 1 + vexp) * nnz
         res["whole_step"] = fr(step_ms, n_steps * 2 * tens + 4 * tens + 19 * tens,
-                               (n_steps * 2 + 4 + 24) * d * nnz, whole_exps,
+                               (n_steps * 2 + 4 + VJP_R2_FLOPS_PER_ENTRY_D) * d * nnz, whole_exps,
                                {"per": f"forward ({n_steps} steps, output) + VJP"})
     return res
 
@@ -214,12 +221,13 @@ def timed_region(run, steps: int, stream, instrumented: int = 1):
 
 def tail_pass_flops_per_entry(R: int, d: int) -> int:
     """Matrix-core flops per band entry of the one-reference adjoint at tail depth R >= 1, with
-    one score recompute per sweep over the band: dv^(R) (score and value scores g = dO . V, 4 d),
-    du^(R) (4 d), one sweep per level a = R-1 .. 1 that both reduces its row sums and emits the
-    next level's column partials (score, 2 d each), dQ (score, g and the contraction, 6 d), dK and
-    dV (score, g and two contractions, 8 d): (20 + 2 R) d.  The streaming passes run exactly this;
-    the wide engine's passes, with two sweeps per level, do more."""
-    return (20 + 2 * R) * d
+    one score recompute per sweep over the band: dV and dv^(R) = V . dV (score and the dV
+    contraction, 4 d), du^(R) (score and value scores g = dO . V, 4 d), one sweep per level
+    a = R-1 .. 1 that both reduces its row sums and emits the next level's column partials
+    (score, 2 d each), dQ (score, g and the contraction, 6 d) and dK (the same, 6 d):
+    (18 + 2 R) d.  The streaming passes run exactly this (without the forward's output, as the
+    certificate runs them); the wide engine's passes, with two sweeps per level, do more."""
+    return (18 + 2 * R) * d
 
 
 def contraction_main(args):
@@ -496,7 +504,7 @@ def certificate_main(args):
         "vjp_call_us": round(vjp_s * 1e6, 2),
         "calls_timed": args.steps,
         "algorithmic_flops": flops,
-        "algorithmic_work": f"(20 + 2 x {Rf}) x {w.d} flops x {nnz} band entries per VJP",
+        "algorithmic_work": f"(18 + 2 x {Rf}) x {w.d} flops x {nnz} band entries per VJP",
     }
     out = {
         "metric": f"bias certificate eta_R tokens/s at L={L} W={w.W} d={w.d} T={w.T}, R=2; "

@@ -123,7 +123,8 @@ def test_bench_band_entries_and_roofline_constants():
             assert bench.band_entries(L, h) == brute
     assert bench.VALU_LANE_OPS_PER_S == pytest.approx(78.6432e12)     # 157.3 TFLOP/s / 2
     assert bench.SLOTS_PER_ENTRY_STEP == 7
-    assert bench.tail_pass_flops_per_entry(2, 64) == 24 * 64
+    assert bench.tail_pass_flops_per_entry(2, 64) == 22 * 64
+    assert bench.VJP_R2_FLOPS_PER_ENTRY_D == 4 + 2 + 8 + 6
     nnz = bench.band_entries(262144, 128) * 4
     cyc = nnz * (2 * bench.BF16_MFMA_CYCLES / 256 + bench.SLOTS_PER_ENTRY_STEP * bench.VALU_SLOT_CYCLES / 64)
     assert cyc / (bench.N_SIMD * bench.CLOCK_HZ) == pytest.approx(37.69e-6, rel=1e-3)
