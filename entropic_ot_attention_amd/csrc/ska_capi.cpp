@@ -518,7 +518,7 @@ ska_status run_vjp(const ska_problem* p, ska_op op, const void* Q, const void* K
       w.R = p->R;
       if (p->R >= 1) {
         if (deep) {
-          // the wide pass A gives dv^(R) and dV (the streaming dK/dV pass is not run)
+          // the wide pass A gives dv^(R) and dV (the streaming dK pass is not run)
           w.out0 = dV;
           SKA_LAUNCH(ska::kTimedVjp, st, ska::launch_tail_pass(pl.elt, 0, w, st));
         } else {

@@ -104,10 +104,10 @@ struct VjpArgs {
 // cover this band; the chunked passes handle it) and the register-resident tile count.
 int vjp_stream_waves(int elt, int h, int* nt);
 // General tail depth on the streaming engine, vectors in the general-depth layout of
-// tail_vecs(R): pass 1 (dv^(R)) and pass 2 (du^(R), column partials) as for R = 2, then for
+// tail_vecs(R): pass 1 (dV, dv^(R)) and pass 2 (du^(R), column partials) as for R = 2, then for
 // a = R-1 .. 1 a level pass 5 (F_a from the partials, C_a, the next partials) (any R up to
-// kTailMaxR), then pass 6 (dQ) and pass 7 (dK, dV) with the 2 R-term modifier on the matrix cores
-// (R <= kStreamMaxR).
+// kTailMaxR), then pass 6 (dQ) and pass 7 (dK; and dV at R = 0) with the 2 R-term modifier on the
+// matrix cores (R <= kStreamMaxR).
 constexpr int kStreamMaxR = 4;
 hipError_t launch_vjp_stream_general(int elt, int nt, int nw, int pass, const VjpArgs& a,
                                      hipStream_t st);

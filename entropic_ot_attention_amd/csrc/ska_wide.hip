@@ -21,8 +21,8 @@
 // wide_pass_kernel runs the output and five VJP passes, each owning the side it reduces over, so
 // no pass needs partial sums across workgroups:
 //   out (owns queries)  O_i = sum_j P22_ij V_j
-//   A   (owns keys)     dv2_j = sum_i P22 g,  dV_j = sum_i P22_ij dO_i
-//   B   (owns queries)  du2_i = sum_j P22 (g - dv2_j)
+//   A   (owns keys)     dV_j = sum_i P22_ij dO_i,  dv2_j = sum_i P22 g = V_j . dV_j
+//   B   (owns queries)  du2_i = sum_j P22 (g - dv2_j)  (given O: dO_i . O_i - sum_j P22 dv2_j)
 //   C   (owns keys)     dv1_j = -e^{dv1_j} sum_i P22 du2_i          (direct: -sum_i P21 du2_i)
 //   D   (owns queries)  du1_i = -e^{du1_i} sum_j P22 E_j dv1_j      (direct: -sum_j P11 dv1_j)
 //                       dQ_i = s sum_j dS_ij k_j with dS = Z1 - C_i Z2, so du1_i (known only at
@@ -796,13 +796,14 @@ __global__ void tail_prep_kernel(const float* __restrict__ duals, float* __restr
 
 enum TailPass : int { kTA = 0, kTB, kTC, kTD, kTQ, kTE };
 
+// A forms dV = P^T dO and takes dv^(R)_j = sum_i P g = V_j . dV_j, without g.
 template <int GP> struct TailTraits {
   static constexpr bool owns_keys = (GP == kTA || GP == kTC || GP == kTE);
-  static constexpr bool needs_g = (GP != kTC && GP != kTD);
-  static constexpr int nstage = needs_g ? 2 : 1;
+  static constexpr bool needs_g = (GP != kTA && GP != kTC && GP != kTD);
+  static constexpr int nstage = (needs_g || GP == kTA) ? 2 : 1;
   // staged tensor the contraction reads: 0 = the score operand, 1 = the second tensor, -1 none
   static constexpr int csrc = (GP == kTA) ? 1 : (GP == kTQ || GP == kTE) ? 0 : -1;
-  static constexpr bool has_red = (GP <= kTD);
+  static constexpr bool has_red = (GP == kTB || GP == kTC || GP == kTD);
 };
 
 // RT: the tail depth for the dQ and dK passes (0..4 at compile time: their 2 RT modifier terms
@@ -917,7 +918,6 @@ __global__ __launch_bounds__(kWideThreads) void tail_pass_kernel(WideArgs a) {
         const bool keep = in_band(wb + r, o, h, Lr);
         const float p = fast_exp2(fmaf(sc[r], c2, own_d + wd[r]));
         if constexpr (GP == kTA) {
-          red = keep ? fmaf(p, gv[r], red) : red;
           z[tt][r] = keep ? p : 0.f;
         } else if constexpr (GP == kTB) {
           red = keep ? fmaf(p, gv[r] - wsv[r], red) : red;
@@ -994,7 +994,15 @@ __global__ __launch_bounds__(kWideThreads) void tail_pass_kernel(WideArgs a) {
   if (o >= Lr) return;
   T* out_row = static_cast<T*>(a.out0) + tb + (int64_t)o * kD;
   if constexpr (GP == kTA) {
-    if (g == 0 && a.R > 0) vec(tv.f(a.R))[o] = red;         // dv^(R) (EV_R = 1)
+    // dv^(R) = V . dV over the lane's columns 16 b + 4 g + r, summed over the lane groups (the
+    // four lanes of a key share its validity)
+    float vd = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vd = fmaf((float)Vp[(int64_t)o * kD + 16 * b + 4 * g + r], acc[b][r], vd);
+    vd = group_sum(vd);
+    if (g == 0 && a.R > 0) vec(tv.f(a.R))[o] = vd;          // dv^(R) (EV_R = 1)
     store_row(out_row, acc, 1.f, g);                        // dV
   } else if constexpr (GP == kTB) {
     if (g == 0) vec(tv.c(a.R))[o] = red;                    // du^(R) (EU_R = 1)
