@@ -209,6 +209,27 @@ def test_one_reference_equals_direct_four_entrywise():
         np.testing.assert_allclose(x, y, atol=1e-13)
 
 
+@pytest.mark.parametrize("L,W,R", [(45, 16, 2), (60, 200, 2), (50, 12, 1), (40, 20, 4)])
+def test_vector_cotangents_of_the_last_level_through_O_and_dV(L, W, R):
+    """The last tail level's vector cotangents are contractions the forward and dV already hold:
+    dv^(R)_j = sum_i P_ij (dO_i . V_j) = V_j . dV_j with dV_j = sum_i P_ij dO_i, and the row
+    sum sum_j P_ij (dO_i . V_j) = dO_i . O_i with O_i = sum_j P_ij V_j (P = P^(R,R); exact
+    algebra, here at fp64 rounding).  The GPU passes take them this way; a transposed reduction
+    (row sums for dv, say) would fail this."""
+    Q, K, V, dO = _qkv(L, seed=23 + R)
+    prob = sb.BandProblem(W=W, T=2, R=R, eps=0.8)
+    O, duals = oracle.forward(Q, K, V, prob)
+    if R == 2:
+        _, _, dV, parts = oracle.vjp_one_reference(Q, K, V, dO, duals, prob, want_parts=True)
+        dv, P, g = parts["dv2"], parts["P22"], parts["g"]
+    else:
+        _, _, dV, parts = oracle.vjp_tail(Q, K, V, dO, duals, prob, want_parts=True)
+        dv, P, g = parts["dv"][-1], parts["P"], parts["g"]
+    np.testing.assert_allclose(dv, np.einsum("jd,jd->j", V, dV), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(sb._row_sum(P * g), np.einsum("id,id->i", dO, O),
+                               rtol=1e-12, atol=1e-12)
+
+
 def test_gauge_shift_of_stopped_base_is_a_no_op():
     """Centering the stopped dual (v0 -> v0 - c) changes no plan: u^(1) absorbs +c and
     every later v absorbs -c, so O and all gradients are unchanged."""
