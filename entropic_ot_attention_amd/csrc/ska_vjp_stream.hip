@@ -8,7 +8,9 @@
 //
 //   0 (owns queries)  forward output O_i = sum_j P22_ij V_j   [the reference plan applied to V]
 //   1 (owns keys)     dV_j = sum_i P22_ij dO_i,  dv2_j = sum_i P22 g = V_j . dV_j
-//   2 (owns queries)  du2_i = sum_j P22 (g - dv2_j);  per-segment column sums sum_i P22 du2_i
+//   2 (owns queries)  du2_i = sum_j P22 (g - dv2_j), or given the forward's output O,
+//                     dO_i . O_i - sum_j P22 dv2_j (no V window, no g);
+//                     per-segment column sums sum_i P22 du2_i
 //   3 (owns queries)  dv1_j = -e^{dv1_j} (column sums)  (finished for the window on arrival)
 //                     du1_i = -e^{du1_i} sum_j P22 e^{dv1_j} dv1_j
 //                     dQ_i  = s sum_j dS_ij k_j,  dS = Z1 - C_i Z2 with
@@ -270,10 +272,10 @@ template <int PASS, bool D4, int GEN, bool DELTA> struct VjpPass {
 //                     window on arrival; C_a = -EU_a^2 sum_j P F_a;  column partials sum_i P C_a
 //                     for level a - 1
 //   6 (owns queries)  dQ_i = s sum_j P M k_j,   7 (owns keys) dK_j = s sum_i P M q_i (and
-//                     dV_j = sum_i P dO_i at R = 0), with M = g - sum_k alpha_k(i) beta_k(j) over the 2 R
-//                     pairs (alpha, beta) = (EU_a, F_a), (C_a, EV_(a-1)), a = 1 .. R: a rank-2R
-//                     product formed per tile on the matrix cores (fp32, GEN = ceil(2 R / 4)
-//                     k-steps of 4).
+//                     dV_j = sum_i P dO_i at R = 0), with M = g - sum_k alpha_k(i) beta_k(j)
+//                     over the 2 R pairs (alpha, beta) = (EU_a, F_a), (C_a, EV_(a-1)),
+//                     a = 1 .. R: a rank-2R product formed per tile on the matrix cores (fp32,
+//                     GEN = ceil(2 R / 4) k-steps of 4).
 template <typename T, int NT, int NW, int PASS, bool D4 = false, int GEN = -1, bool DELTA = false>
 __global__ __launch_bounds__(NW * 64) void vjp_stream_kernel(VjpArgs a) {
   using P = VjpPass<PASS, D4, GEN, DELTA>;
